@@ -1,0 +1,242 @@
+/*
+ * Oracle for the paged decode path: append, whole-block copy and decode
+ * attention in plain C, float64 arithmetic.
+ *
+ * TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py load this library.  It shares no code, header
+ * or table with the HIP library: the pool layout below is restated here from
+ * its definition, not included.
+ *
+ * What it computes:
+ *
+ *  - Attention of one decode step: the new token's query is dotted with the
+ *    key of every cached token, scaled by 1/sqrt(d_h), passed through a
+ *    softmax over all of the sequence's tokens, and the weights average the
+ *    cached values [KV Cache 与 PagedAttention, "注意力机制的计算";
+ *    PagedAttention：大模型KV Cache内存管理革新 §3.2 (its per-page softmax
+ *    is not followed: the softmax spans the whole context)].  The step attends
+ *    over the 1 x i row of step i [KV Cache 工程学 §15.1].
+ *  - Paging only changes where a token's K/V live: token j of a sequence
+ *    sits in slot j % 16 of the physical block named by entry j / 16 of the
+ *    sequence's block table [KV Cache 工程学 §15.5; 新一代 KV Cache 管理
+ *    §8.1].  The result therefore equals attention over the contiguous
+ *    per-sequence cache [KV Cache 工程学 §15.2].
+ *  - Grouped-query heads: query head h reads kv head h / (h_q / h_kv)
+ *    (contiguous groups; the pages only say h_kv < h_q [§15.2, §15.7]).
+ *
+ * Pool layout (a choice of this build; the pages only say "flat pool"):
+ *    X = 16 / element size (8 for bf16, 4 for f32)
+ *    K element (blk, g, t, d) at (((blk*Hkv + g)*(D/X) + d/X)*16 + t)*X + d%X
+ *    V element (blk, g, t, d) at  ((blk*Hkv + g)*D + d)*16 + t
+ *
+ * Element types: 0 = float32, 1 = bfloat16 (raw uint16 bits).  Every element
+ * is widened exactly to double before use.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define BLOCK 16
+
+static double elem(const void *base, size_t i, int dtype) {
+  if (dtype == 0) return (double)((const float *)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static size_t esize(int dtype) { return dtype == 0 ? 4 : 2; }
+
+static size_t k_at(int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) {
+  int X = (int)(16 / esize(dtype));
+  return ((((size_t)blk * Hkv + g) * (size_t)(D / X) + (size_t)(d / X)) * BLOCK + (size_t)t) * X + (size_t)(d % X);
+}
+
+static size_t v_at(int64_t blk, int g, int t, int d, int Hkv, int D) {
+  return (((size_t)blk * Hkv + g) * (size_t)D + (size_t)d) * BLOCK + (size_t)t;
+}
+
+static void copy_elem(void *dst, size_t di, const void *src, size_t si, int dtype) {
+  size_t s = esize(dtype);
+  memcpy((char *)dst + di * s, (const char *)src + si * s, s);
+}
+
+/* Write token t's K and V (rows of k_new/v_new [T][Hkv][D]) into slot
+ * slots[t] = block*16 + offset.  Negative slots are skipped.  Bits are
+ * copied unchanged. */
+void orc_append(int dtype, int Hkv, int D, void *kpool, void *vpool, const void *k_new,
+                const void *v_new, const int64_t *slots, int64_t T) {
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t s = slots[t];
+    if (s < 0) continue;
+    int64_t blk = s / BLOCK;
+    int off = (int)(s % BLOCK);
+    for (int g = 0; g < Hkv; ++g)
+      for (int d = 0; d < D; ++d) {
+        size_t src = ((size_t)t * Hkv + g) * D + d;
+        copy_elem(kpool, k_at(blk, g, off, d, Hkv, D, dtype), k_new, src, dtype);
+        copy_elem(vpool, v_at(blk, g, off, d, Hkv, D), v_new, src, dtype);
+      }
+  }
+}
+
+/* Copy-on-write support: copy every slot, head and element of block
+ * pairs[2i] into block pairs[2i+1], for K and V. */
+void orc_copy_blocks(int dtype, int Hkv, int D, void *kpool, void *vpool, const int32_t *pairs,
+                     int n) {
+  for (int i = 0; i < n; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    for (int g = 0; g < Hkv; ++g)
+      for (int t = 0; t < BLOCK; ++t)
+        for (int d = 0; d < D; ++d) {
+          copy_elem(kpool, k_at(dst, g, t, d, Hkv, D, dtype), kpool, k_at(src, g, t, d, Hkv, D, dtype), dtype);
+          copy_elem(vpool, v_at(dst, g, t, d, Hkv, D), vpool, v_at(src, g, t, d, Hkv, D), dtype);
+        }
+  }
+}
+
+/* Decode attention over the paged pool.  q [B][Hq][D], tables [B][max_blocks],
+ * ctx [B], out [B][Hq][D] (double).  A sequence with ctx 0 gets output 0. */
+void orc_paged_attention(int dtype, int Hq, int Hkv, int D, const void *q, const void *kpool,
+                         const void *vpool, const int32_t *tables, int max_blocks,
+                         const int32_t *ctx, int B, double scale, double *out) {
+  int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
+    int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
+    int n = ctx[b];
+    double *o = out + (size_t)bh * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (n <= 0) continue;
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+      int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d)
+        acc += elem(q, (size_t)bh * D + d, dtype) * elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
+      s[j] = scale * acc;
+      if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) {
+      int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
+      double w = exp(s[j] - m);
+      l += w;
+      for (int d = 0; d < D; ++d) o[d] += w * elem(vpool, v_at(blk, g, j % BLOCK, d, Hkv, D), dtype);
+    }
+    for (int d = 0; d < D; ++d) o[d] /= l;
+    free(s);
+  }
+}
+
+/* The same attention for one sequence whose cache is contiguous:
+ * q [Hq][D], k and v [n][Hkv][D], out [Hq][D]. */
+void orc_contiguous_attention(int dtype, int Hq, int Hkv, int D, const void *q, const void *k,
+                              const void *v, int n, double scale, double *out) {
+  int G = Hq / Hkv;
+  for (int h = 0; h < Hq; ++h) {
+    int g = h / G;
+    double *o = out + (size_t)h * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (n <= 0) continue;
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d)
+        acc += elem(q, (size_t)h * D + d, dtype) * elem(k, ((size_t)j * Hkv + g) * D + d, dtype);
+      s[j] = scale * acc;
+      if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) {
+      double w = exp(s[j] - m);
+      l += w;
+      for (int d = 0; d < D; ++d) o[d] += w * elem(v, ((size_t)j * Hkv + g) * D + d, dtype);
+    }
+    for (int d = 0; d < D; ++d) o[d] /= l;
+    free(s);
+  }
+}
+
+/* Split-context form: the context is cut into spans of P tokens; each span
+ * keeps its own maximum m_i, weight sum l_i and unnormalised output o_i, and
+ * the spans are combined with M = max m_i, L = sum l_i e^(m_i - M),
+ * O = sum o_i e^(m_i - M) / L.  Algebraically equal to orc_paged_attention. */
+void orc_partitioned_attention(int dtype, int Hq, int Hkv, int D, const void *q,
+                               const void *kpool, const void *vpool, const int32_t *tables,
+                               int max_blocks, const int32_t *ctx, int B, double scale, int P,
+                               double *out) {
+  int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
+    int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
+    int n = ctx[b];
+    double *o = out + (size_t)bh * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (n <= 0) continue;
+    int np = (n + P - 1) / P;
+    double *pm = (double *)malloc(sizeof(double) * (size_t)np);
+    double *pl = (double *)malloc(sizeof(double) * (size_t)np);
+    double *po = (double *)calloc((size_t)np * D, sizeof(double));
+    for (int p = 0; p < np; ++p) {
+      int j0 = p * P, j1 = j0 + P < n ? j0 + P : n;
+      double m = -INFINITY;
+      for (int j = j0; j < j1; ++j) {
+        int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+          acc += elem(q, (size_t)bh * D + d, dtype) * elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
+        if (scale * acc > m) m = scale * acc;
+      }
+      double l = 0.0;
+      for (int j = j0; j < j1; ++j) {
+        int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+          acc += elem(q, (size_t)bh * D + d, dtype) * elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
+        double w = exp(scale * acc - m);
+        l += w;
+        for (int d = 0; d < D; ++d) po[(size_t)p * D + d] += w * elem(vpool, v_at(blk, g, j % BLOCK, d, Hkv, D), dtype);
+      }
+      pm[p] = m;
+      pl[p] = l;
+    }
+    double M = -INFINITY;
+    for (int p = 0; p < np; ++p) if (pm[p] > M) M = pm[p];
+    double L = 0.0;
+    for (int p = 0; p < np; ++p) L += pl[p] * exp(pm[p] - M);
+    for (int p = 0; p < np; ++p) {
+      double f = exp(pm[p] - M);
+      for (int d = 0; d < D; ++d) o[d] += po[(size_t)p * D + d] * f;
+    }
+    for (int d = 0; d < D; ++d) o[d] /= L;
+    free(pm);
+    free(pl);
+    free(po);
+  }
+}
+
+/* Read back the K or V of token j of a paged sequence into row-major
+ * [Hkv][D] doubles (used to check that reads through different tables agree). */
+void orc_gather_token(int dtype, int Hkv, int D, const void *kpool, const void *vpool,
+                      const int32_t *table, int j, double *k_out, double *v_out) {
+  int64_t blk = table[j / BLOCK];
+  for (int g = 0; g < Hkv; ++g)
+    for (int d = 0; d < D; ++d) {
+      k_out[(size_t)g * D + d] = elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
+      v_out[(size_t)g * D + d] = elem(vpool, v_at(blk, g, j % BLOCK, d, Hkv, D), dtype);
+    }
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

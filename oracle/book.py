@@ -1,0 +1,224 @@
+"""Oracle model of the KV block manager (plain Python, slow, obviously correct).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything under ``oracle/``.
+It shares no code with the HIP library and never calls it.
+
+What it follows:
+
+* The physical KV cache is cut into fixed 16-token blocks held in one flat
+  pool; a sequence owns a block table whose entry i names the physical block
+  of its i-th logical block; a new block is taken only when the current one
+  is full; a finished sequence hands every block back to the free pool
+  [KV Cache 工程学 §15.5; 新一代 KV Cache 管理 §8.1].
+* Several block tables may name the same physical block; each block carries
+  a reference count [新一代 KV Cache 管理 §8.1], and sharing of a common
+  prompt uses copy-on-write [KV Cache 与 PagedAttention, "PagedAttention
+  如何解决这个问题"].
+
+Readings where the pages are silent (each one is listed in the design notes):
+
+* free pool = a LIFO stack seeded so that the first allocation returns
+  ``free_order[0]``; a freed block is pushed on top;
+* a sequence being freed releases its blocks in table order;
+* copy-on-write fires only when a token is written into a tail block whose
+  reference count is above one: a fresh block is taken, the pair
+  (old, new) is reported for a whole-block copy, the old block loses one
+  reference and the table points at the new block; the last holder of a
+  block writes in place;
+* an append reserves all of its tokens or none (state unchanged on
+  failure); a batch append is all-or-nothing over the whole batch;
+* sequence ids are handed out 0, 1, 2, ... and never reused.
+
+Parity unpinned items: none; every behaviour here is checked by the
+invariant and worked-number tests in ``tests/test_oracle_book.py``.
+"""
+from __future__ import annotations
+
+import copy
+
+BLOCK_SIZE = 16
+
+
+class BookError(Exception):
+    """Raised with a ``code`` matching the library's status names."""
+
+    def __init__(self, code: str, msg: str = ""):
+        super().__init__(f"{code}: {msg}")
+        self.code = code
+
+
+class Book:
+    def __init__(self, num_blocks: int, free_order=None):
+        if num_blocks <= 0:
+            raise BookError("INVALID", "num_blocks must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise BookError("INVALID", "free_order must be a permutation of the block ids")
+        self.num_blocks = num_blocks
+        self.free = order[::-1]          # top of the stack is the list's end
+        self.ref = [0] * num_blocks
+        self.seqs = {}                   # id -> {"table": [...], "len": n}
+        self.next_id = 0
+
+    # -- blocks ---------------------------------------------------------------
+    def alloc(self) -> int:
+        if not self.free:
+            raise BookError("NO_BLOCKS", "pool exhausted")
+        blk = self.free.pop()
+        self.ref[blk] = 1
+        return blk
+
+    def _check(self, blk: int):
+        if not (0 <= blk < self.num_blocks):
+            raise BookError("BAD_BLOCK", str(blk))
+
+    def incref(self, blk: int):
+        self._check(blk)
+        if self.ref[blk] <= 0:
+            raise BookError("REFCOUNT", f"incref of free block {blk}")
+        self.ref[blk] += 1
+
+    def decref(self, blk: int):
+        self._check(blk)
+        if self.ref[blk] <= 0:
+            raise BookError("REFCOUNT", f"free of free block {blk}")
+        self.ref[blk] -= 1
+        if self.ref[blk] == 0:
+            self.free.append(blk)
+
+    def refcount(self, blk: int) -> int:
+        self._check(blk)
+        return self.ref[blk]
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    # -- sequences ------------------------------------------------------------
+    def _seq(self, sid: int):
+        if sid not in self.seqs:
+            raise BookError("BAD_SEQ", str(sid))
+        return self.seqs[sid]
+
+    def create(self) -> int:
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = {"table": [], "len": 0}
+        return sid
+
+    def fork(self, parent: int) -> int:
+        p = self._seq(parent)
+        for blk in p["table"]:
+            self.incref(blk)
+        sid = self.create()
+        self.seqs[sid] = {"table": list(p["table"]), "len": p["len"]}
+        return sid
+
+    def _append_one_seq(self, sid: int, n: int, slots: list, cow: list):
+        s = self._seq(sid)
+        for _ in range(n):
+            pos = s["len"]
+            if pos % BLOCK_SIZE == 0:
+                s["table"].append(self.alloc())
+            elif self.ref[s["table"][-1]] > 1:
+                old = s["table"][-1]
+                new = self.alloc()
+                cow.append((old, new))
+                self.decref(old)
+                s["table"][-1] = new
+            slots.append(s["table"][pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE)
+            s["len"] = pos + 1
+
+    def append_slots(self, sid: int, n: int):
+        """Reserve n token slots at the end of sequence sid.
+        Returns (slots, cow_pairs); all-or-nothing."""
+        return self.batch_append_slots([sid], n)
+
+    def batch_append_slots(self, sids, n: int):
+        """Reserve n slots for each sequence of the batch, in batch order."""
+        if n < 0:
+            raise BookError("INVALID", "negative token count")
+        for sid in sids:
+            self._seq(sid)
+        saved = (list(self.free), list(self.ref), copy.deepcopy(self.seqs))
+        slots, cow = [], []
+        try:
+            for sid in sids:
+                self._append_one_seq(sid, n, slots, cow)
+        except BookError:
+            self.free, self.ref, self.seqs = saved[0], saved[1], saved[2]
+            raise
+        return slots, cow
+
+    def free_seq(self, sid: int):
+        s = self._seq(sid)
+        for blk in s["table"]:
+            self.decref(blk)
+        del self.seqs[sid]
+
+    def seq_len(self, sid: int) -> int:
+        return self._seq(sid)["len"]
+
+    def block_table(self, sid: int):
+        return list(self._seq(sid)["table"])
+
+    # -- statistics -----------------------------------------------------------
+    def stats(self) -> dict:
+        used = self.num_blocks - len(self.free)
+        shared = sum(1 for r in self.ref if r > 1)
+        logical = sum(s["len"] for s in self.seqs.values())
+        # A block's fill is the largest number of its slots any holder uses.
+        fill = {}
+        for s in self.seqs.values():
+            for j, blk in enumerate(s["table"]):
+                f = min(BLOCK_SIZE, s["len"] - j * BLOCK_SIZE)
+                fill[blk] = max(fill.get(blk, 0), f)
+        stored = sum(fill.values())
+        return {
+            "num_blocks": self.num_blocks,
+            "num_free": len(self.free),
+            "num_used": used,
+            "num_shared": shared,
+            "num_seqs": len(self.seqs),
+            "tokens_logical": logical,
+            "tokens_stored": stored,
+            "usage": used / self.num_blocks,
+            "internal_fragmentation": (1.0 - stored / (used * BLOCK_SIZE)) if used else 0.0,
+        }
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: float) -> float:
+    """K and V of one token across all layers: two tensors of h_kv x d_h
+    elements per layer [KV Cache 工程学 §15.2]."""
+    return num_layers * 2 * num_kv_heads * head_dim * elem_bytes
+
+
+def blocks_for_tokens(n: int) -> int:
+    """Blocks a sequence of n tokens occupies: whole blocks, the last one
+    possibly part-filled [KV Cache 工程学 §15.5]."""
+    return -(-n // BLOCK_SIZE)
+
+
+def build_workload(inst):
+    """Run a workload's build script and decode-step append on a fresh Book.
+
+    Returns (book, seq_ids, prefill_slots, step_slots, cow_pairs): slots of
+    every prefill token in append order, and the step's slot per sequence."""
+    wl = inst.wl
+    book = Book(inst.num_blocks, inst.free_order)
+    prefill_slots, cow = [], []
+    if wl.prefix_len:
+        root = book.create()
+        s, c = book.append_slots(root, wl.prefix_len)
+        prefill_slots += s
+        cow += c
+        ids = [root] + [book.fork(root) for _ in range(wl.batch - 1)]
+    else:
+        ids = [book.create() for _ in range(wl.batch)]
+    for b, sid in enumerate(ids):
+        s, c = book.append_slots(sid, int(inst.own_prefill[b]))
+        prefill_slots += s
+        cow += c
+    step_slots, c = book.batch_append_slots(ids, 1)
+    cow += c
+    return book, ids, prefill_slots, step_slots, cow

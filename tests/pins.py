@@ -1,0 +1,276 @@
+"""Pins of the CPU oracle: checks against facts fixed by the pages or by
+mathematics, never against the oracle itself.
+
+Each ``check_*`` function raises AssertionError when the oracle is wrong.
+``test_oracle_attention.py`` runs them on the real oracle and
+``test_oracle_mutants.py`` runs them on deliberately broken copies of it, to
+show that a plausible mistake anywhere in the oracle fails at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import attn as orc
+from oracle.book import Book
+from workloads.configs import normal_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored elements -> float64, computed here independently of the oracle."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+class Problem:
+    """A small paged decode problem built with the oracle's own bookkeeping
+    and append: logical K/V per sequence, pools, tables, lengths."""
+
+    def __init__(self, dtype, B, Hq, Hkv, D, ctx, num_blocks, seed, identity=False, kv=None, q=None):
+        self.dtype, self.B, self.Hq, self.Hkv, self.D = dtype, B, Hq, Hkv, D
+        self.ctx = np.asarray(ctx, dtype=np.int32)
+        rng = np.random.default_rng(seed)
+        order = np.arange(num_blocks) if identity else rng.permutation(num_blocks)
+        self.book = Book(num_blocks, order)
+        self.ids = [self.book.create() for _ in range(B)]
+        if kv is None:
+            kv = [(normal_bits(seed * 7919 + 2 * b, (int(ctx[b]), Hkv, D), dtype),
+                   normal_bits(seed * 7919 + 2 * b + 1, (int(ctx[b]), Hkv, D), dtype)) for b in range(B)]
+        self.kv = kv
+        self.q = normal_bits(seed * 7919 + 99991, (B, Hq, D), dtype) if q is None else q
+        self.kpool, self.vpool = orc.new_pool(num_blocks, Hkv, D, dtype)
+        for b, sid in enumerate(self.ids):
+            slots, _ = self.book.append_slots(sid, int(ctx[b]))
+            orc.append(dtype, Hkv, D, self.kpool, self.vpool, kv[b][0], kv[b][1], np.asarray(slots))
+        self.tables, got_ctx = orc.tables_of(self.book, self.ids)
+        assert (got_ctx == self.ctx).all()
+        self.scale = 1.0 / math.sqrt(D)
+
+    def paged(self):
+        return orc.paged_attention(self.dtype, self.q, self.kpool, self.vpool, self.tables, self.ctx,
+                                   self.Hkv, self.scale)
+
+    def contiguous(self, b):
+        k, v = self.kv[b]
+        return orc.contiguous_attention(self.dtype, self.q[b], k, v, self.scale)
+
+
+def brute_attention(q, K, V, scale):
+    """Textbook softmax attention of one query row in pure Python floats
+    with exactly rounded sums (math.fsum) and no max subtraction."""
+    n, D = len(K), len(q)
+    s = [scale * math.fsum(q[d] * K[j][d] for d in range(D)) for j in range(n)]
+    e = [math.exp(x) for x in s]
+    z = math.fsum(e)
+    return [math.fsum(e[j] * V[j][d] for j in range(n)) / z for d in range(D)]
+
+
+# --------------------------------------------------------------------------
+def check_brute_force():
+    """Oracle == exactly-summed textbook attention on tiny inputs."""
+    for dtype in ("f32", "bf16"):
+        p = Problem(dtype, 3, 4, 2, 8, [1, 17, 40], 12, seed=11)
+        out = p.paged()
+        G = p.Hq // p.Hkv
+        for b in range(p.B):
+            K, V = widen(p.kv[b][0], dtype), widen(p.kv[b][1], dtype)
+            for h in range(p.Hq):
+                ref = brute_attention(list(widen(p.q[b, h], dtype)), K[:, h // G, :].tolist(),
+                                      V[:, h // G, :].tolist(), p.scale)
+                err = np.abs(out[b, h] - np.asarray(ref)).max()
+                assert err <= 1e-13, (dtype, b, h, err)
+
+
+def check_library_sdpa():
+    """Oracle == torch's scaled_dot_product_attention in float64 on the
+    contiguous cache, with its grouped-query option (h -> h // G)."""
+    p = Problem("bf16", 2, 8, 2, 64, [100, 257], 30, seed=5)
+    out = p.paged()
+    for b in range(p.B):
+        q = torch.from_numpy(widen(p.q[b], "bf16"))[None, :, None, :]            # [1,Hq,1,D]
+        k = torch.from_numpy(widen(p.kv[b][0], "bf16")).permute(1, 0, 2)[None]    # [1,Hkv,n,D]
+        v = torch.from_numpy(widen(p.kv[b][1], "bf16")).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k.contiguous(), v.contiguous(),
+                                                               scale=p.scale, enable_gqa=True)
+        err = np.abs(out[b] - ref[0, :, 0, :].numpy()).max()
+        assert err <= 1e-12, (b, err)
+
+
+def check_paged_equals_contiguous():
+    """Shuffled physical blocks give exactly the contiguous-cache result."""
+    for dtype in ("f32", "bf16"):
+        p = Problem(dtype, 4, 4, 4, 16, [1, 16, 33, 100], 20, seed=3)
+        out = p.paged()
+        for b in range(p.B):
+            assert np.array_equal(out[b], p.contiguous(b)), (dtype, b)
+
+
+def check_placement_invariance():
+    """Identity and shuffled block hand-out orders give bitwise-equal results."""
+    a = Problem("bf16", 3, 8, 2, 32, [5, 48, 70], 16, seed=9, identity=True)
+    b = Problem("bf16", 3, 8, 2, 32, [5, 48, 70], 16, seed=9, identity=False)
+    assert not np.array_equal(a.tables, b.tables)
+    assert np.array_equal(a.paged(), b.paged())
+
+
+def check_special_cases():
+    dt = "f32"
+    # One cached token: the softmax weight is exactly 1, so out == v.
+    p = Problem(dt, 2, 2, 2, 8, [1, 1], 4, seed=21)
+    out = p.paged()
+    for b in range(2):
+        for h in range(2):
+            assert np.array_equal(out[b, h], widen(p.kv[b][1][0, h], dt))
+    # Every key identical: uniform weights, so out == mean of V.
+    n = 37
+    k1 = normal_bits(77, (1, 1, 8), dt)
+    K = np.repeat(k1, n, axis=0)
+    V = normal_bits(78, (n, 1, 8), dt)
+    p = Problem(dt, 1, 1, 1, 8, [n], 4, seed=22, kv=[(K, V)])
+    out = p.paged()[0, 0]
+    mean = np.array([math.fsum(widen(V[:, 0, d], dt)) / n for d in range(8)])
+    assert np.abs(out - mean).max() <= 1e-13
+    # One key far more aligned with q than the rest: out ~= its value row.
+    q = np.zeros((1, 1, 8), np.float32)
+    q[0, 0, 0] = 1.0
+    K = normal_bits(79, (n, 1, 8), dt)
+    K[13, 0, :] = 0.0
+    for big in (400.0, 4000.0):  # the second puts the top score far past exp's range
+        K[13, 0, 0] = big
+        p = Problem(dt, 1, 1, 1, 8, [n], 4, seed=23, kv=[(K, V)], q=q)
+        assert np.abs(p.paged()[0, 0] - widen(V[13, 0], dt)).max() <= 1e-12
+    # Adding one vector c to every key shifts all scores by q.c: no change.
+    K = normal_bits(80, (n, 1, 8), dt)
+    c = normal_bits(81, (1, 1, 8), dt)
+    K2 = (K.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
+    q = normal_bits(82, (1, 1, 8), dt)
+    base = Problem(dt, 1, 1, 1, 8, [n], 4, seed=24, kv=[(K2, V)], q=q).paged()[0, 0]
+    # reference: the same problem with the exact shifted keys computed in float64 by brute force
+    qs = widen(q[0, 0], dt).tolist()
+    ref = brute_attention(qs, widen(K2[:, 0], dt).tolist(), widen(V[:, 0], dt).tolist(), 1 / math.sqrt(8))
+    assert np.abs(base - np.asarray(ref)).max() <= 1e-13
+    ref_shift = brute_attention(qs, (widen(K2[:, 0], dt) - widen(c[0, 0], dt)[None]).tolist(),
+                                widen(V[:, 0], dt).tolist(), 1 / math.sqrt(8))
+    assert np.abs(base - np.asarray(ref_shift)).max() <= 1e-12
+    # Reordering the cached tokens (keys with their values) changes nothing.
+    perm = np.random.default_rng(5).permutation(n)
+    pa = Problem(dt, 1, 1, 1, 8, [n], 4, seed=25, kv=[(K, V)], q=q).paged()[0, 0]
+    pb = Problem(dt, 1, 1, 1, 8, [n], 4, seed=25, kv=[(K[perm].copy(), V[perm].copy())], q=q).paged()[0, 0]
+    assert np.abs(pa - pb).max() <= 1e-14
+
+
+def check_merge_identity():
+    """Any split of the context into 16-token-aligned spans, merged by
+    log-sum-exp, equals the single-pass result."""
+    p = Problem("bf16", 3, 8, 2, 32, [16, 300, 1000], 100, seed=31)
+    ref = p.paged()
+    for P in (16, 32, 48, 512):
+        out = orc.partitioned_attention("bf16", p.q, p.kpool, p.vpool, p.tables, p.ctx, p.Hkv, p.scale, P)
+        assert np.abs(out - ref).max() <= 1e-13, P
+
+
+def check_gqa_reduces_to_mha():
+    """Grouped-query attention == multi-head attention whose kv heads are
+    repeated per group of h_q / h_kv consecutive query heads."""
+    Hq, Hkv, D, n = 8, 2, 16, 50
+    K = normal_bits(41, (n, Hkv, D), "bf16")
+    V = normal_bits(42, (n, Hkv, D), "bf16")
+    q = normal_bits(43, (1, Hq, D), "bf16")
+    gqa = Problem("bf16", 1, Hq, Hkv, D, [n], 8, seed=44, kv=[(K, V)], q=q).paged()
+    Kr = np.repeat(K, Hq // Hkv, axis=1).copy()
+    Vr = np.repeat(V, Hq // Hkv, axis=1).copy()
+    mha = Problem("bf16", 1, Hq, Hq, D, [n], 8, seed=44, kv=[(Kr, Vr)], q=q).paged()
+    assert np.array_equal(gqa, mha)
+    # and the groups do read different heads
+    assert np.abs(gqa[0, 0] - gqa[0, Hq - 1]).max() > 1e-3
+
+
+def check_append_roundtrip():
+    """Every appended token reads back bit-for-bit through its block table;
+    slots never written keep the sentinel; whole-block copies are exact."""
+    for dtype in ("f32", "bf16"):
+        p = Problem(dtype, 3, 4, 2, 16, [1, 16, 45], 8, seed=51, identity=True)
+        written = 0
+        for b in range(p.B):
+            for j in range(int(p.ctx[b])):
+                k, v = orc.gather_token(dtype, p.Hkv, p.D, p.kpool, p.vpool, p.tables[b], j)
+                assert np.array_equal(k, widen(p.kv[b][0][j], dtype))
+                assert np.array_equal(v, widen(p.kv[b][1][j], dtype))
+                written += 1
+        for pool in (p.kpool, p.vpool):
+            nan = np.isnan(widen(pool, dtype))
+            assert int((~nan).sum()) == written * p.Hkv * p.D
+        k0, v0 = p.kpool.copy(), p.vpool.copy()
+        src = int(p.tables[2][1])
+        dst = int(p.book.free[-1])
+        orc.copy_blocks(dtype, p.Hkv, p.D, p.kpool, p.vpool, [(src, dst)])
+        blk = p.Hkv * 16 * p.D
+        for pool, old in ((p.kpool, k0), (p.vpool, v0)):
+            assert np.array_equal(pool[dst * blk:(dst + 1) * blk], old[src * blk:(src + 1) * blk])
+            rest = np.ones(pool.size, bool)
+            rest[dst * blk:(dst + 1) * blk] = False
+            assert np.array_equal(pool[rest].view(np.uint8 if dtype == "bf16" else np.uint32),
+                                  old[rest].view(np.uint8 if dtype == "bf16" else np.uint32))
+
+
+def check_layout_golden():
+    """The flat pool indices of hand-worked examples (tests/golden/pool_layout.txt)."""
+    H, D = 2, 16
+    for dtype, slot, head, d, ki, vi in read_golden("pool_layout.txt"):
+        slot, head, d, ki, vi = int(slot), int(head), int(d), int(ki), int(vi)
+        kpool, vpool = orc.new_pool(slot // 16 + 1, H, D, dtype)
+        kn = np.zeros((1, H, D), np.float32)
+        kn[0, head, d] = 3.0
+        vn = np.zeros((1, H, D), np.float32)
+        vn[0, head, d] = 5.0
+        if dtype == "bf16":
+            kn = (kn.view(np.uint32) >> 16).astype(np.uint16)
+            vn = (vn.view(np.uint32) >> 16).astype(np.uint16)
+        orc.append(dtype, H, D, kpool, vpool, kn, vn, np.array([slot]))
+        kw, vw = widen(kpool, dtype), widen(vpool, dtype)
+        assert np.flatnonzero(kw == 3.0).tolist() == [ki], (dtype, slot, head, d)
+        assert np.flatnonzero(vw == 5.0).tolist() == [vi], (dtype, slot, head, d)
+
+
+def check_rejects_per_page_softmax():
+    """The per-page softmax of the vendor article's pseudo-code
+    [PagedAttention：大模型KV Cache内存管理革新 §3.2] agrees with the oracle
+    only while the context fits in one page; beyond that the oracle keeps one
+    softmax over the whole context."""
+    p = Problem("f32", 2, 1, 1, 16, [16, 80], 8, seed=61)
+    out = p.paged()
+    for b in range(p.B):
+        K, V = widen(p.kv[b][0][:, 0], "f32"), widen(p.kv[b][1][:, 0], "f32")
+        q = widen(p.q[b, 0], "f32")
+        acc = np.zeros(16)
+        for s0 in range(0, int(p.ctx[b]), 16):
+            s = K[s0:s0 + 16] @ q * p.scale
+            w = np.exp(s - s.max())
+            acc += (w / w.sum()) @ V[s0:s0 + 16]
+        diff = np.abs(out[b, 0] - acc).max()
+        if p.ctx[b] <= 16:
+            assert diff <= 1e-13
+        else:
+            assert diff > 1e-2
+
+
+ALL_CHECKS = [check_brute_force, check_library_sdpa, check_paged_equals_contiguous,
+              check_placement_invariance, check_special_cases, check_merge_identity,
+              check_gqa_reduces_to_mha, check_append_roundtrip, check_layout_golden,
+              check_rejects_per_page_softmax]

@@ -1,0 +1,87 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each case copies ``oracle/attn.c``, applies one textual mutation (a dropped
+term, a wrong index, a transposed layout, a wrong sign...), compiles it with
+gcc into a temporary library, swaps it in for the real oracle and runs every
+pin.  The real oracle is restored afterwards.  CPU only.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as orc_build
+
+SRC = os.path.join(os.path.dirname(orc_build.LIB), "attn.c")
+
+MUTANTS = {
+    "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "no_normalisation": ("o[d] /= l;", "o[d] /= 1.0;"),
+    "block_index_mod": ("max_blocks + j / BLOCK]", "max_blocks + j % BLOCK]"),
+    "slot_offset_div": ("j % BLOCK, d", "j / BLOCK, d"),
+    "gqa_map_modulo": ("g = h / G;", "g = h % Hkv;"),
+    "k_layout_chunk_swapped": ("(size_t)(d / X)) * BLOCK + (size_t)t) * X + (size_t)(d % X)",
+                               "(size_t)(d % X)) * BLOCK + (size_t)t) * X + (size_t)(d / X)"),
+    "v_layout_transposed": ("(size_t)D + (size_t)d) * BLOCK + (size_t)t",
+                            "(size_t)BLOCK + (size_t)t) * D + (size_t)d"),
+    "merge_sign": ("L += pl[p] * exp(pm[p] - M);", "L += pl[p] * exp(M - pm[p]);"),
+    "merge_drop_rescale": ("o[d] += po[(size_t)p * D + d] * f;", "o[d] += po[(size_t)p * D + d];"),
+    "bf16_widen_shift": ("<< 16;", "<< 15;"),
+    "query_row_of_head0": ("elem(q, (size_t)bh * D + d, dtype)", "elem(q, (size_t)b * Hq * D + d, dtype)"),
+    "context_off_by_one": ("int n = ctx[b];", "int n = ctx[b] - 1;"),
+    "append_skips_slot0": ("if (s < 0) continue;", "if (s <= 0) continue;"),
+    "copy_only_k": ("copy_elem(vpool, v_at(dst,", "if (0) copy_elem(vpool, v_at(dst,"),
+    "value_of_next_token": ("w * elem(vpool, v_at(blk, g, j % BLOCK, d",
+                            "w * elem(vpool, v_at(blk, g, (j + 1) % BLOCK, d"),
+    "max_from_first_token_only": ("if (s[j] > m) m = s[j];", "if (j == 0) m = s[j];"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC, encoding="utf-8").read()
+    assert old in src, f"mutation {name} does not apply"
+    out = tmp_path / f"attn_{name}.c"
+    out.write_text(src.replace(old, new), encoding="utf-8")
+    lib = tmp_path / f"liborc_{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", str(lib), str(out), "-lm"], check=True)
+    return str(lib)
+
+
+_RUNNER = r"""
+import ctypes, sys
+sys.path[:0] = [sys.argv[2], sys.argv[3]]
+import pins
+from oracle import attn as orc
+real = orc.lib()
+mutant = ctypes.CDLL(sys.argv[1])
+for fn in ("orc_append", "orc_copy_blocks", "orc_paged_attention", "orc_contiguous_attention",
+           "orc_partitioned_attention", "orc_gather_token", "orc_num_threads"):
+    getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
+    getattr(mutant, fn).restype = getattr(real, fn).restype
+orc._lib = mutant
+for check in pins.ALL_CHECKS:
+    print("RUN", check.__name__, flush=True)
+    try:
+        check()
+    except Exception as e:
+        print("FAILED", check.__name__, type(e).__name__, flush=True)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    """Runs the pins in a child process: an out-of-bounds mutant may crash it,
+    which also counts as caught."""
+    old, new = MUTANTS[name]
+    path = _build_mutant(tmp_path, name, old, new)
+    tests_dir = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(tests_dir)
+    r = subprocess.run([sys.executable, "-c", _RUNNER, path, tests_dir, root],
+                       capture_output=True, text=True, timeout=300)
+    assert "RUN check_brute_force" in r.stdout, r.stderr
+    failed = [ln for ln in r.stdout.splitlines() if ln.startswith("FAILED")]
+    crashed = r.returncode < 0  # killed by a signal inside a check
+    assert r.returncode <= 0, r.stderr
+    assert failed or crashed, f"no pin caught mutation {name}:\n{r.stdout}\n{r.stderr}"
