@@ -1,0 +1,236 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV cache and PagedAttention decode path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The problem, as the sources state it:
+ *   - The KV cache is cut into fixed blocks of 16 tokens held in one flat
+ *     physical pool; each sequence keeps a block table whose entry i names
+ *     the physical block of its i-th logical block; a block is taken only
+ *     when the sequence's current block is full and every block returns to
+ *     the free pool when the sequence ends [KV Cache 工程学 §15.5;
+ *     新一代 KV Cache 管理 §8.1].
+ *   - Block tables of different sequences may point at the same physical
+ *     block, counted by reference, so shared prompts and parallel samples are
+ *     stored once [新一代 KV Cache 管理 §8.1; KV Cache 工程学 §15.6]; a write
+ *     into a shared block copies it first [KV Cache 与 PagedAttention,
+ *     first article, "PagedAttention 如何解决这个问题"].
+ *   - The attention kernel takes the block table as an extra input and
+ *     fetches K and V through it [KV Cache 工程学 §15.5 "PagedAttention 的代价";
+ *     新一代 KV Cache 管理 §8.1].
+ *   - A decode step computes only the new token's K/V, stores them, and
+ *     attends once over the i cached tokens [KV Cache 工程学 §15.1].
+ *   - Usage (used / total blocks) is what an engine watches to refuse work
+ *     [KV Cache 工程学 §15.9].
+ *
+ * Conventions
+ *   - Every function returns a pkv_status (0 = success, negative = error),
+ *     except the size queries, which return 0 on invalid input.  On error a
+ *     thread-local message is available from pkv_last_error().  Nothing
+ *     aborts; a failed call leaves all host state unchanged.
+ *   - The library owns host bookkeeping objects only (pkv_pool and the
+ *     sequences inside it, addressed by int64 id).  Every device buffer is
+ *     owned by the caller and only borrowed for the duration of the call; the
+ *     library allocates no device memory.
+ *   - Device calls are asynchronous on the given stream (a hipStream_t passed
+ *     as void*; NULL = the legacy default stream) and never synchronize.
+ *   - Host-visible arguments are validated; device-resident tables and
+ *     lengths are trusted, but kernels clamp block ids into [0, num_blocks)
+ *     and lengths into [0, 16 * max_blocks_per_seq] so that bad tables give
+ *     wrong numbers, never out-of-bounds accesses.  pkv_validate_tables()
+ *     checks host copies of them.
+ *   - A pool object is not thread-safe; use one per thread or lock around it.
+ *
+ * Pool layout in device memory (one K pool and one V pool per layer):
+ *   X = 16 bytes / element size (8 for bf16, 4 for f32)
+ *   K element (blk, g, t, d) at (((blk*H + g)*(D/X) + d/X)*16 + t)*X + d%X
+ *   V element (blk, g, t, d) at  ((blk*H + g)*D + d)*16 + t
+ *   blk = physical block, g = kv head (H of them), t = slot in block
+ *   (0..15), d = element of the head (D of them).  One (blk, g) tile is
+ *   16*D elements (4 KiB for bf16 at D = 128) and contiguous in both pools.
+ *   A token's slot id is blk*16 + t.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,   /* bad argument (null pointer, unsupported shape...) */
+  PKV_ERR_NO_BLOCKS = -2, /* the free pool cannot satisfy the request */
+  PKV_ERR_BAD_BLOCK = -3, /* block id outside [0, num_blocks) */
+  PKV_ERR_REFCOUNT = -4,  /* free/incref of a block that is not allocated */
+  PKV_ERR_CAPACITY = -5,  /* caller's output array is too small */
+  PKV_ERR_HIP = -6,       /* a HIP runtime call failed (message has details) */
+  PKV_ERR_WORKSPACE = -7, /* workspace missing or smaller than required */
+  PKV_ERR_BAD_SEQ = -8    /* unknown sequence id */
+};
+
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+#define PKV_BLOCK_SIZE 16
+
+typedef struct {
+  int32_t num_blocks;   /* physical blocks in the pool (> 0) */
+  int32_t block_size;   /* tokens per block; must be 16 */
+  int32_t num_kv_heads; /* H (> 0) */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t kv_dtype;     /* PKV_F32 or PKV_BF16; Q uses the same type */
+} pkv_layout;
+
+/* Thread-local description of the last error raised on this thread. */
+const char *pkv_last_error(void);
+/* Library version string. */
+const char *pkv_version(void);
+
+/* ------------------------------------------------------------ block pool */
+typedef struct pkv_pool pkv_pool;
+
+/* Create the host block manager for a pool.  free_order (nullable) is a
+ * permutation of [0, num_blocks): the order in which blocks are first handed
+ * out (NULL = 0, 1, 2, ...).  The free pool is a stack: a freed block is the
+ * next one handed out.  *out receives the new pool. */
+int pkv_pool_create(const pkv_layout *layout, const int32_t *free_order, pkv_pool **out);
+/* Destroy a pool (NULL is accepted). */
+int pkv_pool_destroy(pkv_pool *pool);
+
+/* Take one free block; its reference count becomes 1. */
+int pkv_block_alloc(pkv_pool *pool, int32_t *block_out);
+/* Add a reference to an allocated block. */
+int pkv_block_incref(pkv_pool *pool, int32_t block);
+/* Drop a reference; at zero the block returns to the free pool. */
+int pkv_block_free(pkv_pool *pool, int32_t block);
+/* Reference count of a block (0 = free) into *out. */
+int pkv_block_refcount(const pkv_pool *pool, int32_t block, int32_t *out);
+/* Number of free blocks into *out. */
+int pkv_pool_num_free(const pkv_pool *pool, int32_t *out);
+
+/* --------------------------------------------------------------- sequences */
+/* New empty sequence; ids are 0, 1, 2, ... in creation order, never reused. */
+int pkv_seq_create(pkv_pool *pool, int64_t *id_out);
+/* New sequence sharing every block of parent (each gains one reference). */
+int pkv_seq_fork(pkv_pool *pool, int64_t parent, int64_t *child_out);
+/* Reserve slots for n more tokens at the end of a sequence, all or none.
+ * For each token at position p: when p % 16 == 0 a block is taken and
+ * appended to the table; otherwise, when the tail block is shared (count
+ * > 1), a block is taken, the pair (old, new) is written to cow_pairs_out
+ * for a whole-block copy (pkv_copy_blocks) that must run before the token
+ * is stored, the old block loses a reference and the table points at the
+ * new one.  slots_out[i] = table[p / 16] * 16 + p % 16.
+ * slots_out has room for n entries; cow_pairs_out for cow_cap pairs
+ * (int32 src, dst); *n_cow receives the number of pairs written.
+ * Errors: PKV_ERR_NO_BLOCKS, PKV_ERR_CAPACITY (cow_cap too small). */
+int pkv_seq_append_slots(pkv_pool *pool, int64_t id, int32_t n, int64_t *slots_out,
+                         int32_t *cow_pairs_out, int32_t cow_cap, int32_t *n_cow);
+/* The same for a batch of sequences, n tokens each, processed in batch
+ * order; slots_out is [num_seqs][n].  All or none over the whole batch. */
+int pkv_batch_append_slots(pkv_pool *pool, const int64_t *ids, int32_t num_seqs, int32_t n,
+                           int64_t *slots_out, int32_t *cow_pairs_out, int32_t cow_cap,
+                           int32_t *n_cow);
+/* Release a sequence: its blocks lose a reference in table order; blocks
+ * reaching zero are pushed onto the free pool in that order. */
+int pkv_seq_free(pkv_pool *pool, int64_t id);
+/* Number of tokens of a sequence into *len_out. */
+int pkv_seq_len(const pkv_pool *pool, int64_t id, int32_t *len_out);
+/* Copy a sequence's block table into out (room for cap entries); *n_out
+ * receives its length.  PKV_ERR_CAPACITY if cap is too small. */
+int pkv_seq_block_table(const pkv_pool *pool, int64_t id, int32_t *out, int32_t cap,
+                        int32_t *n_out);
+/* Block tables and lengths of a batch, as paged_attention_decode reads them:
+ * tables_out [num_seqs][max_blocks_per_seq] (entries past a sequence's
+ * blocks are set to 0), context_lens_out [num_seqs]. */
+int pkv_batch_block_tables(const pkv_pool *pool, const int64_t *ids, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, int32_t *tables_out,
+                           int32_t *context_lens_out);
+
+/* -------------------------------------------------------------- statistics */
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_free;
+  int32_t num_used;
+  int32_t num_shared;      /* blocks with reference count > 1 */
+  int64_t num_seqs;        /* live sequences */
+  int64_t tokens_logical;  /* sum of live sequence lengths */
+  int64_t tokens_stored;   /* distinct token slots in use (shared ones once) */
+  double usage;            /* num_used / num_blocks [KV Cache 工程学 §15.9] */
+  double internal_fragmentation; /* 1 - tokens_stored / (num_used * 16)
+                                    [新一代 KV Cache 管理 §8.1] */
+} pkv_stats;
+
+int pkv_pool_stats(const pkv_pool *pool, pkv_stats *out);
+/* K and V bytes of one token across num_layers layers:
+ * num_layers * 2 * num_kv_heads * head_dim * element size
+ * [KV Cache 工程学 §15.2].  0 on invalid input. */
+int64_t pkv_kv_bytes_per_token(const pkv_layout *layout, int32_t num_layers);
+/* Bytes of one pool (K or V; both have this size).  0 on invalid input. */
+int64_t pkv_pool_bytes(const pkv_layout *layout);
+/* Check host copies of block tables and lengths: every entry a sequence
+ * uses is in [0, num_blocks) and every length is in [0, 16 * max_blocks]. */
+int pkv_validate_tables(const pkv_layout *layout, const int32_t *tables, const int32_t *context_lens,
+                        int32_t num_seqs, int32_t max_blocks_per_seq);
+
+/* ---------------------------------------------------------- device calls */
+/* Store the new tokens' K and V into their slots [KV Cache 工程学 §15.1,
+ * §15.5].  k_new, v_new: [num_tokens][H][D] of kv_dtype (device);
+ * d_slots: int64 [num_tokens] (device), slot = blk*16 + t; a negative slot
+ * is skipped.  Bits are copied unchanged.  Slots must be distinct. */
+int paged_kv_append(const pkv_layout *layout, void *k_pool, void *v_pool, const void *k_new,
+                    const void *v_new, const int64_t *d_slots, int32_t num_tokens, void *stream);
+
+/* Copy whole blocks (all heads, all slots, K and V): d_pairs is int32
+ * [num_pairs][2] of (src, dst) on the device, as pkv_seq_append_slots
+ * reports them for copy-on-write.  Destinations must be distinct and not
+ * also sources. */
+int pkv_copy_blocks(const pkv_layout *layout, void *k_pool, void *v_pool, const int32_t *d_pairs,
+                    int32_t num_pairs, void *stream);
+
+/* Decode options (all fields may be zero / NULL for defaults). */
+typedef struct {
+  int32_t partition_tokens; /* tokens per split-context partition: a positive
+                               multiple of 32, or 0 for the default (512) */
+  int32_t kernel;           /* 0 auto; 1 the wavefront-reduction kernel;
+                               2 the matrix-core kernel (bf16, 2 <= G <= 16) */
+  void *ev_begin;           /* optional hipEvent_t recorded before the first kernel */
+  void *ev_partition_done;  /* optional hipEvent_t recorded after the partition kernel */
+  void *ev_end;             /* optional hipEvent_t recorded after the last kernel */
+} pkv_decode_opts;
+
+/* Bytes of workspace paged_attention_decode needs (0 when no sequence can
+ * span more than one partition).  opts may be NULL. */
+size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len,
+                                       const pkv_decode_opts *opts);
+
+/* PagedAttention decode [KV Cache 工程学 §15.5; 新一代 KV Cache 管理 §8.1]:
+ * for every sequence b and query head h (kv head g = h / (Hq / H)),
+ *   out[b][h] = sum_j softmax_j(scale * q[b][h] . K_j) * V_j
+ * over the context_lens[b] tokens j, where token j is slot j % 16 of block
+ * d_block_tables[b][j / 16].  The softmax spans the whole context.
+ *   out: float32 [num_seqs][num_q_heads][D] (device, written)
+ *   q:   kv_dtype [num_seqs][num_q_heads][D] (device)
+ *   d_block_tables: int32 [num_seqs][max_blocks_per_seq] (device)
+ *   d_context_lens: int32 [num_seqs] (device); a length of 0 gives zeros
+ *   max_context_len: an upper bound of every context length (sizes the grid);
+ *   a longer length is treated as max_context_len
+ *   scale: usually 1 / sqrt(D)
+ *   workspace: device scratch of paged_attention_workspace_bytes() bytes
+ *   (may be NULL when that is 0); its contents are not preserved.
+ * Requires num_q_heads % num_kv_heads == 0, G = num_q_heads / num_kv_heads
+ * <= 16, D in {64, 128}, max_context_len <= 16 * max_blocks_per_seq. */
+int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
+                           const void *v_pool, const int32_t *d_block_tables,
+                           const int32_t *d_context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                           void *workspace, size_t workspace_bytes, const pkv_decode_opts *opts,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

@@ -108,6 +108,9 @@ class Book:
 
     def fork(self, parent: int) -> int:
         p = self._seq(parent)
+        for blk in p["table"]:  # a table naming a freed block is corrupt: refuse before changing anything
+            if self.ref[blk] <= 0:
+                raise BookError("REFCOUNT", f"fork of a sequence holding free block {blk}")
         for blk in p["table"]:
             self.incref(blk)
         sid = self.create()
@@ -152,6 +155,9 @@ class Book:
 
     def free_seq(self, sid: int):
         s = self._seq(sid)
+        for blk in s["table"]:  # refuse a corrupt table before changing anything
+            if self.ref[blk] <= 0:
+                raise BookError("REFCOUNT", f"free of a sequence holding free block {blk}")
         for blk in s["table"]:
             self.decref(blk)
         del self.seqs[sid]

@@ -1,0 +1,348 @@
+"""ctypes binding of libpagedkv.so: the C ABI of include/pagedkv.h under the
+same names.  Argument marshalling only -- every step of the decode path runs
+in the library's HIP kernels.  Shapes and sizes of torch tensors are checked
+here because the C side receives bare pointers and cannot.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_NO_BLOCKS, PKV_ERR_BAD_BLOCK = 0, -1, -2, -3
+PKV_ERR_REFCOUNT, PKV_ERR_CAPACITY, PKV_ERR_HIP, PKV_ERR_WORKSPACE, PKV_ERR_BAD_SEQ = -4, -5, -6, -7, -8
+PKV_F32, PKV_BF16 = 0, 1
+BLOCK_SIZE = 16
+
+STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "NO_BLOCKS", -3: "BAD_BLOCK", -4: "REFCOUNT", -5: "CAPACITY",
+                -6: "HIP", -7: "WORKSPACE", -8: "BAD_SEQ"}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+        self.name = STATUS_NAMES.get(code, str(code))
+
+
+class pkv_layout(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.kv_dtype == PKV_F32 else 2
+
+    @property
+    def pool_elems(self) -> int:
+        return self.num_blocks * self.num_kv_heads * BLOCK_SIZE * self.head_dim
+
+
+class pkv_stats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_free", ctypes.c_int32), ("num_used", ctypes.c_int32),
+                ("num_shared", ctypes.c_int32), ("num_seqs", ctypes.c_int64), ("tokens_logical", ctypes.c_int64),
+                ("tokens_stored", ctypes.c_int64), ("usage", ctypes.c_double),
+                ("internal_fragmentation", ctypes.c_double)]
+
+
+class pkv_decode_opts(ctypes.Structure):
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("ev_begin", ctypes.c_void_p),
+                ("ev_partition_done", ctypes.c_void_p), ("ev_end", ctypes.c_void_p)]
+
+
+# name -> (restype, argtypes) of every exported symbol of include/pagedkv.h
+_P, _I32, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_PL = ctypes.POINTER(pkv_layout)
+_PO = ctypes.POINTER(pkv_decode_opts)
+SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_pool_create": (ctypes.c_int, [_PL, _P, ctypes.POINTER(_P)]),
+    "pkv_pool_destroy": (ctypes.c_int, [_P]),
+    "pkv_block_alloc": (ctypes.c_int, [_P, ctypes.POINTER(_I32)]),
+    "pkv_block_incref": (ctypes.c_int, [_P, _I32]),
+    "pkv_block_free": (ctypes.c_int, [_P, _I32]),
+    "pkv_block_refcount": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_pool_num_free": (ctypes.c_int, [_P, ctypes.POINTER(_I32)]),
+    "pkv_seq_create": (ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
+    "pkv_seq_fork": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I64)]),
+    "pkv_seq_append_slots": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_batch_append_slots": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_seq_free": (ctypes.c_int, [_P, _I64]),
+    "pkv_seq_len": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I32)]),
+    "pkv_seq_block_table": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_batch_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
+    "pkv_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(pkv_stats)]),
+    "pkv_kv_bytes_per_token": (_I64, [_PL, _I32]),
+    "pkv_pool_bytes": (_I64, [_PL]),
+    "pkv_validate_tables": (ctypes.c_int, [_PL, _P, _P, _I32, _I32]),
+    "paged_kv_append": (ctypes.c_int, [_PL, _P, _P, _P, _P, _P, _I32, _P]),
+    "pkv_copy_blocks": (ctypes.c_int, [_PL, _P, _P, _P, _I32, _P]),
+    "paged_attention_workspace_bytes": (_SZ, [_PL, _I32, _I32, _I32, _PO]),
+    "paged_attention_decode": (ctypes.c_int, [_PL, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _SZ,
+                                              _PO, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load the in-tree library; fail loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != PKV_OK:
+        raise PagedKVError(rc, lib().pkv_last_error().decode(errors="replace"))
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pkv_last_error() -> str:
+    return lib().pkv_last_error().decode(errors="replace")
+
+
+def pkv_version() -> str:
+    return lib().pkv_version().decode()
+
+
+def make_layout(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str) -> pkv_layout:
+    return pkv_layout(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), int(head_dim),
+                      PKV_BF16 if dtype == "bf16" else PKV_F32)
+
+
+# ------------------------------------------------------------------ host pool
+def pkv_pool_create(layout: pkv_layout, free_order=None):
+    h = ctypes.c_void_p()
+    fo = None
+    if free_order is not None:
+        fo = np.ascontiguousarray(free_order, dtype=np.int32)
+        if fo.size != layout.num_blocks:
+            raise ValueError("free_order must hold num_blocks entries")
+    _check(lib().pkv_pool_create(ctypes.byref(layout), None if fo is None else _np_ptr(fo), ctypes.byref(h)))
+    return h
+
+
+def pkv_pool_destroy(pool):
+    _check(lib().pkv_pool_destroy(pool))
+
+
+def pkv_block_alloc(pool) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pkv_block_alloc(pool, ctypes.byref(out)))
+    return out.value
+
+
+def pkv_block_incref(pool, block: int):
+    _check(lib().pkv_block_incref(pool, int(block)))
+
+
+def pkv_block_free(pool, block: int):
+    _check(lib().pkv_block_free(pool, int(block)))
+
+
+def pkv_block_refcount(pool, block: int) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pkv_block_refcount(pool, int(block), ctypes.byref(out)))
+    return out.value
+
+
+def pkv_pool_num_free(pool) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pkv_pool_num_free(pool, ctypes.byref(out)))
+    return out.value
+
+
+def pkv_seq_create(pool) -> int:
+    out = ctypes.c_int64()
+    _check(lib().pkv_seq_create(pool, ctypes.byref(out)))
+    return out.value
+
+
+def pkv_seq_fork(pool, parent: int) -> int:
+    out = ctypes.c_int64()
+    _check(lib().pkv_seq_fork(pool, int(parent), ctypes.byref(out)))
+    return out.value
+
+
+def pkv_batch_append_slots(pool, ids, n: int, cow_cap: int | None = None, slots_out: np.ndarray | None = None):
+    """Returns (slots int64 [len(ids) * n], cow pairs int32 [k][2])."""
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    cap = len(ids) if cow_cap is None else int(cow_cap)
+    if slots_out is None:
+        slots_out = np.empty(len(ids) * n, dtype=np.int64)
+    elif slots_out.dtype != np.int64 or slots_out.size < len(ids) * n or not slots_out.flags["C_CONTIGUOUS"]:
+        raise ValueError("slots_out must be a contiguous int64 array of len(ids) * n entries")
+    cow = np.empty((max(cap, 1), 2), dtype=np.int32)
+    ncow = ctypes.c_int32(0)
+    _check(lib().pkv_batch_append_slots(pool, _np_ptr(ids), len(ids), int(n), _np_ptr(slots_out), _np_ptr(cow), cap,
+                                        ctypes.byref(ncow)))
+    return slots_out, cow[:ncow.value].copy()
+
+
+def pkv_seq_append_slots(pool, seq: int, n: int, cow_cap: int = 1):
+    slots = np.empty(n, dtype=np.int64)
+    cow = np.empty((max(cow_cap, 1), 2), dtype=np.int32)
+    ncow = ctypes.c_int32(0)
+    _check(lib().pkv_seq_append_slots(pool, int(seq), int(n), _np_ptr(slots), _np_ptr(cow), int(cow_cap),
+                                      ctypes.byref(ncow)))
+    return slots, cow[:ncow.value].copy()
+
+
+def pkv_seq_free(pool, seq: int):
+    _check(lib().pkv_seq_free(pool, int(seq)))
+
+
+def pkv_seq_len(pool, seq: int) -> int:
+    out = ctypes.c_int32()
+    _check(lib().pkv_seq_len(pool, int(seq), ctypes.byref(out)))
+    return out.value
+
+
+def pkv_seq_block_table(pool, seq: int) -> list:
+    n = ctypes.c_int32()
+    rc = lib().pkv_seq_block_table(pool, int(seq), None, 0, ctypes.byref(n))
+    if rc not in (PKV_OK, PKV_ERR_CAPACITY):
+        _check(rc)
+    out = np.empty(max(n.value, 1), dtype=np.int32)
+    _check(lib().pkv_seq_block_table(pool, int(seq), _np_ptr(out), out.size, ctypes.byref(n)))
+    return out[:n.value].tolist()
+
+
+def pkv_batch_block_tables(pool, ids, max_blocks: int, tables_out: np.ndarray | None = None,
+                           ctx_out: np.ndarray | None = None):
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    B = len(ids)
+    if tables_out is None:
+        tables_out = np.empty((B, max_blocks), dtype=np.int32)
+    if ctx_out is None:
+        ctx_out = np.empty(B, dtype=np.int32)
+    if tables_out.dtype != np.int32 or tables_out.size != B * max_blocks or not tables_out.flags["C_CONTIGUOUS"]:
+        raise ValueError("tables_out must be a contiguous int32 [B][max_blocks] array")
+    if ctx_out.dtype != np.int32 or ctx_out.size != B or not ctx_out.flags["C_CONTIGUOUS"]:
+        raise ValueError("ctx_out must be a contiguous int32 [B] array")
+    _check(lib().pkv_batch_block_tables(pool, _np_ptr(ids), B, int(max_blocks), _np_ptr(tables_out),
+                                        _np_ptr(ctx_out)))
+    return tables_out, ctx_out
+
+
+def pkv_pool_stats(pool) -> dict:
+    s = pkv_stats()
+    _check(lib().pkv_pool_stats(pool, ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in pkv_stats._fields_}
+
+
+def pkv_kv_bytes_per_token(layout: pkv_layout, num_layers: int) -> int:
+    return lib().pkv_kv_bytes_per_token(ctypes.byref(layout), int(num_layers))
+
+
+def pkv_pool_bytes(layout: pkv_layout) -> int:
+    return lib().pkv_pool_bytes(ctypes.byref(layout))
+
+
+def pkv_validate_tables(layout: pkv_layout, tables: np.ndarray, ctx: np.ndarray):
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx, dtype=np.int32)
+    _check(lib().pkv_validate_tables(ctypes.byref(layout), _np_ptr(tables), _np_ptr(ctx), ctx.size,
+                                     tables.shape[1] if tables.ndim == 2 else 0))
+
+
+# ---------------------------------------------------------------- device side
+def _dev(t, what, dtype=None, numel=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA (HIP) torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what} must hold {numel} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _kv_torch_dtype(layout):
+    import torch
+    return torch.bfloat16 if layout.kv_dtype == PKV_BF16 else torch.float32
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def paged_kv_append(layout, k_pool, v_pool, k_new, v_new, slots, stream=None):
+    import torch
+    dt = _kv_torch_dtype(layout)
+    T = slots.numel()
+    row = layout.num_kv_heads * layout.head_dim
+    args = (ctypes.byref(layout), _dev(k_pool, "k_pool", dt, layout.pool_elems),
+            _dev(v_pool, "v_pool", dt, layout.pool_elems), _dev(k_new, "k_new", dt, T * row),
+            _dev(v_new, "v_new", dt, T * row), _dev(slots, "slots", torch.int64), T, _stream(stream))
+    _check(lib().paged_kv_append(*args))
+
+
+def pkv_copy_blocks(layout, k_pool, v_pool, pairs, stream=None):
+    import torch
+    dt = _kv_torch_dtype(layout)
+    if pairs.numel() % 2:
+        raise ValueError("pairs must be [n][2]")
+    _check(lib().pkv_copy_blocks(ctypes.byref(layout), _dev(k_pool, "k_pool", dt, layout.pool_elems),
+                                 _dev(v_pool, "v_pool", dt, layout.pool_elems), _dev(pairs, "pairs", torch.int32),
+                                 pairs.numel() // 2, _stream(stream)))
+
+
+def decode_opts(partition_tokens=0, kernel=0, events=None) -> pkv_decode_opts:
+    ev = list(events) if events else [None, None, None]
+    return pkv_decode_opts(int(partition_tokens), int(kernel), *[e if e else None for e in ev])
+
+
+def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, partition_tokens=0) -> int:
+    o = decode_opts(partition_tokens)
+    return lib().paged_attention_workspace_bytes(ctypes.byref(layout), int(num_seqs), int(num_q_heads),
+                                                 int(max_context_len), ctypes.byref(o))
+
+
+def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
+                           workspace=None, partition_tokens=0, kernel=0, events=None, stream=None):
+    """events: optional (begin, partition_done, end) raw hipEvent_t handles."""
+    import torch
+    dt = _kv_torch_dtype(layout)
+    if q.dim() != 3 or q.shape[2] != layout.head_dim:
+        raise ValueError("q must be [num_seqs][num_q_heads][head_dim]")
+    B, Hq, D = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    mb = block_tables.shape[1]
+    ws_need = paged_attention_workspace_bytes(layout, B, Hq, max_context_len, partition_tokens)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < ws_need:
+        raise ValueError(f"workspace of {ws_need} bytes needed, got {ws_bytes}")
+    o = decode_opts(partition_tokens, kernel, events)
+    _check(lib().paged_attention_decode(
+        ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", dt),
+        _dev(k_pool, "k_pool", dt, layout.pool_elems), _dev(v_pool, "v_pool", dt, layout.pool_elems),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32, B),
+        B, Hq, mb, int(max_context_len), float(scale), ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))

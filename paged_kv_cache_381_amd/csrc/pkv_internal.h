@@ -1,0 +1,48 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+// Record a thread-local error message and return code.
+int pkv_set_error(int code, const char *fmt, ...);
+// Validate a pkv_layout; PKV_OK or PKV_ERR_INVALID with a message.
+int pkv_check_layout(const pkv_layout *L);
+
+inline int pkv_elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+// Default tokens per split-context partition of the decode kernels.
+#define PKV_DEFAULT_PARTITION 512
+// Partition sizes must be a multiple of this (two blocks: one MFMA chunk).
+#define PKV_PARTITION_QUANTUM 32
+
+// Kernel launchers (decode_*.hip, kv_append.hip).  They return a HIP error
+// code (0 = success); arguments were validated by the caller.
+struct pkv_decode_args {
+  const pkv_layout *L;
+  float *out;
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *tables;
+  const int32_t *ctx;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t part_tokens;
+  int32_t num_parts;
+  float scale_log2;  // scale * log2(e): scores are kept in base 2
+  float *ws_o;       // [B][Hq][num_parts][D]
+  float *ws_ml;      // [B][Hq][num_parts][2]
+  void *stream;
+};
+
+int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                      const int64_t *slots, int32_t num_tokens, void *stream);
+int pkv_launch_copy_blocks(const pkv_layout *L, void *k_pool, void *v_pool, const int32_t *pairs,
+                           int32_t num_pairs, void *stream);
+int pkv_launch_decode_valu(const pkv_decode_args &a);
+int pkv_launch_decode_mfma(const pkv_decode_args &a);
+int pkv_launch_merge(const pkv_decode_args &a);

@@ -1,0 +1,385 @@
+// Host-side KV block manager behind the pkv_pool / pkv_seq_* / pkv_block_*
+// entry points of include/pagedkv.h.
+//
+// The pool is a flat set of fixed 16-token blocks; a sequence is a block table
+// plus a length; a new block is taken only when the sequence's current block
+// is full, and a finished sequence returns its blocks [KV Cache 工程学 §15.5].
+// Blocks are shared between tables by reference count, which is how parallel
+// samples and common prompts are stored once [新一代 KV Cache 管理 §8.1];
+// writing into a shared block copies it first [KV Cache 与 PagedAttention,
+// first article].  Batch appends are all-or-nothing: every mutation is logged
+// and undone in reverse order when the free pool runs dry part-way.
+//
+// Plain C++17 with no HIP dependency, so it also builds with the host
+// compiler and its sanitizers.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int pkv_set_error(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+extern "C" const char *pkv_last_error(void) { return g_last_error.c_str(); }
+extern "C" const char *pkv_version(void) { return "pagedkv 0.1 gfx950"; }
+
+int pkv_check_layout(const pkv_layout *L) {
+  if (!L) return pkv_set_error(PKV_ERR_INVALID, "layout is NULL");
+  if (L->num_blocks <= 0) return pkv_set_error(PKV_ERR_INVALID, "num_blocks must be > 0 (got %d)", L->num_blocks);
+  if (L->block_size != PKV_BLOCK_SIZE)
+    return pkv_set_error(PKV_ERR_INVALID, "block_size must be 16 (got %d)", L->block_size);
+  if (L->num_kv_heads <= 0) return pkv_set_error(PKV_ERR_INVALID, "num_kv_heads must be > 0");
+  if (L->head_dim != 64 && L->head_dim != 128)
+    return pkv_set_error(PKV_ERR_INVALID, "head_dim must be 64 or 128 (got %d)", L->head_dim);
+  if (L->kv_dtype != PKV_F32 && L->kv_dtype != PKV_BF16)
+    return pkv_set_error(PKV_ERR_INVALID, "kv_dtype must be PKV_F32 or PKV_BF16");
+  return PKV_OK;
+}
+
+struct pkv_pool {
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  pkv_layout layout{};
+  std::vector<int32_t> free_stack;  // top is back()
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t next_id = 0;
+
+  // Undo log of one all-or-nothing operation.
+  enum class Op { Alloc, TablePush, CowSwap, Len };
+  struct Undo {
+    Op op;
+    int64_t seq;
+    int32_t a, b;
+  };
+  std::vector<Undo> log;
+
+  bool valid_block(int32_t b) const { return b >= 0 && b < layout.num_blocks; }
+
+  int alloc(int32_t *out) {
+    if (free_stack.empty()) return pkv_set_error(PKV_ERR_NO_BLOCKS, "no free blocks (pool of %d)", layout.num_blocks);
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    ref[b] = 1;
+    *out = b;
+    return PKV_OK;
+  }
+
+  void rollback() {
+    for (auto it = log.rbegin(); it != log.rend(); ++it) {
+      switch (it->op) {
+        case Op::Alloc:  // popped from the top: push back on top
+          ref[it->a] = 0;
+          free_stack.push_back(it->a);
+          break;
+        case Op::TablePush:
+          seqs[it->seq].table.pop_back();
+          break;
+        case Op::CowSwap:  // table tail went a -> b and a lost one reference
+          seqs[it->seq].table.back() = it->a;
+          ref[it->a] += 1;
+          break;
+        case Op::Len:
+          seqs[it->seq].len = it->a;
+          break;
+      }
+    }
+    log.clear();
+  }
+
+  // Append n tokens to one sequence, logging every change.
+  int append_one(int64_t id, int32_t n, int64_t *slots, int32_t *cow, int32_t cow_cap, int32_t *n_cow) {
+    Seq &s = seqs[id];
+    for (int32_t k = 0; k < n; ++k) {
+      int32_t pos = s.len;
+      if (pos % PKV_BLOCK_SIZE == 0) {
+        int32_t b;
+        if (int rc = alloc(&b)) return rc;
+        log.push_back({Op::Alloc, id, b, 0});
+        s.table.push_back(b);
+        log.push_back({Op::TablePush, id, 0, 0});
+      } else if (ref[s.table.back()] > 1) {
+        if (*n_cow >= cow_cap)
+          return pkv_set_error(PKV_ERR_CAPACITY, "copy-on-write pair buffer too small (cap %d)", cow_cap);
+        int32_t old = s.table.back(), b;
+        if (int rc = alloc(&b)) return rc;
+        log.push_back({Op::Alloc, id, b, 0});
+        ref[old] -= 1;  // stays >= 1: another table still holds it
+        s.table.back() = b;
+        log.push_back({Op::CowSwap, id, old, b});
+        cow[2 * *n_cow] = old;
+        cow[2 * *n_cow + 1] = b;
+        ++*n_cow;
+      }
+      slots[k] = (int64_t)s.table[pos / PKV_BLOCK_SIZE] * PKV_BLOCK_SIZE + pos % PKV_BLOCK_SIZE;
+      log.push_back({Op::Len, id, pos, 0});
+      s.len = pos + 1;
+    }
+    return PKV_OK;
+  }
+};
+
+namespace {
+int need_pool(const pkv_pool *p) { return p ? PKV_OK : pkv_set_error(PKV_ERR_INVALID, "pool is NULL"); }
+}  // namespace
+
+extern "C" int pkv_pool_create(const pkv_layout *layout, const int32_t *free_order, pkv_pool **out) {
+  if (int rc = pkv_check_layout(layout)) return rc;
+  if (!out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
+  const int32_t n = layout->num_blocks;
+  std::vector<int32_t> order(n);
+  if (free_order) {
+    std::vector<char> seen(n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= n || seen[b])
+        return pkv_set_error(PKV_ERR_INVALID, "free_order is not a permutation of [0, %d)", n);
+      seen[b] = 1;
+      order[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < n; ++i) order[i] = i;
+  }
+  pkv_pool *p = new (std::nothrow) pkv_pool();
+  if (!p) return pkv_set_error(PKV_ERR_INVALID, "out of host memory");
+  p->layout = *layout;
+  p->free_stack.assign(order.rbegin(), order.rend());  // first hand-out = order[0]
+  p->ref.assign(n, 0);
+  *out = p;
+  return PKV_OK;
+}
+
+extern "C" int pkv_pool_destroy(pkv_pool *pool) {
+  delete pool;
+  return PKV_OK;
+}
+
+extern "C" int pkv_block_alloc(pkv_pool *pool, int32_t *block_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!block_out) return pkv_set_error(PKV_ERR_INVALID, "block_out is NULL");
+  return pool->alloc(block_out);
+}
+
+extern "C" int pkv_block_incref(pkv_pool *pool, int32_t block) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!pool->valid_block(block)) return pkv_set_error(PKV_ERR_BAD_BLOCK, "block %d out of range", block);
+  if (pool->ref[block] <= 0) return pkv_set_error(PKV_ERR_REFCOUNT, "incref of free block %d", block);
+  pool->ref[block] += 1;
+  return PKV_OK;
+}
+
+extern "C" int pkv_block_free(pkv_pool *pool, int32_t block) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!pool->valid_block(block)) return pkv_set_error(PKV_ERR_BAD_BLOCK, "block %d out of range", block);
+  if (pool->ref[block] <= 0) return pkv_set_error(PKV_ERR_REFCOUNT, "free of free block %d", block);
+  if (--pool->ref[block] == 0) pool->free_stack.push_back(block);
+  return PKV_OK;
+}
+
+extern "C" int pkv_block_refcount(const pkv_pool *pool, int32_t block, int32_t *out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
+  if (!pool->valid_block(block)) return pkv_set_error(PKV_ERR_BAD_BLOCK, "block %d out of range", block);
+  *out = pool->ref[block];
+  return PKV_OK;
+}
+
+extern "C" int pkv_pool_num_free(const pkv_pool *pool, int32_t *out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
+  *out = (int32_t)pool->free_stack.size();
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_create(pkv_pool *pool, int64_t *id_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!id_out) return pkv_set_error(PKV_ERR_INVALID, "id_out is NULL");
+  int64_t id = pool->next_id++;
+  pool->seqs.emplace(id, pkv_pool::Seq{});
+  *id_out = id;
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_fork(pkv_pool *pool, int64_t parent, int64_t *child_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!child_out) return pkv_set_error(PKV_ERR_INVALID, "child_out is NULL");
+  auto it = pool->seqs.find(parent);
+  if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)parent);
+  pkv_pool::Seq child = it->second;  // copy before inserting (rehash safety)
+  for (int32_t b : child.table)
+    if (pool->ref[b] <= 0)
+      return pkv_set_error(PKV_ERR_REFCOUNT, "fork of sequence %lld holding free block %d", (long long)parent, b);
+  for (int32_t b : child.table) pool->ref[b] += 1;
+  int64_t id = pool->next_id++;
+  pool->seqs.emplace(id, std::move(child));
+  *child_out = id;
+  return PKV_OK;
+}
+
+extern "C" int pkv_batch_append_slots(pkv_pool *pool, const int64_t *ids, int32_t num_seqs, int32_t n,
+                                      int64_t *slots_out, int32_t *cow_pairs_out, int32_t cow_cap,
+                                      int32_t *n_cow) {
+  if (int rc = need_pool(pool)) return rc;
+  if (num_seqs < 0 || n < 0) return pkv_set_error(PKV_ERR_INVALID, "negative count");
+  if (num_seqs > 0 && !ids) return pkv_set_error(PKV_ERR_INVALID, "ids is NULL");
+  if ((int64_t)num_seqs * n > 0 && !slots_out) return pkv_set_error(PKV_ERR_INVALID, "slots_out is NULL");
+  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out)) return pkv_set_error(PKV_ERR_INVALID, "bad cow buffer");
+  for (int32_t i = 0; i < num_seqs; ++i)
+    if (!pool->seqs.count(ids[i])) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)ids[i]);
+  int32_t ncow = 0;
+  pool->log.clear();
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    int rc = pool->append_one(ids[i], n, slots_out + (int64_t)i * n, cow_pairs_out, cow_cap, &ncow);
+    if (rc) {
+      pool->rollback();
+      return rc;
+    }
+  }
+  pool->log.clear();
+  if (n_cow) *n_cow = ncow;
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_append_slots(pkv_pool *pool, int64_t id, int32_t n, int64_t *slots_out,
+                                    int32_t *cow_pairs_out, int32_t cow_cap, int32_t *n_cow) {
+  return pkv_batch_append_slots(pool, &id, 1, n, slots_out, cow_pairs_out, cow_cap, n_cow);
+}
+
+extern "C" int pkv_seq_free(pkv_pool *pool, int64_t id) {
+  if (int rc = need_pool(pool)) return rc;
+  auto it = pool->seqs.find(id);
+  if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)id);
+  for (int32_t b : it->second.table)
+    if (pool->ref[b] <= 0)
+      return pkv_set_error(PKV_ERR_REFCOUNT, "free of sequence %lld holding free block %d", (long long)id, b);
+  for (int32_t b : it->second.table)
+    if (--pool->ref[b] == 0) pool->free_stack.push_back(b);
+  pool->seqs.erase(it);
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_len(const pkv_pool *pool, int64_t id, int32_t *len_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!len_out) return pkv_set_error(PKV_ERR_INVALID, "len_out is NULL");
+  auto it = pool->seqs.find(id);
+  if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)id);
+  *len_out = it->second.len;
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_block_table(const pkv_pool *pool, int64_t id, int32_t *out, int32_t cap, int32_t *n_out) {
+  if (int rc = need_pool(pool)) return rc;
+  auto it = pool->seqs.find(id);
+  if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)id);
+  const auto &t = it->second.table;
+  if (n_out) *n_out = (int32_t)t.size();
+  if ((int32_t)t.size() > cap) return pkv_set_error(PKV_ERR_CAPACITY, "table of %zu entries, cap %d", t.size(), cap);
+  if (!t.empty() && !out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
+  std::copy(t.begin(), t.end(), out);
+  return PKV_OK;
+}
+
+extern "C" int pkv_batch_block_tables(const pkv_pool *pool, const int64_t *ids, int32_t num_seqs,
+                                      int32_t max_blocks_per_seq, int32_t *tables_out, int32_t *context_lens_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return pkv_set_error(PKV_ERR_INVALID, "negative count");
+  if (num_seqs > 0 && (!ids || !context_lens_out || (max_blocks_per_seq > 0 && !tables_out)))
+    return pkv_set_error(PKV_ERR_INVALID, "NULL argument");
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = pool->seqs.find(ids[i]);
+    if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)ids[i]);
+    if ((int32_t)it->second.table.size() > max_blocks_per_seq)
+      return pkv_set_error(PKV_ERR_CAPACITY, "sequence %lld holds %zu blocks > %d", (long long)ids[i],
+                           it->second.table.size(), max_blocks_per_seq);
+  }
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const auto &s = pool->seqs.find(ids[i])->second;
+    int32_t *row = tables_out + (int64_t)i * max_blocks_per_seq;
+    std::copy(s.table.begin(), s.table.end(), row);
+    std::fill(row + s.table.size(), row + max_blocks_per_seq, 0);
+    context_lens_out[i] = s.len;
+  }
+  return PKV_OK;
+}
+
+extern "C" int pkv_pool_stats(const pkv_pool *pool, pkv_stats *out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
+  const int32_t n = pool->layout.num_blocks;
+  std::vector<int32_t> fill(n, 0);
+  int64_t logical = 0;
+  for (const auto &kv : pool->seqs) {
+    const auto &s = kv.second;
+    logical += s.len;
+    for (size_t j = 0; j < s.table.size(); ++j) {
+      int32_t f = std::min<int32_t>(PKV_BLOCK_SIZE, s.len - (int32_t)j * PKV_BLOCK_SIZE);
+      fill[s.table[j]] = std::max(fill[s.table[j]], f);
+    }
+  }
+  int64_t stored = 0;
+  int32_t shared = 0;
+  for (int32_t b = 0; b < n; ++b) {
+    stored += fill[b];
+    shared += pool->ref[b] > 1;
+  }
+  out->num_blocks = n;
+  out->num_free = (int32_t)pool->free_stack.size();
+  out->num_used = n - out->num_free;
+  out->num_shared = shared;
+  out->num_seqs = (int64_t)pool->seqs.size();
+  out->tokens_logical = logical;
+  out->tokens_stored = stored;
+  out->usage = (double)out->num_used / n;
+  out->internal_fragmentation = out->num_used ? 1.0 - (double)stored / ((double)out->num_used * PKV_BLOCK_SIZE) : 0.0;
+  return PKV_OK;
+}
+
+extern "C" int64_t pkv_kv_bytes_per_token(const pkv_layout *layout, int32_t num_layers) {
+  if (pkv_check_layout(layout) || num_layers < 0) return 0;
+  return (int64_t)num_layers * 2 * layout->num_kv_heads * layout->head_dim * pkv_elem_bytes(layout->kv_dtype);
+}
+
+extern "C" int64_t pkv_pool_bytes(const pkv_layout *layout) {
+  if (pkv_check_layout(layout)) return 0;
+  return (int64_t)layout->num_blocks * layout->num_kv_heads * PKV_BLOCK_SIZE * layout->head_dim *
+         pkv_elem_bytes(layout->kv_dtype);
+}
+
+extern "C" int pkv_validate_tables(const pkv_layout *layout, const int32_t *tables, const int32_t *context_lens,
+                                   int32_t num_seqs, int32_t max_blocks_per_seq) {
+  if (int rc = pkv_check_layout(layout)) return rc;
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return pkv_set_error(PKV_ERR_INVALID, "negative count");
+  if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !tables)))
+    return pkv_set_error(PKV_ERR_INVALID, "NULL argument");
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    int32_t n = context_lens[i];
+    if (n < 0 || (int64_t)n > (int64_t)PKV_BLOCK_SIZE * max_blocks_per_seq)
+      return pkv_set_error(PKV_ERR_INVALID, "sequence %d: length %d outside [0, %d]", i, n,
+                           PKV_BLOCK_SIZE * max_blocks_per_seq);
+    int32_t nb = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+    for (int32_t j = 0; j < nb; ++j) {
+      int32_t b = tables[(int64_t)i * max_blocks_per_seq + j];
+      if (b < 0 || b >= layout->num_blocks)
+        return pkv_set_error(PKV_ERR_BAD_BLOCK, "sequence %d entry %d: block %d out of range", i, j, b);
+    }
+  }
+  return PKV_OK;
+}

@@ -1,0 +1,158 @@
+"""A paged KV cache on one GPU, driven through the C ABI.
+
+``PagedKVCache`` owns the host block manager (``pkv_pool``) and one K and one
+V pool tensor per layer in HBM; every layer shares the block tables, as in a
+serving engine where the scheduler assigns slots once per step.  All device
+work goes through the library's kernels; torch only allocates memory and
+supplies the stream.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_NAN = {"bf16": 0x7FC0, "f32": float("nan")}
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str, num_layers: int = 1,
+                 free_order=None, device="cuda", fill_nan: bool = True):
+        self.dtype = dtype
+        self.layout = L.make_layout(num_blocks, num_kv_heads, head_dim, dtype)
+        self.pool = L.pkv_pool_create(self.layout, free_order)
+        self.device = torch.device(device)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.k_pools, self.v_pools = [], []
+        for _ in range(num_layers):
+            k = torch.empty(self.layout.pool_elems, dtype=tdt, device=self.device)
+            v = torch.empty_like(k)
+            if fill_nan:  # slots never written hold a NaN sentinel
+                if dtype == "bf16":
+                    k.view(torch.int16).fill_(_NAN["bf16"])
+                    v.view(torch.int16).fill_(_NAN["bf16"])
+                else:
+                    k.fill_(_NAN["f32"])
+                    v.fill_(_NAN["f32"])
+            self.k_pools.append(k)
+            self.v_pools.append(v)
+
+    def close(self):
+        if self.pool is not None:
+            L.pkv_pool_destroy(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- host bookkeeping -----------------------------------------------------
+    def create(self) -> int:
+        return L.pkv_seq_create(self.pool)
+
+    def fork(self, parent: int) -> int:
+        return L.pkv_seq_fork(self.pool, parent)
+
+    def free(self, seq: int):
+        L.pkv_seq_free(self.pool, seq)
+
+    def reserve(self, ids, n: int):
+        """Slots for n more tokens of every sequence in ids (batch order);
+        pending copy-on-write copies run on every layer before returning."""
+        slots, cow = L.pkv_batch_append_slots(self.pool, ids, n, cow_cap=max(1, len(ids)))
+        if len(cow):
+            pairs = torch.from_numpy(np.ascontiguousarray(cow)).to(self.device)
+            for k, v in zip(self.k_pools, self.v_pools):
+                L.pkv_copy_blocks(self.layout, k, v, pairs)
+        return slots, cow
+
+    def tables(self, ids, max_blocks: int):
+        return L.pkv_batch_block_tables(self.pool, ids, max_blocks)
+
+    def stats(self) -> dict:
+        return L.pkv_pool_stats(self.pool)
+
+    # -- device calls ---------------------------------------------------------
+    def write(self, layer: int, slots_dev, k_new, v_new):
+        L.paged_kv_append(self.layout, self.k_pools[layer], self.v_pools[layer], k_new, v_new, slots_dev)
+
+    def decode(self, layer: int, out, q, tables_dev, ctx_dev, max_ctx: int, scale: float, workspace=None,
+               partition_tokens=0, kernel=0, events=None):
+        L.paged_attention_decode(self.layout, out, q, self.k_pools[layer], self.v_pools[layer], tables_dev, ctx_dev,
+                                 max_ctx, scale, workspace, partition_tokens, kernel, events)
+
+    def workspace(self, num_seqs, num_q_heads, max_ctx, partition_tokens=0):
+        nbytes = L.paged_attention_workspace_bytes(self.layout, num_seqs, num_q_heads, max_ctx, partition_tokens)
+        return torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=self.device)
+
+
+def _bits_to_dev(arr: np.ndarray, dtype: str, device):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+class GpuWorkload:
+    """A workload instance built on the GPU path: the instance's build script
+    run through the host block manager, its prefill and decode-step tokens
+    stored by paged_kv_append, and device tables, lengths and query ready for
+    paged_attention_decode."""
+
+    def __init__(self, inst, num_layers: int = 1, device="cuda", extra_blocks: int = 0):
+        wl = inst.wl
+        self.inst, self.wl = inst, wl
+        self.device = torch.device(device)
+        order = np.concatenate([inst.free_order, np.arange(inst.num_blocks, inst.num_blocks + extra_blocks,
+                                                           dtype=np.int32)])
+        self.cache = PagedKVCache(inst.num_blocks + extra_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype,
+                                  num_layers=num_layers, free_order=order, device=device)
+        c = self.cache
+        pre = []
+        if wl.prefix_len:
+            root = c.create()
+            s, _ = c.reserve([root], wl.prefix_len)
+            pre.append(s)
+            self.ids = [root] + [c.fork(root) for _ in range(wl.batch - 1)]
+        else:
+            self.ids = [c.create() for _ in range(wl.batch)]
+        for b, sid in enumerate(self.ids):
+            n = int(inst.own_prefill[b])
+            if n:
+                s, _ = c.reserve([sid], n)
+                pre.append(s)
+        self.prefill_slots = np.concatenate(pre) if pre else np.zeros(0, np.int64)
+        if self.prefill_slots.size:
+            slots_dev = torch.from_numpy(self.prefill_slots).to(self.device)
+            kpre = _bits_to_dev(inst.prefill_tokens("k"), wl.dtype, self.device)
+            vpre = _bits_to_dev(inst.prefill_tokens("v"), wl.dtype, self.device)
+            for layer in range(num_layers):
+                c.write(layer, slots_dev, kpre, vpre)
+            del kpre, vpre
+        self.step_slots, _ = c.reserve(self.ids, 1)
+        self.step_slots_dev = torch.from_numpy(self.step_slots).to(self.device)
+        self.k_step = _bits_to_dev(inst.step_tokens("k"), wl.dtype, self.device)
+        self.v_step = _bits_to_dev(inst.step_tokens("v"), wl.dtype, self.device)
+        for layer in range(num_layers):
+            c.write(layer, self.step_slots_dev, self.k_step, self.v_step)
+        self.max_ctx = int(inst.ctx.max())
+        self.max_blocks = -(-self.max_ctx // 16)
+        tables, ctx = c.tables(self.ids, self.max_blocks)
+        self.tables_host, self.ctx_host = tables, ctx
+        self.tables_dev = torch.from_numpy(tables).to(self.device)
+        self.ctx_dev = torch.from_numpy(ctx).to(self.device)
+        self.q = _bits_to_dev(inst.q(), wl.dtype, self.device)
+        self.scale = 1.0 / math.sqrt(wl.head_dim)
+        self.out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.float32, device=self.device)
+
+    def decode(self, layer=0, partition_tokens=0, kernel=0, events=None, workspace=None, out=None):
+        if workspace is None:
+            workspace = self.cache.workspace(self.wl.batch, self.wl.num_q_heads, self.max_ctx, partition_tokens)
+        out = self.out if out is None else out
+        self.cache.decode(layer, out, self.q, self.tables_dev, self.ctx_dev, self.max_ctx, self.scale, workspace,
+                          partition_tokens, kernel, events)
+        return out

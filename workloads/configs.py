@@ -151,11 +151,18 @@ class Instance:
         return self._cache[key]
 
     def own_kv(self, b: int, which: str) -> np.ndarray:
-        """[ctx[b]-prefix_len][h_kv][d] values of sequence b's private tokens."""
+        """[ctx[b]-prefix_len][h_kv][d] values of sequence b's private tokens
+        (cached: the prefill and the decode step both read them)."""
         w = self.wl
-        n = int(self.ctx[b]) - w.prefix_len
-        a = normal_bits(derive_seed(w.seed, w.name, which, "own", b), (n, w.num_kv_heads, w.head_dim), w.dtype)
-        return self._sinked(a, w.prefix_len)
+        key = ("own", which, b)
+        if key not in self._cache:
+            n = int(self.ctx[b]) - w.prefix_len
+            a = normal_bits(derive_seed(w.seed, w.name, which, "own", b), (n, w.num_kv_heads, w.head_dim), w.dtype)
+            self._cache[key] = self._sinked(a, w.prefix_len)
+        return self._cache[key]
+
+    def drop_cache(self):
+        self._cache.clear()
 
     def seq_kv(self, b: int, which: str) -> np.ndarray:
         """[ctx[b]][h_kv][d] logical K or V of sequence b (all its tokens)."""
