@@ -1,0 +1,284 @@
+"""Paged decode attention benchmark on one MI355X.
+
+One step is one pass of the whole decode path for a batch: the host block
+manager assigns every sequence its next token slot (taking a fresh block at a
+16-token boundary), the slots, block tables and lengths go to HBM in one
+pinned host-to-device copy, and then for every layer the new token's K/V are
+stored (paged_kv_append) and attention runs over the whole paged context
+(paged_attention_decode: partition kernel plus split-context merge).  Layers
+have their own K/V pools and share the block tables; several layers are run
+per step so that the bytes read per step exceed the 256 MB Infinity Cache.
+
+Prints one JSON line: KV GB/s of the whole step (inputs resident in HBM), the
+roofline of the partition kernel from HIP events recorded around it on the
+launch stream, and the CPU oracle timed on the host on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
+MODEL_LAYERS = {"llama3_8b_b64": 32, "llama3_70b_b256": 80, "shared_prefix_b128": 32, "best_of_8": 32,
+                "mha_long": 32, "tiny_fp32": 1}
+PARTITION_KERNELS = ("decode_mfma_kernel", "decode_valu_kernel")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded, so the
+    library can record them between its own launches."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, rc
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the partition kernels' sources: a stored traffic measurement
+    only applies while these are unchanged."""
+    h = hashlib.sha256()
+    for f in ("decode_mfma.hip", "decode_valu.hip", "pkv_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_381_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per partition-kernel launch from the committed PMC summary,
+    or None when there is none for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inst, min_seconds: float):
+    """The oracle (fp64 C, OpenMP) on the host: the decode step's append and
+    attention over the whole batch, repeated for at least min_seconds."""
+    import numpy as np
+    from oracle import attn as orc
+    from oracle.book import build_workload
+
+    wl = inst.wl
+    book, ids, pre_slots, step_slots, _ = build_workload(inst)
+    kpool, vpool = orc.new_pool(inst.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
+    orc.append(wl.dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, inst.prefill_tokens("k"),
+               inst.prefill_tokens("v"), np.asarray(pre_slots, np.int64))
+    tables, ctx = orc.tables_of(book, ids)
+    kstep, vstep, q = inst.step_tokens("k"), inst.step_tokens("v"), inst.q()
+    slots = np.asarray(step_slots, np.int64)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.append(wl.dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, kstep, vstep, slots)
+        orc.paged_attention(wl.dtype, q, kpool, vpool, tables, ctx, wl.num_kv_heads, scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    per_step = dt / reps
+    return {"value": round(inst.kv_bytes_logical() / per_step / 1e9, 4), "unit": "GB/s",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"full {wl.name} decode step (append + fp64 attention over all {wl.batch} sequences, "
+                      f"{int(inst.ctx.sum())} tokens), {reps} repetition(s) in {dt:.1f} s, "
+                      f"{per_step * 1e3:.1f} ms per step; OMP threads = {orc.num_threads()}, "
+                      f"host cores = {os.cpu_count()}"}
+
+
+def copy_probe(gib: float, reps: int):
+    """Plain device-to-device copies of a known size (PMC calibration)."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_b64")
+    ap.add_argument("--layers", type=int, default=0, help="layers per step (0: enough to read >= 1 GiB)")
+    ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0: library default)")
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 wavefront-reduction, 2 matrix-core")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="run only plain 1 GiB copies (PMC calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "sequences or kv heads would shard across GPUs with no exchange.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(1.0, 10)
+        return
+
+    import workloads
+    from paged_kv_cache_381_amd import _lib as L
+    from paged_kv_cache_381_amd.engine import GpuWorkload
+
+    inst = workloads.get(args.workload)
+    wl = inst.wl
+    B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
+    K, W = args.steps, args.warmup
+    tok_bytes = 2 * H * D * wl.elem_bytes  # K and V of one token, one layer
+    layers = args.layers or max(1, math.ceil((1 << 30) / inst.kv_bytes_logical()))
+    total_steps = K + W
+    extra = B * (total_steps // 16 + 2)
+    print(f"[bench] building {wl.name}: B={B} Hq={Hq} H={H} D={D} {wl.dtype}, layers/step={layers}", flush=True)
+    gw = GpuWorkload(inst, num_layers=layers, extra_blocks=extra)
+    inst.drop_cache()
+    cache, ids = gw.cache, np.asarray(gw.ids, np.int64)
+    MB = -(-(int(inst.ctx.max()) + total_steps + 1) // 16)
+    ws = cache.workspace(B, Hq, MB * 16, args.partition)
+    dev = torch.device("cuda")
+    R = 4
+    slots_pin = [torch.empty(B, dtype=torch.int64, pin_memory=True) for _ in range(R)]
+    tables_pin = [torch.empty(B * MB, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    ctx_pin = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    ring_ev = [torch.cuda.Event() for _ in range(R)]
+    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
+    d_tables = torch.empty(B, MB, dtype=torch.int32, device=dev)
+    d_ctx = torch.empty(B, dtype=torch.int32, device=dev)
+    k_new, v_new = gw.k_step, gw.v_step
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    hip = HipEvents()
+    evs = hip.create(2 * K * layers)
+    torch.cuda.synchronize()
+
+    def step(k: int, timed_idx: int):
+        r = k % R
+        ring_ev[r].synchronize()  # the copy that last read this pinned set is done
+        L.pkv_batch_append_slots(cache.pool, ids, 1, slots_out=slots_pin[r].numpy())
+        L.pkv_batch_block_tables(cache.pool, ids, MB, tables_pin[r].numpy().reshape(B, MB), ctx_pin[r].numpy())
+        ctx_np = ctx_pin[r].numpy()
+        max_ctx = int(ctx_np.max())
+        d_slots.copy_(slots_pin[r], non_blocking=True)
+        d_tables.view(-1).copy_(tables_pin[r], non_blocking=True)
+        d_ctx.copy_(ctx_pin[r], non_blocking=True)
+        ring_ev[r].record()
+        for layer in range(layers):
+            ev = None
+            if timed_idx >= 0:
+                i = 2 * (timed_idx * layers + layer)
+                ev = (evs[i], evs[i + 1], None)
+            cache.write(layer, d_slots, k_new, v_new)
+            cache.decode(layer, out, gw.q, d_tables, d_ctx, max_ctx, gw.scale, ws, args.partition, args.kernel, ev)
+        return int(ctx_np.astype(np.int64).sum())
+
+    for k in range(W):
+        step(k, -1)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({W} steps), timing {K} steps", flush=True)
+    ctx_tokens = []
+    t0 = time.perf_counter()
+    for k in range(K):
+        ctx_tokens.append(step(W + k, k))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    assert torch.isfinite(out).all().item(), "non-finite attention output"
+
+    kv_bytes = sum(ctx_tokens) * tok_bytes * layers
+    gbps = kv_bytes / elapsed / 1e9
+    ms_step = elapsed / K * 1e3
+    durs = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(K * layers)]
+    hip.destroy(evs)
+    avg_ms = sum(durs) / len(durs)
+    bytes_per_launch = sum(ctx_tokens) / K * tok_bytes
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    traffic = stored_traffic(wl.name)
+    per_layer_s = elapsed / K / layers
+    print(f"[bench] {K} steps in {elapsed:.3f} s; partition kernel avg {avg_ms * 1e3:.1f} us "
+          f"({achieved:.0f} GB/s)", flush=True)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.description, "name": wl.name, "batch": B, "num_q_heads": Hq,
+                   "num_kv_heads": H, "head_dim": D, "block_size": 16, "layers_per_step": layers,
+                   "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
+                   "partition_tokens": args.partition or 512, "kernel": args.kernel, "parallelism": "none"},
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s_per_layer": round(B / per_layer_s, 1),
+        "decode_tokens_per_s_attention_full_depth": round(B / (per_layer_s * MODEL_LAYERS.get(wl.name, 32)), 1),
+        "roofline": {"kernel": "paged_attention_decode partition kernel", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del gw, cache
+        torch.cuda.empty_cache()
+        print("[bench] timing the CPU oracle", flush=True)
+        res["cpu_baseline"] = cpu_baseline(workloads.get(args.workload), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
