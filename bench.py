@@ -183,7 +183,7 @@ def main():
     inst.drop_cache()
     cache, ids = gw.cache, np.asarray(gw.ids, np.int64)
     MB = -(-(int(inst.ctx.max()) + total_steps + 1) // 16)
-    ws = cache.workspace(B, Hq, MB * 16, args.partition)
+    ws = cache.workspace(B, Hq, MB * 16, args.partition, args.kernel)
     dev = torch.device("cuda")
     R = 4
     slots_pin = [torch.empty(B, dtype=torch.int64, pin_memory=True) for _ in range(R)]

@@ -192,17 +192,22 @@ int pkv_copy_blocks(const pkv_layout *layout, void *k_pool, void *v_pool, const 
 
 /* Decode options (all fields may be zero / NULL for defaults). */
 typedef struct {
-  int32_t partition_tokens; /* tokens per split-context partition: a positive
-                               multiple of 32, or 0 for the default (512) */
-  int32_t kernel;           /* 0 auto; 1 the wavefront-reduction kernel;
-                               2 the matrix-core kernel (bf16, 2 <= G <= 16) */
+  int32_t partition_tokens; /* a positive multiple of 32, or 0 for the default.
+                               Matrix-core kernel: the fewest context tokens one
+                               wave is given by the balanced split (default 128).
+                               Wavefront-reduction kernel: tokens per
+                               split-context partition (default 512). */
+  int32_t kernel;           /* 0 auto (matrix cores for bf16 with G >= 4);
+                               1 the wavefront-reduction kernel;
+                               2 the matrix-core kernel (bf16, G <= 16,
+                               at most 8192 sequences) */
   void *ev_begin;           /* optional hipEvent_t recorded before the first kernel */
   void *ev_partition_done;  /* optional hipEvent_t recorded after the partition kernel */
   void *ev_end;             /* optional hipEvent_t recorded after the last kernel */
 } pkv_decode_opts;
 
-/* Bytes of workspace paged_attention_decode needs (0 when no sequence can
- * span more than one partition).  opts may be NULL. */
+/* Bytes of workspace paged_attention_decode needs for these sizes and
+ * options (0 when the call needs none).  opts may be NULL. */
 size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seqs,
                                        int32_t num_q_heads, int32_t max_context_len,
                                        const pkv_decode_opts *opts);
@@ -222,7 +227,13 @@ size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seq
  *   workspace: device scratch of paged_attention_workspace_bytes() bytes
  *   (may be NULL when that is 0); its contents are not preserved.
  * Requires num_q_heads % num_kv_heads == 0, G = num_q_heads / num_kv_heads
- * <= 16, D in {64, 128}, max_context_len <= 16 * max_blocks_per_seq. */
+ * <= 16, D in {64, 128}, max_context_len <= min(16 * max_blocks_per_seq, 2^22).
+ * Work split: the matrix-core kernel runs a persistent grid in which every
+ * wave takes an equal share of the batch's 32-token chunks whatever the mix
+ * of context lengths; contexts cut between waves are combined by a merge
+ * kernel (log-sum-exp of the partial maxima, sums and outputs).  The
+ * wavefront-reduction kernel cuts every context into fixed partitions merged
+ * the same way. */
 int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
                            const void *v_pool, const int32_t *d_block_tables,
                            const int32_t *d_context_lens, int32_t num_seqs, int32_t num_q_heads,

@@ -155,9 +155,15 @@ class Book:
 
     def free_seq(self, sid: int):
         s = self._seq(sid)
-        for blk in s["table"]:  # refuse a corrupt table before changing anything
-            if self.ref[blk] <= 0:
-                raise BookError("REFCOUNT", f"free of a sequence holding free block {blk}")
+        # Refuse before changing anything when some block has fewer references
+        # than the table holds it (possible only after a caller freed a block
+        # the sequence still held): the release is all or nothing.
+        held = {}
+        for blk in s["table"]:
+            held[blk] = held.get(blk, 0) + 1
+        for blk, k in held.items():
+            if self.ref[blk] < k:
+                raise BookError("REFCOUNT", f"free of a sequence holding block {blk} {k} times, refcount {self.ref[blk]}")
         for blk in s["table"]:
             self.decref(blk)
         del self.seqs[sid]

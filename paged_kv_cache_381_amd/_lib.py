@@ -317,8 +317,9 @@ def decode_opts(partition_tokens=0, kernel=0, events=None) -> pkv_decode_opts:
     return pkv_decode_opts(int(partition_tokens), int(kernel), *[e if e else None for e in ev])
 
 
-def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, partition_tokens=0) -> int:
-    o = decode_opts(partition_tokens)
+def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, partition_tokens=0,
+                                    kernel=0) -> int:
+    o = decode_opts(partition_tokens, kernel)
     return lib().paged_attention_workspace_bytes(ctypes.byref(layout), int(num_seqs), int(num_q_heads),
                                                  int(max_context_len), ctypes.byref(o))
 
@@ -334,7 +335,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
     mb = block_tables.shape[1]
-    ws_need = paged_attention_workspace_bytes(layout, B, Hq, max_context_len, partition_tokens)
+    ws_need = paged_attention_workspace_bytes(layout, B, Hq, max_context_len, partition_tokens, kernel)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace")

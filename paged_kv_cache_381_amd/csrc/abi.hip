@@ -2,6 +2,7 @@
 // sizing and kernel dispatch.  See include/pagedkv.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -37,6 +38,36 @@ int32_t num_partitions(int32_t max_ctx, int32_t part) {
   return np < 1 ? 1 : np;
 }
 
+// Kernel a call runs: 1 wavefront reductions, 2 matrix cores (bf16, G >= 4
+// by default).
+int choose_kernel(const pkv_layout *L, int32_t G, const pkv_decode_opts *opts) {
+  const int k = opts ? opts->kernel : 0;
+  if (k != 0) return k;
+  return (L->kv_dtype == PKV_BF16 && G >= 4) ? 2 : 1;
+}
+
+// Partial slots per (sequence, query head) of the balanced split: a segment
+// of at most ceil(max_ctx / 32) chunks overlaps at most ceil(that / min_cpw) + 1
+// wave shares, since every share holds at least min_cpw chunks.
+int32_t split_maxp(int32_t max_ctx, int32_t min_cpw) {
+  const int32_t chunks = (max_ctx + PKV_CHUNK - 1) / PKV_CHUNK;
+  return (chunks + min_cpw - 1) / min_cpw + 1;
+}
+
+size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Workspace of the balanced split: partial outputs, partial (m, l), header.
+size_t split_ws_bytes(const pkv_layout *L, int32_t B, int32_t Hq, int32_t maxp) {
+  const size_t rows = (size_t)B * Hq * maxp;
+  return align16(rows * L->head_dim * sizeof(float)) + align16(rows * 2 * sizeof(float)) +
+         align16((size_t)(2 + B) * sizeof(int32_t));
+}
+
+// Fewest chunks per wave of the balanced split, from opts->partition_tokens.
+int min_chunks(const pkv_decode_opts *opts) {
+  return (opts && opts->partition_tokens > 0) ? opts->partition_tokens / PKV_CHUNK : PKV_DEFAULT_MIN_CHUNKS;
+}
+
 }  // namespace
 
 extern "C" int paged_kv_append(const pkv_layout *layout, void *k_pool, void *v_pool, const void *k_new,
@@ -68,11 +99,48 @@ extern "C" int pkv_copy_blocks(const pkv_layout *layout, void *k_pool, void *v_p
   return PKV_OK;
 }
 
+int pkv_split_grid(const void *kernel, int block_threads, size_t lds_bytes, const pkv_decode_args &a, int *nwg) {
+  struct Occ {
+    const void *kernel;
+    int device;
+    size_t lds;
+    int per_cu;
+    int cus;
+  };
+  static thread_local Occ cache[8] = {};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return (int)e;
+  Occ *hit = nullptr;
+  for (Occ &c : cache)
+    if (c.kernel == kernel && c.device == dev && c.lds == lds_bytes) hit = &c;
+  if (!hit) {
+    Occ o{kernel, dev, lds_bytes, 0, 0};
+    if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.per_cu, kernel, block_threads, lds_bytes))
+      return (int)e;
+    if (hipError_t e = hipDeviceGetAttribute(&o.cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
+    for (int i = 7; i > 0; --i) cache[i] = cache[i - 1];
+    cache[0] = o;
+    hit = &cache[0];
+  }
+  const int waves_per_wg = block_threads / 64;
+  int64_t grid = (int64_t)std::max(1, hit->per_cu) * std::max(1, hit->cus);
+  // No more workgroups than the largest possible batch of chunks can feed.
+  const int64_t max_chunks = (int64_t)a.num_seqs * a.L->num_kv_heads * ((a.max_ctx + PKV_CHUNK - 1) / PKV_CHUNK);
+  const int64_t need = (max_chunks + (int64_t)a.min_cpw * waves_per_wg - 1) / ((int64_t)a.min_cpw * waves_per_wg);
+  grid = std::min(grid, std::max<int64_t>(need, 1));
+  *nwg = (int)((grid + 7) & ~(int64_t)7);
+  return 0;
+}
+
+
 extern "C" size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seqs, int32_t num_q_heads,
                                                   int32_t max_context_len, const pkv_decode_opts *opts) {
   if (pkv_check_layout(layout) || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
+  if (num_q_heads % layout->num_kv_heads) return 0;
   int32_t part;
   if (partition_tokens(opts, &part)) return 0;
+  if (choose_kernel(layout, num_q_heads / layout->num_kv_heads, opts) == 2)
+    return split_ws_bytes(layout, num_seqs, num_q_heads, split_maxp(max_context_len, min_chunks(opts)));
   const int32_t np = num_partitions(max_context_len, part);
   if (np <= 1) return 0;
   return (size_t)num_seqs * num_q_heads * np * (layout->head_dim + 2) * sizeof(float);
@@ -105,11 +173,15 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
     return pkv_set_error(PKV_ERR_INVALID, "paged_attention_decode: q and pools must be 16-byte aligned");
   int32_t part;
   if (int rc = partition_tokens(opts, &part)) return rc;
-  int kernel = opts ? opts->kernel : 0;
-  if (kernel == 0) kernel = (layout->kv_dtype == PKV_BF16 && G >= 4) ? 2 : 1;
+  const int kernel = choose_kernel(layout, G, opts);
   if (kernel != 1 && kernel != 2) return pkv_set_error(PKV_ERR_INVALID, "unknown kernel %d", kernel);
   if (kernel == 2 && layout->kv_dtype != PKV_BF16)
     return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16 cache");
+  if (kernel == 2 && num_seqs > PKV_MAX_SPLIT_SEQS)
+    return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel takes at most %d sequences (got %d)",
+                         PKV_MAX_SPLIT_SEQS, num_seqs);
+  if (max_context_len > (1 << 22))
+    return pkv_set_error(PKV_ERR_INVALID, "max_context_len %d exceeds %d", max_context_len, 1 << 22);
 
   const int32_t np = num_partitions(max_context_len, part);
   const size_t need = paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, opts);
@@ -132,15 +204,28 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   a.part_tokens = part;
   a.num_parts = np;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.ws_o = need ? static_cast<float *>(workspace) : nullptr;
-  a.ws_ml = need ? static_cast<float *>(workspace) + (size_t)num_seqs * num_q_heads * np * layout->head_dim : nullptr;
   a.stream = stream;
+  if (kernel == 2) {
+    a.min_cpw = min_chunks(opts);
+    a.maxp = split_maxp(max_context_len, a.min_cpw);
+    const size_t rows = (size_t)num_seqs * num_q_heads * a.maxp;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_o = reinterpret_cast<float *>(ws);
+    a.ws_ml = reinterpret_cast<float *>(ws + align16(rows * layout->head_dim * sizeof(float)));
+    a.ws_hdr = reinterpret_cast<int32_t *>(ws + align16(rows * layout->head_dim * sizeof(float)) +
+                                           align16(rows * 2 * sizeof(float)));
+  } else {
+    a.ws_o = need ? static_cast<float *>(workspace) : nullptr;
+    a.ws_ml = need ? static_cast<float *>(workspace) + (size_t)num_seqs * num_q_heads * np * layout->head_dim : nullptr;
+  }
 
   if (int rc = record(opts ? opts->ev_begin : nullptr, stream)) return rc;
   const int rc = kernel == 2 ? pkv_launch_decode_mfma(a) : pkv_launch_decode_valu(a);
   if (rc) return hip_fail(rc, "decode partition kernel launch");
   if (int r = record(opts ? opts->ev_partition_done : nullptr, stream)) return r;
-  if (np > 1) {
+  if (kernel == 2) {
+    if (int r2 = pkv_launch_merge_split(a)) return hip_fail(r2, "merge kernel launch");
+  } else if (np > 1) {
     if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
   }
   return record(opts ? opts->ev_end : nullptr, stream);

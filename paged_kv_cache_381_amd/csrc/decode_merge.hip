@@ -45,3 +45,58 @@ int pkv_launch_merge(const pkv_decode_args &a) {
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   return (int)hipGetLastError();
 }
+
+// Merge of the balanced split (decode_mfma.hip): the partials of segment
+// (g, b) are the waves whose shares overlap the segment's chunks, stored in
+// share order.  The schedule header written by the partition kernel gives the
+// chunk scan and the number of waves used, from which both the segment's
+// position and its first and last wave follow exactly as in the partition
+// kernel.  Segments held by one wave, and empty sequences, were written by the
+// partition kernel.
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(64) void merge_split_kernel(SplitParams P) {
+  const int bh = blockIdx.x;
+  const int b = bh / P.Hq, h = bh - b * P.Hq, g = h / P.G;
+  const int64_t c_tot = (int64_t)P.H * P.ws_hdr[0];
+  const int nwe = P.ws_hdr[1];
+  const int32_t *s_incl = P.ws_hdr + 2;
+  const int cnt = s_incl[b] - (b ? s_incl[b - 1] : 0);
+  if (cnt == 0 || c_tot == 0) return;
+  const int64_t seg0 = (int64_t)g * P.ws_hdr[0] + (s_incl[b] - cnt);
+  const int w0 = wave_of(seg0, c_tot, nwe), w1 = wave_of(seg0 + cnt - 1, c_tot, nwe);
+  const int np = min(w1 - w0 + 1, P.maxp);
+  if (np <= 1) return;
+  const size_t row = (size_t)bh * P.maxp;
+  const float2 *ml = reinterpret_cast<const float2 *>(P.ws_ml) + row;
+  const float *o = P.ws_o + row * D;
+  float M = -INFINITY;
+  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[i].x);
+  float L = 0.f;
+  float acc[D / 64];
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
+  for (int i = 0; i < np; ++i) {
+    const float2 mi = ml[i];
+    const float f = fast_exp2(mi.x - M);
+    L += mi.y * f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) acc[k] += o[(size_t)i * D + 64 * k + threadIdx.x] * f;
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) P.out[(size_t)bh * D + 64 * k + threadIdx.x] = acc[k] * inv;
+}
+
+}  // namespace
+
+int pkv_launch_merge_split(const pkv_decode_args &a) {
+  const SplitParams p = pkv_split_params(a);
+  dim3 grid(a.num_seqs * a.num_q_heads);
+  if (a.L->head_dim == 128)
+    hipLaunchKernelGGL(merge_split_kernel<128>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+  else
+    hipLaunchKernelGGL(merge_split_kernel<64>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+  return (int)hipGetLastError();
+}

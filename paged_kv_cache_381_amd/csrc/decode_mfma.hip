@@ -1,31 +1,41 @@
-// PagedAttention decode, matrix-core kernel (bf16 KV, one GQA group per
-// workgroup).
+// PagedAttention decode, matrix-core kernel (bf16 KV, grouped-query heads).
 //
 // What it computes [KV Cache 工程学 §15.5; 新一代 KV Cache 管理 §8.1]: for a
 // sequence b and its query heads h of kv group g, the new token's query is
 // dotted with the K of every cached token, found by reading block-table entry
 // j/16 and slot j%16; a softmax over the whole context weights the cached V.
-// The context is cut into partitions of part_tokens tokens; each workgroup
-// handles one (partition, kv head, sequence) and keeps a running maximum and
-// sum (online softmax), so the softmax stays global even though the data is
-// visited block by block (the per-page softmax of the vendor article
+// The context is visited 32 tokens at a time with a running maximum and sum
+// (online softmax), so the softmax stays global even though the data arrive
+// block by block (the per-page softmax of the vendor article
 // [PagedAttention：大模型KV Cache内存管理革新 §3.2] is not used).
+//
+// Work split.  Persistent waves each take one equal, contiguous share of the
+// batch's 32-token chunks (pkv_device.h, "Balanced split"): the mix of
+// context lengths does not leave a tail of long sequences running alone.
+// Within its share a wave walks (sequence, kv head) segments in order; a
+// segment it holds entirely is normalised and stored, a segment cut by a share
+// boundary leaves a partial (m, l, o) for the merge kernel.
 //
 // gfx950 mapping.  The G query heads of a group share every K and V tile, so
 // the group-by-block products are small dense contractions and run on
 // v_mfma_f32_16x16x32_bf16, with the G heads padded to 16 columns:
 //   S^T[32 tokens x 16 heads] = K[32 x D] . Q^T[D x 16]   (two 16-row MFMAs)
 //   O^T[D x 16 heads]        += V^T[D x 32] . P^T[32 x 16] (D/16 MFMAs)
-// One wave consumes a chunk of two 16-token blocks (32 tokens) per step.
-// Lane (c = lane%16, j = lane/16) receives S for head c and tokens
-// {8(j%2) + 0..3} (first MFMA) and {8(j%2) + 4..7} (second MFMA) of block
-// j/2 -- exactly the eight token slots it must hand to the PV MFMA, whose V^T
-// operand for lane (d, j) is then 16 contiguous bytes of the [D][16] V tile
-// (tokens 8(j%2)..+7 of block j/2).  No cross-lane shuffle sits between the
-// two contractions; the softmax needs only two xor-shuffles per chunk (max
-// over the four lane groups).  The Q rows of the group are staged once in LDS
-// and read into MFMA operands by every wave; the W waves of a workgroup split
-// the partition's chunks and are merged through LDS at the end.
+// A chunk is two 16-token blocks.  Lane (c = lane%16, j = lane/16) receives S
+// for head c and tokens {8(j%2) + 0..3} (first MFMA) and {8(j%2) + 4..7}
+// (second MFMA) of block j/2 -- exactly the eight token slots it must hand to
+// the PV MFMA, whose V^T operand for lane (d, j) is then 16 contiguous bytes
+// of the [D][16] V tile (tokens 8(j%2)..+7 of block j/2).  No cross-lane
+// shuffle sits between the two contractions; the softmax needs only two
+// xor-shuffles per chunk (max over the four lane groups).  Each lane holds the
+// 8-element slices of the group's query rows that its B operand needs, read
+// straight from memory once per segment: the whole group shares them through
+// the MFMA, and nothing else in the wave would reuse an LDS copy.
+//
+// Memory pipeline.  Block ids and lengths are scalar loads issued one chunk
+// ahead; chunk c+1's K is requested as soon as chunk c's score MFMAs have
+// consumed the K registers and its V once the PV MFMAs have consumed V, so a
+// wave always has a chunk of loads in flight through its own math.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -44,85 +54,168 @@ __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+#ifndef PKV_MFMA_MIN_WAVES_PER_SIMD
+#define PKV_MFMA_MIN_WAVES_PER_SIMD 1
+#endif
+
+// Position of a wave in the chunk list: sequence b, kv head g, chunk j of the
+// segment, the segment's chunk count and length, and the flattened index of
+// the segment's first chunk.  All wave-uniform (SGPRs).
+struct Cursor {
+  int b, g, j, cnt, n;
+  int64_t seg0;
+};
+
 template <int D, int W>
-__global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeParams P) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_MIN_WAVES_PER_SIMD)))
+void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
-  constexpr int CPR = D / 8;   // 16-byte K chunks per token (8 bf16 each)
-  extern __shared__ __align__(16) char smem[];
-  uint4 *q_lds = reinterpret_cast<uint4 *>(smem);                  // [16][CPR]
-  float *red_m = reinterpret_cast<float *>(smem + 16 * CPR * 16);  // [W][16]
-  float *red_l = red_m + W * 16;                                    // [W][16]
-  float *red_o = red_l + W * 16;                                    // [W][G][D]
+  constexpr int TILE = 16 * D;
+  extern __shared__ __align__(16) int32_t s_incl[];  // [B] inclusive chunk scan, then [W] scratch
+  int32_t *s_wave = s_incl + P.B;
 
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int G = P.G;
-  const int n = clamp_len(P.ctx[b], P.max_blocks, P.max_ctx);
-  const int t0 = part * P.part_tokens;
-  float *out_bg = P.out + ((size_t)b * P.Hq + (size_t)g * G) * D;
-  if (n == 0) {
-    if (part == 0)
-      for (int i = tid; i < G * D; i += 64 * W) out_bg[i] = 0.f;
-    return;
-  }
-  if (t0 >= n) return;
-  const int t1 = min(t0 + P.part_tokens, n);
-  const int nchunks = (t1 - t0 + 31) >> 5;
-  const int nparts_b = (n + P.part_tokens - 1) / P.part_tokens;
+  const int H = P.H, G = P.G, B = P.B;
+  const int64_t c_seq = scan_chunks<W>(P, s_incl, s_wave);
+  const int64_t c_tot = (int64_t)H * c_seq;
+  const int nwg = gridDim.x;
+  const int nwe = waves_used(c_tot, nwg * W, P.min_cpw);
 
-  const uint16_t *qg = reinterpret_cast<const uint16_t *>(P.q) + ((size_t)b * P.Hq + (size_t)g * G) * D;
-  for (int i = tid; i < 16 * CPR; i += 64 * W) {
-    const int h = i / CPR, c = i - h * CPR;
-    q_lds[i] = h < G ? *reinterpret_cast<const uint4 *>(qg + (size_t)h * D + c * 8) : make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0) {
+    // Header for the merge kernel, and zeros for empty sequences.
+    if (tid == 0) {
+      P.ws_hdr[0] = (int32_t)c_seq;
+      P.ws_hdr[1] = nwe;
+    }
+    for (int i = tid; i < B; i += 64 * W) P.ws_hdr[2 + i] = s_incl[i];
+    for (int b = 0; b < B; ++b) {
+      const int prev = b ? s_incl[b - 1] : 0;
+      if (s_incl[b] == prev)
+        for (int i = tid; i < P.Hq * D; i += 64 * W) P.out[(size_t)b * P.Hq * D + i] = 0.f;
+    }
   }
-  __syncthreads();
+
+  const int wave = uniform(xcd_logical(blockIdx.x, nwg) * W + w);
+  if (wave >= nwe || c_tot == 0) return;
+  const int64_t lo = (int64_t)wave * c_tot / nwe, hi = (int64_t)(wave + 1) * c_tot / nwe;
+  if (lo >= hi) return;
+
+  auto cnt_of = [&](int b) { return uniform(s_incl[b] - (b ? s_incl[b - 1] : 0)); };
+  auto len_of = [&](int b) { return clamp_len(sload_i32(P.ctx + b), P.max_blocks, P.max_ctx); };
+
+  // Locate the share's first chunk: kv head lo / c_seq, then the first
+  // sequence whose chunks end past the remainder.
+  Cursor cur;
+  {
+    cur.g = (int)(lo / c_seq);
+    const int rem = (int)(lo - (int64_t)cur.g * c_seq);
+    int a = 0, z = B - 1;
+    while (a < z) {
+      const int mid = (a + z) >> 1;
+      if (uniform(s_incl[mid]) > rem) z = mid; else a = mid + 1;
+    }
+    cur.b = a;
+    cur.cnt = cnt_of(a);
+    const int excl = uniform(s_incl[a]) - cur.cnt;
+    cur.j = rem - excl;
+    cur.n = len_of(a);
+    cur.seg0 = (int64_t)cur.g * c_seq + excl;
+  }
+  // Next chunk in list order; segments are contiguous in the list, so the
+  // next segment starts where this one ends.
+  auto advance = [&](Cursor c) {
+    if (++c.j < c.cnt) return c;
+    c.j = 0;
+    c.seg0 += c.cnt;
+    do {
+      if (++c.b == B) {
+        c.b = 0;
+        ++c.g;
+      }
+    } while (cnt_of(c.b) == 0);
+    c.cnt = cnt_of(c.b);
+    c.n = len_of(c.b);
+    return c;
+  };
+  // Physical blocks of a chunk (the second one only if it holds tokens).
+  auto blocks_of = [&](const Cursor &c, int &pa, int &pb) {
+    const int32_t *row = P.tables + (size_t)c.b * P.max_blocks + 2 * c.j;
+    pa = clamp_block(sload_i32(row), P.num_blocks);
+    pb = (32 * c.j + 16 < c.n) ? clamp_block(sload_i32(row + 1), P.num_blocks) : pa;
+  };
 
   const int r16 = lane & 15, grp = lane >> 4;
-  bf16x8_t qb[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) qb[kk] = as_bf16x8(q_lds[r16 * CPR + 4 * kk + grp]);
-
   // Row r16 of the score MFMAs holds a token of block (r16 >> 3); see header.
   const int ksel = r16 >> 3;
   const int ktx = ((r16 >> 2) & 1) * 8 + (r16 & 3);
   const int vsel = grp >> 1, vhalf = grp & 1;
 
-  f32x4_t o[NNN];
-#pragma unroll
-  for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-
-  const int32_t *tbl = P.tables + (size_t)b * P.max_blocks;
   const uint16_t *kpool = reinterpret_cast<const uint16_t *>(P.k_pool);
   const uint16_t *vpool = reinterpret_cast<const uint16_t *>(P.v_pool);
-  constexpr size_t TILE = (size_t)16 * D;
+  const uint16_t *qbase = reinterpret_cast<const uint16_t *>(P.q);
+  bf16x8_t qb[NKK];
+  uint4 ax[NKK], ay[NKK], va[NNN];
 
-  for (int ch = w; ch < nchunks; ch += W) {
-    const int tok0 = t0 + ch * 32;
-    const int jA = tok0 >> 4;
-    const int physA = clamp_block(tbl[jA], P.num_blocks);
-    const int physB = (tok0 + 16 < n) ? clamp_block(tbl[jA + 1], P.num_blocks) : physA;
-    const size_t tA = ((size_t)physA * P.H + g) * TILE, tB = ((size_t)physB * P.H + g) * TILE;
-    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + (ksel ? tB : tA));
-    const uint4 *vt = reinterpret_cast<const uint4 *>(vpool + (vsel ? tB : tA));
-
-    uint4 ax[NKK], ay[NKK], va[NNN];
+  auto load_q = [&](const Cursor &c) {
+    // Columns G..15 of the B operand are zero; their lanes read row G-1 (in
+    // bounds) and discard it.
+    const int h = min(r16, G - 1);
+    const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + h) * D);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint4 u = qr[4 * kk + grp];
+      qb[kk] = as_bf16x8(r16 < G ? u : make_uint4(0, 0, 0, 0));
+    }
+  };
+  auto load_k = [&](int g, int pa, int pb) {
+    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb : pa) * H + g) * TILE);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int c = 4 * kk + grp;
       ax[kk] = kt[c * 16 + ktx];
       ay[kk] = kt[c * 16 + ktx + 4];
     }
+  };
+  auto load_v = [&](int g, int pa, int pb) {
+    const uint4 *vt = reinterpret_cast<const uint4 *>(vpool + ((size_t)(vsel ? pb : pa) * H + g) * TILE);
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) va[nn] = vt[2 * (16 * nn + r16) + vhalf];
+  };
 
+  int pa, pb;
+  blocks_of(cur, pa, pb);
+  load_q(cur);
+  load_k(cur.g, pa, pb);
+  load_v(cur.g, pa, pb);
+  Cursor nxt = cur;
+  int npa = 0, npb = 0;
+  if (lo + 1 < hi) {
+    nxt = advance(cur);
+    blocks_of(nxt, npa, npb);
+  }
+
+  f32x4_t o[NNN];
+#pragma unroll
+  for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  for (int64_t x = lo; x < hi; ++x) {
     f32x4_t sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax[kk]), qb[kk], sx, 0, 0, 0);
       sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ay[kk]), qb[kk], sy, 0, 0, 0);
     }
+    const bool more = x + 1 < hi;
+    const bool seg_end = !more || nxt.j == 0;
+    if (more) {
+      if (nxt.j == 0) load_q(nxt);  // the score MFMAs above have consumed qb
+      load_k(nxt.g, npa, npb);
+    }
+
+    const int n = cur.n;
+    const int tok0 = 32 * cur.j;
     const int tb = tok0 + 16 * (grp >> 1) + 8 * (grp & 1);
     float s[8];
 #pragma unroll
@@ -149,68 +242,70 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeParams P) {
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) o[nn] *= alpha;
     if (tok0 + 32 > n) {  // slots past the context may hold anything, NaN included
-      const int nvalid = min(max(n - (tok0 + 16 * vsel + 8 * vhalf), 0), 8);
+      const int nvalid = min(max(n - tb, 0), 8);  // tb is this lane's first V token
 #pragma unroll
       for (int nn = 0; nn < NNN; ++nn) va[nn] = keep_first(va[nn], nvalid);
     }
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[nn]), pv, o[nn], 0, 0, 0);
-  }
+    if (more) load_v(nxt.g, npa, npb);
 
-  l = rows_sum4(l);
-  if (grp == 0) {
-    red_m[w * 16 + r16] = m;
-    red_l[w * 16 + r16] = l;
-  }
-  if (r16 < G) {
+    if (seg_end) {
+      const float lsum = rows_sum4(l);
+      const bool whole = cur.seg0 >= lo && cur.seg0 + cur.cnt <= hi;
+      if (r16 < G) {
+        const size_t row = (size_t)cur.b * P.Hq + (size_t)cur.g * G + r16;
+        if (whole) {
+          const float inv = 1.f / lsum;
+          float *dst = P.out + row * D + 4 * grp;
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn)
+          for (int nn = 0; nn < NNN; ++nn)
+            *reinterpret_cast<float4 *>(dst + 16 * nn) =
+                make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
+        } else {
+          const int piece = wave - wave_of(cur.seg0, c_tot, nwe);  // < maxp by construction
+          const size_t slot = row * P.maxp + min(piece, P.maxp - 1);
+          float *dst = P.ws_o + slot * D + 4 * grp;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[((size_t)w * G + r16) * D + 16 * nn + 4 * grp + r] = o[nn][r];
-  }
-  __syncthreads();
-
-  for (int i = tid; i < G * D; i += 64 * W) {
-    const int h = i / D, d = i - h * D;
-    float M = -INFINITY;
+          for (int nn = 0; nn < NNN; ++nn)
+            *reinterpret_cast<float4 *>(dst + 16 * nn) = make_float4(o[nn][0], o[nn][1], o[nn][2], o[nn][3]);
+          if (grp == 0) *reinterpret_cast<float2 *>(P.ws_ml + 2 * slot) = make_float2(m, lsum);
+        }
+      }
 #pragma unroll
-    for (int v = 0; v < W; ++v) M = fmaxf(M, red_m[v * 16 + h]);
-    float acc = 0.f, L = 0.f;
-#pragma unroll
-    for (int v = 0; v < W; ++v) {
-      const float f = fast_exp2(red_m[v * 16 + h] - M);
-      acc += f * red_o[((size_t)v * G + h) * D + d];
-      L += f * red_l[v * 16 + h];
+      for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m = -INFINITY;
+      l = 0.f;
     }
-    if (nparts_b == 1) {
-      out_bg[(size_t)h * D + d] = acc / L;
-    } else {
-      const size_t row = ((size_t)b * P.Hq + (size_t)g * G + h) * P.num_parts + part;
-      P.ws_o[row * D + d] = acc;
-      if (d == 0) {
-        P.ws_ml[2 * row] = M;
-        P.ws_ml[2 * row + 1] = L;
+
+    if (more) {
+      cur = nxt;
+      if (x + 2 < hi) {
+        nxt = advance(cur);
+        blocks_of(nxt, npa, npb);
       }
     }
   }
 }
 
-constexpr int kWaves = 4;
+#ifndef PKV_MFMA_WAVES
+#define PKV_MFMA_WAVES 4
+#endif
+constexpr int kWaves = PKV_MFMA_WAVES;
 
 template <int D>
-int launch(const pkv_decode_args &a, const DecodeParams &p) {
-  const size_t lds = 16 * (D / 8) * 16 + (size_t)(2 * kWaves * 16 + kWaves * p.G * D) * sizeof(float);
-  dim3 grid(a.num_parts, a.L->num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, kWaves>), grid, dim3(64 * kWaves), lds,
-                     reinterpret_cast<hipStream_t>(a.stream), p);
+int launch(const pkv_decode_args &a, const SplitParams &p) {
+  auto kern = decode_mfma_kernel<D, kWaves>;
+  const size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves);
+  int nwg = 0;
+  if (int rc = pkv_split_grid(reinterpret_cast<const void *>(kern), 64 * kWaves, lds, a, &nwg)) return rc;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kWaves), lds, reinterpret_cast<hipStream_t>(a.stream), p);
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
 int pkv_launch_decode_mfma(const pkv_decode_args &a) {
-  DecodeParams p{a.out, a.q, a.k_pool, a.v_pool, a.tables, a.ctx, a.ws_o, a.ws_ml,
-                 a.L->num_blocks, a.L->num_kv_heads, a.num_q_heads, a.num_q_heads / a.L->num_kv_heads,
-                 a.max_blocks, a.max_ctx, a.part_tokens, a.num_parts, a.scale_log2};
+  const SplitParams p = pkv_split_params(a);
   return a.L->head_dim == 128 ? launch<128>(a, p) : launch<64>(a, p);
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_internal.h"
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -84,3 +86,136 @@ __device__ __forceinline__ float rows_max4(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Balanced split of a decode batch over persistent waves.
+//
+// The work of a decode step is the list of 32-token chunks of every
+// (kv head g, sequence b) segment, ordered by g, then b, then chunk.  Each
+// wave of the grid takes one contiguous, equal share of that list (+-1
+// chunk), so every wave streams the same number of K/V bytes whatever the
+// mix of context lengths, and all waves finish together.  Head-major order
+// puts each XCD (one contiguous eighth of the shares, xcd_logical) on about
+// one kv head, so blocks read by many sequences -- a shared prompt -- are
+// served from that XCD's L2 after their first read.  A segment cut by a
+// share boundary leaves one partial result (m, l, o) per wave that touched
+// it; the merge kernel combines them.  A segment held by one wave is written
+// out directly.
+
+// Parameters of the balanced decode kernels (passed by value).
+struct SplitParams {
+  float *out;             // [B][Hq][D]
+  const void *q;          // [B][Hq][D]
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *tables;  // [B][max_blocks]
+  const int32_t *ctx;     // [B]
+  float *ws_o;            // [B][Hq][maxp][D]   partial outputs
+  float *ws_ml;           // [B][Hq][maxp][2]   partial (max, sum)
+  int32_t *ws_hdr;        // [2 + B]: chunks per kv head, waves used, inclusive chunk scan
+  int32_t B;
+  int32_t num_blocks;
+  int32_t H;
+  int32_t Hq;
+  int32_t G;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t maxp;           // partial slots per (sequence, query head)
+  int32_t min_cpw;        // fewest chunks a wave is given (bounds maxp)
+  float scale_log2;
+};
+
+// Scalar (uniform) load of a read-only int32 through the constant address
+// space, so block ids and lengths live in SGPRs and never wait behind the
+// vector K/V loads.
+typedef const int32_t __attribute__((address_space(4))) *pkv_const_i32;
+__device__ __forceinline__ int sload_i32(const int32_t *p) { return *(pkv_const_i32)p; }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Chunks of a sequence of (clamped) length n.
+__device__ __forceinline__ int chunks_of(int n) { return (n + 31) >> 5; }
+
+// Inclusive scan of chunk counts over the batch into s_incl[0..B) (LDS), by
+// all 64*W threads of the workgroup.  Returns the total (chunks per kv head).
+template <int W>
+__device__ int scan_chunks(const SplitParams &P, int32_t *s_incl, int32_t *s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NT = 64 * W;
+  const int per = (P.B + NT - 1) / NT;
+  const int i0 = tid * per, i1 = min(i0 + per, P.B);
+  int local = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int c = chunks_of(clamp_len(P.ctx[i], P.max_blocks, P.max_ctx));
+    s_incl[i] = c;
+    local += c;
+  }
+  int v = local;  // inclusive scan across the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) s_wave[w] = v;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    const int t = s_wave[k];
+    base += k < w ? t : 0;
+    total += t;
+  }
+  int run = base + v - local;
+  for (int i = i0; i < i1; ++i) {
+    run += s_incl[i];
+    s_incl[i] = run;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Waves that receive work: all of them, unless that would give a wave fewer
+// than min_cpw chunks.
+__device__ __forceinline__ int waves_used(int64_t c_tot, int nw, int min_cpw) {
+  const int64_t cap = c_tot / min_cpw;
+  return (int)max((int64_t)1, min((int64_t)nw, cap));
+}
+
+// Wave whose share holds flattened chunk x (shares are [w*C/N, (w+1)*C/N)).
+__device__ __forceinline__ int wave_of(int64_t x, int64_t c_tot, int nwe) {
+  return (int)(((x + 1) * nwe - 1) / c_tot);
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
+// XCD holds one contiguous eighth of the shares (neighbouring shares often
+// read the same segment's query and table lines, which then stay in one L2).
+__device__ __forceinline__ int xcd_logical(int wg, int nwg) {
+  return (nwg & 7) ? wg : (wg & 7) * (nwg >> 3) + (wg >> 3);
+}
+
+// LDS of a balanced-split workgroup: the chunk scan and W wave totals.
+inline size_t pkv_split_lds_bytes(int num_seqs, int waves) { return (size_t)(num_seqs + waves) * sizeof(int32_t); }
+
+inline SplitParams pkv_split_params(const pkv_decode_args &a) {
+  SplitParams p;
+  p.out = a.out;
+  p.q = a.q;
+  p.k_pool = a.k_pool;
+  p.v_pool = a.v_pool;
+  p.tables = a.tables;
+  p.ctx = a.ctx;
+  p.ws_o = a.ws_o;
+  p.ws_ml = a.ws_ml;
+  p.ws_hdr = a.ws_hdr;
+  p.B = a.num_seqs;
+  p.num_blocks = a.L->num_blocks;
+  p.H = a.L->num_kv_heads;
+  p.Hq = a.num_q_heads;
+  p.G = a.num_q_heads / a.L->num_kv_heads;
+  p.max_blocks = a.max_blocks;
+  p.max_ctx = a.max_ctx;
+  p.maxp = a.maxp;
+  p.min_cpw = a.min_cpw;
+  p.scale_log2 = a.scale_log2;
+  return p;
+}

@@ -13,7 +13,9 @@ int pkv_check_layout(const pkv_layout *L);
 inline int pkv_elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
 
 // Default tokens per split-context partition of the decode kernels.
+#ifndef PKV_DEFAULT_PARTITION
 #define PKV_DEFAULT_PARTITION 512
+#endif
 // Partition sizes must be a multiple of this (two blocks: one MFMA chunk).
 #define PKV_PARTITION_QUANTUM 32
 
@@ -34,10 +36,26 @@ struct pkv_decode_args {
   int32_t part_tokens;
   int32_t num_parts;
   float scale_log2;  // scale * log2(e): scores are kept in base 2
-  float *ws_o;       // [B][Hq][num_parts][D]
-  float *ws_ml;      // [B][Hq][num_parts][2]
+  float *ws_o;       // [B][Hq][num_parts][D]  (balanced split: [B][Hq][maxp][D])
+  float *ws_ml;      // [B][Hq][num_parts][2]  (balanced split: [B][Hq][maxp][2])
+  int32_t *ws_hdr;   // balanced split only: [2 + B] schedule header
+  int32_t maxp;      // balanced split only: partial slots per (sequence, query head)
+  int32_t min_cpw;   // balanced split only: fewest 32-token chunks per wave
   void *stream;
 };
+
+// Tokens per chunk of the balanced-split kernels.
+#define PKV_CHUNK 32
+// Default fewest chunks given to one wave by the balanced split.
+#ifndef PKV_DEFAULT_MIN_CHUNKS
+#define PKV_DEFAULT_MIN_CHUNKS 4
+#endif
+// Largest batch of the balanced split (its chunk scan lives in LDS).
+#define PKV_MAX_SPLIT_SEQS 8192
+
+// Persistent grid of a balanced-split kernel: workgroups resident at once on
+// the device (occupancy x compute units), capped by the work, a multiple of 8.
+int pkv_split_grid(const void *kernel, int block_threads, size_t lds_bytes, const pkv_decode_args &a, int *nwg);
 
 int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
                       const int64_t *slots, int32_t num_tokens, void *stream);
@@ -46,3 +64,4 @@ int pkv_launch_copy_blocks(const pkv_layout *L, void *k_pool, void *v_pool, cons
 int pkv_launch_decode_valu(const pkv_decode_args &a);
 int pkv_launch_decode_mfma(const pkv_decode_args &a);
 int pkv_launch_merge(const pkv_decode_args &a);
+int pkv_launch_merge_split(const pkv_decode_args &a);

@@ -267,9 +267,15 @@ extern "C" int pkv_seq_free(pkv_pool *pool, int64_t id) {
   if (int rc = need_pool(pool)) return rc;
   auto it = pool->seqs.find(id);
   if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)id);
-  for (int32_t b : it->second.table)
-    if (pool->ref[b] <= 0)
-      return pkv_set_error(PKV_ERR_REFCOUNT, "free of sequence %lld holding free block %d", (long long)id, b);
+  // All or nothing: every block must have at least as many references as
+  // the table holds it (a caller that freed a block the sequence still held
+  // can make it appear twice).
+  std::unordered_map<int32_t, int32_t> held;
+  for (int32_t b : it->second.table) ++held[b];
+  for (const auto &kv : held)
+    if (pool->ref[kv.first] < kv.second)
+      return pkv_set_error(PKV_ERR_REFCOUNT, "free of sequence %lld holding block %d %d times, refcount %d",
+                           (long long)id, kv.first, kv.second, pool->ref[kv.first]);
   for (int32_t b : it->second.table)
     if (--pool->ref[b] == 0) pool->free_stack.push_back(b);
   pool->seqs.erase(it);

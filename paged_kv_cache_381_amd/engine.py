@@ -86,8 +86,9 @@ class PagedKVCache:
         L.paged_attention_decode(self.layout, out, q, self.k_pools[layer], self.v_pools[layer], tables_dev, ctx_dev,
                                  max_ctx, scale, workspace, partition_tokens, kernel, events)
 
-    def workspace(self, num_seqs, num_q_heads, max_ctx, partition_tokens=0):
-        nbytes = L.paged_attention_workspace_bytes(self.layout, num_seqs, num_q_heads, max_ctx, partition_tokens)
+    def workspace(self, num_seqs, num_q_heads, max_ctx, partition_tokens=0, kernel=0):
+        nbytes = L.paged_attention_workspace_bytes(self.layout, num_seqs, num_q_heads, max_ctx, partition_tokens,
+                                                   kernel)
         return torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=self.device)
 
 
@@ -151,7 +152,8 @@ class GpuWorkload:
 
     def decode(self, layer=0, partition_tokens=0, kernel=0, events=None, workspace=None, out=None):
         if workspace is None:
-            workspace = self.cache.workspace(self.wl.batch, self.wl.num_q_heads, self.max_ctx, partition_tokens)
+            workspace = self.cache.workspace(self.wl.batch, self.wl.num_q_heads, self.max_ctx, partition_tokens,
+                                             kernel)
         out = self.out if out is None else out
         self.cache.decode(layer, out, self.q, self.tables_dev, self.ctx_dev, self.max_ctx, self.scale, workspace,
                           partition_tokens, kernel, events)

@@ -53,9 +53,21 @@ def test_sizes():
     assert P.pkv_kv_bytes_per_token(lay, 32) == 128 * 1024  # Llama-3-8B [KV Cache 工程学 §15.2]
     assert P.pkv_kv_bytes_per_token(P.make_layout(10, 8, 128, "bf16"), 80) == 320 * 1024
     assert P.pkv_pool_bytes(lay) == 10 * 8 * 16 * 128 * 2
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 512) == 0
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 513) == 4 * 32 * 2 * 130 * 4
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 4096, partition_tokens=256) == 4 * 32 * 16 * 130 * 4
+    # wavefront-reduction kernel: [B][Hq][partitions][D + 2] floats, none for one partition
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 512, kernel=1) == 0
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 513, kernel=1) == 4 * 32 * 2 * 130 * 4
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 4096, partition_tokens=256, kernel=1) == 4 * 32 * 16 * 130 * 4
+
+    # matrix-core kernel (the default for bf16, G = 4): partial slots per (sequence, query head)
+    # = ceil(ceil(max_ctx / 32) / fewest chunks per wave) + 1, then partial (m, l) and a
+    # header of 2 + B int32, each region padded to 16 bytes
+    def split(B, Hq, D, max_ctx, min_chunks):
+        maxp = -(-(-(-max_ctx // 32)) // min_chunks) + 1
+        pad = lambda x: -(-x // 16) * 16
+        return pad(B * Hq * maxp * D * 4) + pad(B * Hq * maxp * 2 * 4) + pad((2 + B) * 4)
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 512) == split(4, 32, 128, 512, 4)
+    assert P.paged_attention_workspace_bytes(lay, 3, 32, 4096, partition_tokens=256) == split(3, 32, 128, 4096, 8)
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 1) == split(4, 32, 128, 1, 4)
 
 
 def test_validate_tables():
@@ -192,6 +204,30 @@ def test_pool_matches_oracle_random_ops(ops, seed):
                 blk = loose.pop(i % len(loose)) if loose else i
                 both(lambda: P.pkv_block_free(pr.pool, blk), lambda: pr.book.decref(blk))
             pr.same_state(live)
+    finally:
+        P.pkv_pool_destroy(pr.pool)
+
+
+def test_release_refused_when_a_block_is_held_twice():
+    """A caller frees a block its sequence still holds; the block is handed out
+    again to the same sequence, which then holds it twice with one reference.
+    Releasing the sequence must fail before changing anything, on both sides."""
+    pr = Pair(4, [2, 0, 1, 3])
+    try:
+        s = P.pkv_seq_create(pr.pool)
+        assert pr.book.create() == s
+        both(lambda: P.pkv_seq_append_slots(pr.pool, s, 1), lambda: pr.book.append_slots(s, 1))
+        both(lambda: P.pkv_block_free(pr.pool, 2), lambda: pr.book.decref(2))
+        both(lambda: P.pkv_seq_append_slots(pr.pool, s, 16), lambda: pr.book.append_slots(s, 16))
+        assert pr.book.block_table(s) == [2, 2]
+        pr.same_state([s])
+        with pytest.raises(P.PagedKVError) as e:
+            P.pkv_seq_free(pr.pool, s)
+        assert e.value.name == "REFCOUNT"
+        with pytest.raises(BookError) as eb:
+            pr.book.free_seq(s)
+        assert eb.value.code == "REFCOUNT"
+        pr.same_state([s])
     finally:
         P.pkv_pool_destroy(pr.pool)
 

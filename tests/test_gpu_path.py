@@ -242,8 +242,9 @@ def test_empty_and_padding_sequences():
     q = workloads.configs.normal_bits(6, (2, Hq, D), "bf16")
     for kernel in (1, 2):
         out = torch.full((2, Hq, D), 7.0, device="cuda")
+        ws = c.workspace(2, Hq, 5, 0, kernel)
         c.decode(0, out, mk(q), torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(), 5, 1 / math.sqrt(D),
-                 None, 0, kernel)
+                 ws, 0, kernel)
         o = out.cpu().numpy()
         assert (o[0] == 0).all()
         ref = orc.contiguous_attention("bf16", q[1], kv[0], kv[1], 1 / math.sqrt(D))

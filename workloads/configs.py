@@ -76,6 +76,7 @@ class Workload:
     pool_blocks: int = 0         # explicit pool size, else ceil(1.25 x demand)
     sinks: int = 0
     sink_scale: float = 4.0
+    shuffled: bool = True        # blocks handed out in a seeded random order, else 0, 1, 2, ...
     description: str = ""
 
     @property
@@ -111,7 +112,10 @@ class Workload:
         # Demand counts shared prefix blocks once (pool sizing only).
         demand = -(-self.prefix_len // BLOCK) + int(sum(-(-int(n) // BLOCK) for n in (ctx - self.prefix_len)))
         num_blocks = self.pool_blocks or int(np.ceil(1.25 * demand))
-        perm = np.random.default_rng(derive_seed(self.seed, self.name, "perm")).permutation(num_blocks).astype(np.int32)
+        if self.shuffled:
+            perm = np.random.default_rng(derive_seed(self.seed, self.name, "perm")).permutation(num_blocks).astype(np.int32)
+        else:
+            perm = np.arange(num_blocks, dtype=np.int32)
         return Instance(self, ctx.astype(np.int32), own_prefill.astype(np.int32), num_blocks, perm)
 
 
