@@ -23,19 +23,15 @@ int record(void *ev, void *stream) {
   return e == hipSuccess ? PKV_OK : hip_fail((int)e, "hipEventRecord");
 }
 
-int partition_tokens(const pkv_decode_opts *opts, int32_t *out) {
-  int32_t p = (opts && opts->partition_tokens > 0) ? opts->partition_tokens : PKV_DEFAULT_PARTITION;
-  if (opts && opts->partition_tokens < 0) return pkv_set_error(PKV_ERR_INVALID, "partition_tokens < 0");
-  if (p % PKV_PARTITION_QUANTUM != 0 || p > (1 << 24))
-    return pkv_set_error(PKV_ERR_INVALID, "partition_tokens must be a positive multiple of %d (got %d)",
-                         PKV_PARTITION_QUANTUM, p);
-  *out = p;
+// Fewest chunks per wave of the balanced split, from opts->partition_tokens
+// (fewest tokens per wave: a positive multiple of 32, or 0 for the default).
+int min_chunks(const pkv_decode_opts *opts, int32_t *out) {
+  const int32_t p = opts ? opts->partition_tokens : 0;
+  if (p < 0 || p % PKV_CHUNK != 0 || p > (1 << 22))
+    return pkv_set_error(PKV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of %d up to %d (got %d)",
+                         PKV_CHUNK, 1 << 22, p);
+  *out = p > 0 ? p / PKV_CHUNK : PKV_DEFAULT_MIN_CHUNKS;
   return PKV_OK;
-}
-
-int32_t num_partitions(int32_t max_ctx, int32_t part) {
-  int32_t np = (max_ctx + part - 1) / part;
-  return np < 1 ? 1 : np;
 }
 
 // Kernel a call runs: 1 wavefront reductions, 2 matrix cores (bf16, G >= 4
@@ -61,11 +57,6 @@ size_t split_ws_bytes(const pkv_layout *L, int32_t B, int32_t Hq, int32_t maxp) 
   const size_t rows = (size_t)B * Hq * maxp;
   return align16(rows * L->head_dim * sizeof(float)) + align16(rows * 2 * sizeof(float)) +
          align16((size_t)(2 + B) * sizeof(int32_t));
-}
-
-// Fewest chunks per wave of the balanced split, from opts->partition_tokens.
-int min_chunks(const pkv_decode_opts *opts) {
-  return (opts && opts->partition_tokens > 0) ? opts->partition_tokens / PKV_CHUNK : PKV_DEFAULT_MIN_CHUNKS;
 }
 
 }  // namespace
@@ -137,13 +128,9 @@ extern "C" size_t paged_attention_workspace_bytes(const pkv_layout *layout, int3
                                                   int32_t max_context_len, const pkv_decode_opts *opts) {
   if (pkv_check_layout(layout) || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
   if (num_q_heads % layout->num_kv_heads) return 0;
-  int32_t part;
-  if (partition_tokens(opts, &part)) return 0;
-  if (choose_kernel(layout, num_q_heads / layout->num_kv_heads, opts) == 2)
-    return split_ws_bytes(layout, num_seqs, num_q_heads, split_maxp(max_context_len, min_chunks(opts)));
-  const int32_t np = num_partitions(max_context_len, part);
-  if (np <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * np * (layout->head_dim + 2) * sizeof(float);
+  int32_t mc;
+  if (min_chunks(opts, &mc)) return 0;
+  return split_ws_bytes(layout, num_seqs, num_q_heads, split_maxp(max_context_len, mc));
 }
 
 extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
@@ -171,21 +158,19 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
     return pkv_set_error(PKV_ERR_INVALID, "paged_attention_decode: NULL pointer");
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 4))
     return pkv_set_error(PKV_ERR_INVALID, "paged_attention_decode: q and pools must be 16-byte aligned");
-  int32_t part;
-  if (int rc = partition_tokens(opts, &part)) return rc;
+  int32_t mc;
+  if (int rc = min_chunks(opts, &mc)) return rc;
   const int kernel = choose_kernel(layout, G, opts);
   if (kernel != 1 && kernel != 2) return pkv_set_error(PKV_ERR_INVALID, "unknown kernel %d", kernel);
   if (kernel == 2 && layout->kv_dtype != PKV_BF16)
     return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16 cache");
-  if (kernel == 2 && num_seqs > PKV_MAX_SPLIT_SEQS)
-    return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel takes at most %d sequences (got %d)",
-                         PKV_MAX_SPLIT_SEQS, num_seqs);
+  if (num_seqs > PKV_MAX_SPLIT_SEQS)
+    return pkv_set_error(PKV_ERR_INVALID, "at most %d sequences per call (got %d)", PKV_MAX_SPLIT_SEQS, num_seqs);
   if (max_context_len > (1 << 22))
     return pkv_set_error(PKV_ERR_INVALID, "max_context_len %d exceeds %d", max_context_len, 1 << 22);
 
-  const int32_t np = num_partitions(max_context_len, part);
   const size_t need = paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, opts);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
     return pkv_set_error(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                          workspace ? workspace_bytes : (size_t)0);
 
@@ -201,32 +186,21 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   a.num_q_heads = num_q_heads;
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
-  a.part_tokens = part;
-  a.num_parts = np;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.stream = stream;
-  if (kernel == 2) {
-    a.min_cpw = min_chunks(opts);
-    a.maxp = split_maxp(max_context_len, a.min_cpw);
-    const size_t rows = (size_t)num_seqs * num_q_heads * a.maxp;
-    char *ws = static_cast<char *>(workspace);
-    a.ws_o = reinterpret_cast<float *>(ws);
-    a.ws_ml = reinterpret_cast<float *>(ws + align16(rows * layout->head_dim * sizeof(float)));
-    a.ws_hdr = reinterpret_cast<int32_t *>(ws + align16(rows * layout->head_dim * sizeof(float)) +
-                                           align16(rows * 2 * sizeof(float)));
-  } else {
-    a.ws_o = need ? static_cast<float *>(workspace) : nullptr;
-    a.ws_ml = need ? static_cast<float *>(workspace) + (size_t)num_seqs * num_q_heads * np * layout->head_dim : nullptr;
-  }
+  a.min_cpw = mc;
+  a.maxp = split_maxp(max_context_len, mc);
+  const size_t rows = (size_t)num_seqs * num_q_heads * a.maxp;
+  char *ws = static_cast<char *>(workspace);
+  a.ws_o = reinterpret_cast<float *>(ws);
+  a.ws_ml = reinterpret_cast<float *>(ws + align16(rows * layout->head_dim * sizeof(float)));
+  a.ws_hdr = reinterpret_cast<int32_t *>(ws + align16(rows * layout->head_dim * sizeof(float)) +
+                                         align16(rows * 2 * sizeof(float)));
 
   if (int rc = record(opts ? opts->ev_begin : nullptr, stream)) return rc;
   const int rc = kernel == 2 ? pkv_launch_decode_mfma(a) : pkv_launch_decode_valu(a);
   if (rc) return hip_fail(rc, "decode partition kernel launch");
   if (int r = record(opts ? opts->ev_partition_done : nullptr, stream)) return r;
-  if (kernel == 2) {
-    if (int r2 = pkv_launch_merge_split(a)) return hip_fail(r2, "merge kernel launch");
-  } else if (np > 1) {
-    if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
-  }
+  if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
   return record(opts ? opts->ev_end : nullptr, stream);
 }

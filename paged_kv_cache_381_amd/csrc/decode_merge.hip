@@ -1,62 +1,25 @@
-// Split-context merge of the decode partitions.
+// Split-context merge of the decode kernels' partial results.
 //
-// Each partition i of a long context leaves its running maximum m_i (base 2),
-// weight sum l_i and unnormalised output o_i.  The whole-context softmax is
-// recovered with M = max m_i, L = sum l_i 2^(m_i - M),
-// out = sum o_i 2^(m_i - M) / L, which is exact algebra (log-sum-exp), so the
-// result equals a single softmax over all tokens.  Sequences that fit in one
-// partition were already written by the partition kernel and are skipped.
+// A context cut between waves of the balanced split (pkv_device.h) leaves one
+// partial per wave: its running maximum m_i (base 2), weight sum l_i and
+// unnormalised output o_i.  The whole-context softmax is recovered with
+// M = max m_i, L = sum l_i 2^(m_i - M), out = sum o_i 2^(m_i - M) / L, which is
+// exact algebra (log-sum-exp), so the result equals a single softmax over all
+// tokens.
+//
+// The partials of segment (g, b) are those of the waves whose shares overlap
+// the segment's chunks, stored in share order.  The schedule header written by
+// the decode kernel gives the chunk scan and the number of waves used, from
+// which the segment's position and its first and last wave follow exactly as
+// in the decode kernel.  Segments held by one wave, and empty sequences, were
+// written by the decode kernel and are skipped here.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeParams P) {
-  const int bh = blockIdx.x;
-  const int b = bh / P.Hq;
-  const int n = clamp_len(P.ctx[b], P.max_blocks, P.max_ctx);
-  const int np = (n + P.part_tokens - 1) / P.part_tokens;
-  if (np <= 1) return;
-  const float *ml = P.ws_ml + (size_t)bh * P.num_parts * 2;
-  const float *o = P.ws_o + (size_t)bh * P.num_parts * D;
-  float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[2 * i]);
-  float L = 0.f;
-  for (int i = 0; i < np; ++i) L += ml[2 * i + 1] * fast_exp2(ml[2 * i] - M);
-  const float inv = 1.f / L;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float acc = 0.f;
-    for (int i = 0; i < np; ++i) acc += o[(size_t)i * D + d] * fast_exp2(ml[2 * i] - M);
-    P.out[(size_t)bh * D + d] = acc * inv;
-  }
-}
-
-}  // namespace
-
-int pkv_launch_merge(const pkv_decode_args &a) {
-  DecodeParams p{a.out, a.q, a.k_pool, a.v_pool, a.tables, a.ctx, a.ws_o, a.ws_ml,
-                 a.L->num_blocks, a.L->num_kv_heads, a.num_q_heads, a.num_q_heads / a.L->num_kv_heads,
-                 a.max_blocks, a.max_ctx, a.part_tokens, a.num_parts, a.scale_log2};
-  dim3 grid(a.num_seqs * a.num_q_heads);
-  if (a.L->head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
-  return (int)hipGetLastError();
-}
-
-// Merge of the balanced split (decode_mfma.hip): the partials of segment
-// (g, b) are the waves whose shares overlap the segment's chunks, stored in
-// share order.  The schedule header written by the partition kernel gives the
-// chunk scan and the number of waves used, from which both the segment's
-// position and its first and last wave follow exactly as in the partition
-// kernel.  Segments held by one wave, and empty sequences, were written by the
-// partition kernel.
-namespace {
-
-template <int D>
-__global__ __launch_bounds__(64) void merge_split_kernel(SplitParams P) {
+__global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
   const int bh = blockIdx.x;
   const int b = bh / P.Hq, h = bh - b * P.Hq, g = h / P.G;
   const int64_t c_tot = (int64_t)P.H * P.ws_hdr[0];
@@ -91,12 +54,12 @@ __global__ __launch_bounds__(64) void merge_split_kernel(SplitParams P) {
 
 }  // namespace
 
-int pkv_launch_merge_split(const pkv_decode_args &a) {
+int pkv_launch_merge(const pkv_decode_args &a) {
   const SplitParams p = pkv_split_params(a);
   dim3 grid(a.num_seqs * a.num_q_heads);
   if (a.L->head_dim == 128)
-    hipLaunchKernelGGL(merge_split_kernel<128>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   else
-    hipLaunchKernelGGL(merge_split_kernel<64>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   return (int)hipGetLastError();
 }

@@ -58,14 +58,6 @@ __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
 #define PKV_MFMA_MIN_WAVES_PER_SIMD 1
 #endif
 
-// Position of a wave in the chunk list: sequence b, kv head g, chunk j of the
-// segment, the segment's chunk count and length, and the flattened index of
-// the segment's first chunk.  All wave-uniform (SGPRs).
-struct Cursor {
-  int b, g, j, cnt, n;
-  int64_t seg0;
-};
-
 template <int D, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_MIN_WAVES_PER_SIMD)))
 void decode_mfma_kernel(SplitParams P) {
@@ -75,75 +67,12 @@ void decode_mfma_kernel(SplitParams P) {
   extern __shared__ __align__(16) int32_t s_incl[];  // [B] inclusive chunk scan, then [W] scratch
   int32_t *s_wave = s_incl + P.B;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int H = P.H, G = P.G, B = P.B;
-  const int64_t c_seq = scan_chunks<W>(P, s_incl, s_wave);
-  const int64_t c_tot = (int64_t)H * c_seq;
-  const int nwg = gridDim.x;
-  const int nwe = waves_used(c_tot, nwg * W, P.min_cpw);
-
-  if (blockIdx.x == 0) {
-    // Header for the merge kernel, and zeros for empty sequences.
-    if (tid == 0) {
-      P.ws_hdr[0] = (int32_t)c_seq;
-      P.ws_hdr[1] = nwe;
-    }
-    for (int i = tid; i < B; i += 64 * W) P.ws_hdr[2 + i] = s_incl[i];
-    for (int b = 0; b < B; ++b) {
-      const int prev = b ? s_incl[b - 1] : 0;
-      if (s_incl[b] == prev)
-        for (int i = tid; i < P.Hq * D; i += 64 * W) P.out[(size_t)b * P.Hq * D + i] = 0.f;
-    }
-  }
-
-  const int wave = uniform(xcd_logical(blockIdx.x, nwg) * W + w);
-  if (wave >= nwe || c_tot == 0) return;
-  const int64_t lo = (int64_t)wave * c_tot / nwe, hi = (int64_t)(wave + 1) * c_tot / nwe;
-  if (lo >= hi) return;
-
-  auto cnt_of = [&](int b) { return uniform(s_incl[b] - (b ? s_incl[b - 1] : 0)); };
-  auto len_of = [&](int b) { return clamp_len(sload_i32(P.ctx + b), P.max_blocks, P.max_ctx); };
-
-  // Locate the share's first chunk: kv head lo / c_seq, then the first
-  // sequence whose chunks end past the remainder.
-  Cursor cur;
-  {
-    cur.g = (int)(lo / c_seq);
-    const int rem = (int)(lo - (int64_t)cur.g * c_seq);
-    int a = 0, z = B - 1;
-    while (a < z) {
-      const int mid = (a + z) >> 1;
-      if (uniform(s_incl[mid]) > rem) z = mid; else a = mid + 1;
-    }
-    cur.b = a;
-    cur.cnt = cnt_of(a);
-    const int excl = uniform(s_incl[a]) - cur.cnt;
-    cur.j = rem - excl;
-    cur.n = len_of(a);
-    cur.seg0 = (int64_t)cur.g * c_seq + excl;
-  }
-  // Next chunk in list order; segments are contiguous in the list, so the
-  // next segment starts where this one ends.
-  auto advance = [&](Cursor c) {
-    if (++c.j < c.cnt) return c;
-    c.j = 0;
-    c.seg0 += c.cnt;
-    do {
-      if (++c.b == B) {
-        c.b = 0;
-        ++c.g;
-      }
-    } while (cnt_of(c.b) == 0);
-    c.cnt = cnt_of(c.b);
-    c.n = len_of(c.b);
-    return c;
-  };
-  // Physical blocks of a chunk (the second one only if it holds tokens).
-  auto blocks_of = [&](const Cursor &c, int &pa, int &pb) {
-    const int32_t *row = P.tables + (size_t)c.b * P.max_blocks + 2 * c.j;
-    pa = clamp_block(sload_i32(row), P.num_blocks);
-    pb = (32 * c.j + 16 < c.n) ? clamp_block(sload_i32(row + 1), P.num_blocks) : pa;
-  };
+  const int lane = threadIdx.x & 63;
+  const int H = P.H, G = P.G;
+  Share sh;
+  if (!split_begin<W, D>(P, s_incl, s_wave, sh)) return;
+  const int64_t lo = sh.lo, hi = sh.hi;
+  Cursor cur = sh.first();
 
   const int r16 = lane & 15, grp = lane >> 4;
   // Row r16 of the score MFMAs holds a token of block (r16 >> 3); see header.
@@ -184,15 +113,15 @@ void decode_mfma_kernel(SplitParams P) {
   };
 
   int pa, pb;
-  blocks_of(cur, pa, pb);
+  sh.blocks(cur, pa, pb);
   load_q(cur);
   load_k(cur.g, pa, pb);
   load_v(cur.g, pa, pb);
   Cursor nxt = cur;
   int npa = 0, npb = 0;
   if (lo + 1 < hi) {
-    nxt = advance(cur);
-    blocks_of(nxt, npa, npb);
+    nxt = sh.next(cur);
+    sh.blocks(nxt, npa, npb);
   }
 
   f32x4_t o[NNN];
@@ -252,7 +181,7 @@ void decode_mfma_kernel(SplitParams P) {
 
     if (seg_end) {
       const float lsum = rows_sum4(l);
-      const bool whole = cur.seg0 >= lo && cur.seg0 + cur.cnt <= hi;
+      const bool whole = sh.whole(cur);
       if (r16 < G) {
         const size_t row = (size_t)cur.b * P.Hq + (size_t)cur.g * G + r16;
         if (whole) {
@@ -263,8 +192,7 @@ void decode_mfma_kernel(SplitParams P) {
             *reinterpret_cast<float4 *>(dst + 16 * nn) =
                 make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
         } else {
-          const int piece = wave - wave_of(cur.seg0, c_tot, nwe);  // < maxp by construction
-          const size_t slot = row * P.maxp + min(piece, P.maxp - 1);
+          const size_t slot = row * P.maxp + sh.piece(cur, P.maxp);
           float *dst = P.ws_o + slot * D + 4 * grp;
 #pragma unroll
           for (int nn = 0; nn < NNN; ++nn)
@@ -281,8 +209,8 @@ void decode_mfma_kernel(SplitParams P) {
     if (more) {
       cur = nxt;
       if (x + 2 < hi) {
-        nxt = advance(cur);
-        blocks_of(nxt, npa, npb);
+        nxt = sh.next(cur);
+        sh.blocks(nxt, npa, npb);
       }
     }
   }

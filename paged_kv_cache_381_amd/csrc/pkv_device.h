@@ -9,27 +9,6 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Parameters of the decode partition kernels (passed by value).
-struct DecodeParams {
-  float *out;             // [B][Hq][D]
-  const void *q;          // [B][Hq][D]
-  const void *k_pool;
-  const void *v_pool;
-  const int32_t *tables;  // [B][max_blocks]
-  const int32_t *ctx;     // [B]
-  float *ws_o;            // [B][Hq][num_parts][D]
-  float *ws_ml;           // [B][Hq][num_parts][2]
-  int32_t num_blocks;
-  int32_t H;              // kv heads
-  int32_t Hq;             // query heads
-  int32_t G;              // Hq / H
-  int32_t max_blocks;
-  int32_t max_ctx;         // caller's bound on every length (sizes the grid)
-  int32_t part_tokens;
-  int32_t num_parts;
-  float scale_log2;
-};
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -193,8 +172,11 @@ __device__ __forceinline__ int xcd_logical(int wg, int nwg) {
   return (nwg & 7) ? wg : (wg & 7) * (nwg >> 3) + (wg >> 3);
 }
 
-// LDS of a balanced-split workgroup: the chunk scan and W wave totals.
-inline size_t pkv_split_lds_bytes(int num_seqs, int waves) { return (size_t)(num_seqs + waves) * sizeof(int32_t); }
+// LDS of a balanced-split workgroup: the chunk scan and W wave totals,
+// padded to 16 bytes, then extra_floats of per-wave slices.
+inline size_t pkv_split_lds_bytes(int num_seqs, int waves, int extra_floats = 0) {
+  return (size_t)((num_seqs + waves + 3) & ~3) * sizeof(int32_t) + (size_t)extra_floats * sizeof(float);
+}
 
 inline SplitParams pkv_split_params(const pkv_decode_args &a) {
   SplitParams p;
@@ -218,4 +200,121 @@ inline SplitParams pkv_split_params(const pkv_decode_args &a) {
   p.min_cpw = a.min_cpw;
   p.scale_log2 = a.scale_log2;
   return p;
+}
+
+// Position of a wave in the chunk list: sequence b, kv head g, chunk j of the
+// segment, the segment's chunk count and length, and the list index of the
+// segment's first chunk.  All wave-uniform (SGPRs).
+struct Cursor {
+  int b, g, j, cnt, n;
+  int64_t seg0;
+};
+
+// One wave's share [lo, hi) of the chunk list and the walk through it.
+struct Share {
+  const int32_t *s_incl;  // LDS: inclusive chunk scan over the batch
+  const int32_t *ctx;
+  const int32_t *tables;
+  int B, max_blocks, max_ctx, num_blocks;
+  int64_t c_seq, c_tot;
+  int nwe, wave;
+  int64_t lo, hi;
+
+  __device__ int cnt_of(int b) const { return uniform(s_incl[b] - (b ? s_incl[b - 1] : 0)); }
+  __device__ int len_of(int b) const { return clamp_len(sload_i32(ctx + b), max_blocks, max_ctx); }
+
+  // The share's first chunk: kv head lo / c_seq, then the first sequence
+  // whose chunks end past the remainder.
+  __device__ Cursor first() const {
+    Cursor c;
+    c.g = (int)(lo / c_seq);
+    const int rem = (int)(lo - (int64_t)c.g * c_seq);
+    int a = 0, z = B - 1;
+    while (a < z) {
+      const int mid = (a + z) >> 1;
+      if (uniform(s_incl[mid]) > rem)
+        z = mid;
+      else
+        a = mid + 1;
+    }
+    c.b = a;
+    c.cnt = cnt_of(a);
+    const int excl = uniform(s_incl[a]) - c.cnt;
+    c.j = rem - excl;
+    c.n = len_of(a);
+    c.seg0 = (int64_t)c.g * c_seq + excl;
+    return c;
+  }
+
+  // The next chunk in list order (call only while one remains in the share).
+  // Segments are contiguous in the list, so the next one starts where this
+  // one ends; empty sequences are skipped.
+  __device__ Cursor next(Cursor c) const {
+    if (++c.j < c.cnt) return c;
+    c.j = 0;
+    c.seg0 += c.cnt;
+    do {
+      if (++c.b == B) {
+        c.b = 0;
+        ++c.g;
+      }
+    } while (cnt_of(c.b) == 0);
+    c.cnt = cnt_of(c.b);
+    c.n = len_of(c.b);
+    return c;
+  }
+
+  // Physical blocks of a chunk; the second is the first again when the chunk
+  // holds no token of it (only the last chunk of a segment can).
+  __device__ void blocks(const Cursor &c, int &pa, int &pb) const {
+    const int32_t *row = tables + (size_t)c.b * max_blocks + 2 * c.j;
+    pa = clamp_block(sload_i32(row), num_blocks);
+    pb = (32 * c.j + 16 < c.n) ? clamp_block(sload_i32(row + 1), num_blocks) : pa;
+  }
+
+  // Whether this wave holds every chunk of the cursor's segment.
+  __device__ bool whole(const Cursor &c) const { return c.seg0 >= lo && c.seg0 + c.cnt <= hi; }
+
+  // Partial slot of this wave for the cursor's segment (< maxp by
+  // construction; clamped so a broken invariant cannot write out of bounds).
+  __device__ int piece(const Cursor &c, int maxp) const { return min(wave - wave_of(c.seg0, c_tot, nwe), maxp - 1); }
+};
+
+// Common start of the balanced-split kernels: the chunk scan (all threads),
+// the merge kernel's header and zero rows for empty sequences (workgroup 0),
+// and this wave's share.  Returns false when the wave has no work.
+template <int W, int D>
+__device__ bool split_begin(const SplitParams &P, int32_t *s_incl, int32_t *s_wave, Share &sh) {
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int64_t c_seq = scan_chunks<W>(P, s_incl, s_wave);
+  const int64_t c_tot = (int64_t)P.H * c_seq;
+  const int nwg = gridDim.x;
+  const int nwe = waves_used(c_tot, nwg * W, P.min_cpw);
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      P.ws_hdr[0] = (int32_t)c_seq;
+      P.ws_hdr[1] = nwe;
+    }
+    for (int i = tid; i < P.B; i += 64 * W) P.ws_hdr[2 + i] = s_incl[i];
+    for (int b = 0; b < P.B; ++b) {
+      const int prev = b ? s_incl[b - 1] : 0;
+      if (s_incl[b] == prev)
+        for (int i = tid; i < P.Hq * D; i += 64 * W) P.out[(size_t)b * P.Hq * D + i] = 0.f;
+    }
+  }
+  sh.s_incl = s_incl;
+  sh.ctx = P.ctx;
+  sh.tables = P.tables;
+  sh.B = P.B;
+  sh.max_blocks = P.max_blocks;
+  sh.max_ctx = P.max_ctx;
+  sh.num_blocks = P.num_blocks;
+  sh.c_seq = c_seq;
+  sh.c_tot = c_tot;
+  sh.nwe = nwe;
+  sh.wave = uniform(xcd_logical(blockIdx.x, nwg) * W + w);
+  if (sh.wave >= nwe || c_tot == 0) return false;
+  sh.lo = (int64_t)sh.wave * c_tot / nwe;
+  sh.hi = (int64_t)(sh.wave + 1) * c_tot / nwe;
+  return sh.lo < sh.hi;
 }

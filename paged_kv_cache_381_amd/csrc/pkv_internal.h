@@ -12,12 +12,6 @@ int pkv_check_layout(const pkv_layout *L);
 
 inline int pkv_elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
 
-// Default tokens per split-context partition of the decode kernels.
-#ifndef PKV_DEFAULT_PARTITION
-#define PKV_DEFAULT_PARTITION 512
-#endif
-// Partition sizes must be a multiple of this (two blocks: one MFMA chunk).
-#define PKV_PARTITION_QUANTUM 32
 
 // Kernel launchers (decode_*.hip, kv_append.hip).  They return a HIP error
 // code (0 = success); arguments were validated by the caller.
@@ -33,14 +27,12 @@ struct pkv_decode_args {
   int32_t num_q_heads;
   int32_t max_blocks;
   int32_t max_ctx;
-  int32_t part_tokens;
-  int32_t num_parts;
   float scale_log2;  // scale * log2(e): scores are kept in base 2
-  float *ws_o;       // [B][Hq][num_parts][D]  (balanced split: [B][Hq][maxp][D])
-  float *ws_ml;      // [B][Hq][num_parts][2]  (balanced split: [B][Hq][maxp][2])
-  int32_t *ws_hdr;   // balanced split only: [2 + B] schedule header
-  int32_t maxp;      // balanced split only: partial slots per (sequence, query head)
-  int32_t min_cpw;   // balanced split only: fewest 32-token chunks per wave
+  float *ws_o;       // [B][Hq][maxp][D] partial outputs
+  float *ws_ml;      // [B][Hq][maxp][2] partial (max, sum)
+  int32_t *ws_hdr;   // [2 + B] schedule header
+  int32_t maxp;      // partial slots per (sequence, query head)
+  int32_t min_cpw;   // fewest 32-token chunks per wave
   void *stream;
 };
 
@@ -64,4 +56,3 @@ int pkv_launch_copy_blocks(const pkv_layout *L, void *k_pool, void *v_pool, cons
 int pkv_launch_decode_valu(const pkv_decode_args &a);
 int pkv_launch_decode_mfma(const pkv_decode_args &a);
 int pkv_launch_merge(const pkv_decode_args &a);
-int pkv_launch_merge_split(const pkv_decode_args &a);

@@ -53,12 +53,7 @@ def test_sizes():
     assert P.pkv_kv_bytes_per_token(lay, 32) == 128 * 1024  # Llama-3-8B [KV Cache 工程学 §15.2]
     assert P.pkv_kv_bytes_per_token(P.make_layout(10, 8, 128, "bf16"), 80) == 320 * 1024
     assert P.pkv_pool_bytes(lay) == 10 * 8 * 16 * 128 * 2
-    # wavefront-reduction kernel: [B][Hq][partitions][D + 2] floats, none for one partition
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 512, kernel=1) == 0
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 513, kernel=1) == 4 * 32 * 2 * 130 * 4
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 4096, partition_tokens=256, kernel=1) == 4 * 32 * 16 * 130 * 4
-
-    # matrix-core kernel (the default for bf16, G = 4): partial slots per (sequence, query head)
+    # Both kernels split the batch the same way: partial slots per (sequence, query head)
     # = ceil(ceil(max_ctx / 32) / fewest chunks per wave) + 1, then partial (m, l) and a
     # header of 2 + B int32, each region padded to 16 bytes
     def split(B, Hq, D, max_ctx, min_chunks):
@@ -68,6 +63,9 @@ def test_sizes():
     assert P.paged_attention_workspace_bytes(lay, 4, 32, 512) == split(4, 32, 128, 512, 4)
     assert P.paged_attention_workspace_bytes(lay, 3, 32, 4096, partition_tokens=256) == split(3, 32, 128, 4096, 8)
     assert P.paged_attention_workspace_bytes(lay, 4, 32, 1) == split(4, 32, 128, 1, 4)
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 513, kernel=1) == split(4, 32, 128, 513, 4)
+    f32 = P.make_layout(10, 4, 64, "f32")
+    assert P.paged_attention_workspace_bytes(f32, 4, 4, 255, partition_tokens=32) == split(4, 4, 64, 255, 1)
 
 
 def test_validate_tables():
