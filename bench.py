@@ -35,13 +35,19 @@ MODEL_LAYERS = {"llama3_8b_b64": 32, "llama3_70b_b256": 80, "shared_prefix_b128"
 PARTITION_KERNELS = ("decode_mfma_kernel", "decode_valu_kernel")
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h: timing only, no system-scope fences
+
+
 class HipEvents:
     """Raw hipEvent_t handles from the HIP runtime torch already loaded, so the
-    library can record them between its own launches."""
+    library can record them between its own launches.  They only time: the
+    system-scope release/acquire fences of a default event (a write-back of
+    the L2s at every record) are turned off."""
 
-    def __init__(self):
+    def __init__(self, flags=HIP_EVENT_DISABLE_SYSTEM_FENCE):
+        self.flags = flags
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
@@ -49,7 +55,7 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.flags) == 0
             out.append(e)
         return out
 
@@ -127,6 +133,67 @@ def cpu_baseline(inst, min_seconds: float):
                       f"host cores = {os.cpu_count()}"}
 
 
+def _pmc_rows(run_dir: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _pmc_mean_kib(rows, name_part: str, counter: str) -> float:
+    vals = [float(r["Counter_Value"]) for r in rows if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for a kernel named like {name_part!r}")
+    return sum(vals) / len(vals)
+
+
+def traffic_summary(args):
+    """Write profiles/decode_<workload>_traffic.txt from four rocprofv3 --pmc
+    runs: FETCH_SIZE and WRITE_SIZE of the bench, and of the plain copy probe
+    (1 GiB read + 1 GiB written per copy), which calibrates each counter."""
+    fetch_dir, write_dir, fetch_copy_dir, write_copy_dir, bench_log = args.traffic_summary
+    kern = next((k for k in PARTITION_KERNELS if any(k in r["Kernel_Name"] for r in _pmc_rows(fetch_dir))), None)
+    if kern is None:
+        raise SystemExit("no partition kernel in the FETCH_SIZE run")
+    fetch = _pmc_mean_kib(_pmc_rows(fetch_dir), kern, "FETCH_SIZE")
+    write = _pmc_mean_kib(_pmc_rows(write_dir), kern, "WRITE_SIZE")
+    copy_bytes = 1 << 30
+    cfetch = _pmc_mean_kib(_pmc_rows(fetch_copy_dir), "copyBuffer", "FETCH_SIZE")
+    cwrite = _pmc_mean_kib(_pmc_rows(write_copy_dir), "copyBuffer", "WRITE_SIZE")
+    fscale, wscale = copy_bytes / (cfetch * 1024), copy_bytes / (cwrite * 1024)
+    hbm = fetch * 1024 * fscale + write * 1024 * wscale
+    algo = None
+    with open(bench_log, encoding="utf-8") as f:
+        for line in f:
+            if line.startswith("{"):
+                algo = json.loads(line)["roofline"]["bytes_per_launch"]
+    lines = [
+        f"# HBM traffic per launch of the decode partition kernel ({kern}), workload {args.workload}",
+        "# from rocprofv3 --pmc runs, one counter per run, each scaled by what it reads for a plain",
+        "# 1 GiB device copy (bench.py --copy-probe):",
+        f"#   cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o b -- python3 <repo>/bench.py "
+        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline",
+        "#   (the same with --pmc WRITE_SIZE, and both counters over python3 <repo>/bench.py --copy-probe)",
+        f"kernel_source_hash = {kernel_source_hash()}",
+        f"fetch_kib_per_dispatch = {fetch:.1f}",
+        f"write_kib_per_dispatch = {write:.1f}",
+        f"copy_fetch_kib_per_gib = {cfetch:.1f}",
+        f"copy_write_kib_per_gib = {cwrite:.1f}",
+        f"fetch_scale = {fscale:.4f}",
+        f"write_scale = {wscale:.4f}",
+        f"hbm_bytes_per_launch = {hbm:.0f}",
+        f"algorithmic_bytes_per_launch = {algo}",
+        f"traffic_over_algorithmic = {hbm / algo:.4f}" if algo else "traffic_over_algorithmic = unknown",
+    ]
+    path = os.path.join(ROOT, "profiles", f"decode_{args.workload}_traffic.txt")
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_probe(gib: float, reps: int):
     """Plain device-to-device copies of a known size (PMC calibration)."""
     import torch
@@ -146,12 +213,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b_b64")
     ap.add_argument("--layers", type=int, default=0, help="layers per step (0: enough to read >= 1 GiB)")
-    ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0: library default)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="fewest context tokens per wave of the balanced split (0: library default, 128)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 wavefront-reduction, 2 matrix-core")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only plain 1 GiB copies (PMC calibration)")
+    ap.add_argument("--traffic-summary", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                          "COPY_WRITE_DIR", "BENCH_LOG"),
+                    help="write profiles/decode_<workload>_traffic.txt from rocprofv3 --pmc output (no GPU)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -185,36 +259,37 @@ def main():
     MB = -(-(int(inst.ctx.max()) + total_steps + 1) // 16)
     ws = cache.workspace(B, Hq, MB * 16, args.partition, args.kernel)
     dev = torch.device("cuda")
+    # Slots (int64), lengths and block tables of a step travel in one pinned
+    # host-to-device copy; R pinned sets rotate so the host never overwrites
+    # one still being copied.
     R = 4
-    slots_pin = [torch.empty(B, dtype=torch.int64, pin_memory=True) for _ in range(R)]
-    tables_pin = [torch.empty(B * MB, dtype=torch.int32, pin_memory=True) for _ in range(R)]
-    ctx_pin = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    n32 = 2 * B + B + B * MB
+    pin = [torch.empty(n32, dtype=torch.int32, pin_memory=True) for _ in range(R)]
     ring_ev = [torch.cuda.Event() for _ in range(R)]
-    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
-    d_tables = torch.empty(B, MB, dtype=torch.int32, device=dev)
-    d_ctx = torch.empty(B, dtype=torch.int32, device=dev)
+    dbuf = torch.empty(n32, dtype=torch.int32, device=dev)
+    d_slots, d_ctx, d_tables = dbuf[:2 * B].view(torch.int64), dbuf[2 * B:3 * B], dbuf[3 * B:].view(B, MB)
     k_new, v_new = gw.k_step, gw.v_step
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     hip = HipEvents()
-    evs = hip.create(2 * K * layers)
+    # One layer per timed step (rotating) carries the HIP events around its
+    # partition kernel: every event record idles the GPU for a few
+    # microseconds, which would otherwise be charged to the whole step.
+    evs = hip.create(2 * K)
     torch.cuda.synchronize()
 
     def step(k: int, timed_idx: int):
         r = k % R
         ring_ev[r].synchronize()  # the copy that last read this pinned set is done
-        L.pkv_batch_append_slots(cache.pool, ids, 1, slots_out=slots_pin[r].numpy())
-        L.pkv_batch_block_tables(cache.pool, ids, MB, tables_pin[r].numpy().reshape(B, MB), ctx_pin[r].numpy())
-        ctx_np = ctx_pin[r].numpy()
+        h = pin[r].numpy()
+        L.pkv_batch_append_slots(cache.pool, ids, 1, slots_out=h[:2 * B].view(np.int64))
+        L.pkv_batch_block_tables(cache.pool, ids, MB, h[3 * B:].reshape(B, MB), h[2 * B:3 * B])
+        ctx_np = h[2 * B:3 * B]
         max_ctx = int(ctx_np.max())
-        d_slots.copy_(slots_pin[r], non_blocking=True)
-        d_tables.view(-1).copy_(tables_pin[r], non_blocking=True)
-        d_ctx.copy_(ctx_pin[r], non_blocking=True)
+        dbuf.copy_(pin[r], non_blocking=True)
         ring_ev[r].record()
+        ev_layer = timed_idx % layers if timed_idx >= 0 else -1
         for layer in range(layers):
-            ev = None
-            if timed_idx >= 0:
-                i = 2 * (timed_idx * layers + layer)
-                ev = (evs[i], evs[i + 1], None)
+            ev = (evs[2 * timed_idx], evs[2 * timed_idx + 1], None) if layer == ev_layer else None
             cache.write(layer, d_slots, k_new, v_new)
             cache.decode(layer, out, gw.q, d_tables, d_ctx, max_ctx, gw.scale, ws, args.partition, args.kernel, ev)
         return int(ctx_np.astype(np.int64).sum())
@@ -235,7 +310,7 @@ def main():
     kv_bytes = sum(ctx_tokens) * tok_bytes * layers
     gbps = kv_bytes / elapsed / 1e9
     ms_step = elapsed / K * 1e3
-    durs = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(K * layers)]
+    durs = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(K)]
     hip.destroy(evs)
     avg_ms = sum(durs) / len(durs)
     bytes_per_launch = sum(ctx_tokens) / K * tok_bytes
@@ -261,7 +336,7 @@ def main():
         "config": {"workload": wl.description, "name": wl.name, "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": H, "head_dim": D, "block_size": 16, "layers_per_step": layers,
                    "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
-                   "partition_tokens": args.partition or 512, "kernel": args.kernel, "parallelism": "none"},
+                   "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "parallelism": "none"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s_per_layer": round(B / per_layer_s, 1),
         "decode_tokens_per_s_attention_full_depth": round(B / (per_layer_s * MODEL_LAYERS.get(wl.name, 32)), 1),
