@@ -216,6 +216,8 @@ def main():
     ap.add_argument("--partition", type=int, default=0,
                     help="fewest context tokens per wave of the balanced split (0: library default, 128)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 wavefront-reduction, 2 matrix-core")
+    ap.add_argument("--waves-per-simd", type=int, default=0,
+                    help="matrix-core kernel: 1 or 2 resident waves per SIMD (0: chosen from the pool's sharing)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only plain 1 GiB copies (PMC calibration)")
@@ -270,6 +272,7 @@ def main():
     d_slots, d_ctx, d_tables = dbuf[:2 * B].view(torch.int64), dbuf[2 * B:3 * B], dbuf[3 * B:].view(B, MB)
     k_new, v_new = gw.k_step, gw.v_step
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    wps = args.waves_per_simd or cache.waves_per_simd()
     hip = HipEvents()
     # One layer per timed step (rotating) carries the HIP events around its
     # partition kernel: every event record idles the GPU for a few
@@ -291,7 +294,8 @@ def main():
         for layer in range(layers):
             ev = (evs[2 * timed_idx], evs[2 * timed_idx + 1], None) if layer == ev_layer else None
             cache.write(layer, d_slots, k_new, v_new)
-            cache.decode(layer, out, gw.q, d_tables, d_ctx, max_ctx, gw.scale, ws, args.partition, args.kernel, ev)
+            cache.decode(layer, out, gw.q, d_tables, d_ctx, max_ctx, gw.scale, ws, args.partition, args.kernel, ev,
+                         wps)
         return int(ctx_np.astype(np.int64).sum())
 
     for k in range(W):
@@ -336,7 +340,8 @@ def main():
         "config": {"workload": wl.description, "name": wl.name, "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": H, "head_dim": D, "block_size": 16, "layers_per_step": layers,
                    "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
-                   "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "parallelism": "none"},
+                   "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "waves_per_simd": wps,
+                   "parallelism": "none"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s_per_layer": round(B / per_layer_s, 1),
         "decode_tokens_per_s_attention_full_depth": round(B / (per_layer_s * MODEL_LAYERS.get(wl.name, 32)), 1),

@@ -199,8 +199,12 @@ typedef struct {
                                split-context partition (default 512). */
   int32_t kernel;           /* 0 auto (matrix cores for bf16 with G >= 4);
                                1 the wavefront-reduction kernel;
-                               2 the matrix-core kernel (bf16, G <= 16,
-                               at most 8192 sequences) */
+                               2 the matrix-core kernel (bf16, G <= 16) */
+  int32_t waves_per_simd;   /* matrix-core kernel: resident waves per SIMD,
+                               0 = default (1), 1 or 2.  One streams K/V from
+                               HBM fastest (waves sharing a SIMD do not
+                               progress alike); two serve batches whose blocks
+                               are mostly shared (and so L2-resident) better. */
   void *ev_begin;           /* optional hipEvent_t recorded before the first kernel */
   void *ev_partition_done;  /* optional hipEvent_t recorded after the partition kernel */
   void *ev_end;             /* optional hipEvent_t recorded after the last kernel */

@@ -50,7 +50,8 @@ class pkv_stats(ctypes.Structure):
 
 
 class pkv_decode_opts(ctypes.Structure):
-    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("ev_begin", ctypes.c_void_p),
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("waves_per_simd", ctypes.c_int32),
+                ("ev_begin", ctypes.c_void_p),
                 ("ev_partition_done", ctypes.c_void_p), ("ev_end", ctypes.c_void_p)]
 
 
@@ -312,9 +313,9 @@ def pkv_copy_blocks(layout, k_pool, v_pool, pairs, stream=None):
                                  pairs.numel() // 2, _stream(stream)))
 
 
-def decode_opts(partition_tokens=0, kernel=0, events=None) -> pkv_decode_opts:
+def decode_opts(partition_tokens=0, kernel=0, events=None, waves_per_simd=0) -> pkv_decode_opts:
     ev = list(events) if events else [None, None, None]
-    return pkv_decode_opts(int(partition_tokens), int(kernel), *[e if e else None for e in ev])
+    return pkv_decode_opts(int(partition_tokens), int(kernel), int(waves_per_simd), *[e if e else None for e in ev])
 
 
 def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, partition_tokens=0,
@@ -325,7 +326,7 @@ def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_l
 
 
 def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
-                           workspace=None, partition_tokens=0, kernel=0, events=None, stream=None):
+                           workspace=None, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0):
     """events: optional (begin, partition_done, end) raw hipEvent_t handles."""
     import torch
     dt = _kv_torch_dtype(layout)
@@ -342,7 +343,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
         ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < ws_need:
         raise ValueError(f"workspace of {ws_need} bytes needed, got {ws_bytes}")
-    o = decode_opts(partition_tokens, kernel, events)
+    o = decode_opts(partition_tokens, kernel, events, waves_per_simd)
     _check(lib().paged_attention_decode(
         ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", dt),
         _dev(k_pool, "k_pool", dt, layout.pool_elems), _dev(v_pool, "v_pool", dt, layout.pool_elems),

@@ -20,7 +20,7 @@ def sources():
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-function",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),

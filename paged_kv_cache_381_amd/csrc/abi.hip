@@ -106,6 +106,10 @@ int pkv_split_grid(const void *kernel, int block_threads, size_t lds_bytes, cons
     if (c.kernel == kernel && c.device == dev && c.lds == lds_bytes) hit = &c;
   if (!hit) {
     Occ o{kernel, dev, lds_bytes, 0, 0};
+    if (lds_bytes > 65536) {
+      if (hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes))
+        return (int)e;
+    }
     if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.per_cu, kernel, block_threads, lds_bytes))
       return (int)e;
     if (hipError_t e = hipDeviceGetAttribute(&o.cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
@@ -162,6 +166,8 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   if (int rc = min_chunks(opts, &mc)) return rc;
   const int kernel = choose_kernel(layout, G, opts);
   if (kernel != 1 && kernel != 2) return pkv_set_error(PKV_ERR_INVALID, "unknown kernel %d", kernel);
+  if (opts && (opts->waves_per_simd < 0 || opts->waves_per_simd > 2))
+    return pkv_set_error(PKV_ERR_INVALID, "waves_per_simd must be 0, 1 or 2 (got %d)", opts->waves_per_simd);
   if (kernel == 2 && layout->kv_dtype != PKV_BF16)
     return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16 cache");
   if (num_seqs > PKV_MAX_SPLIT_SEQS)
@@ -189,6 +195,7 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   a.scale_log2 = scale * 1.4426950408889634f;
   a.stream = stream;
   a.min_cpw = mc;
+  a.waves_per_simd = opts && opts->waves_per_simd ? opts->waves_per_simd : 1;
   a.maxp = split_maxp(max_context_len, mc);
   const size_t rows = (size_t)num_seqs * num_q_heads * a.maxp;
   char *ws = static_cast<char *>(workspace);

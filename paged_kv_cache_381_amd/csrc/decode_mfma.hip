@@ -36,6 +36,10 @@
 // ahead; chunk c+1's K is requested as soon as chunk c's score MFMAs have
 // consumed the K registers and its V once the PV MFMAs have consumed V, so a
 // wave always has a chunk of loads in flight through its own math.
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -54,13 +58,14 @@ __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-#ifndef PKV_MFMA_MIN_WAVES_PER_SIMD
-#define PKV_MFMA_MIN_WAVES_PER_SIMD 1
+// Chunks of K/V a wave keeps in registers: the one being computed and
+// NBUF - 1 in flight behind it.
+#ifndef PKV_MFMA_NBUF
+#define PKV_MFMA_NBUF 2
 #endif
 
-template <int D, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_MIN_WAVES_PER_SIMD)))
-void decode_mfma_kernel(SplitParams P) {
+template <int D, int W, int NB>
+__global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
   constexpr int TILE = 16 * D;
@@ -72,80 +77,87 @@ void decode_mfma_kernel(SplitParams P) {
   Share sh;
   if (!split_begin<W, D>(P, s_incl, s_wave, sh)) return;
   const int64_t lo = sh.lo, hi = sh.hi;
-  Cursor cur = sh.first();
 
   const int r16 = lane & 15, grp = lane >> 4;
   // Row r16 of the score MFMAs holds a token of block (r16 >> 3); see header.
   const int ksel = r16 >> 3;
   const int ktx = ((r16 >> 2) & 1) * 8 + (r16 & 3);
   const int vsel = grp >> 1, vhalf = grp & 1;
-
   const uint16_t *kpool = reinterpret_cast<const uint16_t *>(P.k_pool);
   const uint16_t *vpool = reinterpret_cast<const uint16_t *>(P.v_pool);
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(P.q);
-  bf16x8_t qb[NKK];
-  uint4 ax[NKK], ay[NKK], va[NNN];
+  const int qh = min(r16, G - 1);  // columns G..15 are zero; their lanes read row G-1 and discard it
 
-  auto load_q = [&](const Cursor &c) {
-    // Columns G..15 of the B operand are zero; their lanes read row G-1 (in
-    // bounds) and discard it.
-    const int h = min(r16, G - 1);
-    const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + h) * D);
+  // Per buffer: the chunk's cursor, physical blocks, query slices, K and V.
+  Cursor cq[NB];
+  int pa[NB], pb[NB];
+  // With two buffers the next chunk's query slices load after the current
+  // chunk's scores, so one set of registers serves; deeper pipelines keep one
+  // set per buffer.
+  constexpr int NQ = NB == 2 ? 1 : NB;
+  bf16x8_t qb[NQ][NKK];
+  uint4 ax[NB][NKK], ay[NB][NKK], va[NB][NNN];
+
+  auto issue = [&](auto bi) {  // loads of the chunk held in buffer bi
+    constexpr int I = decltype(bi)::value;
+    constexpr int QI = NQ == 1 ? 0 : I;
+    const Cursor &c = cq[I];
+    const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + qh) * D);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint4 u = qr[4 * kk + grp];
-      qb[kk] = as_bf16x8(r16 < G ? u : make_uint4(0, 0, 0, 0));
+      qb[QI][kk] = as_bf16x8(r16 < G ? u : make_uint4(0, 0, 0, 0));
     }
-  };
-  auto load_k = [&](int g, int pa, int pb) {
-    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb : pa) * H + g) * TILE);
+    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + c.g) * TILE);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const int c = 4 * kk + grp;
-      ax[kk] = kt[c * 16 + ktx];
-      ay[kk] = kt[c * 16 + ktx + 4];
+      const int cc = 4 * kk + grp;
+      ax[I][kk] = kt[cc * 16 + ktx];
+      ay[I][kk] = kt[cc * 16 + ktx + 4];
     }
   };
-  auto load_v = [&](int g, int pa, int pb) {
-    const uint4 *vt = reinterpret_cast<const uint4 *>(vpool + ((size_t)(vsel ? pb : pa) * H + g) * TILE);
+  auto issue_v = [&](auto bi) {
+    constexpr int I = decltype(bi)::value;
+    const uint4 *vt = reinterpret_cast<const uint4 *>(vpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + cq[I].g) * TILE);
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn) va[nn] = vt[2 * (16 * nn + r16) + vhalf];
+    for (int nn = 0; nn < NNN; ++nn) va[I][nn] = vt[2 * (16 * nn + r16) + vhalf];
   };
-
-  int pa, pb;
-  sh.blocks(cur, pa, pb);
-  load_q(cur);
-  load_k(cur.g, pa, pb);
-  load_v(cur.g, pa, pb);
-  Cursor nxt = cur;
-  int npa = 0, npb = 0;
-  if (lo + 1 < hi) {
-    nxt = sh.next(cur);
-    sh.blocks(nxt, npa, npb);
-  }
 
   f32x4_t o[NNN];
 #pragma unroll
   for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  for (int64_t x = lo; x < hi; ++x) {
+  // Prologue: chunks lo .. lo+NB-2 are requested, chunk lo+NB-1 located.
+  cq[0] = sh.first();
+  sh.blocks(cq[0], pa[0], pb[0]);
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((lo + Is < hi ? (void)(Is == 0 ? 0 : (cq[Is] = sh.next(cq[Is - (Is > 0)]), sh.blocks(cq[Is], pa[Is], pb[Is]), 0)) : (void)0), ...);
+  }(std::make_integer_sequence<int, NB>{});
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((lo + Is < hi && Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}), issue_v(std::integral_constant<int, Is>{})) : (void)0), ...);
+  }(std::make_integer_sequence<int, NB>{});
+
+  int64_t x = lo;
+  // One step computes chunk x from buffer I, requests chunk x+NB-1 into the
+  // buffer chunk x-1 used, and locates chunk x+NB into buffer I.
+  auto step = [&](auto bi) -> bool {
+    constexpr int I = decltype(bi)::value;
+    constexpr int J = (I + NB - 1) % NB;
+    constexpr int QI = NQ == 1 ? 0 : I;
     f32x4_t sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax[kk]), qb[kk], sx, 0, 0, 0);
-      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ay[kk]), qb[kk], sy, 0, 0, 0);
+      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax[I][kk]), qb[QI][kk], sx, 0, 0, 0);
+      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ay[I][kk]), qb[QI][kk], sy, 0, 0, 0);
     }
-    const bool more = x + 1 < hi;
-    const bool seg_end = !more || nxt.j == 0;
-    if (more) {
-      if (nxt.j == 0) load_q(nxt);  // the score MFMAs above have consumed qb
-      load_k(nxt.g, npa, npb);
-    }
+    const bool far = x + NB - 1 < hi;
+    if (far) issue(std::integral_constant<int, J>{});
 
+    const Cursor &cur = cq[I];
     const int n = cur.n;
     const int tok0 = 32 * cur.j;
-    const int tb = tok0 + 16 * (grp >> 1) + 8 * (grp & 1);
+    const int tb = tok0 + 16 * vsel + 8 * vhalf;  // this lane's first token (scores and V)
     float s[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -171,15 +183,16 @@ void decode_mfma_kernel(SplitParams P) {
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) o[nn] *= alpha;
     if (tok0 + 32 > n) {  // slots past the context may hold anything, NaN included
-      const int nvalid = min(max(n - tb, 0), 8);  // tb is this lane's first V token
+      const int nvalid = min(max(n - tb, 0), 8);
 #pragma unroll
-      for (int nn = 0; nn < NNN; ++nn) va[nn] = keep_first(va[nn], nvalid);
+      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = keep_first(va[I][nn], nvalid);
     }
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[nn]), pv, o[nn], 0, 0, 0);
-    if (more) load_v(nxt.g, npa, npb);
+    for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[I][nn]), pv, o[nn], 0, 0, 0);
+    if (far) issue_v(std::integral_constant<int, J>{});
 
-    if (seg_end) {
+    const bool last = x + 1 >= hi;
+    if (last || cur.j == cur.cnt - 1) {  // the piece ends here
       const float lsum = rows_sum4(l);
       const bool whole = sh.whole(cur);
       if (r16 < G) {
@@ -205,14 +218,19 @@ void decode_mfma_kernel(SplitParams P) {
       m = -INFINITY;
       l = 0.f;
     }
-
-    if (more) {
-      cur = nxt;
-      if (x + 2 < hi) {
-        nxt = sh.next(cur);
-        sh.blocks(nxt, npa, npb);
-      }
+    if (last) return false;
+    if (x + NB < hi) {
+      cq[I] = sh.next(cq[J]);
+      sh.blocks(cq[I], pa[I], pb[I]);
     }
+    ++x;
+    return true;
+  };
+  for (;;) {
+    const bool go = [&]<int... Is>(std::integer_sequence<int, Is...>) {
+      return (step(std::integral_constant<int, Is>{}) && ...);
+    }(std::make_integer_sequence<int, NB>{});
+    if (!go) break;
   }
 }
 
@@ -223,8 +241,12 @@ constexpr int kWaves = PKV_MFMA_WAVES;
 
 template <int D>
 int launch(const pkv_decode_args &a, const SplitParams &p) {
-  auto kern = decode_mfma_kernel<D, kWaves>;
-  const size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves);
+  auto kern = decode_mfma_kernel<D, kWaves, PKV_MFMA_NBUF>;
+  size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves);
+  // One wave per SIMD: a workgroup takes more than half of a CU's 160 KiB of
+  // LDS, so no second one is placed beside it.  Two waves on one SIMD do not
+  // progress alike (the older wins issue), which leaves the younger behind.
+  if (a.waves_per_simd == 1) lds = std::max<size_t>(lds, PKV_LDS_ONE_WG_PER_CU);
   int nwg = 0;
   if (int rc = pkv_split_grid(reinterpret_cast<const void *>(kern), 64 * kWaves, lds, a, &nwg)) return rc;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kWaves), lds, reinterpret_cast<hipStream_t>(a.stream), p);

@@ -33,6 +33,7 @@ struct pkv_decode_args {
   int32_t *ws_hdr;   // [2 + B] schedule header
   int32_t maxp;      // partial slots per (sequence, query head)
   int32_t min_cpw;   // fewest 32-token chunks per wave
+  int32_t waves_per_simd;  // resident waves per SIMD of the matrix-core kernel (1 or 2)
   void *stream;
 };
 
@@ -42,6 +43,8 @@ struct pkv_decode_args {
 #ifndef PKV_DEFAULT_MIN_CHUNKS
 #define PKV_DEFAULT_MIN_CHUNKS 4
 #endif
+// Dynamic LDS that keeps a CU (160 KiB of LDS) to one workgroup.
+#define PKV_LDS_ONE_WG_PER_CU (81 * 1024)
 // Largest batch of the balanced split (its chunk scan lives in LDS).
 #define PKV_MAX_SPLIT_SEQS 8192
 

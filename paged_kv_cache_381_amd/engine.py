@@ -82,9 +82,20 @@ class PagedKVCache:
         L.paged_kv_append(self.layout, self.k_pools[layer], self.v_pools[layer], k_new, v_new, slots_dev)
 
     def decode(self, layer: int, out, q, tables_dev, ctx_dev, max_ctx: int, scale: float, workspace=None,
-               partition_tokens=0, kernel=0, events=None):
+               partition_tokens=0, kernel=0, events=None, waves_per_simd=None):
+        if waves_per_simd is None:
+            waves_per_simd = self.waves_per_simd()
         L.paged_attention_decode(self.layout, out, q, self.k_pools[layer], self.v_pools[layer], tables_dev, ctx_dev,
-                                 max_ctx, scale, workspace, partition_tokens, kernel, events)
+                                 max_ctx, scale, workspace, partition_tokens, kernel, events,
+                                 waves_per_simd=waves_per_simd)
+
+    def waves_per_simd(self) -> int:
+        """Two resident waves per SIMD when the live sequences read their
+        blocks more than twice over on average (shared prompts, parallel
+        samples): such blocks are served from L2, where more waves in flight
+        pay; otherwise one, which streams from HBM fastest."""
+        st = self.stats()
+        return 2 if st["tokens_stored"] and st["tokens_logical"] > 2 * st["tokens_stored"] else 1
 
     def workspace(self, num_seqs, num_q_heads, max_ctx, partition_tokens=0, kernel=0):
         nbytes = L.paged_attention_workspace_bytes(self.layout, num_seqs, num_q_heads, max_ctx, partition_tokens,
@@ -150,11 +161,11 @@ class GpuWorkload:
         self.scale = 1.0 / math.sqrt(wl.head_dim)
         self.out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.float32, device=self.device)
 
-    def decode(self, layer=0, partition_tokens=0, kernel=0, events=None, workspace=None, out=None):
+    def decode(self, layer=0, partition_tokens=0, kernel=0, events=None, workspace=None, out=None, waves_per_simd=None):
         if workspace is None:
             workspace = self.cache.workspace(self.wl.batch, self.wl.num_q_heads, self.max_ctx, partition_tokens,
                                              kernel)
         out = self.out if out is None else out
         self.cache.decode(layer, out, self.q, self.tables_dev, self.ctx_dev, self.max_ctx, self.scale, workspace,
-                          partition_tokens, kernel, events)
+                          partition_tokens, kernel, events, waves_per_simd)
         return out
