@@ -69,13 +69,12 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
   constexpr int TILE = 16 * D;
-  extern __shared__ __align__(16) int32_t s_incl[];  // [B] inclusive chunk scan, then [W] scratch
-  int32_t *s_wave = s_incl + P.B;
+  extern __shared__ __align__(16) int32_t s_lds[];  // chunk scan, lengths, wave totals
 
   const int lane = threadIdx.x & 63;
   const int H = P.H, G = P.G;
   Share sh;
-  if (!split_begin<W, D>(P, s_incl, s_wave, sh)) return;
+  if (!split_begin<W, D>(P, s_lds, sh)) return;
   const int64_t lo = sh.lo, hi = sh.hi;
 
   const int r16 = lane & 15, grp = lane >> 4;

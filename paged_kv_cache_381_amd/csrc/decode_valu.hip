@@ -79,14 +79,13 @@ __global__ __launch_bounds__(64 * W) void decode_valu_kernel(SplitParams P) {
   constexpr int TILE = 16 * D;
   constexpr int QN = GP * D / 64;  // query elements each lane stages
   constexpr bool QREG = GP * NL * X <= 64;
-  extern __shared__ __align__(16) int32_t s_incl[];  // [B] chunk scan, [W] wave totals, then per-wave slices
-  int32_t *s_wave = s_incl + P.B;
+  extern __shared__ __align__(16) int32_t s_lds[];  // chunk scan, lengths, wave totals, then per-wave slices
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float *q_lds = reinterpret_cast<float *>(s_incl + ((P.B + W + 3) & ~3)) + w * wave_lds_floats<D, GP>();
+  float *q_lds = reinterpret_cast<float *>(s_lds + pkv_split_lds_ints(P.B, W)) + w * wave_lds_floats<D, GP>();
   float *p_lds = q_lds + GP * D;  // [GP][32]
 
   Share sh;
-  if (!split_begin<W, D>(P, s_incl, s_wave, sh)) return;
+  if (!split_begin<W, D>(P, s_lds, sh)) return;
   const int64_t lo = sh.lo, hi = sh.hi;
   const int H = P.H, G = P.G;
   const int tok = lane & 15, row = lane >> 4;

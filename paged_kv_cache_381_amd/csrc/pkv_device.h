@@ -115,17 +115,20 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // Chunks of a sequence of (clamped) length n.
 __device__ __forceinline__ int chunks_of(int n) { return (n + 31) >> 5; }
 
-// Inclusive scan of chunk counts over the batch into s_incl[0..B) (LDS), by
-// all 64*W threads of the workgroup.  Returns the total (chunks per kv head).
+// Inclusive scan of chunk counts over the batch into s_incl[0..B) and the
+// clamped lengths into s_len[0..B) (LDS), by all 64*W threads of the
+// workgroup.  Returns the total (chunks per kv head).
 template <int W>
-__device__ int scan_chunks(const SplitParams &P, int32_t *s_incl, int32_t *s_wave) {
+__device__ int scan_chunks(const SplitParams &P, int32_t *s_incl, int32_t *s_len, int32_t *s_wave) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int NT = 64 * W;
   const int per = (P.B + NT - 1) / NT;
   const int i0 = tid * per, i1 = min(i0 + per, P.B);
   int local = 0;
   for (int i = i0; i < i1; ++i) {
-    const int c = chunks_of(clamp_len(P.ctx[i], P.max_blocks, P.max_ctx));
+    const int n = clamp_len(P.ctx[i], P.max_blocks, P.max_ctx);
+    const int c = chunks_of(n);
+    s_len[i] = n;
     s_incl[i] = c;
     local += c;
   }
@@ -172,10 +175,12 @@ __device__ __forceinline__ int xcd_logical(int wg, int nwg) {
   return (nwg & 7) ? wg : (wg & 7) * (nwg >> 3) + (wg >> 3);
 }
 
-// LDS of a balanced-split workgroup: the chunk scan and W wave totals,
-// padded to 16 bytes, then extra_floats of per-wave slices.
+// LDS of a decode workgroup: the chunk scan, the clamped lengths and W wave
+// totals, padded to 16 bytes (int32 units: pkv_split_lds_ints), then
+// extra_floats of per-wave slices.
+__host__ __device__ inline int pkv_split_lds_ints(int num_seqs, int waves) { return (2 * num_seqs + waves + 3) & ~3; }
 inline size_t pkv_split_lds_bytes(int num_seqs, int waves, int extra_floats = 0) {
-  return (size_t)((num_seqs + waves + 3) & ~3) * sizeof(int32_t) + (size_t)extra_floats * sizeof(float);
+  return (size_t)pkv_split_lds_ints(num_seqs, waves) * sizeof(int32_t) + (size_t)extra_floats * sizeof(float);
 }
 
 inline SplitParams pkv_split_params(const pkv_decode_args &a) {
@@ -213,6 +218,7 @@ struct Cursor {
 // One wave's share [lo, hi) of the chunk list and the walk through it.
 struct Share {
   const int32_t *s_incl;  // LDS: inclusive chunk scan over the batch
+  const int32_t *s_len;   // LDS: clamped lengths
   const int32_t *ctx;
   const int32_t *tables;
   int B, max_blocks, max_ctx, num_blocks;
@@ -221,7 +227,7 @@ struct Share {
   int64_t lo, hi;
 
   __device__ int cnt_of(int b) const { return uniform(s_incl[b] - (b ? s_incl[b - 1] : 0)); }
-  __device__ int len_of(int b) const { return clamp_len(sload_i32(ctx + b), max_blocks, max_ctx); }
+  __device__ int len_of(int b) const { return uniform(s_len[b]); }
 
   // The share's first chunk: kv head lo / c_seq, then the first sequence
   // whose chunks end past the remainder.
@@ -266,10 +272,14 @@ struct Share {
 
   // Physical blocks of a chunk; the second is the first again when the chunk
   // holds no token of it (only the last chunk of a segment can).
+  // Both entries are read at once (the second at a row-clamped index, so it
+  // never waits for the length and never leaves the row).
   __device__ void blocks(const Cursor &c, int &pa, int &pb) const {
-    const int32_t *row = tables + (size_t)c.b * max_blocks + 2 * c.j;
-    pa = clamp_block(sload_i32(row), num_blocks);
-    pb = (32 * c.j + 16 < c.n) ? clamp_block(sload_i32(row + 1), num_blocks) : pa;
+    const int32_t *row = tables + (size_t)c.b * max_blocks;
+    const int a = sload_i32(row + 2 * c.j);
+    const int b2 = sload_i32(row + min(2 * c.j + 1, max_blocks - 1));
+    pa = clamp_block(a, num_blocks);
+    pb = (32 * c.j + 16 < c.n) ? clamp_block(b2, num_blocks) : pa;
   }
 
   // Whether this wave holds every chunk of the cursor's segment.
@@ -284,9 +294,10 @@ struct Share {
 // the merge kernel's header and zero rows for empty sequences (workgroup 0),
 // and this wave's share.  Returns false when the wave has no work.
 template <int W, int D>
-__device__ bool split_begin(const SplitParams &P, int32_t *s_incl, int32_t *s_wave, Share &sh) {
+__device__ bool split_begin(const SplitParams &P, int32_t *s_lds, Share &sh) {
   const int tid = threadIdx.x, w = tid >> 6;
-  const int64_t c_seq = scan_chunks<W>(P, s_incl, s_wave);
+  int32_t *s_incl = s_lds, *s_len = s_lds + P.B, *s_wave = s_lds + 2 * P.B;
+  const int64_t c_seq = scan_chunks<W>(P, s_incl, s_len, s_wave);
   const int64_t c_tot = (int64_t)P.H * c_seq;
   const int nwg = gridDim.x;
   const int nwe = waves_used(c_tot, nwg * W, P.min_cpw);
@@ -303,6 +314,7 @@ __device__ bool split_begin(const SplitParams &P, int32_t *s_incl, int32_t *s_wa
     }
   }
   sh.s_incl = s_incl;
+  sh.s_len = s_len;
   sh.ctx = P.ctx;
   sh.tables = P.tables;
   sh.B = P.B;
