@@ -11,9 +11,11 @@
 
 namespace {
 
-// One workgroup per token: K moves as 16-byte chunks (one X-element group of
-// the K layout is contiguous in both source and pool), V element by element
-// (consecutive d of one token are 16 slots apart in the V layout).
+// One workgroup per token.  A thread moves one 16-byte unit of X elements of
+// K and of V: the K unit is contiguous in the pool too (one X-element group of
+// the K layout), the V unit's elements land 16 slots apart (the V layout is
+// [d][16 tokens]).  The token's rows are requested before its slot id is
+// known, so the kernel waits for one round trip of memory, not two.
 template <typename E>
 __global__ __launch_bounds__(256) void append_kernel(E *__restrict__ kpool, E *__restrict__ vpool,
                                                      const E *__restrict__ k_new, const E *__restrict__ v_new,
@@ -21,21 +23,24 @@ __global__ __launch_bounds__(256) void append_kernel(E *__restrict__ kpool, E *_
                                                      int num_blocks) {
   constexpr int X = 16 / sizeof(E);
   const int t = blockIdx.x;
+  const int cpr = D / X;  // 16-byte units per head row
+  const int units = H * cpr;
+  const uint4 *krow = reinterpret_cast<const uint4 *>(k_new + (size_t)t * H * D);
+  const uint4 *vrow = reinterpret_cast<const uint4 *>(v_new + (size_t)t * H * D);
   const int64_t s = slots[t];
-  if (s < 0 || s >= (int64_t)num_blocks * 16) return;
-  const int64_t blk = s >> 4;
-  const int off = (int)(s & 15);
-  const int cpr = D / X;  // 16-byte chunks per head row
-  const E *krow = k_new + (size_t)t * H * D;
-  const E *vrow = v_new + (size_t)t * H * D;
-  for (int i = threadIdx.x; i < H * cpr; i += blockDim.x) {
+  for (int i = threadIdx.x; i < units; i += blockDim.x) {
+    const uint4 kv = krow[i];
+    const uint4 vv = vrow[i];
+    if (s < 0 || s >= (int64_t)num_blocks * 16) return;  // uniform across the workgroup
+    const int64_t blk = s >> 4;
+    const int off = (int)(s & 15);
     const int g = i / cpr, c = i - g * cpr;
-    const uint4 val = *reinterpret_cast<const uint4 *>(krow + (size_t)g * D + c * X);
-    *reinterpret_cast<uint4 *>(kpool + ((((size_t)blk * H + g) * cpr + c) * 16 + off) * X) = val;
-  }
-  for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
-    const int g = i / D, d = i - g * D;
-    vpool[(((size_t)blk * H + g) * D + d) * 16 + off] = vrow[i];
+    *reinterpret_cast<uint4 *>(kpool + ((((size_t)blk * H + g) * cpr + c) * 16 + off) * X) = kv;
+    E ve[X];
+    __builtin_memcpy(ve, &vv, sizeof vv);
+    E *vdst = vpool + (((size_t)blk * H + g) * D + (size_t)c * X) * 16 + off;
+#pragma unroll
+    for (int e = 0; e < X; ++e) vdst[e * 16] = ve[e];
   }
 }
 
@@ -58,7 +63,8 @@ int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const voi
                       const int64_t *slots, int32_t num_tokens, void *stream) {
   if (num_tokens == 0) return 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  dim3 grid(num_tokens), block(128);
+  const int units = L->num_kv_heads * L->head_dim * pkv_elem_bytes(L->kv_dtype) / 16;
+  dim3 grid(num_tokens), block(units < 256 ? (units + 63) / 64 * 64 : 256);
   if (L->kv_dtype == PKV_BF16)
     hipLaunchKernelGGL(append_kernel<uint16_t>, grid, block, 0, st, (uint16_t *)k_pool, (uint16_t *)v_pool,
                        (const uint16_t *)k_new, (const uint16_t *)v_new, slots, L->num_kv_heads, L->head_dim,

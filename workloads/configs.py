@@ -199,8 +199,15 @@ class Instance:
         return np.stack([self.own_kv(b, which)[-1] for b in range(self.wl.batch)], axis=0)
 
     def kv_bytes_logical(self) -> int:
+        """K and V bytes the decode step reads: every sequence's whole context."""
         w = self.wl
         return int(self.ctx.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+
+    def kv_bytes_unique(self) -> int:
+        """K and V bytes of distinct stored tokens (a shared prefix counts once)."""
+        w = self.wl
+        tokens = int(self.ctx.astype(np.int64).sum()) - (w.batch - 1) * w.prefix_len
+        return tokens * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
 
 
 WORKLOADS = {
