@@ -108,7 +108,8 @@ int pkv_block_incref(pkv_pool *pool, int32_t block);
 int pkv_block_free(pkv_pool *pool, int32_t block);
 /* Reference count of a block (0 = free) into *out. */
 int pkv_block_refcount(const pkv_pool *pool, int32_t block, int32_t *out);
-/* Number of free blocks into *out. */
+/* Number of blocks that can be handed out (free, or idle in the prefix cache)
+ * into *out. */
 int pkv_pool_num_free(const pkv_pool *pool, int32_t *out);
 
 /* --------------------------------------------------------------- sequences */
@@ -149,11 +150,51 @@ int pkv_batch_block_tables(const pkv_pool *pool, const int64_t *ids, int32_t num
                            int32_t max_blocks_per_seq, int32_t *tables_out,
                            int32_t *context_lens_out);
 
+/* ------------------------------------------------------------ prefix cache */
+/* Prefix caching [KV Cache 工程学 §15.6; 新一代 KV Cache 管理 §8.3]: a full
+ * 16-token block is identified by a hash of the whole prefix that ends with
+ * it (64-bit FNV-1a over the previous block's key and the block's 16 token
+ * ids, little-endian; the block's tokens and its parent key are checked on a
+ * hit), so a request whose prompt starts with a cached prefix points its
+ * block table at the cached blocks and skips their prefill.  A cached block
+ * whose reference count drops to zero stays cached ("idle"); idle blocks are
+ * evicted least recently used first, only when the free stack is empty.
+ * The blocks of one sequence that turn idle together enter the LRU deepest
+ * first.  Off by default. */
+typedef struct {
+  int64_t lookups;      /* pkv_seq_create_from_prefix calls with the cache on */
+  int64_t query_tokens; /* full-block tokens looked up */
+  int64_t hit_tokens;   /* tokens found cached (prefill skipped) */
+  int64_t registered;   /* blocks entered into the cache */
+  int64_t evictions;    /* idle cached blocks taken for reuse */
+  int32_t cached_blocks; /* blocks in the cache now (in use or idle) */
+  int32_t idle_blocks;   /* cached blocks held by no sequence */
+  double hit_rate;      /* hit_tokens / query_tokens */
+} pkv_prefix_stats;
+
+/* Turn the prefix cache on (enable != 0) or off (idle cached blocks return to
+ * the free pool, oldest first). */
+int pkv_prefix_cache_enable(pkv_pool *pool, int32_t enable);
+/* New sequence whose table starts with the longest run of cached full blocks
+ * matching the first tokens of token_ids[0..n) (each gains a reference);
+ * *n_cached_out receives its length, a multiple of 16.  The caller appends
+ * the remaining n - *n_cached_out tokens, stores their K/V, and registers
+ * the prompt.  With the cache off the sequence starts empty. */
+int pkv_seq_create_from_prefix(pkv_pool *pool, const int32_t *token_ids, int32_t n, int64_t *id_out,
+                               int32_t *n_cached_out);
+/* Enter the full blocks of a sequence's first n tokens (token_ids[0..n),
+ * n <= its length, K/V already stored) into the cache; content that is
+ * already cached is left as it is.  *n_registered (nullable) receives the
+ * number of blocks added. */
+int pkv_seq_register_prefix(pkv_pool *pool, int64_t id, const int32_t *token_ids, int32_t n,
+                            int32_t *n_registered);
+int pkv_prefix_cache_stats(const pkv_pool *pool, pkv_prefix_stats *out);
+
 /* -------------------------------------------------------------- statistics */
 typedef struct {
   int32_t num_blocks;
-  int32_t num_free;
-  int32_t num_used;
+  int32_t num_free;        /* blocks that can be handed out: free, or idle cached */
+  int32_t num_used;        /* blocks held by at least one reference */
   int32_t num_shared;      /* blocks with reference count > 1 */
   int64_t num_seqs;        /* live sequences */
   int64_t tokens_logical;  /* sum of live sequence lengths */

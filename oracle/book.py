@@ -29,9 +29,20 @@ Readings where the pages are silent (each one is listed in the design notes):
 * an append reserves all of its tokens or none (state unchanged on
   failure); a batch append is all-or-nothing over the whole batch;
 * sequence ids are handed out 0, 1, 2, ... and never reused.
+* prefix cache [KV Cache 工程学 §15.6; 新一代 KV Cache 管理 §8.3]: only full
+  blocks are cached; a block is identified by the whole token prefix that
+  ends with it (here the exact tuple of token ids; the library hashes it);
+  a request points its table at the longest run of cached blocks that
+  begins its prompt and stops at the first miss; registration after the
+  prefill adds the prompt's full blocks whose content is not cached yet; a
+  cached block held by no sequence stays cached ("idle") and is taken, least
+  recently used first, only when the free stack is empty; a sequence's
+  cached blocks that turn idle together enter the LRU deepest first; turning
+  the cache off returns idle blocks to the free stack, oldest first.
 
 Parity unpinned items: none; every behaviour here is checked by the
-invariant and worked-number tests in ``tests/test_oracle_book.py``.
+invariant and worked-number tests in ``tests/test_oracle_book.py`` and
+``tests/test_prefix_cache.py`` (the pages' two-user example).
 """
 from __future__ import annotations
 
@@ -60,12 +71,27 @@ class Book:
         self.ref = [0] * num_blocks
         self.seqs = {}                   # id -> {"table": [...], "len": n}
         self.next_id = 0
+        # Prefix cache: exact keys (the whole token prefix ending with a full
+        # block), an idle list of cached blocks held by no sequence (oldest
+        # first) and counters.
+        self.pc_on = False
+        self.pc = {}                     # key tuple -> block
+        self.key_of = {}                 # block -> key tuple
+        self.lru = []
+        self.pst = {"lookups": 0, "query_tokens": 0, "hit_tokens": 0, "registered": 0, "evictions": 0}
 
     # -- blocks ---------------------------------------------------------------
     def alloc(self) -> int:
-        if not self.free:
+        """The top of the free stack, else the least recently used idle
+        cached block, which leaves the cache."""
+        if self.free:
+            blk = self.free.pop()
+        elif self.lru:
+            blk = self.lru.pop(0)
+            del self.pc[self.key_of.pop(blk)]
+            self.pst["evictions"] += 1
+        else:
             raise BookError("NO_BLOCKS", "pool exhausted")
-        blk = self.free.pop()
         self.ref[blk] = 1
         return blk
 
@@ -85,6 +111,12 @@ class Book:
             raise BookError("REFCOUNT", f"free of free block {blk}")
         self.ref[blk] -= 1
         if self.ref[blk] == 0:
+            self._release(blk)
+
+    def _release(self, blk: int):
+        if blk in self.key_of:
+            self.lru.append(blk)
+        else:
             self.free.append(blk)
 
     def refcount(self, blk: int) -> int:
@@ -92,7 +124,8 @@ class Book:
         return self.ref[blk]
 
     def num_free(self) -> int:
-        return len(self.free)
+        """Blocks that can be handed out: free, or idle in the prefix cache."""
+        return len(self.free) + len(self.lru)
 
     # -- sequences ------------------------------------------------------------
     def _seq(self, sid: int):
@@ -143,13 +176,13 @@ class Book:
             raise BookError("INVALID", "negative token count")
         for sid in sids:
             self._seq(sid)
-        saved = (list(self.free), list(self.ref), copy.deepcopy(self.seqs))
+        saved = copy.deepcopy((self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst))
         slots, cow = [], []
         try:
             for sid in sids:
                 self._append_one_seq(sid, n, slots, cow)
         except BookError:
-            self.free, self.ref, self.seqs = saved[0], saved[1], saved[2]
+            self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst = saved
             raise
         return slots, cow
 
@@ -164,9 +197,74 @@ class Book:
         for blk, k in held.items():
             if self.ref[blk] < k:
                 raise BookError("REFCOUNT", f"free of a sequence holding block {blk} {k} times, refcount {self.ref[blk]}")
+        # Blocks reaching zero go back in table order; cached ones turn idle
+        # deepest first (of a prefix released together, the tail is evicted
+        # before the head: a cached block is reachable only through its prefix).
+        idle = []
         for blk in s["table"]:
-            self.decref(blk)
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                if blk in self.key_of:
+                    idle.append(blk)
+                else:
+                    self.free.append(blk)
+        self.lru.extend(reversed(idle))
         del self.seqs[sid]
+
+    # -- prefix cache [KV Cache 工程学 §15.6; 新一代 KV Cache 管理 §8.3] ----------
+    def enable_prefix_cache(self, on: bool):
+        if not on and self.pc_on:
+            while self.lru:
+                self.free.append(self.lru.pop(0))
+            self.pc.clear()
+            self.key_of.clear()
+        self.pc_on = bool(on)
+
+    def create_from_prefix(self, tokens):
+        """New sequence pointing at the longest run of cached full blocks that
+        begins the prompt; returns (id, tokens found cached)."""
+        sid = self.create()
+        s = self.seqs[sid]
+        if self.pc_on:
+            for i in range(len(tokens) // BLOCK_SIZE):
+                blk = self.pc.get(tuple(tokens[:BLOCK_SIZE * (i + 1)]))
+                if blk is None:
+                    break
+                if self.ref[blk] == 0:
+                    self.lru.remove(blk)
+                self.ref[blk] += 1
+                s["table"].append(blk)
+                s["len"] += BLOCK_SIZE
+            self.pst["lookups"] += 1
+            self.pst["query_tokens"] += len(tokens) // BLOCK_SIZE * BLOCK_SIZE
+            self.pst["hit_tokens"] += s["len"]
+        return sid, s["len"]
+
+    def register_prefix(self, sid: int, tokens, n: int) -> int:
+        """Cache the full blocks of the first n tokens of sequence sid (whose
+        K/V are stored); content already cached is left alone."""
+        s = self._seq(sid)
+        if n < 0 or n > s["len"]:
+            raise BookError("INVALID", "register beyond the sequence")
+        added = 0
+        if self.pc_on:
+            for i in range(n // BLOCK_SIZE):
+                key = tuple(tokens[:BLOCK_SIZE * (i + 1)])
+                blk = s["table"][i]
+                if key in self.pc or blk in self.key_of:
+                    continue
+                self.pc[key] = blk
+                self.key_of[blk] = key
+                added += 1
+            self.pst["registered"] += added
+        return added
+
+    def prefix_stats(self) -> dict:
+        st = dict(self.pst)
+        st["cached_blocks"] = len(self.pc)
+        st["idle_blocks"] = len(self.lru)
+        st["hit_rate"] = st["hit_tokens"] / st["query_tokens"] if st["query_tokens"] else 0.0
+        return st
 
     def seq_len(self, sid: int) -> int:
         return self._seq(sid)["len"]
@@ -176,7 +274,7 @@ class Book:
 
     # -- statistics -----------------------------------------------------------
     def stats(self) -> dict:
-        used = self.num_blocks - len(self.free)
+        used = self.num_blocks - self.num_free()
         shared = sum(1 for r in self.ref if r > 1)
         logical = sum(s["len"] for s in self.seqs.values())
         # A block's fill is the largest number of its slots any holder uses.
@@ -188,7 +286,7 @@ class Book:
         stored = sum(fill.values())
         return {
             "num_blocks": self.num_blocks,
-            "num_free": len(self.free),
+            "num_free": self.num_free(),
             "num_used": used,
             "num_shared": shared,
             "num_seqs": len(self.seqs),

@@ -49,6 +49,12 @@ class pkv_stats(ctypes.Structure):
                 ("internal_fragmentation", ctypes.c_double)]
 
 
+class pkv_prefix_stats(ctypes.Structure):
+    _fields_ = [("lookups", ctypes.c_int64), ("query_tokens", ctypes.c_int64), ("hit_tokens", ctypes.c_int64),
+                ("registered", ctypes.c_int64), ("evictions", ctypes.c_int64), ("cached_blocks", ctypes.c_int32),
+                ("idle_blocks", ctypes.c_int32), ("hit_rate", ctypes.c_double)]
+
+
 class pkv_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("waves_per_simd", ctypes.c_int32),
                 ("ev_begin", ctypes.c_void_p),
@@ -78,6 +84,10 @@ SIGNATURES = {
     "pkv_seq_block_table": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
     "pkv_batch_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
     "pkv_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(pkv_stats)]),
+    "pkv_prefix_cache_enable": (ctypes.c_int, [_P, _I32]),
+    "pkv_seq_create_from_prefix": (ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
+    "pkv_seq_register_prefix": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_prefix_cache_stats": (ctypes.c_int, [_P, ctypes.POINTER(pkv_prefix_stats)]),
     "pkv_kv_bytes_per_token": (_I64, [_PL, _I32]),
     "pkv_pool_bytes": (_I64, [_PL]),
     "pkv_validate_tables": (ctypes.c_int, [_PL, _P, _P, _I32, _I32]),
@@ -249,6 +259,34 @@ def pkv_pool_stats(pool) -> dict:
     s = pkv_stats()
     _check(lib().pkv_pool_stats(pool, ctypes.byref(s)))
     return {f: getattr(s, f) for f, _ in pkv_stats._fields_}
+
+
+def pkv_prefix_cache_enable(pool, enable: bool = True):
+    _check(lib().pkv_prefix_cache_enable(pool, 1 if enable else 0))
+
+
+def pkv_seq_create_from_prefix(pool, token_ids):
+    """(sequence id, tokens found cached) for a prompt of token ids."""
+    toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+    sid, nc = ctypes.c_int64(), ctypes.c_int32()
+    _check(lib().pkv_seq_create_from_prefix(pool, _np_ptr(toks), toks.size, ctypes.byref(sid), ctypes.byref(nc)))
+    return sid.value, nc.value
+
+
+def pkv_seq_register_prefix(pool, seq: int, token_ids, n: int | None = None) -> int:
+    toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+    n = toks.size if n is None else int(n)
+    if n > toks.size:
+        raise ValueError("n exceeds the token ids given")
+    added = ctypes.c_int32()
+    _check(lib().pkv_seq_register_prefix(pool, int(seq), _np_ptr(toks), n, ctypes.byref(added)))
+    return added.value
+
+
+def pkv_prefix_cache_stats(pool) -> dict:
+    s = pkv_prefix_stats()
+    _check(lib().pkv_prefix_cache_stats(pool, ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in pkv_prefix_stats._fields_}
 
 
 def pkv_kv_bytes_per_token(layout: pkv_layout, num_layers: int) -> int:

@@ -14,6 +14,7 @@
 // compiler and its sanitizers.
 #include <algorithm>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 #include <unordered_map>
@@ -63,8 +64,25 @@ struct pkv_pool {
   std::unordered_map<int64_t, Seq> seqs;
   int64_t next_id = 0;
 
+  // Prefix cache [KV Cache 工程学 §15.6; 新一代 KV Cache 管理 §8.3]: a full
+  // block is keyed by a hash of the whole prefix that ends with it, so the
+  // same block content after a different prefix never matches.  A cached
+  // block whose reference count drops to zero stays cached ("idle") in an LRU
+  // list and is evicted only when the free stack is empty.
+  struct CacheEntry {
+    uint64_t key, parent;            // chain hash of this block and of the one before
+    int32_t tok[PKV_BLOCK_SIZE];     // the block's token ids (checked on a hit)
+  };
+  bool pc_on = false;
+  std::vector<CacheEntry> pc;        // per block, meaningful while cached[b]
+  std::vector<uint8_t> cached;
+  std::unordered_map<uint64_t, int32_t> pc_map;
+  std::vector<int32_t> lru_prev, lru_next;  // idle cached blocks, oldest at lru_head
+  int32_t lru_head = -1, lru_tail = -1, n_idle = 0;
+  pkv_prefix_stats pst{};
+
   // Undo log of one all-or-nothing operation.
-  enum class Op { Alloc, TablePush, CowSwap, Len };
+  enum class Op { Alloc, AllocEvict, TablePush, CowSwap, Len };
   struct Undo {
     Op op;
     int64_t seq;
@@ -73,14 +91,70 @@ struct pkv_pool {
   std::vector<Undo> log;
 
   bool valid_block(int32_t b) const { return b >= 0 && b < layout.num_blocks; }
+  int32_t available() const { return (int32_t)free_stack.size() + n_idle; }
 
-  int alloc(int32_t *out) {
-    if (free_stack.empty()) return pkv_set_error(PKV_ERR_NO_BLOCKS, "no free blocks (pool of %d)", layout.num_blocks);
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+  void lru_unlink(int32_t b) {
+    const int32_t p = lru_prev[b], n = lru_next[b];
+    (p >= 0 ? lru_next[p] : lru_head) = n;
+    (n >= 0 ? lru_prev[n] : lru_tail) = p;
+    lru_prev[b] = lru_next[b] = -1;
+    --n_idle;
+  }
+  void lru_push_back(int32_t b) {
+    lru_prev[b] = lru_tail;
+    lru_next[b] = -1;
+    (lru_tail >= 0 ? lru_next[lru_tail] : lru_head) = b;
+    lru_tail = b;
+    ++n_idle;
+  }
+  void lru_push_front(int32_t b) {
+    lru_next[b] = lru_head;
+    lru_prev[b] = -1;
+    (lru_head >= 0 ? lru_prev[lru_head] : lru_tail) = b;
+    lru_head = b;
+    ++n_idle;
+  }
+
+  // Take a block: the top of the free stack, else the least recently used
+  // idle cached block, which leaves the cache.  *evicted tells which.
+  int take(int32_t *out, bool *evicted) {
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+      *evicted = false;
+    } else if (lru_head >= 0) {
+      b = lru_head;
+      lru_unlink(b);
+      pc_map.erase(pc[b].key);
+      cached[b] = 0;
+      ++pst.evictions;
+      *evicted = true;
+    } else {
+      return pkv_set_error(PKV_ERR_NO_BLOCKS, "no free blocks (pool of %d)", layout.num_blocks);
+    }
     ref[b] = 1;
     *out = b;
     return PKV_OK;
+  }
+  int alloc(int32_t *out) {
+    bool ev;
+    return take(out, &ev);
+  }
+  // Reference count reached zero: back to the free stack, or idle in the cache.
+  void release(int32_t b) {
+    if (cached[b])
+      lru_push_back(b);
+    else
+      free_stack.push_back(b);
+  }
+  // Undo of an eviction by take(): the block is cached and the oldest idle again.
+  void unevict(int32_t b) {
+    ref[b] = 0;
+    cached[b] = 1;
+    pc_map[pc[b].key] = b;
+    lru_push_front(b);
+    --pst.evictions;
   }
 
   void rollback() {
@@ -89,6 +163,9 @@ struct pkv_pool {
         case Op::Alloc:  // popped from the top: push back on top
           ref[it->a] = 0;
           free_stack.push_back(it->a);
+          break;
+        case Op::AllocEvict:
+          unevict(it->a);
           break;
         case Op::TablePush:
           seqs[it->seq].table.pop_back();
@@ -112,16 +189,18 @@ struct pkv_pool {
       int32_t pos = s.len;
       if (pos % PKV_BLOCK_SIZE == 0) {
         int32_t b;
-        if (int rc = alloc(&b)) return rc;
-        log.push_back({Op::Alloc, id, b, 0});
+        bool ev;
+        if (int rc = take(&b, &ev)) return rc;
+        log.push_back({ev ? Op::AllocEvict : Op::Alloc, id, b, 0});
         s.table.push_back(b);
         log.push_back({Op::TablePush, id, 0, 0});
       } else if (ref[s.table.back()] > 1) {
         if (*n_cow >= cow_cap)
           return pkv_set_error(PKV_ERR_CAPACITY, "copy-on-write pair buffer too small (cap %d)", cow_cap);
         int32_t old = s.table.back(), b;
-        if (int rc = alloc(&b)) return rc;
-        log.push_back({Op::Alloc, id, b, 0});
+        bool ev;
+        if (int rc = take(&b, &ev)) return rc;
+        log.push_back({ev ? Op::AllocEvict : Op::Alloc, id, b, 0});
         ref[old] -= 1;  // stays >= 1: another table still holds it
         s.table.back() = b;
         log.push_back({Op::CowSwap, id, old, b});
@@ -163,6 +242,10 @@ extern "C" int pkv_pool_create(const pkv_layout *layout, const int32_t *free_ord
   p->layout = *layout;
   p->free_stack.assign(order.rbegin(), order.rend());  // first hand-out = order[0]
   p->ref.assign(n, 0);
+  p->pc.resize(n);
+  p->cached.assign(n, 0);
+  p->lru_prev.assign(n, -1);
+  p->lru_next.assign(n, -1);
   *out = p;
   return PKV_OK;
 }
@@ -190,7 +273,7 @@ extern "C" int pkv_block_free(pkv_pool *pool, int32_t block) {
   if (int rc = need_pool(pool)) return rc;
   if (!pool->valid_block(block)) return pkv_set_error(PKV_ERR_BAD_BLOCK, "block %d out of range", block);
   if (pool->ref[block] <= 0) return pkv_set_error(PKV_ERR_REFCOUNT, "free of free block %d", block);
-  if (--pool->ref[block] == 0) pool->free_stack.push_back(block);
+  if (--pool->ref[block] == 0) pool->release(block);
   return PKV_OK;
 }
 
@@ -205,7 +288,7 @@ extern "C" int pkv_block_refcount(const pkv_pool *pool, int32_t block, int32_t *
 extern "C" int pkv_pool_num_free(const pkv_pool *pool, int32_t *out) {
   if (int rc = need_pool(pool)) return rc;
   if (!out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
-  *out = (int32_t)pool->free_stack.size();
+  *out = pool->available();
   return PKV_OK;
 }
 
@@ -276,8 +359,19 @@ extern "C" int pkv_seq_free(pkv_pool *pool, int64_t id) {
     if (pool->ref[kv.first] < kv.second)
       return pkv_set_error(PKV_ERR_REFCOUNT, "free of sequence %lld holding block %d %d times, refcount %d",
                            (long long)id, kv.first, kv.second, pool->ref[kv.first]);
+  // Blocks reaching zero go back in table order; cached ones turn idle
+  // deepest first, so that of a prefix released together the tail is
+  // evicted before the head (a cached block is only reachable through its
+  // prefix).
+  std::vector<int32_t> idle;
   for (int32_t b : it->second.table)
-    if (--pool->ref[b] == 0) pool->free_stack.push_back(b);
+    if (--pool->ref[b] == 0) {
+      if (pool->cached[b])
+        idle.push_back(b);
+      else
+        pool->free_stack.push_back(b);
+    }
+  for (auto r = idle.rbegin(); r != idle.rend(); ++r) pool->lru_push_back(*r);
   pool->seqs.erase(it);
   return PKV_OK;
 }
@@ -347,7 +441,7 @@ extern "C" int pkv_pool_stats(const pkv_pool *pool, pkv_stats *out) {
     shared += pool->ref[b] > 1;
   }
   out->num_blocks = n;
-  out->num_free = (int32_t)pool->free_stack.size();
+  out->num_free = pool->available();
   out->num_used = n - out->num_free;
   out->num_shared = shared;
   out->num_seqs = (int64_t)pool->seqs.size();
@@ -387,5 +481,127 @@ extern "C" int pkv_validate_tables(const pkv_layout *layout, const int32_t *tabl
         return pkv_set_error(PKV_ERR_BAD_BLOCK, "sequence %d entry %d: block %d out of range", i, j, b);
     }
   }
+  return PKV_OK;
+}
+
+// ------------------------------------------------------------- prefix cache
+namespace {
+
+// FNV-1a, 64-bit (offset basis 14695981039346656037, prime 1099511628211),
+// over the little-endian bytes of the previous block's key followed by the
+// block's 16 token ids: the key of block i covers tokens [0, 16 (i + 1)).
+uint64_t fnv1a_block(uint64_t parent, const int32_t *tok) {
+  uint64_t h = 14695981039346656037ull;
+  auto feed = [&h](uint8_t byte) {
+    h ^= byte;
+    h *= 1099511628211ull;
+  };
+  for (int k = 0; k < 8; ++k) feed((uint8_t)(parent >> (8 * k)));
+  for (int t = 0; t < PKV_BLOCK_SIZE; ++t)
+    for (int k = 0; k < 4; ++k) feed((uint8_t)((uint32_t)tok[t] >> (8 * k)));
+  return h;
+}
+
+// The cached block of (parent key, tokens), or -1.
+int32_t lookup(const pkv_pool *p, uint64_t parent, const int32_t *tok, uint64_t *key_out) {
+  const uint64_t key = fnv1a_block(parent, tok);
+  *key_out = key;
+  auto it = p->pc_map.find(key);
+  if (it == p->pc_map.end()) return -1;
+  const auto &e = p->pc[it->second];
+  if (e.parent != parent || !std::equal(tok, tok + PKV_BLOCK_SIZE, e.tok)) return -1;
+  return it->second;
+}
+
+}  // namespace
+
+extern "C" int pkv_prefix_cache_enable(pkv_pool *pool, int32_t enable) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!enable && pool->pc_on) {
+    // Idle cached blocks return to the free stack (oldest first); blocks in
+    // use simply stop being cached.
+    while (pool->lru_head >= 0) {
+      const int32_t b = pool->lru_head;
+      pool->lru_unlink(b);
+      pool->free_stack.push_back(b);
+    }
+    std::fill(pool->cached.begin(), pool->cached.end(), 0);
+    pool->pc_map.clear();
+  }
+  pool->pc_on = enable != 0;
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_create_from_prefix(pkv_pool *pool, const int32_t *token_ids, int32_t n, int64_t *id_out,
+                                          int32_t *n_cached_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!id_out || !n_cached_out || n < 0 || (n > 0 && !token_ids))
+    return pkv_set_error(PKV_ERR_INVALID, "bad arguments");
+  pkv_pool::Seq s;
+  if (pool->pc_on) {
+    uint64_t parent = 0;
+    for (int32_t i = 0; i + 1 <= n / PKV_BLOCK_SIZE; ++i) {
+      uint64_t key;
+      const int32_t b = lookup(pool, parent, token_ids + (int64_t)i * PKV_BLOCK_SIZE, &key);
+      if (b < 0) break;
+      if (pool->ref[b] == 0) pool->lru_unlink(b);
+      ++pool->ref[b];
+      s.table.push_back(b);
+      s.len += PKV_BLOCK_SIZE;
+      parent = key;
+    }
+    ++pool->pst.lookups;
+    pool->pst.query_tokens += n / PKV_BLOCK_SIZE * PKV_BLOCK_SIZE;
+    pool->pst.hit_tokens += s.len;
+  }
+  const int64_t id = pool->next_id++;
+  *n_cached_out = s.len;
+  pool->seqs.emplace(id, std::move(s));
+  *id_out = id;
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_register_prefix(pkv_pool *pool, int64_t id, const int32_t *token_ids, int32_t n,
+                                       int32_t *n_registered) {
+  if (int rc = need_pool(pool)) return rc;
+  auto it = pool->seqs.find(id);
+  if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)id);
+  if (n < 0 || (n > 0 && !token_ids)) return pkv_set_error(PKV_ERR_INVALID, "bad arguments");
+  const auto &s = it->second;
+  if (n > s.len) return pkv_set_error(PKV_ERR_INVALID, "register of %d tokens, sequence holds %d", n, s.len);
+  int32_t added = 0;
+  if (pool->pc_on) {
+    uint64_t parent = 0;
+    for (int32_t i = 0; i + 1 <= n / PKV_BLOCK_SIZE; ++i) {
+      const int32_t *tok = token_ids + (int64_t)i * PKV_BLOCK_SIZE;
+      uint64_t key;
+      const int32_t hit = lookup(pool, parent, tok, &key);
+      const int32_t b = s.table[i];
+      // Content already cached (maybe in another block), or this block
+      // already cached under its own prefix: leave the cache as it is.
+      if (hit < 0 && !pool->cached[b] && !pool->pc_map.count(key)) {
+        auto &e = pool->pc[b];
+        e.key = key;
+        e.parent = parent;
+        std::copy(tok, tok + PKV_BLOCK_SIZE, e.tok);
+        pool->cached[b] = 1;
+        pool->pc_map.emplace(key, b);
+        ++added;
+      }
+      parent = key;
+    }
+    pool->pst.registered += added;
+  }
+  if (n_registered) *n_registered = added;
+  return PKV_OK;
+}
+
+extern "C" int pkv_prefix_cache_stats(const pkv_pool *pool, pkv_prefix_stats *out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
+  *out = pool->pst;
+  out->cached_blocks = (int32_t)pool->pc_map.size();
+  out->idle_blocks = pool->n_idle;
+  out->hit_rate = out->query_tokens ? (double)out->hit_tokens / (double)out->query_tokens : 0.0;
   return PKV_OK;
 }

@@ -71,6 +71,21 @@ class PagedKVCache:
                 L.pkv_copy_blocks(self.layout, k, v, pairs)
         return slots, cow
 
+    # -- prefix cache ---------------------------------------------------------
+    def enable_prefix_cache(self, on: bool = True):
+        L.pkv_prefix_cache_enable(self.pool, on)
+
+    def create_from_prefix(self, token_ids):
+        """(sequence, tokens already cached): the caller stores K/V for the
+        rest of the prompt, then calls register_prefix."""
+        return L.pkv_seq_create_from_prefix(self.pool, token_ids)
+
+    def register_prefix(self, seq: int, token_ids, n=None) -> int:
+        return L.pkv_seq_register_prefix(self.pool, seq, token_ids, n)
+
+    def prefix_stats(self) -> dict:
+        return L.pkv_prefix_cache_stats(self.pool)
+
     def tables(self, ids, max_blocks: int):
         return L.pkv_batch_block_tables(self.pool, ids, max_blocks)
 

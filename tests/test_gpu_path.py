@@ -255,3 +255,44 @@ def test_empty_and_padding_sequences():
         assert (o[0] == 0).all()
         ref = orc.contiguous_attention("bf16", q[1], kv[0], kv[1], 1 / math.sqrt(D))
         check_close(o[1], ref, TOL["bf16"], f"padding kernel={kernel}")
+
+
+def test_prefix_cache_hits_read_like_prefill():
+    """Requests built through the prefix cache (their prompt's cached blocks
+    found, the rest stored) attend exactly over their own prompt: every
+    output within tolerance of the oracle's contiguous attention."""
+    H, Hq, D = 8, 32, 128
+    rng = np.random.default_rng(11)
+    system = rng.integers(0, 32000, size=200, dtype=np.int32)  # 12 full blocks + 8 tokens
+    c = PagedKVCache(256, H, D, "bf16")
+    c.enable_prefix_cache(True)
+    sys_k = workloads.configs.normal_bits(21, (200, H, D), "bf16")
+    sys_v = workloads.configs.normal_bits(22, (200, H, D), "bf16")
+    mk = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    ids, kv = [], []
+    for r in range(6):
+        own = 20 + 31 * r
+        toks = np.concatenate([system, rng.integers(0, 32000, size=own, dtype=np.int32)])
+        k_all = np.concatenate([sys_k, workloads.configs.normal_bits(30 + r, (own, H, D), "bf16")])
+        v_all = np.concatenate([sys_v, workloads.configs.normal_bits(40 + r, (own, H, D), "bf16")])
+        sid, cached = c.create_from_prefix(toks)
+        assert cached == (0 if r == 0 else 192)
+        slots, _ = c.reserve([sid], len(toks) - cached)
+        c.write(0, torch.from_numpy(slots).cuda(), mk(k_all[cached:]), mk(v_all[cached:]))
+        c.register_prefix(sid, toks)
+        ids.append(sid)
+        kv.append((k_all, v_all))
+    st = c.prefix_stats()
+    assert st["hit_tokens"] == 5 * 192
+    mb = max(-(-len(k) // 16) for k, _ in kv)
+    tables, ctx = c.tables(ids, mb)
+    q = workloads.configs.normal_bits(50, (len(ids), Hq, D), "bf16")
+    out = torch.empty(len(ids), Hq, D, device="cuda")
+    for wps in (1, 2):
+        ws = c.workspace(len(ids), Hq, int(ctx.max()))
+        c.decode(0, out, mk(q), torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(), int(ctx.max()),
+                 1 / math.sqrt(D), ws, waves_per_simd=wps)
+        o = out.cpu().numpy()
+        for i, (k_all, v_all) in enumerate(kv):
+            ref = orc.contiguous_attention("bf16", q[i], k_all, v_all, 1 / math.sqrt(D))
+            check_close(o[i], ref, TOL["bf16"], f"prefix-cache request {i} wps={wps}")
