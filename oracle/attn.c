@@ -29,8 +29,21 @@
  *    K element (blk, g, t, d) at (((blk*Hkv + g)*(D/X) + d/X)*16 + t)*X + d%X
  *    V element (blk, g, t, d) at  ((blk*Hkv + g)*D + d)*16 + t
  *
- * Element types: 0 = float32, 1 = bfloat16 (raw uint16 bits).  Every element
- * is widened exactly to double before use.
+ * Element types: 0 = float32, 1 = bfloat16 (raw uint16 bits), 2 = int8 with
+ * a float32 scale per (token, kv head) [KV Cache 工程学 §15.7 "KV Cache 量化":
+ * FP16 -> INT8 halves the cache].  Every element is widened exactly to double
+ * before use; an int8 element stands for code * scale.
+ *
+ * int8 pools (a choice of this build): a (block, kv head) tile is
+ * 16 * D int8 codes followed by 16 float32 scales (one per token slot),
+ * 16 * D + 64 bytes:
+ *    K code (blk, g, t, d) at byte ((blk*Hkv + g)*TB + ((d/16)*16 + t)*16 + d%16)
+ *    V code (blk, g, t, d) at byte ((blk*Hkv + g)*TB + d*16 + t)
+ *    scale of slot t at byte ((blk*Hkv + g)*TB + 16*D + 4*t), in each pool
+ * Queries and the rows handed to append are bfloat16.  Quantisation of a
+ * token's row x[0..D) of one kv head, in float32 as the kernels do it:
+ *    amax = max |x_d|, scale = amax / 127, code_d = rint(x_d / scale)
+ *    clamped to [-127, 127] (round half to even; all zero when amax = 0).
  */
 #include <math.h>
 #include <stdint.h>
@@ -47,7 +60,13 @@ static double elem(const void *base, size_t i, int dtype) {
   return (double)f;
 }
 
-static size_t esize(int dtype) { return dtype == 0 ? 4 : 2; }
+static size_t esize(int dtype) { return dtype == 0 ? 4 : dtype == 1 ? 2 : 1; }
+
+/* Element type of queries and of the rows given to append. */
+static int row_type(int dtype) { return dtype == 2 ? 1 : dtype; }
+
+/* Bytes of one (block, kv head) tile of an int8 pool. */
+static size_t tile_bytes_i8(int D) { return (size_t)16 * D + 64; }
 
 static size_t k_at(int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) {
   int X = (int)(16 / esize(dtype));
@@ -56,6 +75,48 @@ static size_t k_at(int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) 
 
 static size_t v_at(int64_t blk, int g, int t, int d, int Hkv, int D) {
   return (((size_t)blk * Hkv + g) * (size_t)D + (size_t)d) * BLOCK + (size_t)t;
+}
+
+/* int8 code of K or V element (blk, g, t, d) and the scale of slot t. */
+static double i8_value(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int is_v) {
+  const unsigned char *tile = (const unsigned char *)pool + ((size_t)blk * Hkv + g) * tile_bytes_i8(D);
+  size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + t) * 16 + d % 16;
+  float sc;
+  memcpy(&sc, tile + (size_t)16 * D + 4 * (size_t)t, sizeof sc);
+  return (double)(signed char)tile[at] * (double)sc;
+}
+
+/* Value of K element (blk, g, t, d) of a pool, widened to double. */
+static double kval(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) {
+  if (dtype == 2) return i8_value(pool, blk, g, t, d, Hkv, D, 0);
+  return elem(pool, k_at(blk, g, t, d, Hkv, D, dtype), dtype);
+}
+static double vval(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) {
+  if (dtype == 2) return i8_value(pool, blk, g, t, d, Hkv, D, 1);
+  return elem(pool, v_at(blk, g, t, d, Hkv, D), dtype);
+}
+
+/* Quantise one row x[0..D) (bfloat16) into int8 codes at code(d) and its
+ * scale, in float32. */
+static void quantise_row(const uint16_t *x, int D, unsigned char *tile, int t, int is_v) {
+  float amax = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    float v = (float)elem(x, (size_t)d, 1);
+    float a = fabsf(v);
+    if (a > amax) amax = a;
+  }
+  float scale = amax / 127.0f;
+  for (int d = 0; d < D; ++d) {
+    float v = (float)elem(x, (size_t)d, 1);
+    int q = 0;
+    if (amax > 0.0f) {
+      float r = rintf(v / scale);
+      q = r > 127.0f ? 127 : r < -127.0f ? -127 : (int)r;
+    }
+    size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + t) * 16 + d % 16;
+    tile[at] = (unsigned char)(signed char)q;
+  }
+  memcpy(tile + (size_t)16 * D + 4 * (size_t)t, &scale, sizeof scale);
 }
 
 static void copy_elem(void *dst, size_t di, const void *src, size_t si, int dtype) {
@@ -73,6 +134,15 @@ void orc_append(int dtype, int Hkv, int D, void *kpool, void *vpool, const void 
     if (s < 0) continue;
     int64_t blk = s / BLOCK;
     int off = (int)(s % BLOCK);
+    if (dtype == 2) {
+      for (int g = 0; g < Hkv; ++g) {
+        size_t row = ((size_t)t * Hkv + g) * D;
+        size_t tile = ((size_t)blk * Hkv + g) * tile_bytes_i8(D);
+        quantise_row((const uint16_t *)k_new + row, D, (unsigned char *)kpool + tile, off, 0);
+        quantise_row((const uint16_t *)v_new + row, D, (unsigned char *)vpool + tile, off, 1);
+      }
+      continue;
+    }
     for (int g = 0; g < Hkv; ++g)
       for (int d = 0; d < D; ++d) {
         size_t src = ((size_t)t * Hkv + g) * D + d;
@@ -88,6 +158,12 @@ void orc_copy_blocks(int dtype, int Hkv, int D, void *kpool, void *vpool, const 
                      int n) {
   for (int i = 0; i < n; ++i) {
     int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (dtype == 2) {
+      size_t tb = (size_t)Hkv * tile_bytes_i8(D);
+      memcpy((char *)kpool + dst * tb, (const char *)kpool + src * tb, tb);
+      memcpy((char *)vpool + dst * tb, (const char *)vpool + src * tb, tb);
+      continue;
+    }
     for (int g = 0; g < Hkv; ++g)
       for (int t = 0; t < BLOCK; ++t)
         for (int d = 0; d < D; ++d) {
@@ -102,7 +178,7 @@ void orc_copy_blocks(int dtype, int Hkv, int D, void *kpool, void *vpool, const 
 void orc_paged_attention(int dtype, int Hq, int Hkv, int D, const void *q, const void *kpool,
                          const void *vpool, const int32_t *tables, int max_blocks,
                          const int32_t *ctx, int B, double scale, double *out) {
-  int G = Hq / Hkv;
+  int G = Hq / Hkv, qt = row_type(dtype);
 #pragma omp parallel for schedule(dynamic)
   for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
     int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
@@ -116,7 +192,7 @@ void orc_paged_attention(int dtype, int Hq, int Hkv, int D, const void *q, const
       int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
       double acc = 0.0;
       for (int d = 0; d < D; ++d)
-        acc += elem(q, (size_t)bh * D + d, dtype) * elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
+        acc += elem(q, (size_t)bh * D + d, qt) * kval(kpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
       s[j] = scale * acc;
       if (s[j] > m) m = s[j];
     }
@@ -125,7 +201,7 @@ void orc_paged_attention(int dtype, int Hq, int Hkv, int D, const void *q, const
       int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
       double w = exp(s[j] - m);
       l += w;
-      for (int d = 0; d < D; ++d) o[d] += w * elem(vpool, v_at(blk, g, j % BLOCK, d, Hkv, D), dtype);
+      for (int d = 0; d < D; ++d) o[d] += w * vval(vpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
     }
     for (int d = 0; d < D; ++d) o[d] /= l;
     free(s);
@@ -170,7 +246,7 @@ void orc_partitioned_attention(int dtype, int Hq, int Hkv, int D, const void *q,
                                const void *kpool, const void *vpool, const int32_t *tables,
                                int max_blocks, const int32_t *ctx, int B, double scale, int P,
                                double *out) {
-  int G = Hq / Hkv;
+  int G = Hq / Hkv, qt = row_type(dtype);
 #pragma omp parallel for schedule(dynamic)
   for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
     int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
@@ -189,7 +265,7 @@ void orc_partitioned_attention(int dtype, int Hq, int Hkv, int D, const void *q,
         int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
-          acc += elem(q, (size_t)bh * D + d, dtype) * elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
+          acc += elem(q, (size_t)bh * D + d, qt) * kval(kpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
         if (scale * acc > m) m = scale * acc;
       }
       double l = 0.0;
@@ -197,10 +273,10 @@ void orc_partitioned_attention(int dtype, int Hq, int Hkv, int D, const void *q,
         int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
-          acc += elem(q, (size_t)bh * D + d, dtype) * elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
+          acc += elem(q, (size_t)bh * D + d, qt) * kval(kpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
         double w = exp(scale * acc - m);
         l += w;
-        for (int d = 0; d < D; ++d) po[(size_t)p * D + d] += w * elem(vpool, v_at(blk, g, j % BLOCK, d, Hkv, D), dtype);
+        for (int d = 0; d < D; ++d) po[(size_t)p * D + d] += w * vval(vpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
       }
       pm[p] = m;
       pl[p] = l;
@@ -227,8 +303,8 @@ void orc_gather_token(int dtype, int Hkv, int D, const void *kpool, const void *
   int64_t blk = table[j / BLOCK];
   for (int g = 0; g < Hkv; ++g)
     for (int d = 0; d < D; ++d) {
-      k_out[(size_t)g * D + d] = elem(kpool, k_at(blk, g, j % BLOCK, d, Hkv, D, dtype), dtype);
-      v_out[(size_t)g * D + d] = elem(vpool, v_at(blk, g, j % BLOCK, d, Hkv, D), dtype);
+      k_out[(size_t)g * D + d] = kval(kpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
+      v_out[(size_t)g * D + d] = vval(vpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
     }
 }
 

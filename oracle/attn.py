@@ -14,8 +14,11 @@ import numpy as np
 from . import build as _build
 from .book import BLOCK_SIZE, build_workload
 
-_DT = {"f32": 0, "bf16": 1}
-_NP = {"f32": np.float32, "bf16": np.uint16}
+_DT = {"f32": 0, "bf16": 1, "int8": 2}
+_NP = {"f32": np.float32, "bf16": np.uint16, "int8": np.uint8}
+# Element type of queries and of the rows handed to append: an int8 cache is
+# fed bfloat16 rows and quantises them itself.
+ROW = {"f32": "f32", "bf16": "bf16", "int8": "bf16"}
 NAN_BITS = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0)}
 
 _lib = None
@@ -44,8 +47,21 @@ def _p(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def tile_bytes_int8(head_dim: int) -> int:
+    """Bytes of one (block, kv head) tile of an int8 pool: 16 * D codes, then
+    16 float32 scales."""
+    return BLOCK_SIZE * head_dim + 4 * BLOCK_SIZE
+
+
 def new_pool(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
-    """K and V pools filled with a NaN sentinel: slots never written stay NaN."""
+    """K and V pools filled with a NaN sentinel: slots never written stay NaN
+    (for int8, zero codes under a NaN scale)."""
+    if dtype == "int8":
+        tb = tile_bytes_int8(head_dim)
+        tiles = np.zeros((num_blocks * num_kv_heads, tb), dtype=np.uint8)
+        tiles[:, BLOCK_SIZE * head_dim:] = np.full((tiles.shape[0], BLOCK_SIZE), np.nan,
+                                                   dtype=np.float32).view(np.uint8)
+        return tiles.reshape(-1), tiles.reshape(-1).copy()
     n = num_blocks * num_kv_heads * BLOCK_SIZE * head_dim
     k = np.full(n, NAN_BITS[dtype], dtype=_NP[dtype])
     v = np.full(n, NAN_BITS[dtype], dtype=_NP[dtype])
@@ -53,8 +69,8 @@ def new_pool(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
 
 
 def append(dtype, num_kv_heads, head_dim, kpool, vpool, k_new, v_new, slots):
-    k_new = np.ascontiguousarray(k_new, dtype=_NP[dtype])
-    v_new = np.ascontiguousarray(v_new, dtype=_NP[dtype])
+    k_new = np.ascontiguousarray(k_new, dtype=_NP[ROW[dtype]])
+    v_new = np.ascontiguousarray(v_new, dtype=_NP[ROW[dtype]])
     slots = np.ascontiguousarray(slots, dtype=np.int64)
     assert k_new.shape == v_new.shape == (slots.size, num_kv_heads, head_dim)
     lib().orc_append(_DT[dtype], num_kv_heads, head_dim, _p(kpool), _p(vpool), _p(k_new), _p(v_new),
@@ -68,7 +84,7 @@ def copy_blocks(dtype, num_kv_heads, head_dim, kpool, vpool, pairs):
 
 
 def paged_attention(dtype, q, kpool, vpool, tables, ctx, num_kv_heads, scale):
-    q = np.ascontiguousarray(q, dtype=_NP[dtype])
+    q = np.ascontiguousarray(q, dtype=_NP[ROW[dtype]])
     B, Hq, D = q.shape
     tables = np.ascontiguousarray(tables, dtype=np.int32)
     ctx = np.ascontiguousarray(ctx, dtype=np.int32)
@@ -79,7 +95,7 @@ def paged_attention(dtype, q, kpool, vpool, tables, ctx, num_kv_heads, scale):
 
 
 def partitioned_attention(dtype, q, kpool, vpool, tables, ctx, num_kv_heads, scale, part_tokens):
-    q = np.ascontiguousarray(q, dtype=_NP[dtype])
+    q = np.ascontiguousarray(q, dtype=_NP[ROW[dtype]])
     B, Hq, D = q.shape
     tables = np.ascontiguousarray(tables, dtype=np.int32)
     ctx = np.ascontiguousarray(ctx, dtype=np.int32)
@@ -91,7 +107,9 @@ def partitioned_attention(dtype, q, kpool, vpool, tables, ctx, num_kv_heads, sca
 
 
 def contiguous_attention(dtype, q_seq, k_seq, v_seq, scale):
-    """q_seq [Hq][D]; k_seq, v_seq [n][Hkv][D] -> [Hq][D] float64."""
+    """q_seq [Hq][D]; k_seq, v_seq [n][Hkv][D] -> [Hq][D] float64 (f32 or
+    bf16 elements: a contiguous cache is never quantised)."""
+    assert dtype in ("f32", "bf16")
     q_seq = np.ascontiguousarray(q_seq, dtype=_NP[dtype])
     k_seq = np.ascontiguousarray(k_seq, dtype=_NP[dtype])
     v_seq = np.ascontiguousarray(v_seq, dtype=_NP[dtype])
@@ -131,16 +149,16 @@ def run_workload(inst, with_attention=True):
     wl = inst.wl
     book, ids, pre_slots, step_slots, cow = build_workload(inst)
     assert not cow, "the workloads never trigger copy-on-write"
-    kpool, vpool = new_pool(inst.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
-    append(wl.dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, inst.prefill_tokens("k"),
+    kpool, vpool = new_pool(inst.num_blocks, wl.num_kv_heads, wl.head_dim, wl.cache_dtype)
+    append(wl.cache_dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, inst.prefill_tokens("k"),
            inst.prefill_tokens("v"), np.asarray(pre_slots, dtype=np.int64))
-    append(wl.dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, inst.step_tokens("k"),
+    append(wl.cache_dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, inst.step_tokens("k"),
            inst.step_tokens("v"), np.asarray(step_slots, dtype=np.int64))
     tables, ctx = tables_of(book, ids)
     assert (ctx == inst.ctx).all()
     res = {"book": book, "ids": ids, "prefill_slots": pre_slots, "step_slots": step_slots,
            "kpool": kpool, "vpool": vpool, "tables": tables, "ctx": ctx}
     if with_attention:
-        res["out"] = paged_attention(wl.dtype, inst.q(), kpool, vpool, tables, ctx, wl.num_kv_heads,
+        res["out"] = paged_attention(wl.cache_dtype, inst.q(), kpool, vpool, tables, ctx, wl.num_kv_heads,
                                      1.0 / math.sqrt(wl.head_dim))
     return res

@@ -49,11 +49,12 @@ class Problem:
         order = np.arange(num_blocks) if identity else rng.permutation(num_blocks)
         self.book = Book(num_blocks, order)
         self.ids = [self.book.create() for _ in range(B)]
+        rt = orc.ROW[dtype]
         if kv is None:
-            kv = [(normal_bits(seed * 7919 + 2 * b, (int(ctx[b]), Hkv, D), dtype),
-                   normal_bits(seed * 7919 + 2 * b + 1, (int(ctx[b]), Hkv, D), dtype)) for b in range(B)]
+            kv = [(normal_bits(seed * 7919 + 2 * b, (int(ctx[b]), Hkv, D), rt),
+                   normal_bits(seed * 7919 + 2 * b + 1, (int(ctx[b]), Hkv, D), rt)) for b in range(B)]
         self.kv = kv
-        self.q = normal_bits(seed * 7919 + 99991, (B, Hq, D), dtype) if q is None else q
+        self.q = normal_bits(seed * 7919 + 99991, (B, Hq, D), rt) if q is None else q
         self.kpool, self.vpool = orc.new_pool(num_blocks, Hkv, D, dtype)
         for b, sid in enumerate(self.ids):
             slots, _ = self.book.append_slots(sid, int(ctx[b]))
@@ -69,6 +70,22 @@ class Problem:
     def contiguous(self, b):
         k, v = self.kv[b]
         return orc.contiguous_attention(self.dtype, self.q[b], k, v, self.scale)
+
+
+def int8_tile_bytes(D):
+    return 16 * D + 64
+
+
+def int8_read(pool, H, D, blk, g, t, is_v):
+    """(codes[D], scale) of slot t of tile (blk, g) of an int8 pool, read with
+    the byte layout of tests/golden/pool_layout_int8.txt."""
+    tb = int8_tile_bytes(D)
+    tile = pool[(blk * H + g) * tb:(blk * H + g + 1) * tb]
+    d = np.arange(D)
+    at = d * 16 + t if is_v else ((d // 16) * 16 + t) * 16 + d % 16
+    codes = tile[at].view(np.int8).astype(np.int64)
+    scale = tile[16 * D + 4 * t:16 * D + 4 * t + 4].view(np.float32)[0]
+    return codes, scale
 
 
 def brute_attention(q, K, V, scale):
@@ -270,7 +287,124 @@ def check_rejects_per_page_softmax():
             assert diff > 1e-2
 
 
+def _bf16_bits(values):
+    f = np.asarray(values, dtype=np.float32)
+    bits = f.view(np.uint32)
+    assert ((bits & 0xFFFF) == 0).all(), "golden values must be bfloat16-exact"
+    return (bits >> 16).astype(np.uint16)
+
+
+def check_int8_quant_golden():
+    """Append of hand-worked rows stores the hand-worked codes and scale
+    (tests/golden/int8_quant_example.txt), in both pools."""
+    H, D = 1, 16
+    for label, scale_hex, _, *rest in read_golden("int8_quant_example.txt"):
+        values = [float(x) for x in rest[:16]]
+        codes = [int(x) for x in rest[17:33]]
+        assert rest[16] == "|" and len(codes) == 16
+        want_scale = np.array([int(scale_hex, 16)], np.uint32).view(np.float32)[0]
+        kpool, vpool = orc.new_pool(2, H, D, "int8")
+        row = _bf16_bits(values).reshape(1, 1, D)
+        orc.append("int8", H, D, kpool, vpool, row, row, np.array([16 + 6]))
+        for pool, is_v in ((kpool, False), (vpool, True)):
+            got, sc = int8_read(pool, H, D, 1, 0, 6, is_v)
+            assert got.tolist() == codes, (label, is_v, got.tolist())
+            assert sc.view(np.uint32) == want_scale.view(np.uint32), (label, is_v, sc)
+
+
+def check_int8_layout_golden():
+    """Byte offsets of codes and scales in an int8 pool for hand-worked slots
+    (tests/golden/pool_layout_int8.txt)."""
+    H, D = 2, 32
+    for slot, head, d, kb, vb, sb in read_golden("pool_layout_int8.txt"):
+        slot, head, d, kb, vb, sb = (int(x) for x in (slot, head, d, kb, vb, sb))
+        kpool, vpool = orc.new_pool(slot // 16 + 1, H, D, "int8")
+        row = np.zeros((1, H, D), np.float32)
+        row[0, head, d] = 3.0
+        bits = _bf16_bits(row)
+        orc.append("int8", H, D, kpool, vpool, bits, bits, np.array([slot]))
+        tb = int8_tile_bytes(D)
+        is_code = (np.arange(kpool.size) % tb) < 16 * D  # scale bytes (NaN sentinel) hold 0x7f too
+        assert np.flatnonzero((kpool == 127) & is_code).tolist() == [kb], (slot, head, d)
+        assert np.flatnonzero((vpool == 127) & is_code).tolist() == [vb], (slot, head, d)
+        want = np.float32(3.0) / np.float32(127.0)
+        for pool in (kpool, vpool):
+            assert pool[sb:sb + 4].view(np.float32)[0] == want
+        # the other head of the same slot was written with an all-zero row
+        other = sb + (1 - 2 * head) * tb
+        for pool in (kpool, vpool):
+            assert pool[other:other + 4].view(np.float32)[0] == 0.0
+
+
+def check_int8_quant_error_bound():
+    """Every appended row of an int8 cache: |x - code*scale| <= scale/2 (up to
+    the float32 rounding of x/scale), the largest |code| is 127, codes keep
+    the sign of x; slots never written read NaN."""
+    p = Problem("int8", 3, 4, 2, 32, [1, 16, 45], 8, seed=71, identity=True)
+    for b in range(p.B):
+        for j in range(int(p.ctx[b])):
+            blk, t = int(p.tables[b][j // 16]), j % 16
+            for g in range(p.Hkv):
+                for which, pool in ((0, p.kpool), (1, p.vpool)):
+                    x = widen(p.kv[b][which][j, g], "bf16")
+                    codes, sc = int8_read(pool, p.Hkv, p.D, blk, g, t, which == 1)
+                    sc = float(sc)
+                    assert abs(sc - np.abs(x).max() / 127) <= 1e-6 * sc
+                    err = np.abs(x - codes * sc)
+                    assert (err <= 0.5 * sc * (1 + 2.0 ** -16)).all(), (b, j, g, which, err.max() / sc)
+                    assert np.abs(codes).max() == 127
+                    assert (codes * x >= 0).all()
+    # a slot past the last token of sequence 0 is still the sentinel
+    k, v = orc.gather_token("int8", p.Hkv, p.D, p.kpool, p.vpool, p.tables[0], 1)
+    assert np.isnan(k).all() and np.isnan(v).all()
+
+
+def check_int8_brute_force():
+    """Attention over an int8 cache == exactly-summed textbook attention over
+    the dequantised values (code * scale, decoded here from the bytes), for
+    shuffled blocks, and it stays within the quantisation error of the same
+    problem stored in bfloat16."""
+    p = Problem("int8", 3, 4, 2, 16, [1, 17, 40], 12, seed=81)
+    out = p.paged()
+    G = p.Hq // p.Hkv
+    ref16 = Problem("bf16", 3, 4, 2, 16, [1, 17, 40], 12, seed=81).paged()
+    for b in range(p.B):
+        n = int(p.ctx[b])
+        for g in range(p.Hkv):
+            K, V = [], []
+            for j in range(n):
+                blk, t = int(p.tables[b][j // 16]), j % 16
+                kc, ks = int8_read(p.kpool, p.Hkv, p.D, blk, g, t, False)
+                vc, vs = int8_read(p.vpool, p.Hkv, p.D, blk, g, t, True)
+                K.append((kc * float(ks)).tolist())
+                V.append((vc * float(vs)).tolist())
+            for h in range(g * G, (g + 1) * G):
+                ref = brute_attention(list(widen(p.q[b, h], "bf16")), K, V, p.scale)
+                err = np.abs(out[b, h] - np.asarray(ref)).max()
+                assert err <= 1e-13, (b, h, err)
+    assert np.abs(out - ref16).max() <= 0.05
+    # the split pass merges to the same result on an int8 cache too
+    part = orc.partitioned_attention("int8", p.q, p.kpool, p.vpool, p.tables, p.ctx, p.Hkv, p.scale, 16)
+    assert np.abs(part - out).max() <= 1e-13
+
+
+def check_int8_copy_blocks():
+    """Copying an int8 block moves its codes and scales byte for byte."""
+    p = Problem("int8", 2, 2, 2, 32, [20, 33], 8, seed=91, identity=True)
+    src = int(p.tables[1][1])
+    dst = int(p.book.free[-1])
+    k0, v0 = p.kpool.copy(), p.vpool.copy()
+    orc.copy_blocks("int8", p.Hkv, p.D, p.kpool, p.vpool, [(src, dst)])
+    blk = p.Hkv * int8_tile_bytes(p.D)
+    for pool, old in ((p.kpool, k0), (p.vpool, v0)):
+        assert np.array_equal(pool[dst * blk:(dst + 1) * blk], old[src * blk:(src + 1) * blk])
+        rest = np.ones(pool.size, bool)
+        rest[dst * blk:(dst + 1) * blk] = False
+        assert np.array_equal(pool[rest], old[rest])
+
+
 ALL_CHECKS = [check_brute_force, check_library_sdpa, check_paged_equals_contiguous,
               check_placement_invariance, check_special_cases, check_merge_identity,
               check_gqa_reduces_to_mha, check_append_roundtrip, check_layout_golden,
-              check_rejects_per_page_softmax]
+              check_rejects_per_page_softmax, check_int8_quant_golden, check_int8_layout_golden,
+              check_int8_quant_error_bound, check_int8_brute_force, check_int8_copy_blocks]

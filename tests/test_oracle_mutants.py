@@ -28,13 +28,23 @@ MUTANTS = {
     "merge_sign": ("L += pl[p] * exp(pm[p] - M);", "L += pl[p] * exp(M - pm[p]);"),
     "merge_drop_rescale": ("o[d] += po[(size_t)p * D + d] * f;", "o[d] += po[(size_t)p * D + d];"),
     "bf16_widen_shift": ("<< 16;", "<< 15;"),
-    "query_row_of_head0": ("elem(q, (size_t)bh * D + d, dtype)", "elem(q, (size_t)b * Hq * D + d, dtype)"),
+    "query_row_of_head0": ("elem(q, (size_t)bh * D + d, qt)", "elem(q, (size_t)b * Hq * D + d, qt)"),
     "context_off_by_one": ("int n = ctx[b];", "int n = ctx[b] - 1;"),
     "append_skips_slot0": ("if (s < 0) continue;", "if (s <= 0) continue;"),
     "copy_only_k": ("copy_elem(vpool, v_at(dst,", "if (0) copy_elem(vpool, v_at(dst,"),
-    "value_of_next_token": ("w * elem(vpool, v_at(blk, g, j % BLOCK, d",
-                            "w * elem(vpool, v_at(blk, g, (j + 1) % BLOCK, d"),
+    "value_of_next_token": ("w * vval(vpool, blk, g, j % BLOCK, d",
+                            "w * vval(vpool, blk, g, (j + 1) % BLOCK, d"),
     "max_from_first_token_only": ("if (s[j] > m) m = s[j];", "if (j == 0) m = s[j];"),
+    "int8_scale_dropped": ("return (double)(signed char)tile[at] * (double)sc;",
+                           "return (double)(signed char)tile[at];"),
+    "int8_truncating_round": ("float r = rintf(v / scale);", "float r = truncf(v / scale);"),
+    "int8_signed_amax": ("float a = fabsf(v);", "float a = v;"),
+    "int8_scale_of_next_slot": ("memcpy(&sc, tile + (size_t)16 * D + 4 * (size_t)t, sizeof sc);",
+                                "memcpy(&sc, tile + (size_t)16 * D + 4 * (size_t)((t + 1) % BLOCK), sizeof sc);"),
+    "int8_v_read_as_k": ("size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16)",
+                         "size_t at = !is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16)"),
+    "int8_scale_255": ("float scale = amax / 127.0f;", "float scale = amax / 255.0f;"),
+    "int8_copy_k_only": ("memcpy((char *)vpool + dst * tb", "if (0) memcpy((char *)vpool + dst * tb"),
 }
 
 

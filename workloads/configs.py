@@ -67,7 +67,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    dtype: str                   # "f32" | "bf16"
+    dtype: str                   # "f32" | "bf16": queries and the K/V rows handed to append
     ctx_fixed: tuple = ()        # explicit context lengths, or
     ctx_range: tuple = ()        # (lo, hi) inclusive uniform integers
     prefix_len: int = 0          # tokens shared by every sequence (held once)
@@ -77,6 +77,8 @@ class Workload:
     sinks: int = 0
     sink_scale: float = 4.0
     shuffled: bool = True        # blocks handed out in a seeded random order, else 0, 1, 2, ...
+    cache: str = ""              # storage of the cache: "" = dtype, or "int8" (codes + per-token scales)
+    same_data_as: str = ""       # draw lengths, order and values as the named workload does
     description: str = ""
 
     @property
@@ -88,11 +90,27 @@ class Workload:
         return 4 if self.dtype == "f32" else 2
 
     @property
+    def cache_dtype(self) -> str:
+        return self.cache or self.dtype
+
+    @property
+    def data_name(self) -> str:
+        return self.same_data_as or self.name
+
+    @property
+    def row_bytes(self) -> int:
+        """Cache bytes of one token's K (or V) row of one kv head: an int8
+        cache keeps a float32 scale beside its d one-byte codes."""
+        if self.cache_dtype == "int8":
+            return self.head_dim + 4
+        return self.head_dim * self.elem_bytes
+
+    @property
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
 
     def instantiate(self) -> "Instance":
-        rng = np.random.default_rng(derive_seed(self.seed, self.name, "lens"))
+        rng = np.random.default_rng(derive_seed(self.seed, self.data_name, "lens"))
         B = self.batch
         if self.prefix_len:
             if self.suffix_range:
@@ -113,7 +131,7 @@ class Workload:
         demand = -(-self.prefix_len // BLOCK) + int(sum(-(-int(n) // BLOCK) for n in (ctx - self.prefix_len)))
         num_blocks = self.pool_blocks or int(np.ceil(1.25 * demand))
         if self.shuffled:
-            perm = np.random.default_rng(derive_seed(self.seed, self.name, "perm")).permutation(num_blocks).astype(np.int32)
+            perm = np.random.default_rng(derive_seed(self.seed, self.data_name, "perm")).permutation(num_blocks).astype(np.int32)
         else:
             perm = np.arange(num_blocks, dtype=np.int32)
         return Instance(self, ctx.astype(np.int32), own_prefill.astype(np.int32), num_blocks, perm)
@@ -134,7 +152,7 @@ class Instance:
         """[B][h_q][d] query of the decode step."""
         w = self.wl
         if "q" not in self._cache:
-            self._cache["q"] = normal_bits(derive_seed(w.seed, w.name, "q"), (w.batch, w.num_q_heads, w.head_dim), w.dtype)
+            self._cache["q"] = normal_bits(derive_seed(w.seed, w.data_name, "q"), (w.batch, w.num_q_heads, w.head_dim), w.dtype)
         return self._cache["q"]
 
     def _sinked(self, arr: np.ndarray, start_pos: int) -> np.ndarray:
@@ -150,7 +168,7 @@ class Instance:
         w = self.wl
         key = "prefix_" + which
         if key not in self._cache:
-            a = normal_bits(derive_seed(w.seed, w.name, which, "prefix"), (w.prefix_len, w.num_kv_heads, w.head_dim), w.dtype)
+            a = normal_bits(derive_seed(w.seed, w.data_name, which, "prefix"), (w.prefix_len, w.num_kv_heads, w.head_dim), w.dtype)
             self._cache[key] = self._sinked(a, 0)
         return self._cache[key]
 
@@ -161,7 +179,7 @@ class Instance:
         key = ("own", which, b)
         if key not in self._cache:
             n = int(self.ctx[b]) - w.prefix_len
-            a = normal_bits(derive_seed(w.seed, w.name, which, "own", b), (n, w.num_kv_heads, w.head_dim), w.dtype)
+            a = normal_bits(derive_seed(w.seed, w.data_name, which, "own", b), (n, w.num_kv_heads, w.head_dim), w.dtype)
             self._cache[key] = self._sinked(a, w.prefix_len)
         return self._cache[key]
 
@@ -201,13 +219,13 @@ class Instance:
     def kv_bytes_logical(self) -> int:
         """K and V bytes the decode step reads: every sequence's whole context."""
         w = self.wl
-        return int(self.ctx.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+        return int(self.ctx.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.row_bytes
 
     def kv_bytes_unique(self) -> int:
         """K and V bytes of distinct stored tokens (a shared prefix counts once)."""
         w = self.wl
         tokens = int(self.ctx.astype(np.int64).sum()) - (w.batch - 1) * w.prefix_len
-        return tokens * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+        return tokens * 2 * w.num_kv_heads * w.row_bytes
 
 
 WORKLOADS = {
@@ -219,6 +237,11 @@ WORKLOADS = {
         "llama3_8b_b64", 2, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
         ctx_range=(128, 4096),
         description="Llama-3-8B-shaped single-layer decode: B 64, 32 q / 8 kv heads, d 128, bf16, ctx U[128,4096], shuffled pool 1.25x demand"),
+    "llama3_8b_b64_int8": Workload(
+        "llama3_8b_b64_int8", 2, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+        ctx_range=(128, 4096), cache="int8", same_data_as="llama3_8b_b64",
+        description="llama3_8b_b64 with an int8 cache: the same lengths, order and bf16 rows, quantised "
+                    "on append to int8 codes with a float32 scale per token and kv head"),
     "llama3_70b_b256": Workload(
         "llama3_70b_b256", 3, batch=256, num_q_heads=64, num_kv_heads=8, head_dim=128, dtype="bf16",
         ctx_fixed=(4096,) * 256,
