@@ -109,8 +109,8 @@ def cpu_baseline(inst, min_seconds: float):
 
     wl = inst.wl
     book, ids, pre_slots, step_slots, _ = build_workload(inst)
-    kpool, vpool = orc.new_pool(inst.num_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype)
-    orc.append(wl.dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, inst.prefill_tokens("k"),
+    kpool, vpool = orc.new_pool(inst.num_blocks, wl.num_kv_heads, wl.head_dim, wl.cache_dtype)
+    orc.append(wl.cache_dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, inst.prefill_tokens("k"),
                inst.prefill_tokens("v"), np.asarray(pre_slots, np.int64))
     tables, ctx = orc.tables_of(book, ids)
     kstep, vstep, q = inst.step_tokens("k"), inst.step_tokens("v"), inst.q()
@@ -118,8 +118,8 @@ def cpu_baseline(inst, min_seconds: float):
     scale = 1.0 / math.sqrt(wl.head_dim)
     reps, t0 = 0, time.perf_counter()
     while True:
-        orc.append(wl.dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, kstep, vstep, slots)
-        orc.paged_attention(wl.dtype, q, kpool, vpool, tables, ctx, wl.num_kv_heads, scale)
+        orc.append(wl.cache_dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, kstep, vstep, slots)
+        orc.paged_attention(wl.cache_dtype, q, kpool, vpool, tables, ctx, wl.num_kv_heads, scale)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -251,13 +251,14 @@ def main():
     wl = inst.wl
     B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
     K, W = args.steps, args.warmup
-    tok_bytes = 2 * H * D * wl.elem_bytes  # K and V of one token, one layer
+    tok_bytes = 2 * H * wl.row_bytes  # K and V of one token, one layer (int8: scales included)
     # Enough layers (own pools) that one step stores more than 1 GiB of
     # distinct K/V, so the 256 MB Infinity Cache cannot hold a step's reads.
     layers = args.layers or min(64, max(1, math.ceil((1 << 30) / inst.kv_bytes_unique())))
     total_steps = K + W
     extra = B * (total_steps // 16 + 2)
-    print(f"[bench] building {wl.name}: B={B} Hq={Hq} H={H} D={D} {wl.dtype}, layers/step={layers}", flush=True)
+    print(f"[bench] building {wl.name}: B={B} Hq={Hq} H={H} D={D} {wl.cache_dtype} cache, layers/step={layers}",
+          flush=True)
     gw = GpuWorkload(inst, num_layers=layers, extra_blocks=extra)
     inst.drop_cache()
     cache, ids = gw.cache, np.asarray(gw.ids, np.int64)
@@ -341,10 +342,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": wl.dtype,  # queries and matrix-core operands; an int8 cache is widened to it exactly
         "data": "synthetic",
         "config": {"workload": wl.description, "name": wl.name, "batch": B, "num_q_heads": Hq,
-                   "num_kv_heads": H, "head_dim": D, "block_size": 16, "layers_per_step": layers,
+                   "num_kv_heads": H, "head_dim": D, "block_size": 16, "kv_cache": wl.cache_dtype,
+                   "layers_per_step": layers,
                    "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
                    "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "waves_per_simd": wps,
                    "parallelism": "none"},

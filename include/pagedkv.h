@@ -72,16 +72,33 @@ enum {
   PKV_ERR_BAD_SEQ = -8    /* unknown sequence id */
 };
 
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+/* Storage of the cache.  PKV_F32 and PKV_BF16 store elements as given; the
+ * queries and the rows handed to paged_kv_append have the same type.
+ * PKV_INT8 stores one byte per element instead of two [KV Cache 工程学
+ * §15.7 (3), KV Cache 量化]: each token's row of one kv head (D values, K and
+ * V separately) keeps int8 codes and one float32 scale,
+ *   amax = max |x_d|, scale = amax / 127, code_d = round-half-even(x_d / scale)
+ *   clamped to [-127, 127] (all codes 0 when amax = 0), value = code * scale,
+ * computed in float32 when paged_kv_append stores the row.  Queries and
+ * appended rows are bfloat16. */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2 };
 
 #define PKV_BLOCK_SIZE 16
 
+/* Pool layout.  A pool is num_blocks * num_kv_heads tiles, tile (blk, g) at
+ * index blk * H + g; a tile holds the 16 token slots of one block for one kv
+ * head.  With X = 16 / element size (X = 16 for int8 codes):
+ *   K element (blk, g, t, d) at tile offset ((d / X) * 16 + t) * X + d % X
+ *   V element (blk, g, t, d) at tile offset d * 16 + t
+ * (in elements; for PKV_INT8 in bytes).  An f32/bf16 tile is 16 * D
+ * elements.  A PKV_INT8 tile is 16 * D + 64 bytes: the codes, then the 16
+ * float32 scales of slots 0..15 at byte 16 * D + 4 * t. */
 typedef struct {
   int32_t num_blocks;   /* physical blocks in the pool (> 0) */
   int32_t block_size;   /* tokens per block; must be 16 */
   int32_t num_kv_heads; /* H (> 0) */
   int32_t head_dim;     /* D: 64 or 128 */
-  int32_t kv_dtype;     /* PKV_F32 or PKV_BF16; Q uses the same type */
+  int32_t kv_dtype;     /* PKV_F32, PKV_BF16 or PKV_INT8 */
 } pkv_layout;
 
 /* Thread-local description of the last error raised on this thread. */
@@ -207,7 +224,8 @@ typedef struct {
 int pkv_pool_stats(const pkv_pool *pool, pkv_stats *out);
 /* K and V bytes of one token across num_layers layers:
  * num_layers * 2 * num_kv_heads * head_dim * element size
- * [KV Cache 工程学 §15.2].  0 on invalid input. */
+ * [KV Cache 工程学 §15.2]; for PKV_INT8 each row also carries its 4-byte
+ * scale: num_layers * 2 * num_kv_heads * (head_dim + 4).  0 on invalid input. */
 int64_t pkv_kv_bytes_per_token(const pkv_layout *layout, int32_t num_layers);
 /* Bytes of one pool (K or V; both have this size).  0 on invalid input. */
 int64_t pkv_pool_bytes(const pkv_layout *layout);
@@ -218,9 +236,11 @@ int pkv_validate_tables(const pkv_layout *layout, const int32_t *tables, const i
 
 /* ---------------------------------------------------------- device calls */
 /* Store the new tokens' K and V into their slots [KV Cache 工程学 §15.1,
- * §15.5].  k_new, v_new: [num_tokens][H][D] of kv_dtype (device);
- * d_slots: int64 [num_tokens] (device), slot = blk*16 + t; a negative slot
- * is skipped.  Bits are copied unchanged.  Slots must be distinct. */
+ * §15.5].  k_new, v_new: [num_tokens][H][D] of kv_dtype, bf16 for
+ * PKV_INT8 (device); d_slots: int64 [num_tokens] (device), slot = blk*16 + t;
+ * a negative slot or one past the pool is skipped.  f32 and bf16 bits are
+ * copied unchanged; PKV_INT8 rows are quantised as described at PKV_INT8.
+ * Slots must be distinct. */
 int paged_kv_append(const pkv_layout *layout, void *k_pool, void *v_pool, const void *k_new,
                     const void *v_new, const int64_t *d_slots, int32_t num_tokens, void *stream);
 
@@ -238,9 +258,10 @@ typedef struct {
                                wave is given by the balanced split (default 128).
                                Wavefront-reduction kernel: tokens per
                                split-context partition (default 512). */
-  int32_t kernel;           /* 0 auto (matrix cores for bf16 with G >= 4);
-                               1 the wavefront-reduction kernel;
-                               2 the matrix-core kernel (bf16, G <= 16) */
+  int32_t kernel;           /* 0 auto (matrix cores for int8, and for bf16
+                               with G >= 4); 1 the wavefront-reduction kernel
+                               (f32, bf16); 2 the matrix-core kernel (bf16,
+                               int8) */
   int32_t waves_per_simd;   /* matrix-core kernel: resident waves per SIMD,
                                0 = default (1), 1 or 2.  One streams K/V from
                                HBM fastest (waves sharing a SIMD do not
@@ -263,7 +284,7 @@ size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seq
  * over the context_lens[b] tokens j, where token j is slot j % 16 of block
  * d_block_tables[b][j / 16].  The softmax spans the whole context.
  *   out: float32 [num_seqs][num_q_heads][D] (device, written)
- *   q:   kv_dtype [num_seqs][num_q_heads][D] (device)
+ *   q:   kv_dtype [num_seqs][num_q_heads][D], bf16 for PKV_INT8 (device)
  *   d_block_tables: int32 [num_seqs][max_blocks_per_seq] (device)
  *   d_context_lens: int32 [num_seqs] (device); a length of 0 gives zeros
  *   max_context_len: an upper bound of every context length (sizes the grid);

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_NO_BLOCKS, PKV_ERR_BAD_BLOCK = 0, -1, -2, -3
 PKV_ERR_REFCOUNT, PKV_ERR_CAPACITY, PKV_ERR_HIP, PKV_ERR_WORKSPACE, PKV_ERR_BAD_SEQ = -4, -5, -6, -7, -8
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_INT8 = 0, 1, 2
+_DTYPE_CODE = {"f32": PKV_F32, "bf16": PKV_BF16, "int8": PKV_INT8}
 BLOCK_SIZE = 16
 
 STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "NO_BLOCKS", -3: "BAD_BLOCK", -4: "REFCOUNT", -5: "CAPACITY",
@@ -35,10 +36,19 @@ class pkv_layout(ctypes.Structure):
 
     @property
     def elem_bytes(self) -> int:
-        return 4 if self.kv_dtype == PKV_F32 else 2
+        """Bytes of one stored element (an int8 code for PKV_INT8)."""
+        return {PKV_F32: 4, PKV_BF16: 2}.get(self.kv_dtype, 1)
+
+    @property
+    def tile_bytes(self) -> int:
+        """Bytes of one (block, kv head) tile; int8 tiles end with 16 float32 scales."""
+        return BLOCK_SIZE * self.head_dim * self.elem_bytes + (4 * BLOCK_SIZE if self.kv_dtype == PKV_INT8 else 0)
 
     @property
     def pool_elems(self) -> int:
+        """Elements of a pool tensor: stored elements, or bytes for PKV_INT8."""
+        if self.kv_dtype == PKV_INT8:
+            return self.num_blocks * self.num_kv_heads * self.tile_bytes
         return self.num_blocks * self.num_kv_heads * BLOCK_SIZE * self.head_dim
 
 
@@ -136,8 +146,7 @@ def pkv_version() -> str:
 
 
 def make_layout(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str) -> pkv_layout:
-    return pkv_layout(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), int(head_dim),
-                      PKV_BF16 if dtype == "bf16" else PKV_F32)
+    return pkv_layout(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), int(head_dim), _DTYPE_CODE[dtype])
 
 
 # ------------------------------------------------------------------ host pool
@@ -318,9 +327,16 @@ def _dev(t, what, dtype=None, numel=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _kv_torch_dtype(layout):
+def pool_torch_dtype(layout):
+    """torch dtype of a pool tensor (uint8 bytes for an int8 cache)."""
     import torch
-    return torch.bfloat16 if layout.kv_dtype == PKV_BF16 else torch.float32
+    return {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16}.get(layout.kv_dtype, torch.uint8)
+
+
+def row_torch_dtype(layout):
+    """torch dtype of queries and of the rows handed to append."""
+    import torch
+    return torch.float32 if layout.kv_dtype == PKV_F32 else torch.bfloat16
 
 
 def _stream(stream):
@@ -332,18 +348,18 @@ def _stream(stream):
 
 def paged_kv_append(layout, k_pool, v_pool, k_new, v_new, slots, stream=None):
     import torch
-    dt = _kv_torch_dtype(layout)
+    pdt, rdt = pool_torch_dtype(layout), row_torch_dtype(layout)
     T = slots.numel()
     row = layout.num_kv_heads * layout.head_dim
-    args = (ctypes.byref(layout), _dev(k_pool, "k_pool", dt, layout.pool_elems),
-            _dev(v_pool, "v_pool", dt, layout.pool_elems), _dev(k_new, "k_new", dt, T * row),
-            _dev(v_new, "v_new", dt, T * row), _dev(slots, "slots", torch.int64), T, _stream(stream))
+    args = (ctypes.byref(layout), _dev(k_pool, "k_pool", pdt, layout.pool_elems),
+            _dev(v_pool, "v_pool", pdt, layout.pool_elems), _dev(k_new, "k_new", rdt, T * row),
+            _dev(v_new, "v_new", rdt, T * row), _dev(slots, "slots", torch.int64), T, _stream(stream))
     _check(lib().paged_kv_append(*args))
 
 
 def pkv_copy_blocks(layout, k_pool, v_pool, pairs, stream=None):
     import torch
-    dt = _kv_torch_dtype(layout)
+    dt = pool_torch_dtype(layout)
     if pairs.numel() % 2:
         raise ValueError("pairs must be [n][2]")
     _check(lib().pkv_copy_blocks(ctypes.byref(layout), _dev(k_pool, "k_pool", dt, layout.pool_elems),
@@ -367,7 +383,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
                            workspace=None, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0):
     """events: optional (begin, partition_done, end) raw hipEvent_t handles."""
     import torch
-    dt = _kv_torch_dtype(layout)
+    pdt, rdt = pool_torch_dtype(layout), row_torch_dtype(layout)
     if q.dim() != 3 or q.shape[2] != layout.head_dim:
         raise ValueError("q must be [num_seqs][num_q_heads][head_dim]")
     B, Hq, D = q.shape
@@ -383,7 +399,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
         raise ValueError(f"workspace of {ws_need} bytes needed, got {ws_bytes}")
     o = decode_opts(partition_tokens, kernel, events, waves_per_simd)
     _check(lib().paged_attention_decode(
-        ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", dt),
-        _dev(k_pool, "k_pool", dt, layout.pool_elems), _dev(v_pool, "v_pool", dt, layout.pool_elems),
+        ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", rdt),
+        _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32, B),
         B, Hq, mb, int(max_context_len), float(scale), ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))

@@ -1,7 +1,8 @@
 """Build libpagedkv.so in-tree with hipcc for gfx950.
 
 All HIP sources are compiled with packed-FP32 instruction selection turned
-off; the host block manager is plain C++ compiled by the same driver.
+off and MFMA results kept in VGPRs; the host block manager is plain C++
+compiled by the same driver.
 """
 import glob
 import os
@@ -22,6 +23,9 @@ def sources():
 def build(verbose: bool = False, extra=()) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in VGPRs: the decode kernel rescales them with
+           # vector ops, which cannot read AGPRs without a copy each way.
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wall", "-Wno-unused-function",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
            *extra, "-o", LIB + ".tmp", *sources()]

@@ -34,11 +34,12 @@ int min_chunks(const pkv_decode_opts *opts, int32_t *out) {
   return PKV_OK;
 }
 
-// Kernel a call runs: 1 wavefront reductions, 2 matrix cores (bf16, G >= 4
-// by default).
+// Kernel a call runs: 1 wavefront reductions, 2 matrix cores (int8, and bf16
+// with G >= 4, by default).
 int choose_kernel(const pkv_layout *L, int32_t G, const pkv_decode_opts *opts) {
   const int k = opts ? opts->kernel : 0;
   if (k != 0) return k;
+  if (L->kv_dtype == PKV_INT8) return 2;
   return (L->kv_dtype == PKV_BF16 && G >= 4) ? 2 : 1;
 }
 
@@ -71,6 +72,8 @@ extern "C" int paged_kv_append(const pkv_layout *layout, void *k_pool, void *v_p
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
       !aligned(d_slots, 8))
     return pkv_set_error(PKV_ERR_INVALID, "paged_kv_append: pools and token rows must be 16-byte aligned");
+  if ((int64_t)num_tokens * layout->num_kv_heads > ((int64_t)1 << 34))
+    return pkv_set_error(PKV_ERR_INVALID, "paged_kv_append: too many rows");
   if (int rc = pkv_launch_append(layout, k_pool, v_pool, k_new, v_new, d_slots, num_tokens, stream))
     return hip_fail(rc, "paged_kv_append launch");
   return PKV_OK;
@@ -168,8 +171,10 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   if (kernel != 1 && kernel != 2) return pkv_set_error(PKV_ERR_INVALID, "unknown kernel %d", kernel);
   if (opts && (opts->waves_per_simd < 0 || opts->waves_per_simd > 2))
     return pkv_set_error(PKV_ERR_INVALID, "waves_per_simd must be 0, 1 or 2 (got %d)", opts->waves_per_simd);
-  if (kernel == 2 && layout->kv_dtype != PKV_BF16)
-    return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16 cache");
+  if (kernel == 2 && layout->kv_dtype == PKV_F32)
+    return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16 or int8 cache");
+  if (kernel == 1 && layout->kv_dtype == PKV_INT8)
+    return pkv_set_error(PKV_ERR_INVALID, "an int8 cache is read by the matrix-core kernel only");
   if (num_seqs > PKV_MAX_SPLIT_SEQS)
     return pkv_set_error(PKV_ERR_INVALID, "at most %d sequences per call (got %d)", PKV_MAX_SPLIT_SEQS, num_seqs);
   if (max_context_len > (1 << 22))

@@ -1,4 +1,5 @@
-// PagedAttention decode, matrix-core kernel (bf16 KV, grouped-query heads).
+// PagedAttention decode, matrix-core kernel (bf16 or int8 KV, grouped-query
+// heads).
 //
 // What it computes [KV Cache 工程学 §15.5; 新一代 KV Cache 管理 §8.1]: for a
 // sequence b and its query heads h of kv group g, the new token's query is
@@ -7,7 +8,11 @@
 // The context is visited 32 tokens at a time with a running maximum and sum
 // (online softmax), so the softmax stays global even though the data arrive
 // block by block (the per-page softmax of the vendor article
-// [PagedAttention：大模型KV Cache内存管理革新 §3.2] is not used).
+// [PagedAttention：大模型KV Cache内存管理革新 §3.2] is not used).  The
+// maximum used as the exponent's reference only moves when new scores exceed
+// it by more than 2^8 in weight; any reference gives the same quotient, and
+// skipping the rescale of the D/16 accumulator tiles saves most of the
+// per-chunk vector work.
 //
 // Work split.  Persistent waves each take one equal, contiguous share of the
 // batch's 32-token chunks (pkv_device.h, "Balanced split"): the mix of
@@ -32,6 +37,16 @@
 // straight from memory once per segment: the whole group shares them through
 // the MFMA, and nothing else in the wave would reuse an LDS copy.
 //
+// int8 cache [KV Cache 工程学 §15.7 (3)].  Codes are loaded 8 bytes per lane
+// where bf16 takes 16 and widened to bf16 exactly (|code| <= 127 needs 7
+// significant bits), so the same MFMAs run on the same lane layout.  A
+// token's K scale multiplies its score after the score MFMA; its V scale
+// multiplies its softmax weight before the weight is rounded to bf16 for the
+// PV MFMA, while the running sum takes the weight itself.  Each lane reads the
+// 8 scales of its 8 token slots (32 contiguous bytes) of K and of V.  Codes of
+// slots past the context are finite whatever they hold, so a zero weight
+// masks them; their scales may be anything and are never used.
+//
 // Memory pipeline.  Block ids and lengths are scalar loads issued one chunk
 // ahead; chunk c+1's K is requested as soon as chunk c's score MFMAs have
 // consumed the K registers and its V once the PV MFMAs have consumed V, so a
@@ -47,6 +62,17 @@ namespace {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// Eight int8 codes, widened exactly to bf16.
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint2 u) {
+  bf16x8_t r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[k] = (__bf16)(float)(int8_t)(u.x >> (8 * k));
+    r[4 + k] = (__bf16)(float)(int8_t)(u.y >> (8 * k));
+  }
+  return r;
+}
+
 // Zero the bf16 elements of u whose index is >= nvalid (0..8).
 __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
   uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -58,17 +84,22 @@ __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Headroom of the running maximum, in base-2 exponent units: a chunk whose
+// scores stay within 2^kSlack of it leaves the accumulators unscaled.
+constexpr float kSlack = 8.0f;
+
 // Chunks of K/V a wave keeps in registers: the one being computed and
 // NBUF - 1 in flight behind it.
 #ifndef PKV_MFMA_NBUF
 #define PKV_MFMA_NBUF 2
 #endif
 
-template <int D, int W, int NB>
+template <int D, int W, int NB, bool I8>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
-  constexpr int TILE = 16 * D;
+  constexpr int TB = I8 ? 16 * D + 64 : 32 * D;  // bytes per (block, kv head) tile
+  using Unit = std::conditional_t<I8, uint2, uint4>;  // 8 elements of K or V
   extern __shared__ __align__(16) int32_t s_lds[];  // chunk scan, lengths, wave totals
 
   const int lane = threadIdx.x & 63;
@@ -82,8 +113,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   const int ksel = r16 >> 3;
   const int ktx = ((r16 >> 2) & 1) * 8 + (r16 & 3);
   const int vsel = grp >> 1, vhalf = grp & 1;
-  const uint16_t *kpool = reinterpret_cast<const uint16_t *>(P.k_pool);
-  const uint16_t *vpool = reinterpret_cast<const uint16_t *>(P.v_pool);
+  const uint8_t *kpool = reinterpret_cast<const uint8_t *>(P.k_pool);
+  const uint8_t *vpool = reinterpret_cast<const uint8_t *>(P.v_pool);
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(P.q);
   const int qh = min(r16, G - 1);  // columns G..15 are zero; their lanes read row G-1 and discard it
 
@@ -95,7 +126,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   // set per buffer.
   constexpr int NQ = NB == 2 ? 1 : NB;
   bf16x8_t qb[NQ][NKK];
-  uint4 ax[NB][NKK], ay[NB][NKK], va[NB][NNN];
+  Unit ax[NB][NKK], ay[NB][NKK], va[NB][NNN];
+  float4 ksc[NB][2], vsc[NB][2];  // int8: scales of this lane's 8 token slots
 
   auto issue = [&](auto bi) {  // loads of the chunk held in buffer bi
     constexpr int I = decltype(bi)::value;
@@ -107,19 +139,41 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       const uint4 u = qr[4 * kk + grp];
       qb[QI][kk] = as_bf16x8(r16 < G ? u : make_uint4(0, 0, 0, 0));
     }
-    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + c.g) * TILE);
+    const uint8_t *kt = kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + c.g) * TB;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const int cc = 4 * kk + grp;
-      ax[I][kk] = kt[cc * 16 + ktx];
-      ay[I][kk] = kt[cc * 16 + ktx + 4];
+      const int cc = 4 * kk + grp;  // elements 8cc .. 8cc+7 of the row
+      if constexpr (I8) {
+        const uint8_t *u = kt + ((cc >> 1) * 16 + ktx) * 16 + (cc & 1) * 8;
+        ax[I][kk] = *reinterpret_cast<const uint2 *>(u);
+        ay[I][kk] = *reinterpret_cast<const uint2 *>(u + 64);
+      } else {
+        const uint4 *u = reinterpret_cast<const uint4 *>(kt);
+        ax[I][kk] = u[cc * 16 + ktx];
+        ay[I][kk] = u[cc * 16 + ktx + 4];
+      }
+    }
+    if constexpr (I8) {
+      const float4 *sc = reinterpret_cast<const float4 *>(
+          kpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + c.g) * TB + 16 * D + 32 * vhalf);
+      ksc[I][0] = sc[0];
+      ksc[I][1] = sc[1];
     }
   };
   auto issue_v = [&](auto bi) {
     constexpr int I = decltype(bi)::value;
-    const uint4 *vt = reinterpret_cast<const uint4 *>(vpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + cq[I].g) * TILE);
+    const uint8_t *vt = vpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + cq[I].g) * TB;
+    if constexpr (I8) {
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn) va[I][nn] = vt[2 * (16 * nn + r16) + vhalf];
+      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = *reinterpret_cast<const uint2 *>(vt + (16 * nn + r16) * 16 + 8 * vhalf);
+      const float4 *sc = reinterpret_cast<const float4 *>(vt + 16 * D + 32 * vhalf);
+      vsc[I][0] = sc[0];
+      vsc[I][1] = sc[1];
+    } else {
+      const uint4 *u = reinterpret_cast<const uint4 *>(vt);
+#pragma unroll
+      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = u[2 * (16 * nn + r16) + vhalf];
+    }
   };
 
   f32x4_t o[NNN];
@@ -158,33 +212,62 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     const int tok0 = 32 * cur.j;
     const int tb = tok0 + 16 * vsel + 8 * vhalf;  // this lane's first token (scores and V)
     float s[8];
+    if constexpr (I8) {
+      const float ks[8] = {ksc[I][0].x, ksc[I][0].y, ksc[I][0].z, ksc[I][0].w,
+                           ksc[I][1].x, ksc[I][1].y, ksc[I][1].z, ksc[I][1].w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r] = (tb + r < n) ? sx[r] * P.scale_log2 : -INFINITY;
-      s[4 + r] = (tb + 4 + r < n) ? sy[r] * P.scale_log2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        s[r] = (tb + r < n) ? sx[r] * ks[r] * P.scale_log2 : -INFINITY;
+        s[4 + r] = (tb + 4 + r < n) ? sy[r] * ks[4 + r] * P.scale_log2 : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[r] = (tb + r < n) ? sx[r] * P.scale_log2 : -INFINITY;
+        s[4 + r] = (tb + 4 + r < n) ? sy[r] * P.scale_log2 : -INFINITY;
+      }
     }
     float cmax = s[0];
 #pragma unroll
     for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, s[r]);
     cmax = rows_max4(cmax);
-    const float mnew = fmaxf(m, cmax);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
+    // The reference maximum moves only when some head's scores pass it by
+    // more than kSlack (base 2), and then for the whole wave at once: weights
+    // stay below 2^kSlack, and most chunks skip rescaling the accumulators.
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m + kSlack) != 0, 0)) {
+      const float mnew = fmaxf(m, cmax);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int nn = 0; nn < NNN; ++nn) o[nn] *= alpha;
+    }
     bf16x8_t pv;
     float psum = 0.f;
+    if constexpr (I8) {
+      const float vs[8] = {vsc[I][0].x, vsc[I][0].y, vsc[I][0].z, vsc[I][0].w,
+                           vsc[I][1].x, vsc[I][1].y, vsc[I][1].z, vsc[I][1].w};
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const __bf16 pr = (__bf16)fast_exp2(s[r] - mnew);
-      pv[r] = pr;
-      psum += (float)pr;  // the PV numerator uses the rounded weights too
+      for (int r = 0; r < 8; ++r) {
+        const float e = fast_exp2(s[r] - m);
+        psum += e;
+        pv[r] = (__bf16)((tb + r < n) ? e * vs[r] : 0.f);  // scales past the context may be NaN
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const __bf16 pr = (__bf16)fast_exp2(s[r] - m);
+        pv[r] = pr;
+        psum += (float)pr;  // the PV numerator uses the rounded weights too
+      }
     }
-    l = l * alpha + psum;
+    l += psum;
+    if constexpr (!I8) {
+      if (tok0 + 32 > n) {  // slots past the context may hold anything, NaN included
+        const int nvalid = min(max(n - tb, 0), 8);
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn) o[nn] *= alpha;
-    if (tok0 + 32 > n) {  // slots past the context may hold anything, NaN included
-      const int nvalid = min(max(n - tb, 0), 8);
-#pragma unroll
-      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = keep_first(va[I][nn], nvalid);
+        for (int nn = 0; nn < NNN; ++nn) va[I][nn] = keep_first(va[I][nn], nvalid);
+      }
     }
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[I][nn]), pv, o[nn], 0, 0, 0);
@@ -238,9 +321,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
 #endif
 constexpr int kWaves = PKV_MFMA_WAVES;
 
-template <int D>
+template <int D, bool I8>
 int launch(const pkv_decode_args &a, const SplitParams &p) {
-  auto kern = decode_mfma_kernel<D, kWaves, PKV_MFMA_NBUF>;
+  auto kern = decode_mfma_kernel<D, kWaves, PKV_MFMA_NBUF, I8>;
   size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves);
   // One wave per SIMD: a workgroup takes more than half of a CU's 160 KiB of
   // LDS, so no second one is placed beside it.  Two waves on one SIMD do not
@@ -256,5 +339,6 @@ int launch(const pkv_decode_args &a, const SplitParams &p) {
 
 int pkv_launch_decode_mfma(const pkv_decode_args &a) {
   const SplitParams p = pkv_split_params(a);
-  return a.L->head_dim == 128 ? launch<128>(a, p) : launch<64>(a, p);
+  if (a.L->kv_dtype == PKV_INT8) return a.L->head_dim == 128 ? launch<128, true>(a, p) : launch<64, true>(a, p);
+  return a.L->head_dim == 128 ? launch<128, false>(a, p) : launch<64, false>(a, p);
 }

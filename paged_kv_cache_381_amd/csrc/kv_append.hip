@@ -4,7 +4,8 @@
 // cache [KV Cache 工程学 §15.1]; with paging the store goes to slot t of the
 // physical block named by the sequence's table [§15.5].  The host block
 // manager turns (sequence, position) into slot = block*16 + t, so the kernel
-// is a bit-exact scatter.  Copy-on-write duplicates a whole shared block
+// is a bit-exact scatter -- or, for an int8 cache [§15.7 (3)], a per-row
+// quantisation followed by the scatter.  Copy-on-write duplicates a whole shared block
 // before a sequence writes into it [KV Cache 与 PagedAttention, first article].
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -44,8 +45,76 @@ __global__ __launch_bounds__(256) void append_kernel(E *__restrict__ kpool, E *_
   }
 }
 
+// int8 cache.  A group of D/8 lanes quantises one (token, kv head) row of K
+// and one of V; a lane holds 8 consecutive bf16 elements of each.  The row's
+// largest magnitude comes from xor-shuffles inside the group, then every
+// lane divides its elements by scale = amax / 127 in float32 (correctly
+// rounded division), rounds half to even and clamps to [-127, 127].  Codes go
+// to the tile's K and V layouts and lane 0 of the group writes the two scales
+// after the tile's codes.
+template <int D>
+__global__ __launch_bounds__(256) void append_int8_kernel(uint8_t *__restrict__ kpool, uint8_t *__restrict__ vpool,
+                                                          const uint16_t *__restrict__ k_new,
+                                                          const uint16_t *__restrict__ v_new,
+                                                          const int64_t *__restrict__ slots, int64_t rows, int H,
+                                                          int num_blocks) {
+  constexpr int LPR = D / 8;  // lanes per row
+  constexpr int TB = 16 * D + 64;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  const int64_t r = row < rows ? row : 0;  // surplus groups work on row 0 and store nothing
+  const int64_t t = r / H;
+  const int g = (int)(r - t * H);
+  const uint4 kx = *reinterpret_cast<const uint4 *>(k_new + r * D + 8 * part);
+  const uint4 vx = *reinterpret_cast<const uint4 *>(v_new + r * D + 8 * part);
+  const int64_t s = slots[t];
+  float kf[8], vf[8];
+  const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w}, vw[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kf[2 * e] = __uint_as_float(kw[e] << 16);
+    kf[2 * e + 1] = __uint_as_float(kw[e] & 0xffff0000u);
+    vf[2 * e] = __uint_as_float(vw[e] << 16);
+    vf[2 * e + 1] = __uint_as_float(vw[e] & 0xffff0000u);
+  }
+  float ka = 0.f, va = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ka = fmaxf(ka, fabsf(kf[e]));
+    va = fmaxf(va, fabsf(vf[e]));
+  }
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) {
+    ka = fmaxf(ka, __shfl_xor(ka, o, LPR));
+    va = fmaxf(va, __shfl_xor(va, o, LPR));
+  }
+  if (row >= rows || s < 0 || s >= (int64_t)num_blocks * 16) return;
+  const float ks = ka / 127.0f, vs = va / 127.0f;
+  uint32_t kc[2] = {0u, 0u};
+  uint8_t vc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int kq = ka > 0.f ? (int)fminf(fmaxf(rintf(kf[e] / ks), -127.f), 127.f) : 0;
+    const int vq = va > 0.f ? (int)fminf(fmaxf(rintf(vf[e] / vs), -127.f), 127.f) : 0;
+    kc[e >> 2] |= (uint32_t)(kq & 0xff) << (8 * (e & 3));
+    vc[e] = (uint8_t)(vq & 0xff);
+  }
+  const int64_t blk = s >> 4;
+  const int off = (int)(s & 15);
+  const int d0 = 8 * part;
+  uint8_t *kt = kpool + ((size_t)blk * H + g) * TB;
+  uint8_t *vt = vpool + ((size_t)blk * H + g) * TB;
+  *reinterpret_cast<uint2 *>(kt + ((d0 >> 4) * 16 + off) * 16 + (d0 & 15)) = make_uint2(kc[0], kc[1]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vt[(d0 + e) * 16 + off] = vc[e];
+  if (part == 0) {
+    *reinterpret_cast<float *>(kt + 16 * D + 4 * off) = ks;
+    *reinterpret_cast<float *>(vt + 16 * D + 4 * off) = vs;
+  }
+}
+
 // One workgroup per (pair, pool): a block's tiles for all heads are one
-// contiguous run of H*16*D elements in either pool.
+// contiguous run of H tiles in either pool.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4 *__restrict__ kpool, uint4 *__restrict__ vpool,
                                                           const int32_t *__restrict__ pairs, int units_per_block,
                                                           int num_blocks) {
@@ -63,6 +132,15 @@ int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const voi
                       const int64_t *slots, int32_t num_tokens, void *stream) {
   if (num_tokens == 0) return 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (L->kv_dtype == PKV_INT8) {
+    const int64_t rows = (int64_t)num_tokens * L->num_kv_heads;
+    const int per_block = 256 / (L->head_dim / 8);
+    const dim3 grid((unsigned)((rows + per_block - 1) / per_block));
+    auto kern = L->head_dim == 128 ? append_int8_kernel<128> : append_int8_kernel<64>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (uint8_t *)k_pool, (uint8_t *)v_pool, (const uint16_t *)k_new,
+                       (const uint16_t *)v_new, slots, rows, L->num_kv_heads, L->num_blocks);
+    return (int)hipGetLastError();
+  }
   const int units = L->num_kv_heads * L->head_dim * pkv_elem_bytes(L->kv_dtype) / 16;
   dim3 grid(num_tokens), block(units < 256 ? (units + 63) / 64 * 64 : 256);
   if (L->kv_dtype == PKV_BF16)
@@ -79,7 +157,7 @@ int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const voi
 int pkv_launch_copy_blocks(const pkv_layout *L, void *k_pool, void *v_pool, const int32_t *pairs,
                            int32_t num_pairs, void *stream) {
   if (num_pairs == 0) return 0;
-  const int units = L->num_kv_heads * 16 * L->head_dim * pkv_elem_bytes(L->kv_dtype) / 16;
+  const int units = (int)(L->num_kv_heads * pkv_tile_bytes(L) / 16);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      (uint4 *)k_pool, (uint4 *)v_pool, pairs, units, L->num_blocks);
   return (int)hipGetLastError();

@@ -48,8 +48,8 @@ int pkv_check_layout(const pkv_layout *L) {
   if (L->num_kv_heads <= 0) return pkv_set_error(PKV_ERR_INVALID, "num_kv_heads must be > 0");
   if (L->head_dim != 64 && L->head_dim != 128)
     return pkv_set_error(PKV_ERR_INVALID, "head_dim must be 64 or 128 (got %d)", L->head_dim);
-  if (L->kv_dtype != PKV_F32 && L->kv_dtype != PKV_BF16)
-    return pkv_set_error(PKV_ERR_INVALID, "kv_dtype must be PKV_F32 or PKV_BF16");
+  if (L->kv_dtype != PKV_F32 && L->kv_dtype != PKV_BF16 && L->kv_dtype != PKV_INT8)
+    return pkv_set_error(PKV_ERR_INVALID, "kv_dtype must be PKV_F32, PKV_BF16 or PKV_INT8");
   return PKV_OK;
 }
 
@@ -454,13 +454,12 @@ extern "C" int pkv_pool_stats(const pkv_pool *pool, pkv_stats *out) {
 
 extern "C" int64_t pkv_kv_bytes_per_token(const pkv_layout *layout, int32_t num_layers) {
   if (pkv_check_layout(layout) || num_layers < 0) return 0;
-  return (int64_t)num_layers * 2 * layout->num_kv_heads * layout->head_dim * pkv_elem_bytes(layout->kv_dtype);
+  return (int64_t)num_layers * 2 * layout->num_kv_heads * pkv_row_bytes(layout);
 }
 
 extern "C" int64_t pkv_pool_bytes(const pkv_layout *layout) {
   if (pkv_check_layout(layout)) return 0;
-  return (int64_t)layout->num_blocks * layout->num_kv_heads * PKV_BLOCK_SIZE * layout->head_dim *
-         pkv_elem_bytes(layout->kv_dtype);
+  return (int64_t)layout->num_blocks * layout->num_kv_heads * pkv_tile_bytes(layout);
 }
 
 extern "C" int pkv_validate_tables(const pkv_layout *layout, const int32_t *tables, const int32_t *context_lens,

@@ -21,22 +21,26 @@ _NAN = {"bf16": 0x7FC0, "f32": float("nan")}
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str, num_layers: int = 1,
                  free_order=None, device="cuda", fill_nan: bool = True):
-        self.dtype = dtype
+        self.dtype = dtype  # storage of the cache: "f32", "bf16" or "int8"
         self.layout = L.make_layout(num_blocks, num_kv_heads, head_dim, dtype)
         self.pool = L.pkv_pool_create(self.layout, free_order)
         self.device = torch.device(device)
-        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        tdt = L.pool_torch_dtype(self.layout)
         self.k_pools, self.v_pools = [], []
         for _ in range(num_layers):
             k = torch.empty(self.layout.pool_elems, dtype=tdt, device=self.device)
             v = torch.empty_like(k)
             if fill_nan:  # slots never written hold a NaN sentinel
-                if dtype == "bf16":
-                    k.view(torch.int16).fill_(_NAN["bf16"])
-                    v.view(torch.int16).fill_(_NAN["bf16"])
-                else:
-                    k.fill_(_NAN["f32"])
-                    v.fill_(_NAN["f32"])
+                for t in (k, v):
+                    if dtype == "bf16":
+                        t.view(torch.int16).fill_(_NAN["bf16"])
+                    elif dtype == "f32":
+                        t.fill_(_NAN["f32"])
+                    else:  # zero codes under a NaN scale
+                        tiles = t.view(-1, self.layout.tile_bytes)
+                        tiles[:, :16 * head_dim].zero_()
+                        sc = torch.full((tiles.shape[0], 16), float("nan"), dtype=torch.float32, device=self.device)
+                        tiles[:, 16 * head_dim:] = sc.view(torch.uint8).view(tiles.shape[0], 64)
             self.k_pools.append(k)
             self.v_pools.append(v)
 
@@ -136,7 +140,7 @@ class GpuWorkload:
         self.device = torch.device(device)
         order = np.concatenate([inst.free_order, np.arange(inst.num_blocks, inst.num_blocks + extra_blocks,
                                                            dtype=np.int32)])
-        self.cache = PagedKVCache(inst.num_blocks + extra_blocks, wl.num_kv_heads, wl.head_dim, wl.dtype,
+        self.cache = PagedKVCache(inst.num_blocks + extra_blocks, wl.num_kv_heads, wl.head_dim, wl.cache_dtype,
                                   num_layers=num_layers, free_order=order, device=device)
         c = self.cache
         pre = []

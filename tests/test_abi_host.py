@@ -53,6 +53,12 @@ def test_sizes():
     assert P.pkv_kv_bytes_per_token(lay, 32) == 128 * 1024  # Llama-3-8B [KV Cache 工程学 §15.2]
     assert P.pkv_kv_bytes_per_token(P.make_layout(10, 8, 128, "bf16"), 80) == 320 * 1024
     assert P.pkv_pool_bytes(lay) == 10 * 8 * 16 * 128 * 2
+    # int8: one byte per element [KV Cache 工程学 §15.7 (3)] plus a float32 scale per
+    # (token, kv head) row: 16 * D + 64 bytes per (block, kv head) tile
+    i8 = P.make_layout(10, 8, 128, "int8")
+    assert P.pkv_kv_bytes_per_token(i8, 32) == 32 * 2 * 8 * (128 + 4)
+    assert P.pkv_pool_bytes(i8) == 10 * 8 * (16 * 128 + 64) == i8.pool_elems
+    assert P.pkv_pool_bytes(P.make_layout(3, 2, 64, "int8")) == 3 * 2 * (16 * 64 + 64)
     # Both kernels split the batch the same way: partial slots per (sequence, query head)
     # = ceil(ceil(max_ctx / 32) / fewest chunks per wave) + 1, then partial (m, l) and a
     # header of 2 + B int32, each region padded to 16 bytes
@@ -66,6 +72,7 @@ def test_sizes():
     assert P.paged_attention_workspace_bytes(lay, 4, 32, 513, kernel=1) == split(4, 32, 128, 513, 4)
     f32 = P.make_layout(10, 4, 64, "f32")
     assert P.paged_attention_workspace_bytes(f32, 4, 4, 255, partition_tokens=32) == split(4, 4, 64, 255, 1)
+    assert P.paged_attention_workspace_bytes(i8, 4, 32, 512) == split(4, 32, 128, 512, 4)
 
 
 def test_validate_tables():
@@ -99,6 +106,10 @@ def test_decode_argument_errors_before_any_launch():
     assert call(part=48) == L.PKV_ERR_INVALID
     assert call(kernel=7) == L.PKV_ERR_INVALID
     assert call(kernel=2, lay_=P.make_layout(16, 2, 128, "f32")) == L.PKV_ERR_INVALID
+    assert call(kernel=1, lay_=P.make_layout(16, 2, 128, "int8")) == L.PKV_ERR_INVALID
+    bad = P.make_layout(16, 2, 128, "int8")
+    bad.kv_dtype = 3
+    assert call(lay_=bad) == L.PKV_ERR_INVALID
     assert call(mb=64, mctx=1024) == L.PKV_ERR_WORKSPACE
     assert lib.paged_attention_decode(ctypes.byref(lay), None, fake, fake, fake, fake, fake, 2, 4, 8, 64, 0.1,
                                       None, 0, ctypes.byref(o), None) == L.PKV_ERR_INVALID
