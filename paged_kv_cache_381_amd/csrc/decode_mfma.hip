@@ -84,6 +84,10 @@ __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// s_waitcnt immediate of gfx9 waiting for no outstanding vector memory
+// operation (vmcnt 0) and leaving the other counters unchecked.
+constexpr int kDrainVm = 0x0F70;
+
 // Headroom of the running maximum, in base-2 exponent units: a chunk whose
 // scores stay within 2^kSlack of it leaves the accumulators unscaled.
 constexpr float kSlack = 8.0f;
@@ -93,13 +97,21 @@ constexpr float kSlack = 8.0f;
 #ifndef PKV_MFMA_NBUF
 #define PKV_MFMA_NBUF 2
 #endif
+// An int8 chunk is half the bytes in half the registers: more of them stay in
+// flight to keep as many bytes on the way from memory.
+#ifndef PKV_MFMA_NBUF_I8
+#define PKV_MFMA_NBUF_I8 4
+#endif
 
 template <int D, int W, int NB, bool I8>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
   constexpr int TB = I8 ? 16 * D + 64 : 32 * D;  // bytes per (block, kv head) tile
-  using Unit = std::conditional_t<I8, uint2, uint4>;  // 8 elements of K or V
+  // K registers per 16-row token set: one 16-byte unit per score MFMA for
+  // bf16; for int8 one unit holds the codes of two MFMAs (16 elements).
+  constexpr int NKU = I8 ? NKK / 2 : NKK;
+  using VUnit = std::conditional_t<I8, uint2, uint4>;  // 8 elements of V
   extern __shared__ __align__(16) int32_t s_lds[];  // chunk scan, lengths, wave totals
 
   const int lane = threadIdx.x & 63;
@@ -113,10 +125,17 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   const int ksel = r16 >> 3;
   const int ktx = ((r16 >> 2) & 1) * 8 + (r16 & 3);
   const int vsel = grp >> 1, vhalf = grp & 1;
+  // Element group (8 elements of a row) that lane group grp feeds to score
+  // MFMA kk.  Any one-to-one choice gives the same dot products as long as K
+  // and Q follow it; int8 pairs the two halves of one 16-byte unit.
+  auto kgroup = [&](int kk) { return I8 ? 8 * (kk >> 1) + 2 * grp + (kk & 1) : 4 * kk + grp; };
   const uint8_t *kpool = reinterpret_cast<const uint8_t *>(P.k_pool);
   const uint8_t *vpool = reinterpret_cast<const uint8_t *>(P.v_pool);
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(P.q);
-  const int qh = min(r16, G - 1);  // columns G..15 are zero; their lanes read row G-1 and discard it
+  // Columns G..15 repeat head G-1: the columns of both products never mix,
+  // and those lanes store nothing.  (Their load is not masked: a load under
+  // a lane mask would leave the memory counter unknown after it.)
+  const int qh = min(r16, G - 1);
 
   // Per buffer: the chunk's cursor, physical blocks, query slices, K and V.
   Cursor cq[NB];
@@ -126,7 +145,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   // set per buffer.
   constexpr int NQ = NB == 2 ? 1 : NB;
   bf16x8_t qb[NQ][NKK];
-  Unit ax[NB][NKK], ay[NB][NKK], va[NB][NNN];
+  uint4 ax[NB][NKU], ay[NB][NKU];
+  VUnit va[NB][NNN];
   float4 ksc[NB][2], vsc[NB][2];  // int8: scales of this lane's 8 token slots
 
   auto issue = [&](auto bi) {  // loads of the chunk held in buffer bi
@@ -136,22 +156,17 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + qh) * D);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 u = qr[4 * kk + grp];
-      qb[QI][kk] = as_bf16x8(r16 < G ? u : make_uint4(0, 0, 0, 0));
+      const uint4 u = qr[kgroup(kk)];
+      qb[QI][kk] = as_bf16x8(u);
     }
-    const uint8_t *kt = kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + c.g) * TB;
+    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + c.g) * TB);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int cc = 4 * kk + grp;  // elements 8cc .. 8cc+7 of the row
-      if constexpr (I8) {
-        const uint8_t *u = kt + ((cc >> 1) * 16 + ktx) * 16 + (cc & 1) * 8;
-        ax[I][kk] = *reinterpret_cast<const uint2 *>(u);
-        ay[I][kk] = *reinterpret_cast<const uint2 *>(u + 64);
-      } else {
-        const uint4 *u = reinterpret_cast<const uint4 *>(kt);
-        ax[I][kk] = u[cc * 16 + ktx];
-        ay[I][kk] = u[cc * 16 + ktx + 4];
-      }
+    for (int ku = 0; ku < NKU; ++ku) {
+      // 16-byte unit of the lane's token row: int8 unit 4ku+grp holds the
+      // element groups 2(4ku+grp) and +1 of score MFMAs 2ku and 2ku+1.
+      const int cu = 4 * ku + grp;
+      ax[I][ku] = kt[cu * 16 + ktx];
+      ay[I][ku] = kt[cu * 16 + ktx + 4];
     }
     if constexpr (I8) {
       const float4 *sc = reinterpret_cast<const float4 *>(
@@ -181,34 +196,65 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
+  // Every load is issued whatever the share's length: a chunk past the
+  // share's end re-reads the last real chunk's lines (cached, never used).
+  // Loads issued on some paths only would leave the count of loads in
+  // flight unknown, and the waits would then drain every buffer each step.
+  auto same_as = [&](int to, int from) {
+    cq[to] = cq[from];
+    pa[to] = pa[from];
+    pb[to] = pb[from];
+  };
   // Prologue: chunks lo .. lo+NB-2 are requested, chunk lo+NB-1 located.
   cq[0] = sh.first();
   sh.blocks(cq[0], pa[0], pb[0]);
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
-    ((lo + Is < hi ? (void)(Is == 0 ? 0 : (cq[Is] = sh.next(cq[Is - (Is > 0)]), sh.blocks(cq[Is], pa[Is], pb[Is]), 0)) : (void)0), ...);
+    ((Is == 0 ? (void)0
+              : (lo + Is < hi ? (void)(cq[Is] = sh.next(cq[Is - 1]), sh.blocks(cq[Is], pa[Is], pb[Is]))
+                              : same_as(Is, Is - 1))), ...);
   }(std::make_integer_sequence<int, NB>{});
+  // Requests leave in the order the loop issues them (K then V of each
+  // chunk): waits at the loop head are counted over both entries, and a
+  // prologue that sent a chunk's K last would make the first of them wait
+  // for everything.
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
-    ((lo + Is < hi && Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}), issue_v(std::integral_constant<int, Is>{})) : (void)0), ...);
+    ((Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0),
+                     issue_v(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0))
+                  : (void)0),
+     ...);
   }(std::make_integer_sequence<int, NB>{});
 
   int64_t x = lo;
   // One step computes chunk x from buffer I, requests chunk x+NB-1 into the
   // buffer chunk x-1 used, and locates chunk x+NB into buffer I.
-  auto step = [&](auto bi) -> bool {
+  auto step = [&](auto bi) {
     constexpr int I = decltype(bi)::value;
     constexpr int J = (I + NB - 1) % NB;
     constexpr int QI = NQ == 1 ? 0 : I;
     f32x4_t sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax[I][kk]), qb[QI][kk], sx, 0, 0, 0);
-      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ay[I][kk]), qb[QI][kk], sy, 0, 0, 0);
+      bf16x8_t kx, ky;
+      if constexpr (I8) {
+        const uint4 ux = ax[I][kk >> 1], uy = ay[I][kk >> 1];
+        kx = as_bf16x8((kk & 1) ? make_uint2(ux.z, ux.w) : make_uint2(ux.x, ux.y));
+        ky = as_bf16x8((kk & 1) ? make_uint2(uy.z, uy.w) : make_uint2(uy.x, uy.y));
+      } else {
+        kx = as_bf16x8(ax[I][kk]);
+        ky = as_bf16x8(ay[I][kk]);
+      }
+      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[QI][kk], sx, 0, 0, 0);
+      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[QI][kk], sy, 0, 0, 0);
     }
-    const bool far = x + NB - 1 < hi;
-    if (far) issue(std::integral_constant<int, J>{});
+    if (x + NB - 1 >= hi) same_as(J, I);  // no chunk x + NB - 1 in the share
+    issue(std::integral_constant<int, J>{});
 
     const Cursor &cur = cq[I];
-    const int n = cur.n;
+    // Past the share's end the loop runs on to the end of its group of NB
+    // steps over a copy of the last chunk with no token counted: nothing is
+    // stored, and the loop keeps one exit, after a whole group.
+    const bool real = x < hi;
+    const int n = real ? cur.n : 0;
     const int tok0 = 32 * cur.j;
     const int tb = tok0 + 16 * vsel + 8 * vhalf;  // this lane's first token (scores and V)
     float s[8];
@@ -271,10 +317,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     }
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[I][nn]), pv, o[nn], 0, 0, 0);
-    if (far) issue_v(std::integral_constant<int, J>{});
+    issue_v(std::integral_constant<int, J>{});
 
-    const bool last = x + 1 >= hi;
-    if (last || cur.j == cur.cnt - 1) {  // the piece ends here
+    if (real && (x + 1 >= hi || cur.j == cur.cnt - 1)) {  // the piece ends here
       const float lsum = rows_sum4(l);
       const bool whole = sh.whole(cur);
       if (r16 < G) {
@@ -295,24 +340,25 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
           if (grp == 0) *reinterpret_cast<float2 *>(P.ws_ml + 2 * slot) = make_float2(m, lsum);
         }
       }
+      // Stores share the memory counter with loads: drain it here, once per
+      // piece, so that the loads in flight are counted exactly on every path
+      // (otherwise each chunk's waits would assume the worst and drain it).
+      __builtin_amdgcn_s_waitcnt(kDrainVm);
 #pragma unroll
       for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m = -INFINITY;
       l = 0.f;
     }
-    if (last) return false;
     if (x + NB < hi) {
       cq[I] = sh.next(cq[J]);
       sh.blocks(cq[I], pa[I], pb[I]);
     }
     ++x;
-    return true;
   };
-  for (;;) {
-    const bool go = [&]<int... Is>(std::integer_sequence<int, Is...>) {
-      return (step(std::integral_constant<int, Is>{}) && ...);
+  while (x < hi) {
+    [&]<int... Is>(std::integer_sequence<int, Is...>) {
+      (step(std::integral_constant<int, Is>{}), ...);
     }(std::make_integer_sequence<int, NB>{});
-    if (!go) break;
   }
 }
 
@@ -323,7 +369,7 @@ constexpr int kWaves = PKV_MFMA_WAVES;
 
 template <int D, bool I8>
 int launch(const pkv_decode_args &a, const SplitParams &p) {
-  auto kern = decode_mfma_kernel<D, kWaves, PKV_MFMA_NBUF, I8>;
+  auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8>;
   size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves);
   // One wave per SIMD: a workgroup takes more than half of a CU's 160 KiB of
   // LDS, so no second one is placed beside it.  Two waves on one SIMD do not
