@@ -298,6 +298,52 @@ void orc_partitioned_attention(int dtype, int Hq, int Hkv, int D, const void *q,
 
 /* Read back the K or V of token j of a paged sequence into row-major
  * [Hkv][D] doubles (used to check that reads through different tables agree). */
+/* Causal prefill over a paged cache [KV Cache 工程学 §15.1: a prompt of i
+ * tokens is an i x i causal attention; §15.6 and 新一代 KV Cache 管理 §8.3:
+ * the tokens of a cached prefix are not recomputed].  Sequence b holds
+ * ctx[b] tokens in its table, the last nq_b = qstart[b+1] - qstart[b] of them
+ * new; their K/V are already stored.  New token t (query row qstart[b] + t)
+ * sits at position p_b + t with p_b = ctx[b] - nq_b and attends to positions
+ * 0 .. p_b + t.  q: [T][Hq][D] (T = qstart[B]) of the row type; out:
+ * [T][Hq][D] double. */
+void orc_paged_prefill(int dtype, int Hq, int Hkv, int D, const void *q, const void *kpool,
+                       const void *vpool, const int32_t *tables, int max_blocks, const int32_t *ctx,
+                       const int32_t *qstart, int B, double scale, double *out) {
+  int G = Hq / Hkv, qt = row_type(dtype);
+  int64_t T = qstart[B];
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t rh = 0; rh < T * Hq; ++rh) {
+    int64_t r = rh / Hq;
+    int h = (int)(rh % Hq), g = h / G;
+    int b = 0;
+    while (qstart[b + 1] <= r) ++b;
+    int nq = qstart[b + 1] - qstart[b];
+    int t = (int)(r - qstart[b]);
+    int n = ctx[b] - nq + t + 1; /* keys 0 .. p_b + t */
+    double *o = out + (size_t)rh * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+      int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d)
+        acc += elem(q, (size_t)rh * D + d, qt) * kval(kpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
+      s[j] = scale * acc;
+      if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) {
+      int64_t blk = tables[(size_t)b * max_blocks + j / BLOCK];
+      double w = exp(s[j] - m);
+      l += w;
+      for (int d = 0; d < D; ++d) o[d] += w * vval(vpool, blk, g, j % BLOCK, d, Hkv, D, dtype);
+    }
+    for (int d = 0; d < D; ++d) o[d] /= l;
+    free(s);
+  }
+}
+
 void orc_gather_token(int dtype, int Hkv, int D, const void *kpool, const void *vpool,
                       const int32_t *table, int j, double *k_out, double *v_out) {
   int64_t blk = table[j / BLOCK];

@@ -37,6 +37,7 @@ def lib():
         L.orc_contiguous_attention.argtypes = [I, I, I, I, P, P, P, I, D, P]
         L.orc_partitioned_attention.argtypes = [I, I, I, I, P, P, P, P, I, P, I, D, I, P]
         L.orc_gather_token.argtypes = [I, I, I, P, P, P, I, P, P]
+        L.orc_paged_prefill.argtypes = [I, I, I, I, P, P, P, P, I, P, P, I, D, P]
         L.orc_num_threads.restype = I
         _lib = L
     return _lib
@@ -103,6 +104,25 @@ def partitioned_attention(dtype, q, kpool, vpool, tables, ctx, num_kv_heads, sca
     lib().orc_partitioned_attention(_DT[dtype], Hq, num_kv_heads, D, _p(q), _p(kpool), _p(vpool),
                                     _p(tables), tables.shape[1], _p(ctx), B, float(scale),
                                     int(part_tokens), _p(out))
+    return out
+
+
+def paged_prefill(dtype, q, kpool, vpool, tables, ctx, qstart, num_kv_heads, scale):
+    """Causal attention of every new token of every sequence: q [T][Hq][D]
+    (rows of sequence b are qstart[b] .. qstart[b+1]-1, the last tokens of its
+    ctx[b]) -> [T][Hq][D] float64."""
+    q = np.ascontiguousarray(q, dtype=_NP[ROW[dtype]])
+    T, Hq, D = q.shape
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx, dtype=np.int32)
+    qstart = np.ascontiguousarray(qstart, dtype=np.int32)
+    B = ctx.size
+    assert qstart.size == B + 1 and qstart[0] == 0 and qstart[-1] == T
+    assert (np.diff(qstart) >= 0).all() and (np.diff(qstart) <= ctx).all()
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    if T:
+        lib().orc_paged_prefill(_DT[dtype], Hq, num_kv_heads, D, _p(q), _p(kpool), _p(vpool), _p(tables),
+                                tables.shape[1], _p(ctx), _p(qstart), B, float(scale), _p(out))
     return out
 
 

@@ -403,8 +403,101 @@ def check_int8_copy_blocks():
         assert np.array_equal(pool[rest], old[rest])
 
 
+class PrefillProblem:
+    """Sequences whose last nq_b of ctx_b tokens are new (queries), stored
+    with the oracle's own bookkeeping and append; queries packed by row."""
+
+    def __init__(self, dtype, Hq, Hkv, D, ctx, nq, num_blocks, seed, kv=None):
+        self.dtype, self.Hq, self.Hkv, self.D = dtype, Hq, Hkv, D
+        self.ctx = np.asarray(ctx, np.int32)
+        self.nq = np.asarray(nq, np.int32)
+        self.qstart = np.concatenate([[0], np.cumsum(self.nq)]).astype(np.int32)
+        B = len(ctx)
+        rt = orc.ROW[dtype]
+        rng = np.random.default_rng(seed)
+        self.book = Book(num_blocks, rng.permutation(num_blocks))
+        self.ids = [self.book.create() for _ in range(B)]
+        self.kv = kv or [(normal_bits(seed * 31 + 2 * b, (int(ctx[b]), Hkv, D), rt),
+                          normal_bits(seed * 31 + 2 * b + 1, (int(ctx[b]), Hkv, D), rt)) for b in range(B)]
+        self.q = normal_bits(seed * 31 + 777, (int(self.qstart[-1]), Hq, D), rt)
+        self.kpool, self.vpool = orc.new_pool(num_blocks, Hkv, D, dtype)
+        for b, sid in enumerate(self.ids):
+            slots, _ = self.book.append_slots(sid, int(ctx[b]))
+            orc.append(dtype, Hkv, D, self.kpool, self.vpool, self.kv[b][0], self.kv[b][1], np.asarray(slots))
+        self.tables, _ = orc.tables_of(self.book, self.ids)
+        self.scale = 1.0 / math.sqrt(D)
+
+    def out(self):
+        return orc.paged_prefill(self.dtype, self.q, self.kpool, self.vpool, self.tables, self.ctx, self.qstart,
+                                 self.Hkv, self.scale)
+
+
+def check_prefill_brute_force():
+    """Causal prefill == exactly-summed textbook attention of each new token
+    over the positions up to and including its own (cached prefix + new
+    tokens), for shuffled blocks, with and without a prefix."""
+    for dtype in ("f32", "bf16"):
+        p = PrefillProblem(dtype, 4, 2, 8, ctx=[5, 19, 27, 1], nq=[5, 3, 20, 1], num_blocks=12, seed=13)
+        out = p.out()
+        G = p.Hq // p.Hkv
+        for b in range(len(p.ctx)):
+            p0 = int(p.ctx[b] - p.nq[b])
+            K, V = widen(p.kv[b][0], dtype), widen(p.kv[b][1], dtype)
+            for t in range(int(p.nq[b])):
+                r = int(p.qstart[b]) + t
+                for h in range(p.Hq):
+                    n = p0 + t + 1
+                    ref = brute_attention(list(widen(p.q[r, h], dtype)), K[:n, h // G].tolist(),
+                                          V[:n, h // G].tolist(), p.scale)
+                    err = np.abs(out[r, h] - np.asarray(ref)).max()
+                    assert err <= 1e-13, (dtype, b, t, h, err)
+
+
+def check_prefill_library_sdpa():
+    """Causal prefill == torch's scaled_dot_product_attention in float64 with
+    an explicit mask (query t of the new tokens sees keys 0 .. prefix + t)
+    and grouped-query heads."""
+    p = PrefillProblem("bf16", 8, 2, 64, ctx=[70, 33], nq=[30, 33], num_blocks=16, seed=17)
+    out = p.out()
+    for b in range(2):
+        n, nq = int(p.ctx[b]), int(p.nq[b])
+        rows = slice(int(p.qstart[b]), int(p.qstart[b + 1]))
+        q = torch.from_numpy(widen(p.q[rows], "bf16")).permute(1, 0, 2)[None]             # [1,Hq,nq,D]
+        k = torch.from_numpy(widen(p.kv[b][0], "bf16")).permute(1, 0, 2)[None].contiguous()  # [1,Hkv,n,D]
+        v = torch.from_numpy(widen(p.kv[b][1], "bf16")).permute(1, 0, 2)[None].contiguous()
+        mask = torch.arange(n)[None, :] <= (n - nq + torch.arange(nq))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q.contiguous(), k, v, attn_mask=mask,
+                                                               scale=p.scale, enable_gqa=True)
+        err = np.abs(out[rows] - ref[0].permute(1, 0, 2).numpy()).max()
+        assert err <= 1e-12, (b, err)
+
+
+def check_prefill_int8():
+    """Prefill over an int8 cache == textbook attention over the values
+    decoded from the bytes."""
+    p = PrefillProblem("int8", 4, 2, 16, ctx=[40, 9], nq=[12, 9], num_blocks=8, seed=19)
+    out = p.out()
+    G = p.Hq // p.Hkv
+    for b in range(2):
+        p0 = int(p.ctx[b] - p.nq[b])
+        for g in range(p.Hkv):
+            K, V = [], []
+            for j in range(int(p.ctx[b])):
+                blk, t = int(p.tables[b][j // 16]), j % 16
+                kc, ks = int8_read(p.kpool, p.Hkv, p.D, blk, g, t, False)
+                vc, vs = int8_read(p.vpool, p.Hkv, p.D, blk, g, t, True)
+                K.append((kc * float(ks)).tolist())
+                V.append((vc * float(vs)).tolist())
+            for t in range(int(p.nq[b])):
+                r = int(p.qstart[b]) + t
+                for h in range(g * G, (g + 1) * G):
+                    ref = brute_attention(list(widen(p.q[r, h], "bf16")), K[:p0 + t + 1], V[:p0 + t + 1], p.scale)
+                    assert np.abs(out[r, h] - np.asarray(ref)).max() <= 1e-13, (b, t, h)
+
+
 ALL_CHECKS = [check_brute_force, check_library_sdpa, check_paged_equals_contiguous,
               check_placement_invariance, check_special_cases, check_merge_identity,
               check_gqa_reduces_to_mha, check_append_roundtrip, check_layout_golden,
               check_rejects_per_page_softmax, check_int8_quant_golden, check_int8_layout_golden,
-              check_int8_quant_error_bound, check_int8_brute_force, check_int8_copy_blocks]
+              check_int8_quant_error_bound, check_int8_brute_force, check_int8_copy_blocks,
+              check_prefill_brute_force, check_prefill_library_sdpa, check_prefill_int8]

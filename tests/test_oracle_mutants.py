@@ -44,6 +44,10 @@ MUTANTS = {
     "int8_v_read_as_k": ("size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16)",
                          "size_t at = !is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16)"),
     "int8_scale_255": ("float scale = amax / 127.0f;", "float scale = amax / 255.0f;"),
+    "prefill_causal_exclusive": ("int n = ctx[b] - nq + t + 1;", "int n = ctx[b] - nq + t;"),
+    "prefill_without_prefix": ("int n = ctx[b] - nq + t + 1;", "int n = t + 1;"),
+    "prefill_whole_context": ("int n = ctx[b] - nq + t + 1;", "int n = ctx[b];"),
+    "prefill_query_of_first_token": ("elem(q, (size_t)rh * D + d, qt)", "elem(q, ((size_t)qstart[b] * Hq + h) * D + d, qt)"),
     "int8_copy_k_only": ("memcpy((char *)vpool + dst * tb", "if (0) memcpy((char *)vpool + dst * tb"),
 }
 
@@ -67,7 +71,7 @@ from oracle import attn as orc
 real = orc.lib()
 mutant = ctypes.CDLL(sys.argv[1])
 for fn in ("orc_append", "orc_copy_blocks", "orc_paged_attention", "orc_contiguous_attention",
-           "orc_partitioned_attention", "orc_gather_token", "orc_num_threads"):
+           "orc_partitioned_attention", "orc_gather_token", "orc_num_threads", "orc_paged_prefill"):
     getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
     getattr(mutant, fn).restype = getattr(real, fn).restype
 orc._lib = mutant
