@@ -194,6 +194,104 @@ def traffic_summary(args):
     print("\n".join(lines))
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+PREFILL_METRIC = "paged prefill attention TFLOP/s (% of bf16 MFMA peak), 1 GPU"
+
+
+def cpu_baseline_prefill(inst, min_seconds: float):
+    """The fp64 oracle's causal prefill on the host, on a bounded sample: the
+    last new tokens of sequence 0 (the rows that see the most keys), doubled
+    until the run lasts min_seconds; reported in GFLOP/s of the same count."""
+    import numpy as np
+    from oracle import attn as orc
+    wl = inst.wl
+    built = orc.build_prefill(inst)
+    q = inst.q()
+    qs = inst.qstart
+    rows, reps = 1, 0
+    while True:
+        last = min(rows, int(inst.nq[0]))
+        sub = q[int(qs[1]) - last:int(qs[1])]
+        t0 = time.perf_counter()
+        orc.paged_prefill(wl.cache_dtype, sub, built["kpool"], built["vpool"], built["tables"][:1], built["ctx"][:1],
+                          np.array([0, last], np.int32), wl.num_kv_heads, 1.0 / math.sqrt(wl.head_dim))
+        dt = time.perf_counter() - t0
+        reps += 1
+        if dt >= min_seconds or last == int(inst.nq[0]):
+            break
+        rows *= 2
+    n0 = int(inst.ctx[0]) - int(inst.nq[0])
+    keys = sum(n0 + t + 1 for t in range(int(inst.nq[0]) - last, int(inst.nq[0])))
+    flops = 4 * wl.head_dim * wl.num_q_heads * keys
+    return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"the last {last} new tokens of sequence 0 of {wl.name} ({keys} query-key pairs per head, "
+                      f"{flops / 1e9:.2f} GFLOP) in {dt:.1f} s; OMP threads = {orc.num_threads()}, "
+                      f"host cores = {os.cpu_count()}"}
+
+
+def bench_prefill(args):
+    """A prefill step per layer: store the new tokens' K/V into their slots
+    (paged_kv_append), then the causal attention of every new token over its
+    paged context (paged_attention_prefill).  Reports whole-step TFLOP/s and
+    the prefill kernel against the bf16 matrix-core peak."""
+    import torch
+    from workloads import prefill as PW
+    from paged_kv_cache_381_amd.engine import GpuPrefill
+
+    inst = PW.get(args.workload)
+    wl = inst.wl
+    K, W = args.steps, args.warmup
+    layers = args.layers or 2
+    print(f"[bench] building {wl.name}: B={wl.batch} Hq={wl.num_q_heads} H={wl.num_kv_heads} D={wl.head_dim} "
+          f"{wl.cache_dtype} cache, layers/step={layers}, new tokens {int(inst.nq.sum())}", flush=True)
+    gp = GpuPrefill(inst, num_layers=layers)
+    flops = inst.flops()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def step(timed):
+        for layer in range(layers):
+            gp.cache.write(layer, gp.new_slots_dev, gp.k_new, gp.v_new)
+            if timed is not None and layer == timed % layers:
+                ev[timed][0].record()
+                gp.run(layer)
+                ev[timed][1].record()
+            else:
+                gp.run(layer)
+
+    for _ in range(W):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert torch.isfinite(gp.out).all().item(), "non-finite prefill output"
+    avg_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    tflops = flops * layers * K / elapsed / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    print(f"[bench] {K} steps in {elapsed:.3f} s; prefill kernel avg {avg_ms * 1e3:.1f} us "
+          f"({achieved:.1f} TFLOP/s)", flush=True)
+    res = {
+        "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.description, "name": wl.name, "batch": wl.batch, "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": 16,
+                   "kv_cache": wl.cache_dtype, "layers_per_step": layers, "new_tokens": int(inst.nq.sum()),
+                   "cached_prefix": wl.shared_prefix, "parallelism": "none"},
+        "prefill_tokens_per_s_per_layer": round(int(inst.nq.sum()) * K * layers / elapsed, 1),
+        "roofline": {"kernel": "paged_attention_prefill", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "flops_per_launch": flops, "kv_bytes_distinct": inst.kv_bytes(), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(inst, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(gib: float, reps: int):
     """Plain device-to-device copies of a known size (PMC calibration)."""
     import torch
@@ -244,9 +342,13 @@ def main():
         return
 
     import workloads
+    from workloads import prefill as PW
     from paged_kv_cache_381_amd import _lib as L
     from paged_kv_cache_381_amd.engine import GpuWorkload
 
+    if args.workload in PW.PREFILL_WORKLOADS:
+        bench_prefill(args)
+        return
     inst = workloads.get(args.workload)
     wl = inst.wl
     B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim

@@ -307,6 +307,36 @@ int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, 
                            void *workspace, size_t workspace_bytes, const pkv_decode_opts *opts,
                            void *stream);
 
+/* Causal prefill over a paged cache [KV Cache 工程学 §15.1: a prompt of i
+ * tokens is an i x i causal attention; §15.6 and 新一代 KV Cache 管理 §8.3:
+ * a cached prefix is attended to, not prefilled again].  Sequence b holds
+ * d_context_lens[b] tokens in its table (slot j % 16 of block
+ * d_block_tables[b][j / 16]); its last nq_b = d_query_start[b+1] -
+ * d_query_start[b] tokens are new and their K and V must already be stored
+ * (paged_kv_append).  New token t, at position p_b + t with
+ * p_b = d_context_lens[b] - nq_b, attends to positions 0 .. p_b + t:
+ *   out[r][h] = sum_{j <= p_b + t} softmax_j(scale * q[r][h] . K_j) * V_j,
+ *   r = d_query_start[b] + t, kv head g = h / (num_q_heads / H).
+ *   out: float32 [T][num_q_heads][D] (device, written), T = d_query_start[num_seqs]
+ *   q:   bf16 [T][num_q_heads][D] (device), also for PKV_INT8
+ *   d_block_tables: int32 [num_seqs][max_blocks_per_seq] (device)
+ *   d_context_lens: int32 [num_seqs] (device); d_query_start: int32 [num_seqs + 1]
+ *   (device), non-decreasing from 0, with nq_b <= d_context_lens[b] (a larger
+ *   nq_b is cut to d_context_lens[b]) and nq_b <= max_query_len (rows past it
+ *   are not written)
+ *   max_context_len: bounds every context (a longer one is treated as it)
+ * Requires a bf16 or int8 cache, num_q_heads % num_kv_heads == 0,
+ * G = num_q_heads / num_kv_heads <= 16, D in {64, 128},
+ * max_query_len <= max_context_len <= min(16 * max_blocks_per_seq, 2^22).
+ * Runs on the matrix cores: a wave takes 16 / G consecutive new tokens of one
+ * (sequence, kv head) times its G query heads and walks the keys its last
+ * token sees.  Needs no workspace. */
+int paged_attention_prefill(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
+                            const void *v_pool, const int32_t *d_block_tables, const int32_t *d_context_lens,
+                            const int32_t *d_query_start, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_context_len,
+                            float scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -182,3 +182,39 @@ def run_workload(inst, with_attention=True):
         res["out"] = paged_attention(wl.cache_dtype, inst.q(), kpool, vpool, tables, ctx, wl.num_kv_heads,
                                      1.0 / math.sqrt(wl.head_dim))
     return res
+
+
+def build_prefill(inst):
+    """The build script of a prefill workload instance through the
+    bookkeeping model and the oracle's append: tables, lengths and pools."""
+    from .book import Book
+    wl = inst.wl
+    book = Book(inst.num_blocks, inst.free_order)
+    kpool, vpool = new_pool(inst.num_blocks, wl.num_kv_heads, wl.head_dim, wl.cache_dtype)
+
+    def put(sid, n, k, v):
+        slots, cow = book.append_slots(sid, n)
+        assert not cow
+        append(wl.cache_dtype, wl.num_kv_heads, wl.head_dim, kpool, vpool, k, v, np.asarray(slots, np.int64))
+
+    if wl.shared_prefix:
+        root = book.create()
+        put(root, wl.shared_prefix, inst.shared_kv("k"), inst.shared_kv("v"))
+        ids = [root] + [book.fork(root) for _ in range(wl.batch - 1)]
+    else:
+        ids = [book.create() for _ in range(wl.batch)]
+    for b, sid in enumerate(ids):
+        put(sid, int(inst.own_prefix[b] + inst.nq[b]), inst.own_kv(b, "k"), inst.own_kv(b, "v"))
+    tables, ctx = tables_of(book, ids)
+    assert (ctx == inst.ctx).all()
+    return {"book": book, "ids": ids, "tables": tables, "ctx": ctx, "kpool": kpool, "vpool": vpool}
+
+
+def run_prefill(inst):
+    """The oracle's own prefill of a prefill workload instance: the build,
+    then causal attention of every new token."""
+    res = build_prefill(inst)
+    wl = inst.wl
+    res["out"] = paged_prefill(wl.cache_dtype, inst.q(), res["kpool"], res["vpool"], res["tables"], res["ctx"],
+                               inst.qstart, wl.num_kv_heads, 1.0 / math.sqrt(wl.head_dim))
+    return res

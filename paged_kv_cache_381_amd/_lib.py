@@ -106,6 +106,8 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_SZ, [_PL, _I32, _I32, _I32, _PO]),
     "paged_attention_decode": (ctypes.c_int, [_PL, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _SZ,
                                               _PO, _P]),
+    "paged_attention_prefill": (ctypes.c_int, [_PL, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F,
+                                               _P]),
 }
 
 _lib = None
@@ -403,3 +405,24 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
         _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32, B),
         B, Hq, mb, int(max_context_len), float(scale), ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
+
+
+def paged_attention_prefill(layout, out, q, k_pool, v_pool, block_tables, context_lens, query_start, max_query_len,
+                            max_context_len, scale, stream=None):
+    """Causal attention of the new tokens of every sequence: q and out are
+    [T][num_q_heads][head_dim] with sequence b's rows query_start[b] ..
+    query_start[b+1]-1, the last tokens of its context_lens[b]."""
+    import torch
+    pdt = pool_torch_dtype(layout)
+    if q.dim() != 3 or q.shape[2] != layout.head_dim:
+        raise ValueError("q must be [T][num_q_heads][head_dim]")
+    T, Hq, D = q.shape
+    B = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    _check(lib().paged_attention_prefill(
+        ctypes.byref(layout), _dev(out, "out", torch.float32, T * Hq * D), _dev(q, "q", torch.bfloat16),
+        _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32, B),
+        _dev(query_start, "query_start", torch.int32, B + 1), B, Hq, block_tables.shape[1], int(max_query_len),
+        int(max_context_len), float(scale), _stream(stream)))

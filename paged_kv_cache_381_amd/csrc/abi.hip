@@ -216,3 +216,52 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
   return record(opts ? opts->ev_end : nullptr, stream);
 }
+
+extern "C" int paged_attention_prefill(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
+                                       const void *v_pool, const int32_t *d_block_tables,
+                                       const int32_t *d_context_lens, const int32_t *d_query_start,
+                                       int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                       int32_t max_query_len, int32_t max_context_len, float scale, void *stream) {
+  if (int rc = pkv_check_layout(layout)) return rc;
+  const int32_t H = layout->num_kv_heads;
+  if (layout->kv_dtype == PKV_F32)
+    return pkv_set_error(PKV_ERR_INVALID, "paged_attention_prefill needs a bf16 or int8 cache");
+  if (num_seqs < 0) return pkv_set_error(PKV_ERR_INVALID, "num_seqs < 0");
+  if (num_q_heads <= 0 || num_q_heads % H != 0)
+    return pkv_set_error(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                         num_q_heads, H);
+  if (num_q_heads / H > 16)
+    return pkv_set_error(PKV_ERR_INVALID, "query heads per kv head must be <= 16 (got %d)", num_q_heads / H);
+  if (max_blocks_per_seq <= 0) return pkv_set_error(PKV_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)PKV_BLOCK_SIZE * max_blocks_per_seq ||
+      max_context_len > (1 << 22))
+    return pkv_set_error(PKV_ERR_INVALID, "max_context_len %d outside [0, min(16 * max_blocks_per_seq, 2^22)]",
+                         max_context_len);
+  if (max_query_len < 0 || max_query_len > max_context_len)
+    return pkv_set_error(PKV_ERR_INVALID, "max_query_len %d outside [0, max_context_len]", max_query_len);
+  if (!std::isfinite(scale)) return pkv_set_error(PKV_ERR_INVALID, "scale is not finite");
+  if (num_seqs > 65535 || H > 65535) return pkv_set_error(PKV_ERR_INVALID, "grid too large");
+  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !d_block_tables || !d_context_lens || !d_query_start)
+    return pkv_set_error(PKV_ERR_INVALID, "paged_attention_prefill: NULL pointer");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
+    return pkv_set_error(PKV_ERR_INVALID, "paged_attention_prefill: q, out and pools must be 16-byte aligned");
+  pkv_prefill_args a{};
+  a.L = layout;
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tables = d_block_tables;
+  a.ctx = d_context_lens;
+  a.qstart = d_query_start;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.stream = stream;
+  if (int rc = pkv_launch_prefill_mfma(a)) return hip_fail(rc, "prefill kernel launch");
+  return PKV_OK;
+}

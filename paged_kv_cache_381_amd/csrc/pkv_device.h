@@ -104,6 +104,24 @@ struct SplitParams {
   float scale_log2;
 };
 
+// Parameters of the paged prefill kernel (passed by value).
+struct PrefillParams {
+  float *out;             // [T][Hq][D]
+  const void *q;          // [T][Hq][D] bf16
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *tables;  // [B][max_blocks]
+  const int32_t *ctx;     // [B] tokens held, the new ones included
+  const int32_t *qstart;  // [B + 1] first query row of each sequence
+  int32_t num_blocks;
+  int32_t H;
+  int32_t Hq;
+  int32_t G;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  float scale_log2;
+};
+
 // Scalar (uniform) load of a read-only int32 through the constant address
 // space, so block ids and lengths live in SGPRs and never wait behind the
 // vector K/V loads.

@@ -67,6 +67,24 @@ int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const voi
                       const int64_t *slots, int32_t num_tokens, void *stream);
 int pkv_launch_copy_blocks(const pkv_layout *L, void *k_pool, void *v_pool, const int32_t *pairs,
                            int32_t num_pairs, void *stream);
+struct pkv_prefill_args {
+  const pkv_layout *L;
+  float *out;
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *tables;
+  const int32_t *ctx;
+  const int32_t *qstart;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t max_query_len;
+  float scale_log2;
+  void *stream;
+};
+int pkv_launch_prefill_mfma(const pkv_prefill_args &a);
 int pkv_launch_decode_valu(const pkv_decode_args &a);
 int pkv_launch_decode_mfma(const pkv_decode_args &a);
 int pkv_launch_merge(const pkv_decode_args &a);

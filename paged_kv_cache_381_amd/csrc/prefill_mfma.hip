@@ -1,0 +1,315 @@
+// Paged prefill: causal attention of a sequence's new tokens over its paged
+// cache, on the matrix cores (bf16 or int8 cache).
+//
+// What it computes [KV Cache 工程学 §15.1: a prompt is a causal i x i
+// attention; §15.6 and 新一代 KV Cache 管理 §8.3: a cached prefix is not
+// prefilled again]: sequence b holds ctx_b tokens in its table, the last
+// nq_b of them new (their K/V already stored by paged_kv_append).  New token t
+// sits at position p_b + t, p_b = ctx_b - nq_b, and attends to positions
+// 0 .. p_b + t -- the cached prefix and the new tokens up to itself.
+//
+// gfx950 mapping.  The decode kernel's contractions are reused with the
+// padding gone: a wave takes 16 query columns, TQ = 16 / G consecutive new
+// tokens times the G query heads of one kv head g, so every column of
+//   S^T[32 keys x 16 columns] = K[32 x D] . Q^T[D x 16]
+//   O^T[D x 16 columns]      += V^T[D x 32] . P^T[32 x 16]
+// is a real query row.  The operand layouts, the lane holding 8 keys of one
+// column between the two products and the online softmax per column are the
+// decode kernel's; the causal limit differs per column and masks scores per
+// lane.  A wave walks keys 0 .. its last token's position in 32-key chunks
+// (two blocks through the table), with NB chunks of K/V in registers, every
+// load issued on every path so that the memory-counter waits stay exact.
+// Tiles of one (sequence, kv head) that run longest (the last tokens) are
+// dispatched first.
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace {
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Eight int8 codes, widened exactly to bf16.
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint2 u) {
+  bf16x8_t r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[k] = (__bf16)(float)(int8_t)(u.x >> (8 * k));
+    r[4 + k] = (__bf16)(float)(int8_t)(u.y >> (8 * k));
+  }
+  return r;
+}
+
+// Zero the bf16 elements of u whose index is >= nvalid (0..8).
+__device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t mask = (2 * k + 1 < nvalid) ? 0xffffffffu : (2 * k < nvalid ? 0x0000ffffu : 0u);
+    w[k] &= mask;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+constexpr float kSlack = 8.0f;  // headroom of the running maximum (base 2)
+
+template <int D, int NB, bool I8>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
+  constexpr int NKK = D / 32;
+  constexpr int NNN = D / 16;
+  constexpr int TB = I8 ? 16 * D + 64 : 32 * D;
+  constexpr int NKU = I8 ? NKK / 2 : NKK;
+  using VUnit = std::conditional_t<I8, uint2, uint4>;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int G = P.G, TQ = 16 / G;
+  const int q0 = sload_i32(P.qstart + b);
+  const int n = clamp_len(sload_i32(P.ctx + b), P.max_blocks, P.max_ctx);
+  // A sequence claiming more new tokens than it holds keeps its last n.
+  const int nq = min(sload_i32(P.qstart + b + 1) - q0, n);
+  const int ntile = (nq + TQ - 1) / TQ;
+  const int tile = ntile - 1 - (int)(blockIdx.x * 4 + w);  // longest tiles first
+  if (tile < 0) return;
+  const int p0 = n - nq;  // position of new token 0
+  const int tlast = min(tile * TQ + TQ, nq) - 1;
+  const int kend = p0 + tlast + 1;  // keys the tile's last token sees
+  const int nch = (kend + 31) >> 5;
+
+  const int r16 = lane & 15, grp = lane >> 4;
+  // Column r16: token tile*TQ + r16/G, head r16%G of group g.  Columns past
+  // TQ*G or past the last new token repeat the tile's last real column and
+  // store nothing.
+  const int cc = min(r16, TQ * G - 1);
+  const int tcol = min(tile * TQ + cc / G, tlast);
+  const bool store_col = r16 < TQ * G && tile * TQ + r16 / G <= tlast;
+  const int pos = p0 + tcol;  // the column's causal limit (inclusive)
+  const size_t qrow = ((size_t)(q0 + tcol) * P.Hq + (size_t)g * G + cc % G);
+
+  const int ksel = r16 >> 3;
+  const int ktx = ((r16 >> 2) & 1) * 8 + (r16 & 3);
+  const int vsel = grp >> 1, vhalf = grp & 1;
+  auto kgroup = [&](int kk) { return I8 ? 8 * (kk >> 1) + 2 * grp + (kk & 1) : 4 * kk + grp; };
+  const uint8_t *kpool = reinterpret_cast<const uint8_t *>(P.k_pool);
+  const uint8_t *vpool = reinterpret_cast<const uint8_t *>(P.v_pool);
+  const int32_t *trow = P.tables + (size_t)b * P.max_blocks;
+  const int H = P.H;
+
+  // The query slices stay in registers for the whole walk.
+  bf16x8_t qb[NKK];
+  {
+    const uint4 *qr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.q) + qrow * D);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qb[kk] = as_bf16x8(qr[kgroup(kk)]);
+  }
+
+  int cj[NB], pa[NB], pb[NB];
+  uint4 ax[NB][NKU], ay[NB][NKU];
+  VUnit va[NB][NNN];
+  float4 ksc[NB][2], vsc[NB][2];
+
+  auto locate = [&](int i, int c) {
+    cj[i] = c;
+    pa[i] = clamp_block(sload_i32(trow + 2 * c), P.num_blocks);
+    const int b2 = clamp_block(sload_i32(trow + min(2 * c + 1, P.max_blocks - 1)), P.num_blocks);
+    pb[i] = 32 * c + 16 < kend ? b2 : pa[i];
+  };
+  auto same_as = [&](int to, int from) {
+    cj[to] = cj[from];
+    pa[to] = pa[from];
+    pb[to] = pb[from];
+  };
+  auto issue = [&](auto bi) {
+    constexpr int I = decltype(bi)::value;
+    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + g) * TB);
+#pragma unroll
+    for (int ku = 0; ku < NKU; ++ku) {
+      const int cu = 4 * ku + grp;
+      ax[I][ku] = kt[cu * 16 + ktx];
+      ay[I][ku] = kt[cu * 16 + ktx + 4];
+    }
+    if constexpr (I8) {
+      const float4 *sc = reinterpret_cast<const float4 *>(kpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + g) * TB +
+                                                          16 * D + 32 * vhalf);
+      ksc[I][0] = sc[0];
+      ksc[I][1] = sc[1];
+    }
+  };
+  auto issue_v = [&](auto bi) {
+    constexpr int I = decltype(bi)::value;
+    const uint8_t *vt = vpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + g) * TB;
+    if constexpr (I8) {
+#pragma unroll
+      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = *reinterpret_cast<const uint2 *>(vt + (16 * nn + r16) * 16 + 8 * vhalf);
+      const float4 *sc = reinterpret_cast<const float4 *>(vt + 16 * D + 32 * vhalf);
+      vsc[I][0] = sc[0];
+      vsc[I][1] = sc[1];
+    } else {
+      const uint4 *u = reinterpret_cast<const uint4 *>(vt);
+#pragma unroll
+      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = u[2 * (16 * nn + r16) + vhalf];
+    }
+  };
+
+  f32x4_t o[NNN];
+#pragma unroll
+  for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  locate(0, 0);
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((Is == 0 ? (void)0 : (Is < nch ? locate(Is, Is) : same_as(Is, Is - 1))), ...);
+  }(std::make_integer_sequence<int, NB>{});
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0),
+                     issue_v(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0))
+                  : (void)0),
+     ...);
+  }(std::make_integer_sequence<int, NB>{});
+
+  int x = 0;
+  auto step = [&](auto bi) {
+    constexpr int I = decltype(bi)::value;
+    constexpr int J = (I + NB - 1) % NB;
+    f32x4_t sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8_t kx, ky;
+      if constexpr (I8) {
+        const uint4 ux = ax[I][kk >> 1], uy = ay[I][kk >> 1];
+        kx = as_bf16x8((kk & 1) ? make_uint2(ux.z, ux.w) : make_uint2(ux.x, ux.y));
+        ky = as_bf16x8((kk & 1) ? make_uint2(uy.z, uy.w) : make_uint2(uy.x, uy.y));
+      } else {
+        kx = as_bf16x8(ax[I][kk]);
+        ky = as_bf16x8(ay[I][kk]);
+      }
+      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[kk], sx, 0, 0, 0);
+      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[kk], sy, 0, 0, 0);
+    }
+    if (x + NB - 1 >= nch) same_as(J, I);
+    issue(std::integral_constant<int, J>{});
+
+    // Keys of this lane: 8 consecutive positions from tb.  Past the walk's
+    // end (x >= nch) nothing is counted.
+    const bool real = x < nch;
+    const int tb = 32 * cj[I] + 16 * vsel + 8 * vhalf;
+    const int lim = real ? pos : -1;
+    float s[8];
+    if constexpr (I8) {
+      const float ks[8] = {ksc[I][0].x, ksc[I][0].y, ksc[I][0].z, ksc[I][0].w,
+                           ksc[I][1].x, ksc[I][1].y, ksc[I][1].z, ksc[I][1].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[r] = (tb + r <= lim) ? sx[r] * ks[r] * P.scale_log2 : -INFINITY;
+        s[4 + r] = (tb + 4 + r <= lim) ? sy[r] * ks[4 + r] * P.scale_log2 : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[r] = (tb + r <= lim) ? sx[r] * P.scale_log2 : -INFINITY;
+        s[4 + r] = (tb + 4 + r <= lim) ? sy[r] * P.scale_log2 : -INFINITY;
+      }
+    }
+    float cmax = s[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, s[r]);
+    cmax = rows_max4(cmax);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m + kSlack) != 0, 0)) {
+      const float mnew = fmaxf(m, cmax);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int nn = 0; nn < NNN; ++nn) o[nn] *= alpha;
+    }
+    bf16x8_t pv;
+    float psum = 0.f;
+    if constexpr (I8) {
+      const float vs[8] = {vsc[I][0].x, vsc[I][0].y, vsc[I][0].z, vsc[I][0].w,
+                           vsc[I][1].x, vsc[I][1].y, vsc[I][1].z, vsc[I][1].w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float e = fast_exp2(s[r] - m);
+        psum += e;
+        pv[r] = (__bf16)((tb + r <= lim) ? e * vs[r] : 0.f);  // scales past the context may be NaN
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const __bf16 pr = (__bf16)fast_exp2(s[r] - m);
+        pv[r] = pr;
+        psum += (float)pr;
+      }
+      // Keys at or past the walk's end may be unwritten (NaN); a zero weight
+      // alone would not cancel them.
+      const int nvalid = real ? min(max(kend - tb, 0), 8) : 0;
+      if (nvalid < 8) {
+#pragma unroll
+        for (int nn = 0; nn < NNN; ++nn) va[I][nn] = keep_first(va[I][nn], nvalid);
+      }
+    }
+    l += psum;
+#pragma unroll
+    for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[I][nn]), pv, o[nn], 0, 0, 0);
+    issue_v(std::integral_constant<int, J>{});
+    if (x + NB < nch) locate(I, x + NB);
+    ++x;
+  };
+  while (x < nch) {
+    [&]<int... Is>(std::integer_sequence<int, Is...>) {
+      (step(std::integral_constant<int, Is>{}), ...);
+    }(std::make_integer_sequence<int, NB>{});
+  }
+
+  const float lsum = rows_sum4(l);
+  if (store_col) {
+    const float inv = 1.f / lsum;
+    float *dst = P.out + qrow * D + 4 * grp;
+#pragma unroll
+    for (int nn = 0; nn < NNN; ++nn)
+      *reinterpret_cast<float4 *>(dst + 16 * nn) =
+          make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
+  }
+}
+
+#ifndef PKV_PREFILL_NBUF
+#define PKV_PREFILL_NBUF 2
+#endif
+#ifndef PKV_PREFILL_NBUF_I8
+#define PKV_PREFILL_NBUF_I8 4
+#endif
+
+template <int D, bool I8>
+int launch(const pkv_prefill_args &a, const PrefillParams &p) {
+  auto kern = prefill_mfma_kernel<D, I8 ? PKV_PREFILL_NBUF_I8 : PKV_PREFILL_NBUF, I8>;
+  const int tq = 16 / p.G;
+  const int tiles = (a.max_query_len + tq - 1) / tq;
+  const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)p.H, (unsigned)a.num_seqs);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int pkv_launch_prefill_mfma(const pkv_prefill_args &a) {
+  PrefillParams p;
+  p.out = a.out;
+  p.q = a.q;
+  p.k_pool = a.k_pool;
+  p.v_pool = a.v_pool;
+  p.tables = a.tables;
+  p.ctx = a.ctx;
+  p.qstart = a.qstart;
+  p.num_blocks = a.L->num_blocks;
+  p.H = a.L->num_kv_heads;
+  p.Hq = a.num_q_heads;
+  p.G = a.num_q_heads / a.L->num_kv_heads;
+  p.max_blocks = a.max_blocks;
+  p.max_ctx = a.max_ctx;
+  p.scale_log2 = a.scale_log2;
+  if (a.L->kv_dtype == PKV_INT8) return a.L->head_dim == 128 ? launch<128, true>(a, p) : launch<64, true>(a, p);
+  return a.L->head_dim == 128 ? launch<128, false>(a, p) : launch<64, false>(a, p);
+}

@@ -108,6 +108,12 @@ class PagedKVCache:
                                  max_ctx, scale, workspace, partition_tokens, kernel, events,
                                  waves_per_simd=waves_per_simd)
 
+    def prefill(self, layer: int, out, q, tables_dev, ctx_dev, qstart_dev, max_query_len: int, max_ctx: int,
+                scale: float):
+        """Causal attention of each sequence's new tokens (already stored)."""
+        L.paged_attention_prefill(self.layout, out, q, self.k_pools[layer], self.v_pools[layer], tables_dev, ctx_dev,
+                                  qstart_dev, max_query_len, max_ctx, scale)
+
     def waves_per_simd(self) -> int:
         """Two resident waves per SIMD when the live sequences read their
         blocks more than twice over on average (shared prompts, parallel
@@ -187,4 +193,60 @@ class GpuWorkload:
         out = self.out if out is None else out
         self.cache.decode(layer, out, self.q, self.tables_dev, self.ctx_dev, self.max_ctx, self.scale, workspace,
                           partition_tokens, kernel, events, waves_per_simd)
+        return out
+
+
+class GpuPrefill:
+    """A prefill workload instance built on the GPU path: the build script
+    through the host block manager, every token (cached prefix and new ones)
+    stored by paged_kv_append, and the queries, tables, lengths and query
+    offsets on the device for paged_attention_prefill."""
+
+    def __init__(self, inst, num_layers: int = 1, device="cuda"):
+        wl = inst.wl
+        self.inst, self.wl = inst, wl
+        self.device = torch.device(device)
+        self.cache = PagedKVCache(inst.num_blocks, wl.num_kv_heads, wl.head_dim, wl.cache_dtype,
+                                  num_layers=num_layers, free_order=inst.free_order, device=device)
+        c = self.cache
+
+        def put(sid, k, v):
+            slots, cow = c.reserve([sid], k.shape[0])
+            assert len(cow) == 0
+            sd = torch.from_numpy(slots).to(self.device)
+            kd, vd = _bits_to_dev(k, wl.dtype, self.device), _bits_to_dev(v, wl.dtype, self.device)
+            for layer in range(num_layers):
+                c.write(layer, sd, kd, vd)
+            return slots
+
+        if wl.shared_prefix:
+            root = c.create()
+            put(root, inst.shared_kv("k"), inst.shared_kv("v"))
+            self.ids = [root] + [c.fork(root) for _ in range(wl.batch - 1)]
+        else:
+            self.ids = [c.create() for _ in range(wl.batch)]
+        new_slots = []
+        for b, sid in enumerate(self.ids):
+            new_slots.append(put(sid, inst.own_kv(b, "k"), inst.own_kv(b, "v"))[-int(inst.nq[b]):])
+        # The new tokens' slots and rows: a prefill step stores them, then attends.
+        self.new_slots_dev = torch.from_numpy(np.concatenate(new_slots)).to(self.device)
+        self.k_new = _bits_to_dev(np.concatenate([inst.own_kv(b, "k")[-int(inst.nq[b]):] for b in range(wl.batch)]),
+                                  wl.dtype, self.device)
+        self.v_new = _bits_to_dev(np.concatenate([inst.own_kv(b, "v")[-int(inst.nq[b]):] for b in range(wl.batch)]),
+                                  wl.dtype, self.device)
+        self.max_ctx = int(inst.ctx.max())
+        self.max_q = int(inst.nq.max())
+        tables, ctx = c.tables(self.ids, -(-self.max_ctx // 16))
+        self.tables_host = tables
+        self.tables_dev = torch.from_numpy(tables).to(self.device)
+        self.ctx_dev = torch.from_numpy(ctx).to(self.device)
+        self.qstart_dev = torch.from_numpy(inst.qstart).to(self.device)
+        self.q = _bits_to_dev(inst.q(), wl.dtype, self.device)
+        self.scale = 1.0 / math.sqrt(wl.head_dim)
+        self.out = torch.empty(self.q.shape, dtype=torch.float32, device=self.device)
+
+    def run(self, layer=0, out=None):
+        out = self.out if out is None else out
+        self.cache.prefill(layer, out, self.q, self.tables_dev, self.ctx_dev, self.qstart_dev, self.max_q, self.max_ctx,
+                           self.scale)
         return out

@@ -118,6 +118,17 @@ def test_decode_argument_errors_before_any_launch():
     assert lib.paged_kv_append(ctypes.byref(lay), fake, odd, fake, fake, fake, 3, None) == L.PKV_ERR_INVALID
     assert lib.paged_kv_append(ctypes.byref(lay), fake, fake, fake, fake, fake, -1, None) == L.PKV_ERR_INVALID
     assert lib.pkv_copy_blocks(ctypes.byref(lay), fake, fake, None, 2, None) == L.PKV_ERR_INVALID
+    def prefill(hq=4, mb=8, mq=16, mctx=64, lay_=lay, scale=0.1, q=fake):
+        return lib.paged_attention_prefill(ctypes.byref(lay_), fake, q, fake, fake, fake, fake, fake, 2, hq, mb, mq,
+                                           mctx, scale, None)
+    assert prefill(hq=3) == L.PKV_ERR_INVALID
+    assert prefill(hq=2 * 17) == L.PKV_ERR_INVALID
+    assert prefill(mq=65) == L.PKV_ERR_INVALID
+    assert prefill(mctx=8 * 16 + 1) == L.PKV_ERR_INVALID
+    assert prefill(scale=float("nan")) == L.PKV_ERR_INVALID
+    assert prefill(q=None) == L.PKV_ERR_INVALID
+    assert prefill(lay_=P.make_layout(16, 2, 128, "f32")) == L.PKV_ERR_INVALID
+    assert prefill(mq=0) == 0  # nothing to compute
     # zero-work calls succeed without launching anything
     assert lib.paged_kv_append(ctypes.byref(lay), fake, fake, fake, fake, fake, 0, None) == 0
     assert lib.pkv_copy_blocks(ctypes.byref(lay), fake, fake, fake, 0, None) == 0
