@@ -234,6 +234,57 @@ int64_t pkv_pool_bytes(const pkv_layout *layout);
 int pkv_validate_tables(const pkv_layout *layout, const int32_t *tables, const int32_t *context_lens,
                         int32_t num_seqs, int32_t max_blocks_per_seq);
 
+/* ------------------------------------------------- swap to host memory */
+/* When device memory is short, single blocks move to host memory instead of
+ * whole sequences ("fine-grained eviction" [KV Cache 与 PagedAttention,
+ * summary]; offloading of KV not needed right away [KV Cache 工程学 §15.7
+ * (4)]), chosen by the Clock (second chance) policy [PagedAttention：大模型KV
+ * Cache内存管理革新 §3.3].  Host memory holds num_host_blocks block slots in
+ * caller-owned K and V buffers of the pool's tile layout (num_host_blocks *
+ * num_kv_heads tiles each; pinned memory the GPU can address).  Every device
+ * block has a reference bit, set when the block is taken, when a token slot
+ * in it is assigned and when pkv_batch_block_tables exports a table naming
+ * it (pkv_seq_block_table only inspects).  A table entry e < 0 names
+ * host slot -e-1: such a sequence is not resident, and appends and
+ * pkv_batch_block_tables refuse it (PKV_ERR_INVALID) until pkv_seq_swap_in. */
+typedef struct {
+  int32_t host_blocks;   /* configured host slots */
+  int32_t host_used;     /* slots holding a block */
+  int32_t host_free;
+  int32_t clock_hand;    /* next device block the hand looks at */
+  int64_t swapped_out;   /* blocks moved to the host so far */
+  int64_t swapped_in;    /* blocks moved back */
+} pkv_swap_stats;
+
+/* Set the number of host slots (0 .. n-1, handed out LIFO, slot 0 first).
+ * Refused while a slot holds a block. */
+int pkv_swap_configure(pkv_pool *pool, int32_t num_host_blocks);
+/* Choose up to `want` victims with the Clock hand, which moves over device
+ * block ids from where it stopped: a block held by some sequence, not in the
+ * prefix cache and not held by a sequence of protect_ids (the batch about to
+ * run) is a candidate; a candidate whose reference bit is set has it cleared
+ * and is passed over; one whose bit is clear moves to a host slot: every
+ * table entry naming it becomes -(slot+1), its references move to the slot
+ * and the device block returns to the free stack.  Stops after `want`
+ * victims, when host slots run out, or after two turns of the hand.
+ * pairs_out (cap pairs, cap >= want) receives int32 (device block, host slot)
+ * pairs; *n_out their number.  The caller copies them (pkv_swap_copy, device
+ * pool to host slots) before any later device call can write the freed
+ * blocks: on the same stream, enqueue the copy first. */
+int pkv_swap_out(pkv_pool *pool, int32_t want, const int64_t *protect_ids, int32_t n_protect, int32_t *pairs_out,
+                 int32_t cap, int32_t *n_out);
+/* Bring every host entry of a sequence back, in table order, all or nothing:
+ * each takes a device block (free stack first, then idle cached blocks, as an
+ * append does); every sequence sharing the block becomes resident for it.
+ * pairs_out receives int32 (host slot, device block) pairs to copy host ->
+ * device (pkv_swap_copy) before the sequence's next device call; *n_out
+ * their number (also on PKV_ERR_CAPACITY).  PKV_ERR_NO_BLOCKS when the pool
+ * cannot hold them (nothing changes). */
+int pkv_seq_swap_in(pkv_pool *pool, int64_t id, int32_t *pairs_out, int32_t cap, int32_t *n_out);
+/* 1 when every table entry of the sequence is a device block, else 0. */
+int pkv_seq_resident(const pkv_pool *pool, int64_t id, int32_t *resident_out);
+int pkv_swap_space_stats(const pkv_pool *pool, pkv_swap_stats *out);
+
 /* ---------------------------------------------------------- device calls */
 /* Store the new tokens' K and V into their slots [KV Cache 工程学 §15.1,
  * §15.5].  k_new, v_new: [num_tokens][H][D] of kv_dtype, bf16 for
@@ -250,6 +301,15 @@ int paged_kv_append(const pkv_layout *layout, void *k_pool, void *v_pool, const 
  * also sources. */
 int pkv_copy_blocks(const pkv_layout *layout, void *k_pool, void *v_pool, const int32_t *d_pairs,
                     int32_t num_pairs, void *stream);
+
+/* Copy whole blocks (all heads, K and V) from one pool to another of the
+ * same layout: d_pairs is int32 [num_pairs][2] of (source block, destination
+ * block), readable by the device.  Either pool may be pinned host memory
+ * (the swap space of pkv_swap_out / pkv_seq_swap_in); src_blocks and
+ * dst_blocks are the pools' sizes in blocks, and a pair outside them is
+ * skipped.  Destinations must be distinct. */
+int pkv_swap_copy(const pkv_layout *layout, void *dst_k, void *dst_v, int32_t dst_blocks, const void *src_k,
+                  const void *src_v, int32_t src_blocks, const int32_t *d_pairs, int32_t num_pairs, void *stream);
 
 /* Decode options (all fields may be zero / NULL for defaults). */
 typedef struct {

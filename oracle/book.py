@@ -39,6 +39,23 @@ Readings where the pages are silent (each one is listed in the design notes):
   recently used first, only when the free stack is empty; a sequence's
   cached blocks that turn idle together enter the LRU deepest first; turning
   the cache off returns idle blocks to the free stack, oldest first.
+* swap to host memory ("fine-grained eviction": small pages move to the CPU
+  instead of whole sequences [KV Cache 与 PagedAttention, summary]; Clock
+  replacement [PagedAttention：大模型KV Cache内存管理革新 §3.3]): host memory
+  holds ``num_host`` block slots, handed out from a LIFO stack seeded
+  0, 1, 2, ...; every device block has a reference bit, set when the block is
+  taken, when a token slot in it is assigned and when a batch's tables naming
+  it are exported for a device call; ``swap_out(want, protect)`` moves the Clock hand over device block
+  ids from where it stopped: a block held by some sequence, not in the prefix
+  cache and not held by a protected sequence is a candidate; a candidate whose
+  bit is set has it cleared and is passed over, one whose bit is clear is
+  swapped out (a host slot is taken, every table entry naming the block
+  becomes ``-(slot + 1)``, the block's references move to the slot and the
+  block goes back to the free stack); it stops after ``want`` victims, when
+  host slots run out, or after two turns of the hand; ``swap_in(seq)`` brings
+  back every host entry of a sequence in table order, all or nothing, each
+  into a freshly taken block (sharers follow); a sequence holding host
+  entries cannot append or export its table.
 
 Parity unpinned items: none; every behaviour here is checked by the
 invariant and worked-number tests in ``tests/test_oracle_book.py`` and
@@ -79,6 +96,13 @@ class Book:
         self.key_of = {}                 # block -> key tuple
         self.lru = []
         self.pst = {"lookups": 0, "query_tokens": 0, "hit_tokens": 0, "registered": 0, "evictions": 0}
+        # Host swap space and the Clock state.
+        self.refbit = [0] * num_blocks
+        self.hand = 0
+        self.num_host = 0
+        self.host_free = []
+        self.host_ref = []
+        self.sst = {"swapped_out": 0, "swapped_in": 0}
 
     # -- blocks ---------------------------------------------------------------
     def alloc(self) -> int:
@@ -93,6 +117,7 @@ class Book:
         else:
             raise BookError("NO_BLOCKS", "pool exhausted")
         self.ref[blk] = 1
+        self.refbit[blk] = 1
         return blk
 
     def _check(self, blk: int):
@@ -142,10 +167,13 @@ class Book:
     def fork(self, parent: int) -> int:
         p = self._seq(parent)
         for blk in p["table"]:  # a table naming a freed block is corrupt: refuse before changing anything
-            if self.ref[blk] <= 0:
+            if blk >= 0 and self.ref[blk] <= 0:
                 raise BookError("REFCOUNT", f"fork of a sequence holding free block {blk}")
         for blk in p["table"]:
-            self.incref(blk)
+            if blk >= 0:
+                self.incref(blk)
+            else:
+                self.host_ref[-blk - 1] += 1
         sid = self.create()
         self.seqs[sid] = {"table": list(p["table"]), "len": p["len"]}
         return sid
@@ -162,7 +190,9 @@ class Book:
                 cow.append((old, new))
                 self.decref(old)
                 s["table"][-1] = new
-            slots.append(s["table"][pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE)
+            blk = s["table"][pos // BLOCK_SIZE]
+            self.refbit[blk] = 1
+            slots.append(blk * BLOCK_SIZE + pos % BLOCK_SIZE)
             s["len"] = pos + 1
 
     def append_slots(self, sid: int, n: int):
@@ -176,13 +206,17 @@ class Book:
             raise BookError("INVALID", "negative token count")
         for sid in sids:
             self._seq(sid)
-        saved = copy.deepcopy((self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst))
+        for sid in sids:
+            if not self.resident(sid):
+                raise BookError("INVALID", f"sequence {sid} has blocks swapped out")
+        saved = copy.deepcopy((self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst,
+                               self.refbit))
         slots, cow = [], []
         try:
             for sid in sids:
                 self._append_one_seq(sid, n, slots, cow)
         except BookError:
-            self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst = saved
+            self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst, self.refbit = saved
             raise
         return slots, cow
 
@@ -193,7 +227,8 @@ class Book:
         # the sequence still held): the release is all or nothing.
         held = {}
         for blk in s["table"]:
-            held[blk] = held.get(blk, 0) + 1
+            if blk >= 0:
+                held[blk] = held.get(blk, 0) + 1
         for blk, k in held.items():
             if self.ref[blk] < k:
                 raise BookError("REFCOUNT", f"free of a sequence holding block {blk} {k} times, refcount {self.ref[blk]}")
@@ -202,6 +237,12 @@ class Book:
         # before the head: a cached block is reachable only through its prefix).
         idle = []
         for blk in s["table"]:
+            if blk < 0:
+                slot = -blk - 1
+                self.host_ref[slot] -= 1
+                if self.host_ref[slot] == 0:
+                    self.host_free.append(slot)
+                continue
             self.ref[blk] -= 1
             if self.ref[blk] == 0:
                 if blk in self.key_of:
@@ -251,6 +292,8 @@ class Book:
             for i in range(n // BLOCK_SIZE):
                 key = tuple(tokens[:BLOCK_SIZE * (i + 1)])
                 blk = s["table"][i]
+                if blk < 0:  # swapped out: the cache names device blocks only
+                    break
                 if key in self.pc or blk in self.key_of:
                     continue
                 self.pc[key] = blk
@@ -270,7 +313,91 @@ class Book:
         return self._seq(sid)["len"]
 
     def block_table(self, sid: int):
+        """The table as stored (host entries as -(slot + 1))."""
         return list(self._seq(sid)["table"])
+
+    def export_tables(self, sids):
+        """Tables and lengths of a batch for a device call (every sequence
+        must be resident); sets the reference bits of the blocks named."""
+        for sid in sids:
+            self._seq(sid)
+        for sid in sids:
+            if not self.resident(sid):
+                raise BookError("INVALID", f"sequence {sid} has blocks swapped out")
+        tables = [self.block_table(sid) for sid in sids]
+        for t in tables:
+            for blk in t:
+                self.refbit[blk] = 1
+        return tables, [self.seq_len(sid) for sid in sids]
+
+    # -- swap to host memory -----------------------------------------------
+    def resident(self, sid: int) -> bool:
+        return all(blk >= 0 for blk in self._seq(sid)["table"])
+
+    def configure_swap(self, num_host: int):
+        if num_host < 0:
+            raise BookError("INVALID", "negative host slot count")
+        if any(r > 0 for r in self.host_ref):
+            raise BookError("INVALID", "host slots in use")
+        self.num_host = num_host
+        self.host_free = list(range(num_host))[::-1]
+        self.host_ref = [0] * num_host
+
+    def swap_out(self, want: int, protect=()):
+        """Clock victims: list of (device block, host slot) to copy out."""
+        if want < 0:
+            raise BookError("INVALID", "negative count")
+        for sid in protect:
+            self._seq(sid)
+        guarded = {blk for sid in protect for blk in self.seqs[sid]["table"] if blk >= 0}
+        named = {blk for q in self.seqs.values() for blk in q["table"] if blk >= 0}
+        pairs = []
+        examined = 0
+        while len(pairs) < want and self.host_free and examined < 2 * self.num_blocks:
+            blk = self.hand
+            self.hand = (self.hand + 1) % self.num_blocks
+            examined += 1
+            if blk not in named or blk in self.key_of or blk in guarded:
+                continue
+            if self.refbit[blk]:
+                self.refbit[blk] = 0
+                continue
+            slot = self.host_free.pop()
+            self.host_ref[slot] = self.ref[blk]
+            for s in self.seqs.values():
+                s["table"] = [-(slot + 1) if b == blk else b for b in s["table"]]
+            self.ref[blk] = 0
+            self.free.append(blk)
+            pairs.append((blk, slot))
+        self.sst["swapped_out"] += len(pairs)
+        return pairs
+
+    def swap_in(self, sid: int):
+        """Every host entry of sequence sid back on the device, in table
+        order: list of (host slot, device block) to copy in."""
+        s = self._seq(sid)
+        slots = []
+        for blk in s["table"]:
+            if blk < 0 and -blk - 1 not in slots:
+                slots.append(-blk - 1)
+        if len(slots) > self.num_free():
+            raise BookError("NO_BLOCKS", "not enough device blocks to swap in")
+        pairs = []
+        for slot in slots:
+            blk = self.alloc()
+            self.ref[blk] = self.host_ref[slot]
+            self.host_ref[slot] = 0
+            self.host_free.append(slot)
+            for q in self.seqs.values():
+                q["table"] = [blk if b == -(slot + 1) else b for b in q["table"]]
+            pairs.append((slot, blk))
+        self.sst["swapped_in"] += len(pairs)
+        return pairs
+
+    def swap_stats(self) -> dict:
+        used = sum(1 for r in self.host_ref if r > 0)
+        return {"host_blocks": self.num_host, "host_used": used, "host_free": len(self.host_free),
+                "swapped_out": self.sst["swapped_out"], "swapped_in": self.sst["swapped_in"], "clock_hand": self.hand}
 
     # -- statistics -----------------------------------------------------------
     def stats(self) -> dict:
@@ -281,6 +408,8 @@ class Book:
         fill = {}
         for s in self.seqs.values():
             for j, blk in enumerate(s["table"]):
+                if blk < 0:  # on the host: not stored on the device
+                    continue
                 f = min(BLOCK_SIZE, s["len"] - j * BLOCK_SIZE)
                 fill[blk] = max(fill.get(blk, 0), f)
         stored = sum(fill.values())

@@ -65,6 +65,11 @@ class pkv_prefix_stats(ctypes.Structure):
                 ("idle_blocks", ctypes.c_int32), ("hit_rate", ctypes.c_double)]
 
 
+class pkv_swap_stats(ctypes.Structure):
+    _fields_ = [("host_blocks", ctypes.c_int32), ("host_used", ctypes.c_int32), ("host_free", ctypes.c_int32),
+                ("clock_hand", ctypes.c_int32), ("swapped_out", ctypes.c_int64), ("swapped_in", ctypes.c_int64)]
+
+
 class pkv_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("waves_per_simd", ctypes.c_int32),
                 ("ev_begin", ctypes.c_void_p),
@@ -98,6 +103,12 @@ SIGNATURES = {
     "pkv_seq_create_from_prefix": (ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
     "pkv_seq_register_prefix": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
     "pkv_prefix_cache_stats": (ctypes.c_int, [_P, ctypes.POINTER(pkv_prefix_stats)]),
+    "pkv_swap_configure": (ctypes.c_int, [_P, _I32]),
+    "pkv_swap_out": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_seq_swap_in": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_seq_resident": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I32)]),
+    "pkv_swap_space_stats": (ctypes.c_int, [_P, ctypes.POINTER(pkv_swap_stats)]),
+    "pkv_swap_copy": (ctypes.c_int, [_PL, _P, _P, _I32, _P, _P, _I32, _P, _I32, _P]),
     "pkv_kv_bytes_per_token": (_I64, [_PL, _I32]),
     "pkv_pool_bytes": (_I64, [_PL]),
     "pkv_validate_tables": (ctypes.c_int, [_PL, _P, _P, _I32, _I32]),
@@ -300,6 +311,44 @@ def pkv_prefix_cache_stats(pool) -> dict:
     return {f: getattr(s, f) for f, _ in pkv_prefix_stats._fields_}
 
 
+def pkv_swap_configure(pool, num_host_blocks: int):
+    _check(lib().pkv_swap_configure(pool, int(num_host_blocks)))
+
+
+def pkv_swap_out(pool, want: int, protect=()) -> np.ndarray:
+    """Clock victims: int32 [n][2] of (device block, host slot)."""
+    prot = np.ascontiguousarray(np.asarray(list(protect), dtype=np.int64))
+    out = np.empty((max(int(want), 1), 2), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(lib().pkv_swap_out(pool, int(want), _np_ptr(prot) if prot.size else None, prot.size, _np_ptr(out),
+                              int(want), ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def pkv_seq_swap_in(pool, seq: int) -> np.ndarray:
+    """int32 [n][2] of (host slot, device block) to copy back."""
+    n = ctypes.c_int32()
+    rc = lib().pkv_seq_swap_in(pool, int(seq), None, 0, ctypes.byref(n))
+    if rc == PKV_ERR_CAPACITY or (rc == PKV_OK and n.value > 0):
+        out = np.empty((max(n.value, 1), 2), dtype=np.int32)
+        _check(lib().pkv_seq_swap_in(pool, int(seq), _np_ptr(out), n.value, ctypes.byref(n)))
+        return out[:n.value].copy()
+    _check(rc)
+    return np.zeros((0, 2), dtype=np.int32)
+
+
+def pkv_seq_resident(pool, seq: int) -> bool:
+    r = ctypes.c_int32()
+    _check(lib().pkv_seq_resident(pool, int(seq), ctypes.byref(r)))
+    return bool(r.value)
+
+
+def pkv_swap_space_stats(pool) -> dict:
+    s = pkv_swap_stats()
+    _check(lib().pkv_swap_space_stats(pool, ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in pkv_swap_stats._fields_}
+
+
 def pkv_kv_bytes_per_token(layout: pkv_layout, num_layers: int) -> int:
     return lib().pkv_kv_bytes_per_token(ctypes.byref(layout), int(num_layers))
 
@@ -426,3 +475,23 @@ def paged_attention_prefill(layout, out, q, k_pool, v_pool, block_tables, contex
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32, B),
         _dev(query_start, "query_start", torch.int32, B + 1), B, Hq, block_tables.shape[1], int(max_query_len),
         int(max_context_len), float(scale), _stream(stream)))
+
+
+def pkv_swap_copy(layout, dst_k, dst_v, dst_blocks, src_k, src_v, src_blocks, pairs, stream=None):
+    """Whole blocks from one pool to another (either may be pinned host
+    memory): pairs int32 [n][2] of (source, destination) readable by the
+    device."""
+    import torch
+    if pairs.numel() % 2:
+        raise ValueError("pairs must be [n][2]")
+    pdt = pool_torch_dtype(layout)
+    per_block = layout.pool_elems // layout.num_blocks
+    for t, what, nb in ((dst_k, "dst_k", dst_blocks), (dst_v, "dst_v", dst_blocks), (src_k, "src_k", src_blocks),
+                        (src_v, "src_v", src_blocks)):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous() or t.dtype != pdt or t.numel() != nb * per_block:
+            raise ValueError(f"{what} must be a contiguous {pdt} tensor of {nb} blocks")
+    if not (pairs.is_cuda or pairs.is_pinned()) or pairs.dtype != torch.int32:
+        raise ValueError("pairs must be int32 on the device or in pinned memory")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    _check(lib().pkv_swap_copy(ctypes.byref(layout), p(dst_k), p(dst_v), int(dst_blocks), p(src_k), p(src_v),
+                               int(src_blocks), p(pairs), pairs.numel() // 2, _stream(stream)))

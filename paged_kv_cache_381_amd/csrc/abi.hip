@@ -265,3 +265,18 @@ extern "C" int paged_attention_prefill(const pkv_layout *layout, float *out, con
   if (int rc = pkv_launch_prefill_mfma(a)) return hip_fail(rc, "prefill kernel launch");
   return PKV_OK;
 }
+
+extern "C" int pkv_swap_copy(const pkv_layout *layout, void *dst_k, void *dst_v, int32_t dst_blocks,
+                             const void *src_k, const void *src_v, int32_t src_blocks, const int32_t *d_pairs,
+                             int32_t num_pairs, void *stream) {
+  if (int rc = pkv_check_layout(layout)) return rc;
+  if (num_pairs < 0 || dst_blocks < 0 || src_blocks < 0) return pkv_set_error(PKV_ERR_INVALID, "negative count");
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !d_pairs) return pkv_set_error(PKV_ERR_INVALID, "pkv_swap_copy: NULL pointer");
+  if (!aligned(dst_k, 16) || !aligned(dst_v, 16) || !aligned(src_k, 16) || !aligned(src_v, 16))
+    return pkv_set_error(PKV_ERR_INVALID, "pkv_swap_copy: pools must be 16-byte aligned");
+  if (num_pairs > 65535 * 32767) return pkv_set_error(PKV_ERR_INVALID, "too many pairs");
+  if (int rc = pkv_launch_swap(layout, dst_k, dst_v, dst_blocks, src_k, src_v, src_blocks, d_pairs, num_pairs, stream))
+    return hip_fail(rc, "pkv_swap_copy launch");
+  return PKV_OK;
+}

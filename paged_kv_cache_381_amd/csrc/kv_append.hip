@@ -126,7 +126,32 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4 *__restrict__ kp
   for (int i = threadIdx.x; i < units_per_block; i += blockDim.x) to[i] = from[i];
 }
 
+// Blocks between two pools of the same layout (either may be pinned host
+// memory, read or written over PCIe): workgroup (pair, pool) moves one block's
+// tiles for all heads.  Pairs naming a block outside either pool are skipped.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(uint4 *__restrict__ dst_k, uint4 *__restrict__ dst_v,
+                                                          const uint4 *__restrict__ src_k,
+                                                          const uint4 *__restrict__ src_v,
+                                                          const int32_t *__restrict__ pairs, int units_per_block,
+                                                          int src_blocks, int dst_blocks) {
+  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4 *from = (blockIdx.y == 0 ? src_k : src_v) + (size_t)src * units_per_block;
+  uint4 *to = (blockIdx.y == 0 ? dst_k : dst_v) + (size_t)dst * units_per_block;
+  for (int i = threadIdx.x; i < units_per_block; i += blockDim.x) to[i] = from[i];
+}
+
 }  // namespace
+
+int pkv_launch_swap(const pkv_layout *L, void *dst_k, void *dst_v, int32_t dst_blocks, const void *src_k,
+                    const void *src_v, int32_t src_blocks, const int32_t *pairs, int32_t num_pairs, void *stream) {
+  if (num_pairs == 0) return 0;
+  const int units = (int)(L->num_kv_heads * pkv_tile_bytes(L) / 16);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     (uint4 *)dst_k, (uint4 *)dst_v, (const uint4 *)src_k, (const uint4 *)src_v, pairs, units,
+                     src_blocks, dst_blocks);
+  return (int)hipGetLastError();
+}
 
 int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
                       const int64_t *slots, int32_t num_tokens, void *stream) {

@@ -65,6 +65,8 @@ int pkv_split_grid(const void *kernel, int block_threads, size_t lds_bytes, cons
 
 int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
                       const int64_t *slots, int32_t num_tokens, void *stream);
+int pkv_launch_swap(const pkv_layout *L, void *dst_k, void *dst_v, int32_t dst_blocks, const void *src_k,
+                    const void *src_v, int32_t src_blocks, const int32_t *pairs, int32_t num_pairs, void *stream);
 int pkv_launch_copy_blocks(const pkv_layout *L, void *k_pool, void *v_pool, const int32_t *pairs,
                            int32_t num_pairs, void *stream);
 struct pkv_prefill_args {

@@ -81,8 +81,20 @@ struct pkv_pool {
   int32_t lru_head = -1, lru_tail = -1, n_idle = 0;
   pkv_prefix_stats pst{};
 
+  // Swap to host memory ("fine-grained eviction" [KV Cache 与
+  // PagedAttention, summary]; Clock replacement [PagedAttention：大模型KV
+  // Cache内存管理革新 §3.3]).  A table entry e < 0 names host slot -e-1.
+  // refbit is the Clock reference bit of each device block: set when the
+  // block is taken, written, or named in an exported table.
+  mutable std::vector<uint8_t> refbit;
+  int32_t hand = 0;
+  int32_t num_host = 0;
+  std::vector<int32_t> host_free;  // top is back()
+  std::vector<int32_t> host_ref;
+  int64_t swapped_out = 0, swapped_in = 0;
+
   // Undo log of one all-or-nothing operation.
-  enum class Op { Alloc, AllocEvict, TablePush, CowSwap, Len };
+  enum class Op { Alloc, AllocEvict, TablePush, CowSwap, Len, RefBit };
   struct Undo {
     Op op;
     int64_t seq;
@@ -91,6 +103,17 @@ struct pkv_pool {
   std::vector<Undo> log;
 
   bool valid_block(int32_t b) const { return b >= 0 && b < layout.num_blocks; }
+  static bool resident(const Seq &s) {
+    for (int32_t e : s.table)
+      if (e < 0) return false;
+    return true;
+  }
+  // Point every table entry naming `from` at `to` (block ids or host entries).
+  void retarget(int32_t from, int32_t to) {
+    for (auto &kv : seqs)
+      for (int32_t &e : kv.second.table)
+        if (e == from) e = to;
+  }
   int32_t available() const { return (int32_t)free_stack.size() + n_idle; }
 
   void lru_unlink(int32_t b) {
@@ -134,6 +157,7 @@ struct pkv_pool {
       return pkv_set_error(PKV_ERR_NO_BLOCKS, "no free blocks (pool of %d)", layout.num_blocks);
     }
     ref[b] = 1;
+    refbit[b] = 1;
     *out = b;
     return PKV_OK;
   }
@@ -177,6 +201,9 @@ struct pkv_pool {
         case Op::Len:
           seqs[it->seq].len = it->a;
           break;
+        case Op::RefBit:
+          refbit[it->a] = (uint8_t)it->b;
+          break;
       }
     }
     log.clear();
@@ -208,7 +235,10 @@ struct pkv_pool {
         cow[2 * *n_cow + 1] = b;
         ++*n_cow;
       }
-      slots[k] = (int64_t)s.table[pos / PKV_BLOCK_SIZE] * PKV_BLOCK_SIZE + pos % PKV_BLOCK_SIZE;
+      const int32_t blk = s.table[pos / PKV_BLOCK_SIZE];
+      log.push_back({Op::RefBit, id, blk, refbit[blk]});
+      refbit[blk] = 1;
+      slots[k] = (int64_t)blk * PKV_BLOCK_SIZE + pos % PKV_BLOCK_SIZE;
       log.push_back({Op::Len, id, pos, 0});
       s.len = pos + 1;
     }
@@ -246,6 +276,7 @@ extern "C" int pkv_pool_create(const pkv_layout *layout, const int32_t *free_ord
   p->cached.assign(n, 0);
   p->lru_prev.assign(n, -1);
   p->lru_next.assign(n, -1);
+  p->refbit.assign(n, 0);
   *out = p;
   return PKV_OK;
 }
@@ -308,9 +339,14 @@ extern "C" int pkv_seq_fork(pkv_pool *pool, int64_t parent, int64_t *child_out) 
   if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)parent);
   pkv_pool::Seq child = it->second;  // copy before inserting (rehash safety)
   for (int32_t b : child.table)
-    if (pool->ref[b] <= 0)
+    if (b >= 0 && pool->ref[b] <= 0)
       return pkv_set_error(PKV_ERR_REFCOUNT, "fork of sequence %lld holding free block %d", (long long)parent, b);
-  for (int32_t b : child.table) pool->ref[b] += 1;
+  for (int32_t b : child.table) {
+    if (b >= 0)
+      pool->ref[b] += 1;
+    else
+      pool->host_ref[-b - 1] += 1;
+  }
   int64_t id = pool->next_id++;
   pool->seqs.emplace(id, std::move(child));
   *child_out = id;
@@ -327,6 +363,10 @@ extern "C" int pkv_batch_append_slots(pkv_pool *pool, const int64_t *ids, int32_
   if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out)) return pkv_set_error(PKV_ERR_INVALID, "bad cow buffer");
   for (int32_t i = 0; i < num_seqs; ++i)
     if (!pool->seqs.count(ids[i])) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)ids[i]);
+  for (int32_t i = 0; i < num_seqs; ++i)
+    if (!pkv_pool::resident(pool->seqs[ids[i]]))
+      return pkv_set_error(PKV_ERR_INVALID, "sequence %lld has blocks swapped out; swap it in first",
+                           (long long)ids[i]);
   int32_t ncow = 0;
   pool->log.clear();
   for (int32_t i = 0; i < num_seqs; ++i) {
@@ -354,7 +394,8 @@ extern "C" int pkv_seq_free(pkv_pool *pool, int64_t id) {
   // the table holds it (a caller that freed a block the sequence still held
   // can make it appear twice).
   std::unordered_map<int32_t, int32_t> held;
-  for (int32_t b : it->second.table) ++held[b];
+  for (int32_t b : it->second.table)
+    if (b >= 0) ++held[b];
   for (const auto &kv : held)
     if (pool->ref[kv.first] < kv.second)
       return pkv_set_error(PKV_ERR_REFCOUNT, "free of sequence %lld holding block %d %d times, refcount %d",
@@ -364,13 +405,18 @@ extern "C" int pkv_seq_free(pkv_pool *pool, int64_t id) {
   // evicted before the head (a cached block is only reachable through its
   // prefix).
   std::vector<int32_t> idle;
-  for (int32_t b : it->second.table)
+  for (int32_t b : it->second.table) {
+    if (b < 0) {  // a host entry
+      if (--pool->host_ref[-b - 1] == 0) pool->host_free.push_back(-b - 1);
+      continue;
+    }
     if (--pool->ref[b] == 0) {
       if (pool->cached[b])
         idle.push_back(b);
       else
         pool->free_stack.push_back(b);
     }
+  }
   for (auto r = idle.rbegin(); r != idle.rend(); ++r) pool->lru_push_back(*r);
   pool->seqs.erase(it);
   return PKV_OK;
@@ -409,6 +455,9 @@ extern "C" int pkv_batch_block_tables(const pkv_pool *pool, const int64_t *ids, 
     if ((int32_t)it->second.table.size() > max_blocks_per_seq)
       return pkv_set_error(PKV_ERR_CAPACITY, "sequence %lld holds %zu blocks > %d", (long long)ids[i],
                            it->second.table.size(), max_blocks_per_seq);
+    if (!pkv_pool::resident(it->second))
+      return pkv_set_error(PKV_ERR_INVALID, "sequence %lld has blocks swapped out; swap it in first",
+                           (long long)ids[i]);
   }
   for (int32_t i = 0; i < num_seqs; ++i) {
     const auto &s = pool->seqs.find(ids[i])->second;
@@ -416,6 +465,7 @@ extern "C" int pkv_batch_block_tables(const pkv_pool *pool, const int64_t *ids, 
     std::copy(s.table.begin(), s.table.end(), row);
     std::fill(row + s.table.size(), row + max_blocks_per_seq, 0);
     context_lens_out[i] = s.len;
+    for (int32_t b : s.table) pool->refbit[b] = 1;
   }
   return PKV_OK;
 }
@@ -430,6 +480,7 @@ extern "C" int pkv_pool_stats(const pkv_pool *pool, pkv_stats *out) {
     const auto &s = kv.second;
     logical += s.len;
     for (size_t j = 0; j < s.table.size(); ++j) {
+      if (s.table[j] < 0) continue;  // on the host
       int32_t f = std::min<int32_t>(PKV_BLOCK_SIZE, s.len - (int32_t)j * PKV_BLOCK_SIZE);
       fill[s.table[j]] = std::max(fill[s.table[j]], f);
     }
@@ -574,8 +625,9 @@ extern "C" int pkv_seq_register_prefix(pkv_pool *pool, int64_t id, const int32_t
     for (int32_t i = 0; i + 1 <= n / PKV_BLOCK_SIZE; ++i) {
       const int32_t *tok = token_ids + (int64_t)i * PKV_BLOCK_SIZE;
       uint64_t key;
-      const int32_t hit = lookup(pool, parent, tok, &key);
       const int32_t b = s.table[i];
+      if (b < 0) break;  // swapped out: the cache names device blocks only
+      const int32_t hit = lookup(pool, parent, tok, &key);
       // Content already cached (maybe in another block), or this block
       // already cached under its own prefix: leave the cache as it is.
       if (hit < 0 && !pool->cached[b] && !pool->pc_map.count(key)) {
@@ -602,5 +654,114 @@ extern "C" int pkv_prefix_cache_stats(const pkv_pool *pool, pkv_prefix_stats *ou
   out->cached_blocks = (int32_t)pool->pc_map.size();
   out->idle_blocks = pool->n_idle;
   out->hit_rate = out->query_tokens ? (double)out->hit_tokens / (double)out->query_tokens : 0.0;
+  return PKV_OK;
+}
+
+// ------------------------------------------------------------ host swap
+extern "C" int pkv_swap_configure(pkv_pool *pool, int32_t num_host_blocks) {
+  if (int rc = need_pool(pool)) return rc;
+  if (num_host_blocks < 0) return pkv_set_error(PKV_ERR_INVALID, "num_host_blocks < 0");
+  for (int32_t r : pool->host_ref)
+    if (r > 0) return pkv_set_error(PKV_ERR_INVALID, "host slots still hold swapped-out blocks");
+  pool->num_host = num_host_blocks;
+  pool->host_ref.assign(num_host_blocks, 0);
+  pool->host_free.resize(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i) pool->host_free[i] = num_host_blocks - 1 - i;  // slot 0 first
+  return PKV_OK;
+}
+
+extern "C" int pkv_swap_out(pkv_pool *pool, int32_t want, const int64_t *protect_ids, int32_t n_protect,
+                            int32_t *pairs_out, int32_t cap, int32_t *n_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (want < 0 || n_protect < 0 || cap < 0) return pkv_set_error(PKV_ERR_INVALID, "negative count");
+  if ((n_protect > 0 && !protect_ids) || (want > 0 && !pairs_out) || !n_out)
+    return pkv_set_error(PKV_ERR_INVALID, "NULL argument");
+  if (want > cap) return pkv_set_error(PKV_ERR_CAPACITY, "want %d blocks, pair buffer holds %d", want, cap);
+  std::vector<uint8_t> guarded(pool->layout.num_blocks, 0), named(pool->layout.num_blocks, 0);
+  for (const auto &kv : pool->seqs)
+    for (int32_t b : kv.second.table)
+      if (b >= 0) named[b] = 1;
+  for (int32_t i = 0; i < n_protect; ++i) {
+    auto it = pool->seqs.find(protect_ids[i]);
+    if (it == pool->seqs.end())
+      return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)protect_ids[i]);
+    for (int32_t b : it->second.table)
+      if (b >= 0) guarded[b] = 1;
+  }
+  // Clock: the hand passes over device blocks from where it last stopped; a
+  // candidate with its reference bit set gets a second chance.
+  const int32_t N = pool->layout.num_blocks;
+  int32_t got = 0;
+  for (int64_t examined = 0; got < want && !pool->host_free.empty() && examined < 2 * (int64_t)N; ++examined) {
+    const int32_t b = pool->hand;
+    pool->hand = (pool->hand + 1) % N;
+    if (!named[b] || pool->cached[b] || guarded[b]) continue;
+    if (pool->refbit[b]) {
+      pool->refbit[b] = 0;
+      continue;
+    }
+    const int32_t slot = pool->host_free.back();
+    pool->host_free.pop_back();
+    pool->host_ref[slot] = pool->ref[b];
+    pool->retarget(b, -slot - 1);
+    pool->ref[b] = 0;
+    pool->free_stack.push_back(b);
+    pairs_out[2 * got] = b;
+    pairs_out[2 * got + 1] = slot;
+    ++got;
+  }
+  pool->swapped_out += got;
+  *n_out = got;
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_swap_in(pkv_pool *pool, int64_t id, int32_t *pairs_out, int32_t cap, int32_t *n_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!n_out || cap < 0 || (cap > 0 && !pairs_out)) return pkv_set_error(PKV_ERR_INVALID, "bad arguments");
+  auto it = pool->seqs.find(id);
+  if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)id);
+  std::vector<int32_t> slots;  // distinct host entries in table order
+  for (int32_t e : it->second.table)
+    if (e < 0 && std::find(slots.begin(), slots.end(), -e - 1) == slots.end()) slots.push_back(-e - 1);
+  *n_out = (int32_t)slots.size();
+  if ((int32_t)slots.size() > cap)
+    return pkv_set_error(PKV_ERR_CAPACITY, "%zu blocks to swap in, pair buffer holds %d", slots.size(), cap);
+  if ((int32_t)slots.size() > pool->available())
+    return pkv_set_error(PKV_ERR_NO_BLOCKS, "%zu blocks to swap in, %d available", slots.size(), pool->available());
+  for (size_t k = 0; k < slots.size(); ++k) {
+    int32_t b;
+    pool->alloc(&b);  // cannot fail: enough blocks were counted above
+    const int32_t slot = slots[k];
+    pool->ref[b] = pool->host_ref[slot];
+    pool->host_ref[slot] = 0;
+    pool->host_free.push_back(slot);
+    pool->retarget(-slot - 1, b);
+    pairs_out[2 * k] = slot;
+    pairs_out[2 * k + 1] = b;
+  }
+  pool->swapped_in += (int64_t)slots.size();
+  return PKV_OK;
+}
+
+extern "C" int pkv_seq_resident(const pkv_pool *pool, int64_t id, int32_t *resident_out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!resident_out) return pkv_set_error(PKV_ERR_INVALID, "resident_out is NULL");
+  auto it = pool->seqs.find(id);
+  if (it == pool->seqs.end()) return pkv_set_error(PKV_ERR_BAD_SEQ, "unknown sequence %lld", (long long)id);
+  *resident_out = pkv_pool::resident(it->second) ? 1 : 0;
+  return PKV_OK;
+}
+
+extern "C" int pkv_swap_space_stats(const pkv_pool *pool, pkv_swap_stats *out) {
+  if (int rc = need_pool(pool)) return rc;
+  if (!out) return pkv_set_error(PKV_ERR_INVALID, "out is NULL");
+  int32_t used = 0;
+  for (int32_t r : pool->host_ref) used += r > 0;
+  out->host_blocks = pool->num_host;
+  out->host_used = used;
+  out->host_free = (int32_t)pool->host_free.size();
+  out->clock_hand = pool->hand;
+  out->swapped_out = pool->swapped_out;
+  out->swapped_in = pool->swapped_in;
   return PKV_OK;
 }

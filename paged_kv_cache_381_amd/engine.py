@@ -75,6 +75,41 @@ class PagedKVCache:
                 L.pkv_copy_blocks(self.layout, k, v, pairs)
         return slots, cow
 
+    # -- swap to host memory ------------------------------------------------
+    def enable_swap(self, num_host_blocks: int):
+        """Pinned host pools (one K and one V per layer) of num_host_blocks
+        block slots, in the device pools' tile layout."""
+        L.pkv_swap_configure(self.pool, num_host_blocks)
+        per_block = self.layout.pool_elems // self.layout.num_blocks
+        tdt = L.pool_torch_dtype(self.layout)
+        self.num_host_blocks = num_host_blocks
+        self.host_k = [torch.empty(num_host_blocks * per_block, dtype=tdt, pin_memory=True)
+                       for _ in self.k_pools]
+        self.host_v = [torch.empty(num_host_blocks * per_block, dtype=tdt, pin_memory=True)
+                       for _ in self.v_pools]
+
+    def swap_out(self, want: int, protect=()):
+        """Clock victims moved to host slots on every layer; returns the
+        (device block, host slot) pairs."""
+        pairs = L.pkv_swap_out(self.pool, want, protect)
+        if len(pairs):
+            d = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
+            for layer in range(len(self.k_pools)):
+                L.pkv_swap_copy(self.layout, self.host_k[layer], self.host_v[layer], self.num_host_blocks,
+                                self.k_pools[layer], self.v_pools[layer], self.layout.num_blocks, d)
+        return pairs
+
+    def swap_in(self, seq: int):
+        """Every host block of a sequence back on the device, every layer;
+        returns the (host slot, device block) pairs."""
+        pairs = L.pkv_seq_swap_in(self.pool, seq)
+        if len(pairs):
+            d = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
+            for layer in range(len(self.k_pools)):
+                L.pkv_swap_copy(self.layout, self.k_pools[layer], self.v_pools[layer], self.layout.num_blocks,
+                                self.host_k[layer], self.host_v[layer], self.num_host_blocks, d)
+        return pairs
+
     # -- prefix cache ---------------------------------------------------------
     def enable_prefix_cache(self, on: bool = True):
         L.pkv_prefix_cache_enable(self.pool, on)
