@@ -292,6 +292,81 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+PCIE_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+SWAP_METRIC = "block swap GB/s between HBM and pinned host memory (% of PCIe 5.0 x16), 1 GPU"
+
+
+def bench_swap(args):
+    """Swap of a decode workload's blocks: every block of the second half of
+    the batch moves to pinned host memory (Clock victims, the first half
+    protected) and back, K and V, one layer.  Times the two copy kernels with
+    events on the launch stream; the host bookkeeping is reported apart."""
+    import numpy as np
+    import torch
+    import workloads
+    from paged_kv_cache_381_amd import _lib as L
+    from paged_kv_cache_381_amd.engine import GpuWorkload
+
+    name = args.workload.split(":", 1)[1]
+    inst = workloads.get(name)
+    wl = inst.wl
+    gw = GpuWorkload(inst)
+    c = gw.cache
+    B = wl.batch
+    keep, move = gw.ids[:B // 2], gw.ids[B // 2:]
+    need = int(sum(-(-int(n) // 16) for n in inst.ctx[B // 2:]))
+    c.enable_swap(need + 16)
+    tile = c.layout.pool_elems // c.layout.num_blocks * (c.k_pools[0].element_size())
+    K, W = args.steps, args.warmup
+    out_ms, in_ms, book_s, moved = [], [], 0.0, 0
+    for k in range(W + K):
+        c.tables(keep, gw.max_blocks)  # the running half: its blocks are protected and referenced
+        t0 = time.perf_counter()
+        pairs = L.pkv_swap_out(c.pool, 10 ** 6, keep)
+        book_s += time.perf_counter() - t0 if k >= W else 0.0
+        d = torch.from_numpy(np.ascontiguousarray(pairs)).cuda()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        L.pkv_swap_copy(c.layout, c.host_k[0], c.host_v[0], c.num_host_blocks, c.k_pools[0], c.v_pools[0],
+                        c.layout.num_blocks, d)
+        e[1].record()
+        back = []
+        t0 = time.perf_counter()
+        for sid in move:
+            back.append(L.pkv_seq_swap_in(c.pool, sid))
+        book_s += time.perf_counter() - t0 if k >= W else 0.0
+        d2 = torch.from_numpy(np.ascontiguousarray(np.concatenate(back))).cuda()
+        e[2].record()
+        L.pkv_swap_copy(c.layout, c.k_pools[0], c.v_pools[0], c.layout.num_blocks, c.host_k[0], c.host_v[0],
+                        c.num_host_blocks, d2)
+        e[3].record()
+        torch.cuda.synchronize()
+        assert len(pairs) == need and len(d2) == need
+        if k >= W:
+            out_ms.append(e[0].elapsed_time(e[1]))
+            in_ms.append(e[2].elapsed_time(e[3]))
+            moved += len(pairs)
+    nbytes = need * 2 * tile  # K and V of every block, per direction
+    o_ms, i_ms = sum(out_ms) / K, sum(in_ms) / K
+    out_gbps, in_gbps = nbytes / (o_ms * 1e-3) / 1e9, nbytes / (i_ms * 1e-3) / 1e9
+    gbps = 2 * nbytes / ((o_ms + i_ms) * 1e-3) / 1e9
+    print(f"[bench] swap {need} blocks ({nbytes / 1e6:.1f} MB) out {o_ms * 1e3:.0f} us ({out_gbps:.1f} GB/s), "
+          f"in {i_ms * 1e3:.0f} us ({in_gbps:.1f} GB/s); bookkeeping {book_s / K * 1e3:.2f} ms per round trip",
+          flush=True)
+    res = {"metric": SWAP_METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+           "ms_per_step": round(o_ms + i_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": wl.cache_dtype, "data": "synthetic",
+           "config": {"workload": f"swap out and back in the blocks of half of: {wl.description}", "name": wl.name,
+                      "blocks_per_direction": need, "bytes_per_direction": nbytes, "parallelism": "none"},
+           "swap_out_gbps": round(out_gbps, 2), "swap_in_gbps": round(in_gbps, 2),
+           "bookkeeping_ms_per_round_trip": round(book_s / K * 1e3, 3),
+           "roofline": {"kernel": "pkv_swap_copy (swap_blocks_kernel)", "bound": "pcie", "achieved": round(gbps, 2),
+                        "peak": PCIE_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / PCIE_PEAK_GBPS, 4),
+                        "traffic": None},
+           "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(gib: float, reps: int):
     """Plain device-to-device copies of a known size (PMC calibration)."""
     import torch
@@ -348,6 +423,9 @@ def main():
 
     if args.workload in PW.PREFILL_WORKLOADS:
         bench_prefill(args)
+        return
+    if args.workload.startswith("swap:"):
+        bench_swap(args)
         return
     inst = workloads.get(args.workload)
     wl = inst.wl

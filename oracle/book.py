@@ -368,6 +368,7 @@ class Book:
                 s["table"] = [-(slot + 1) if b == blk else b for b in s["table"]]
             self.ref[blk] = 0
             self.free.append(blk)
+            named.discard(blk)  # free now: a second turn of the hand passes it over
             pairs.append((blk, slot))
         self.sst["swapped_out"] += len(pairs)
         return pairs
@@ -393,6 +394,28 @@ class Book:
             pairs.append((slot, blk))
         self.sst["swapped_in"] += len(pairs)
         return pairs
+
+    def check_invariants(self):
+        """Every block is in exactly one of: free stack, idle cache list,
+        held (refcount > 0); refcounts equal table references plus loose
+        ones; host slots likewise."""
+        assert len(set(self.free)) == len(self.free), "block twice on the free stack"
+        assert len(set(self.lru)) == len(self.lru)
+        held = {b for b in range(self.num_blocks) if self.ref[b] > 0}
+        assert not (set(self.free) & set(self.lru)) and not (held & (set(self.free) | set(self.lru)))
+        assert len(self.free) + len(self.lru) + len(held) == self.num_blocks
+        counts = {}
+        for q in self.seqs.values():
+            for e in q["table"]:
+                counts[e] = counts.get(e, 0) + 1
+        for e, k in counts.items():
+            if e >= 0:
+                assert self.ref[e] >= k, (e, self.ref[e], k)
+            else:
+                assert self.host_ref[-e - 1] == k, (e, self.host_ref[-e - 1], k)
+        assert len(set(self.host_free)) == len(self.host_free)
+        used = {i for i, r in enumerate(self.host_ref) if r > 0}
+        assert not (used & set(self.host_free)) and len(used) + len(self.host_free) == self.num_host
 
     def swap_stats(self) -> dict:
         used = sum(1 for r in self.host_ref if r > 0)

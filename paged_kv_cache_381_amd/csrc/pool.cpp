@@ -108,12 +108,7 @@ struct pkv_pool {
       if (e < 0) return false;
     return true;
   }
-  // Point every table entry naming `from` at `to` (block ids or host entries).
-  void retarget(int32_t from, int32_t to) {
-    for (auto &kv : seqs)
-      for (int32_t &e : kv.second.table)
-        if (e == from) e = to;
-  }
+
   int32_t available() const { return (int32_t)free_stack.size() + n_idle; }
 
   void lru_unlink(int32_t b) {
@@ -692,6 +687,7 @@ extern "C" int pkv_swap_out(pkv_pool *pool, int32_t want, const int64_t *protect
   // candidate with its reference bit set gets a second chance.
   const int32_t N = pool->layout.num_blocks;
   int32_t got = 0;
+  std::vector<int32_t> remap;  // device block -> its host entry, for the victims
   for (int64_t examined = 0; got < want && !pool->host_free.empty() && examined < 2 * (int64_t)N; ++examined) {
     const int32_t b = pool->hand;
     pool->hand = (pool->hand + 1) % N;
@@ -703,13 +699,19 @@ extern "C" int pkv_swap_out(pkv_pool *pool, int32_t want, const int64_t *protect
     const int32_t slot = pool->host_free.back();
     pool->host_free.pop_back();
     pool->host_ref[slot] = pool->ref[b];
-    pool->retarget(b, -slot - 1);
+    if (remap.empty()) remap.assign(N, 0);
+    remap[b] = -slot - 1;
+    named[b] = 0;  // free now: a second turn of the hand passes it over
     pool->ref[b] = 0;
     pool->free_stack.push_back(b);
     pairs_out[2 * got] = b;
     pairs_out[2 * got + 1] = slot;
     ++got;
   }
+  if (got)  // every table entry naming a victim now names its host slot
+    for (auto &kv : pool->seqs)
+      for (int32_t &e : kv.second.table)
+        if (e >= 0 && remap[e] < 0) e = remap[e];
   pool->swapped_out += got;
   *n_out = got;
   return PKV_OK;
@@ -728,6 +730,7 @@ extern "C" int pkv_seq_swap_in(pkv_pool *pool, int64_t id, int32_t *pairs_out, i
     return pkv_set_error(PKV_ERR_CAPACITY, "%zu blocks to swap in, pair buffer holds %d", slots.size(), cap);
   if ((int32_t)slots.size() > pool->available())
     return pkv_set_error(PKV_ERR_NO_BLOCKS, "%zu blocks to swap in, %d available", slots.size(), pool->available());
+  std::unordered_map<int32_t, int32_t> back;  // host entry -> new device block
   for (size_t k = 0; k < slots.size(); ++k) {
     int32_t b;
     pool->alloc(&b);  // cannot fail: enough blocks were counted above
@@ -735,10 +738,17 @@ extern "C" int pkv_seq_swap_in(pkv_pool *pool, int64_t id, int32_t *pairs_out, i
     pool->ref[b] = pool->host_ref[slot];
     pool->host_ref[slot] = 0;
     pool->host_free.push_back(slot);
-    pool->retarget(-slot - 1, b);
+    back[-slot - 1] = b;
     pairs_out[2 * k] = slot;
     pairs_out[2 * k + 1] = b;
   }
+  if (!back.empty())  // every sharer of a swapped-in block follows it
+    for (auto &kv : pool->seqs)
+      for (int32_t &e : kv.second.table)
+        if (e < 0) {
+          auto f = back.find(e);
+          if (f != back.end()) e = f->second;
+        }
   pool->swapped_in += (int64_t)slots.size();
   return PKV_OK;
 }

@@ -25,6 +25,7 @@ class Both:
 
     def same(self):
         b = self.book
+        b.check_invariants()
         for blk in range(self.n):
             assert L.pkv_block_refcount(self.pool, blk) == b.refcount(blk)
         assert L.pkv_pool_num_free(self.pool) == b.num_free()
@@ -121,6 +122,25 @@ def test_shared_block_moves_for_every_sharer():
         b.same()
         run(b, "free", A); run(b, "free", F)
         b.same()
+    finally:
+        b.close()
+
+
+def test_turn_one_victims_are_not_taken_twice():
+    """A block evicted on the hand's first turn is free afterwards; when the
+    hand comes round again in the same call it passes the block over.
+    A holds blocks 0, 1.  swap_out(1): the first turn clears both bits, the
+    second evicts 0 and stops on 1.  swap_out(5): block 1 (bit clear) goes at
+    once; the hand then turns twice over blocks that are free or unused, and
+    nothing else is taken."""
+    b = Both(6)
+    try:
+        A = run(b, "create"); run(b, "append", A, 32)
+        run(b, "configure", 6)
+        assert run(b, "swap_out", 1, []) == [(0, 0)]
+        assert run(b, "swap_out", 5, []) == [(1, 1)]
+        b.same()
+        assert b.book.block_table(A) == [-1, -2]
     finally:
         b.close()
 
