@@ -258,6 +258,9 @@ def bench_prefill(args):
             else:
                 gp.run(layer)
 
+    import gc
+    gc.collect()
+    gc.disable()
     for _ in range(W):
         step(None)
     torch.cuda.synchronize()
@@ -266,6 +269,7 @@ def bench_prefill(args):
         step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     assert torch.isfinite(gp.out).all().item(), "non-finite prefill output"
     avg_ms = sum(a.elapsed_time(b) for a, b in ev) / K
     tflops = flops * layers * K / elapsed / 1e12
@@ -464,34 +468,65 @@ def main():
     evs = hip.create(2 * K)
     torch.cuda.synchronize()
 
+    # The step calls the C ABI directly with argument tuples built once: the
+    # binding's per-call checks cost the host more than the GPU work of a
+    # small layer, and a slow host would otherwise set the step's pace.
+    lib = L.lib()
+    V = ctypes.c_void_p
+    stream = L._stream(None)
+    ids_c = np.ascontiguousarray(ids, dtype=np.int64)
+    cow = np.empty((B, 2), dtype=np.int32)
+    ncow = ctypes.c_int32(0)
+    lay = ctypes.byref(cache.layout)
+    wps_opts = L.decode_opts(args.partition, args.kernel, None, wps)
+    ev_opts = [L.decode_opts(args.partition, args.kernel, (evs[2 * i], evs[2 * i + 1], None), wps) for i in range(K)]
+    ws_bytes = ws.numel() * ws.element_size()
+    append_args = [(lay, V(cache.k_pools[i].data_ptr()), V(cache.v_pools[i].data_ptr()), V(k_new.data_ptr()),
+                    V(v_new.data_ptr()), V(d_slots.data_ptr()), B, stream) for i in range(layers)]
+    head = [(lay, V(out.data_ptr()), V(gw.q.data_ptr()), V(cache.k_pools[i].data_ptr()),
+             V(cache.v_pools[i].data_ptr()), V(d_tables.data_ptr()), V(d_ctx.data_ptr()), B, Hq, MB)
+            for i in range(layers)]
+    tail = (ctypes.c_float(gw.scale), V(ws.data_ptr()), ws_bytes)
+    pin_ptr = [(V(p.data_ptr()), V(p.data_ptr() + 12 * B), V(p.data_ptr() + 8 * B)) for p in pin]
+
     def step(k: int, timed_idx: int):
         r = k % R
         ring_ev[r].synchronize()  # the copy that last read this pinned set is done
-        h = pin[r].numpy()
-        L.pkv_batch_append_slots(cache.pool, ids, 1, slots_out=h[:2 * B].view(np.int64))
-        L.pkv_batch_block_tables(cache.pool, ids, MB, h[3 * B:].reshape(B, MB), h[2 * B:3 * B])
-        ctx_np = h[2 * B:3 * B]
+        slots_p, tables_p, ctx_p = pin_ptr[r]
+        L._check(lib.pkv_batch_append_slots(cache.pool, ids_c.ctypes.data_as(V), B, 1, slots_p,
+                                            cow.ctypes.data_as(V), B, ctypes.byref(ncow)))
+        assert ncow.value == 0, "the bench's sequences never share a tail block"
+        L._check(lib.pkv_batch_block_tables(cache.pool, ids_c.ctypes.data_as(V), B, MB, tables_p, ctx_p))
+        ctx_np = pin[r].numpy()[2 * B:3 * B]
         max_ctx = int(ctx_np.max())
         dbuf.copy_(pin[r], non_blocking=True)
         ring_ev[r].record()
         ev_layer = timed_idx % layers if timed_idx >= 0 else -1
         for layer in range(layers):
-            ev = (evs[2 * timed_idx], evs[2 * timed_idx + 1], None) if layer == ev_layer else None
-            cache.write(layer, d_slots, k_new, v_new)
-            cache.decode(layer, out, gw.q, d_tables, d_ctx, max_ctx, gw.scale, ws, args.partition, args.kernel, ev,
-                         wps)
+            opts = ev_opts[timed_idx] if layer == ev_layer else wps_opts
+            L._check(lib.paged_kv_append(*append_args[layer]))
+            L._check(lib.paged_attention_decode(*head[layer], max_ctx, *tail, ctypes.byref(opts), stream))
         return int(ctx_np.astype(np.int64).sum())
 
+    import gc
+    gc.collect()
+    gc.disable()  # a collection pause inside the timed steps would be charged to the GPU path
     for k in range(W):
         step(k, -1)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({W} steps), timing {K} steps", flush=True)
     ctx_tokens = []
+    marks = []
     t0 = time.perf_counter()
     for k in range(K):
         ctx_tokens.append(step(W + k, k))
+        marks.append(time.perf_counter())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
+    if os.environ.get("PKV_BENCH_STEP_TIMES"):
+        gaps = np.diff([t0] + marks) * 1e3
+        print("[bench] host ms per step (issue):", " ".join(f"{g:.2f}" for g in gaps), flush=True)
     elapsed = t1 - t0
     assert torch.isfinite(out).all().item(), "non-finite attention output"
 
@@ -536,7 +571,11 @@ def main():
         "roofline": {"kernel": "paged_attention_decode partition kernel", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": int(unique_per_launch),
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "launch_us_min_median_max": [round(min(durs) * 1e3, 2),
+                                                  round(sorted(durs)[len(durs) // 2] * 1e3, 2),
+                                                  round(max(durs) * 1e3, 2)],
+                     "bytes_per_launch": int(unique_per_launch),
                      "logical_bytes_per_launch": int(bytes_per_launch),
                      "achieved_logical": round(achieved_logical, 2), "traffic": traffic},
         "cpu_baseline": None,
