@@ -56,7 +56,7 @@ __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
 
 constexpr float kSlack = 8.0f;  // headroom of the running maximum (base 2)
 
-template <int D, int NB, bool I8>
+template <int D, int NB, bool I8, int CT>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   constexpr int NKK = D / 32;
   constexpr int NNN = D / 16;
@@ -72,22 +72,31 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   // A sequence claiming more new tokens than it holds keeps its last n.
   const int nq = min(sload_i32(P.qstart + b + 1) - q0, n);
   const int ntile = (nq + TQ - 1) / TQ;
-  const int tile = ntile - 1 - (int)(blockIdx.x * 4 + w);  // longest tiles first
-  if (tile < 0) return;
+  // The wave's CT column tiles, longest first; tiles run longest first too.
+  const int t_first = ntile - 1 - (int)(blockIdx.x * 4 + w) * CT;
+  if (t_first < 0) return;
   const int p0 = n - nq;  // position of new token 0
-  const int tlast = min(tile * TQ + TQ, nq) - 1;
-  const int kend = p0 + tlast + 1;  // keys the tile's last token sees
+  const int kend = p0 + min(t_first * TQ + TQ, nq);  // keys the wave's last token sees
   const int nch = (kend + 31) >> 5;
 
   const int r16 = lane & 15, grp = lane >> 4;
-  // Column r16: token tile*TQ + r16/G, head r16%G of group g.  Columns past
-  // TQ*G or past the last new token repeat the tile's last real column and
-  // store nothing.
+  // Column r16 of tile t: token t*TQ + r16/G, head r16%G of group g.
+  // Columns past TQ*G or past the last new token, and tiles before the
+  // first, repeat a real column and store nothing.
   const int cc = min(r16, TQ * G - 1);
-  const int tcol = min(tile * TQ + cc / G, tlast);
-  const bool store_col = r16 < TQ * G && tile * TQ + r16 / G <= tlast;
-  const int pos = p0 + tcol;  // the column's causal limit (inclusive)
-  const size_t qrow = ((size_t)(q0 + tcol) * P.Hq + (size_t)g * G + cc % G);
+  int pos[CT];
+  bool store_col[CT];
+  size_t qrow[CT];
+#pragma unroll
+  for (int s = 0; s < CT; ++s) {
+    const int t = t_first - s;
+    const int tt = t < 0 ? t_first : t;
+    const int tlast = min(tt * TQ + TQ, nq) - 1;
+    const int tcol = min(tt * TQ + cc / G, tlast);
+    store_col[s] = t >= 0 && r16 < TQ * G && tt * TQ + r16 / G <= tlast;
+    pos[s] = p0 + tcol;  // the column's causal limit (inclusive)
+    qrow[s] = (size_t)(q0 + tcol) * P.Hq + (size_t)g * G + cc % G;
+  }
 
   const int ksel = r16 >> 3;
   const int ktx = ((r16 >> 2) & 1) * 8 + (r16 & 3);
@@ -99,11 +108,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   const int H = P.H;
 
   // The query slices stay in registers for the whole walk.
-  bf16x8_t qb[NKK];
-  {
-    const uint4 *qr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.q) + qrow * D);
+  bf16x8_t qb[CT][NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qb[kk] = as_bf16x8(qr[kgroup(kk)]);
+  for (int s = 0; s < CT; ++s) {
+    const uint4 *qr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.q) + qrow[s] * D);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qb[s][kk] = as_bf16x8(qr[kgroup(kk)]);
   }
 
   int cj[NB], pa[NB], pb[NB];
@@ -154,10 +164,15 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
     }
   };
 
-  f32x4_t o[NNN];
+  f32x4_t o[CT][NNN];
+  float m[CT], l[CT];
 #pragma unroll
-  for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int s = 0; s < CT; ++s) {
+#pragma unroll
+    for (int nn = 0; nn < NNN; ++nn) o[s][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[s] = -INFINITY;
+    l[s] = 0.f;
+  }
 
   locate(0, 0);
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
@@ -174,7 +189,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   auto step = [&](auto bi) {
     constexpr int I = decltype(bi)::value;
     constexpr int J = (I + NB - 1) % NB;
-    f32x4_t sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t sx[CT], sy[CT];
+#pragma unroll
+    for (int s = 0; s < CT; ++s) sx[s] = sy[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8_t kx, ky;
@@ -186,8 +203,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
         kx = as_bf16x8(ax[I][kk]);
         ky = as_bf16x8(ay[I][kk]);
       }
-      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[kk], sx, 0, 0, 0);
-      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[kk], sy, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < CT; ++s) {
+        sx[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[s][kk], sx[s], 0, 0, 0);
+        sy[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[s][kk], sy[s], 0, 0, 0);
+      }
     }
     if (x + NB - 1 >= nch) same_as(J, I);
     issue(std::integral_constant<int, J>{});
@@ -196,53 +216,52 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
     // end (x >= nch) nothing is counted.
     const bool real = x < nch;
     const int tb = 32 * cj[I] + 16 * vsel + 8 * vhalf;
-    const int lim = real ? pos : -1;
-    float s[8];
+    float ks[8], vs[8];
     if constexpr (I8) {
-      const float ks[8] = {ksc[I][0].x, ksc[I][0].y, ksc[I][0].z, ksc[I][0].w,
-                           ksc[I][1].x, ksc[I][1].y, ksc[I][1].z, ksc[I][1].w};
+      ks[0] = ksc[I][0].x; ks[1] = ksc[I][0].y; ks[2] = ksc[I][0].z; ks[3] = ksc[I][0].w;
+      ks[4] = ksc[I][1].x; ks[5] = ksc[I][1].y; ks[6] = ksc[I][1].z; ks[7] = ksc[I][1].w;
+      vs[0] = vsc[I][0].x; vs[1] = vsc[I][0].y; vs[2] = vsc[I][0].z; vs[3] = vsc[I][0].w;
+      vs[4] = vsc[I][1].x; vs[5] = vsc[I][1].y; vs[6] = vsc[I][1].z; vs[7] = vsc[I][1].w;
+    }
+    bf16x8_t pv[CT];
+#pragma unroll
+    for (int s = 0; s < CT; ++s) {
+      const int lim = real ? pos[s] : -1;
+      float sc[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[r] = (tb + r <= lim) ? sx[r] * ks[r] * P.scale_log2 : -INFINITY;
-        s[4 + r] = (tb + 4 + r <= lim) ? sy[r] * ks[4 + r] * P.scale_log2 : -INFINITY;
+        const float kx = I8 ? ks[r] : 1.f, ky = I8 ? ks[4 + r] : 1.f;
+        sc[r] = (tb + r <= lim) ? sx[s][r] * kx * P.scale_log2 : -INFINITY;
+        sc[4 + r] = (tb + 4 + r <= lim) ? sy[s][r] * ky * P.scale_log2 : -INFINITY;
       }
-    } else {
+      float cmax = sc[0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[r] = (tb + r <= lim) ? sx[r] * P.scale_log2 : -INFINITY;
-        s[4 + r] = (tb + 4 + r <= lim) ? sy[r] * P.scale_log2 : -INFINITY;
+      for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, sc[r]);
+      cmax = rows_max4(cmax);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m[s] + kSlack) != 0, 0)) {
+        const float mnew = fmaxf(m[s], cmax);
+        const float alpha = fast_exp2(m[s] - mnew);
+        m[s] = mnew;
+        l[s] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < NNN; ++nn) o[s][nn] *= alpha;
       }
-    }
-    float cmax = s[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, s[r]);
-    cmax = rows_max4(cmax);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m + kSlack) != 0, 0)) {
-      const float mnew = fmaxf(m, cmax);
-      const float alpha = fast_exp2(m - mnew);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int nn = 0; nn < NNN; ++nn) o[nn] *= alpha;
-    }
-    bf16x8_t pv;
-    float psum = 0.f;
-    if constexpr (I8) {
-      const float vs[8] = {vsc[I][0].x, vsc[I][0].y, vsc[I][0].z, vsc[I][0].w,
-                           vsc[I][1].x, vsc[I][1].y, vsc[I][1].z, vsc[I][1].w};
+      float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float e = fast_exp2(s[r] - m);
-        psum += e;
-        pv[r] = (__bf16)((tb + r <= lim) ? e * vs[r] : 0.f);  // scales past the context may be NaN
+        if constexpr (I8) {
+          const float e = fast_exp2(sc[r] - m[s]);
+          psum += e;
+          pv[s][r] = (__bf16)((tb + r <= lim) ? e * vs[r] : 0.f);  // scales past the context may be NaN
+        } else {
+          const __bf16 pr = (__bf16)fast_exp2(sc[r] - m[s]);
+          pv[s][r] = pr;
+          psum += (float)pr;
+        }
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const __bf16 pr = (__bf16)fast_exp2(s[r] - m);
-        pv[r] = pr;
-        psum += (float)pr;
-      }
+      l[s] += psum;
+    }
+    if constexpr (!I8) {
       // Keys at or past the walk's end may be unwritten (NaN); a zero weight
       // alone would not cancel them.
       const int nvalid = real ? min(max(kend - tb, 0), 8) : 0;
@@ -251,9 +270,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
         for (int nn = 0; nn < NNN; ++nn) va[I][nn] = keep_first(va[I][nn], nvalid);
       }
     }
-    l += psum;
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[I][nn]), pv, o[nn], 0, 0, 0);
+    for (int nn = 0; nn < NNN; ++nn) {
+      const bf16x8_t vop = as_bf16x8(va[I][nn]);
+#pragma unroll
+      for (int s = 0; s < CT; ++s) o[s][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pv[s], o[s][nn], 0, 0, 0);
+    }
     issue_v(std::integral_constant<int, J>{});
     if (x + NB < nch) locate(I, x + NB);
     ++x;
@@ -264,14 +286,17 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
     }(std::make_integer_sequence<int, NB>{});
   }
 
-  const float lsum = rows_sum4(l);
-  if (store_col) {
-    const float inv = 1.f / lsum;
-    float *dst = P.out + qrow * D + 4 * grp;
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn)
-      *reinterpret_cast<float4 *>(dst + 16 * nn) =
-          make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
+  for (int s = 0; s < CT; ++s) {
+    const float lsum = rows_sum4(l[s]);
+    if (store_col[s]) {
+      const float inv = 1.f / lsum;
+      float *dst = P.out + qrow[s] * D + 4 * grp;
+#pragma unroll
+      for (int nn = 0; nn < NNN; ++nn)
+        *reinterpret_cast<float4 *>(dst + 16 * nn) =
+            make_float4(o[s][nn][0] * inv, o[s][nn][1] * inv, o[s][nn][2] * inv, o[s][nn][3] * inv);
+    }
   }
 }
 
@@ -282,12 +307,20 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
 #define PKV_PREFILL_NBUF_I8 4
 #endif
 
+// Column tiles (16 query columns each) per wave: the K and V operands of a
+// chunk serve all of them, so each byte read from L2 feeds CT x the math.
+#ifndef PKV_PREFILL_CT
+#define PKV_PREFILL_CT 2
+#endif
+
 template <int D, bool I8>
 int launch(const pkv_prefill_args &a, const PrefillParams &p) {
-  auto kern = prefill_mfma_kernel<D, I8 ? PKV_PREFILL_NBUF_I8 : PKV_PREFILL_NBUF, I8>;
+  constexpr int CT = PKV_PREFILL_CT;
+  auto kern = prefill_mfma_kernel<D, I8 ? PKV_PREFILL_NBUF_I8 : PKV_PREFILL_NBUF, I8, CT>;
   const int tq = 16 / p.G;
   const int tiles = (a.max_query_len + tq - 1) / tq;
-  const dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)p.H, (unsigned)a.num_seqs);
+  const int waves = (tiles + CT - 1) / CT;
+  const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)p.H, (unsigned)a.num_seqs);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   return (int)hipGetLastError();
 }
