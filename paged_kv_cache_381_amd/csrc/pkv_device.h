@@ -64,6 +64,15 @@ __device__ __forceinline__ float rows_max4(float x) {
   return x;
 }
 
+// The same across the four rows with the gfx950 lane swaps: the 32-lane swap
+// pairs lane l with l ^ 32, the 16-lane swap row r with row r ^ 1; no LDS.
+__device__ __forceinline__ float rows_max4_swap(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------

@@ -79,6 +79,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   const int kend = p0 + min(t_first * TQ + TQ, nq);  // keys the wave's last token sees
   const int nch = (kend + 31) >> 5;
 
+  // The earliest column's causal limit: chunks up to it are open to all.
+  const int pos_min = p0 + max(t_first - CT + 1, 0) * TQ;
+
   const int r16 = lane & 15, grp = lane >> 4;
   // Column r16 of tile t: token t*TQ + r16/G, head r16%G of group g.
   // Columns past TQ*G or past the last new token, and tiles before the
@@ -224,8 +227,38 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
       vs[4] = vsc[I][1].x; vs[5] = vsc[I][1].y; vs[6] = vsc[I][1].z; vs[7] = vsc[I][1].w;
     }
     bf16x8_t pv[CT];
+    // A chunk below every column's causal limit needs no mask (most chunks of
+    // a long prefix): the running maximum is taken on raw scores (scale > 0)
+    // and each weight is one fma and one exp2.
+    const bool open = !I8 && real && 32 * cj[I] + 31 <= pos_min && P.scale_log2 > 0.f;
+    if (open) {
 #pragma unroll
-    for (int s = 0; s < CT; ++s) {
+      for (int s = 0; s < CT; ++s) {
+        float cmax = fmaxf(fmaxf(sx[s][0], sx[s][1]), fmaxf(sx[s][2], sx[s][3]));
+        cmax = fmaxf(cmax, fmaxf(fmaxf(sy[s][0], sy[s][1]), fmaxf(sy[s][2], sy[s][3])));
+        cmax = rows_max4_swap(cmax) * P.scale_log2;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m[s] + kSlack) != 0, 0)) {
+          const float mnew = fmaxf(m[s], cmax);
+          const float alpha = fast_exp2(m[s] - mnew);
+          m[s] = mnew;
+          l[s] *= alpha;
+#pragma unroll
+          for (int nn = 0; nn < NNN; ++nn) o[s][nn] *= alpha;
+        }
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const __bf16 px = (__bf16)fast_exp2(__builtin_fmaf(sx[s][r], P.scale_log2, -m[s]));
+          const __bf16 py = (__bf16)fast_exp2(__builtin_fmaf(sy[s][r], P.scale_log2, -m[s]));
+          pv[s][r] = px;
+          pv[s][4 + r] = py;
+          psum += (float)px + (float)py;
+        }
+        l[s] += psum;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < CT && !open; ++s) {
       const int lim = real ? pos[s] : -1;
       float sc[8];
 #pragma unroll
@@ -237,7 +270,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
       float cmax = sc[0];
 #pragma unroll
       for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, sc[r]);
-      cmax = rows_max4(cmax);
+      cmax = rows_max4_swap(cmax);
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m[s] + kSlack) != 0, 0)) {
         const float mnew = fmaxf(m[s], cmax);
         const float alpha = fast_exp2(m[s] - mnew);
