@@ -276,7 +276,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     float cmax = s[0];
 #pragma unroll
     for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, s[r]);
-    cmax = rows_max4(cmax);
+    cmax = rows_max4_swap(cmax);
     // The reference maximum moves only when some head's scores pass it by
     // more than kSlack (base 2), and then for the whole wave at once: weights
     // stay below 2^kSlack, and most chunks skip rescaling the accumulators.
