@@ -9,18 +9,29 @@
 // 0 .. p_b + t -- the cached prefix and the new tokens up to itself.
 //
 // gfx950 mapping.  The decode kernel's contractions are reused with the
-// padding gone: a wave takes 16 query columns, TQ = 16 / G consecutive new
-// tokens times the G query heads of one kv head g, so every column of
+// padding gone: a column tile is 16 query columns, TQ = 16 / G consecutive
+// new tokens times the G query heads of one kv head g, so every column of
 //   S^T[32 keys x 16 columns] = K[32 x D] . Q^T[D x 16]
 //   O^T[D x 16 columns]      += V^T[D x 32] . P^T[32 x 16]
 // is a real query row.  The operand layouts, the lane holding 8 keys of one
 // column between the two products and the online softmax per column are the
 // decode kernel's; the causal limit differs per column and masks scores per
-// lane.  A wave walks keys 0 .. its last token's position in 32-key chunks
-// (two blocks through the table), with NB chunks of K/V in registers, every
-// load issued on every path so that the memory-counter waits stay exact.
-// Tiles of one (sequence, kv head) that run longest (the last tokens) are
-// dispatched first.
+// lane.  A wave takes CT column tiles (the K and V operands of each chunk
+// serve all of them) and walks keys 0 .. its last token's position in
+// 32-key chunks (two blocks through the table), with a ring of NB chunks of
+// K/V in registers, every load issued on every path so that the
+// memory-counter waits stay exact.  Tiles of one (sequence, kv head) that
+// run longest (the last tokens) are dispatched first.
+//
+// Per chunk the wave forms the next chunk's scores while it weighs this
+// one's, so the matrix products and the exponentials of one step are
+// independent.  Weights are checked after the fact: a weight above 2^8 (an
+// overflow against a stale running maximum) sends the wave down a rare path
+// that moves the maximum, rescales and weighs again; bf16 weights are
+// non-negative, so the check is an integer maximum of their bit patterns.
+// Chunks below every column's causal limit skip masking entirely.  bf16 row
+// sums come from the matrix cores (a ones operand against the rounded
+// weights).
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -56,6 +67,21 @@ __device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
 
 constexpr float kSlack = 8.0f;  // headroom of the running maximum (base 2)
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Eight floats rounded to bf16 (nearest even), two per conversion.
+__device__ __forceinline__ bf16x8_t pack_bf16x8(const float (&e)[8]) {
+  uint4 u;
+  u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{e[0], e[1]}, bf16x2_t));
+  u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{e[2], e[3]}, bf16x2_t));
+  u.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{e[4], e[5]}, bf16x2_t));
+  u.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{e[6], e[7]}, bf16x2_t));
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 template <int D, int NB, bool I8, int CT>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   constexpr int NKK = D / 32;
@@ -64,7 +90,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   constexpr int NKU = I8 ? NKK / 2 : NKK;
   using VUnit = std::conditional_t<I8, uint2, uint4>;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: the walk's bounds live in SGPRs
   const int b = blockIdx.z, g = blockIdx.y;
   const int G = P.G, TQ = 16 / G;
   const int q0 = sload_i32(P.qstart + b);
@@ -79,8 +106,14 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   const int kend = p0 + min(t_first * TQ + TQ, nq);  // keys the wave's last token sees
   const int nch = (kend + 31) >> 5;
 
-  // The earliest column's causal limit: chunks up to it are open to all.
+  // Scores stay unscaled (the scale joins the exponent's fma) unless the
+  // scale is not positive or int8 keys carry their own scales.
+  const bool raw = !I8 && P.scale_log2 > 0.f;
+  const float mul = raw ? P.scale_log2 : 1.f;
+  // The earliest column's causal limit: chunks up to it are open to all
+  // columns and need no mask.  The open walk ends on a ring boundary.
   const int pos_min = p0 + max(t_first - CT + 1, 0) * TQ;
+  const int c_open = raw ? min((pos_min + 1) >> 5, nch) / NB * NB : 0;
 
   const int r16 = lane & 15, grp = lane >> 4;
   // Column r16 of tile t: token t*TQ + r16/G, head r16%G of group g.
@@ -119,80 +152,57 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
     for (int kk = 0; kk < NKK; ++kk) qb[s][kk] = as_bf16x8(qr[kgroup(kk)]);
   }
 
-  int cj[NB], pa[NB], pb[NB];
+  // Chunk y lives in ring slot y % NB of the K ring and of the V ring.  Its
+  // K is requested NB steps before its scores are formed (one step before
+  // its weights are applied), its V -- with the int8 scales of K and V -- NB
+  // steps before the V product.  Chunks past the walk's end re-read its
+  // last chunk: every load is issued on every path, and what they bring is
+  // masked.
+  int ka[NB], kb[NB], va_blk[NB], vb_blk[NB];
   uint4 ax[NB][NKU], ay[NB][NKU];
   VUnit va[NB][NNN];
   float4 ksc[NB][2], vsc[NB][2];
 
-  auto locate = [&](int i, int c) {
-    cj[i] = c;
-    pa[i] = clamp_block(sload_i32(trow + 2 * c), P.num_blocks);
+  auto locate = [&](int &pa, int &pb, int y) {
+    const int c = min(y, nch - 1);
+    pa = clamp_block(sload_i32(trow + 2 * c), P.num_blocks);
     const int b2 = clamp_block(sload_i32(trow + min(2 * c + 1, P.max_blocks - 1)), P.num_blocks);
-    pb[i] = 32 * c + 16 < kend ? b2 : pa[i];
+    pb = 32 * c + 16 < kend ? b2 : pa;
   };
-  auto same_as = [&](int to, int from) {
-    cj[to] = cj[from];
-    pa[to] = pa[from];
-    pb[to] = pb[from];
-  };
-  auto issue = [&](auto bi) {
+  auto issue_k = [&](auto bi, int y) {
     constexpr int I = decltype(bi)::value;
-    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + g) * TB);
+    locate(ka[I], kb[I], y);
+    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? kb[I] : ka[I]) * H + g) * TB);
 #pragma unroll
     for (int ku = 0; ku < NKU; ++ku) {
       const int cu = 4 * ku + grp;
       ax[I][ku] = kt[cu * 16 + ktx];
       ay[I][ku] = kt[cu * 16 + ktx + 4];
     }
-    if constexpr (I8) {
-      const float4 *sc = reinterpret_cast<const float4 *>(kpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + g) * TB +
-                                                          16 * D + 32 * vhalf);
-      ksc[I][0] = sc[0];
-      ksc[I][1] = sc[1];
-    }
   };
-  auto issue_v = [&](auto bi) {
+  auto issue_v = [&](auto bi, int y) {
     constexpr int I = decltype(bi)::value;
-    const uint8_t *vt = vpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + g) * TB;
+    locate(va_blk[I], vb_blk[I], y);
+    const size_t tile = ((size_t)(vsel ? vb_blk[I] : va_blk[I]) * H + g) * TB;
+    const uint8_t *vt = vpool + tile;
     if constexpr (I8) {
 #pragma unroll
       for (int nn = 0; nn < NNN; ++nn) va[I][nn] = *reinterpret_cast<const uint2 *>(vt + (16 * nn + r16) * 16 + 8 * vhalf);
-      const float4 *sc = reinterpret_cast<const float4 *>(vt + 16 * D + 32 * vhalf);
-      vsc[I][0] = sc[0];
-      vsc[I][1] = sc[1];
+      const float4 *kq = reinterpret_cast<const float4 *>(kpool + tile + 16 * D + 32 * vhalf);
+      const float4 *vq = reinterpret_cast<const float4 *>(vt + 16 * D + 32 * vhalf);
+      ksc[I][0] = kq[0];
+      ksc[I][1] = kq[1];
+      vsc[I][0] = vq[0];
+      vsc[I][1] = vq[1];
     } else {
       const uint4 *u = reinterpret_cast<const uint4 *>(vt);
 #pragma unroll
       for (int nn = 0; nn < NNN; ++nn) va[I][nn] = u[2 * (16 * nn + r16) + vhalf];
     }
   };
-
-  f32x4_t o[CT][NNN];
-  float m[CT], l[CT];
-#pragma unroll
-  for (int s = 0; s < CT; ++s) {
-#pragma unroll
-    for (int nn = 0; nn < NNN; ++nn) o[s][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m[s] = -INFINITY;
-    l[s] = 0.f;
-  }
-
-  locate(0, 0);
-  [&]<int... Is>(std::integer_sequence<int, Is...>) {
-    ((Is == 0 ? (void)0 : (Is < nch ? locate(Is, Is) : same_as(Is, Is - 1))), ...);
-  }(std::make_integer_sequence<int, NB>{});
-  [&]<int... Is>(std::integer_sequence<int, Is...>) {
-    ((Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0),
-                     issue_v(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0))
-                  : (void)0),
-     ...);
-  }(std::make_integer_sequence<int, NB>{});
-
-  int x = 0;
-  auto step = [&](auto bi) {
+  // Scores of the chunk whose K sits in slot I: 32 keys x 16 columns.
+  auto scores = [&](auto bi, f32x4_t (&sx)[CT], f32x4_t (&sy)[CT]) {
     constexpr int I = decltype(bi)::value;
-    constexpr int J = (I + NB - 1) % NB;
-    f32x4_t sx[CT], sy[CT];
 #pragma unroll
     for (int s = 0; s < CT; ++s) sx[s] = sy[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -212,13 +222,45 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
         sy[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[s][kk], sy[s], 0, 0, 0);
       }
     }
-    if (x + NB - 1 >= nch) same_as(J, I);
-    issue(std::integral_constant<int, J>{});
+  };
 
-    // Keys of this lane: 8 consecutive positions from tb.  Past the walk's
-    // end (x >= nch) nothing is counted.
-    const bool real = x < nch;
-    const int tb = 32 * cj[I] + 16 * vsel + 8 * vhalf;
+  f32x4_t o[CT][NNN];
+  float m[CT];
+  // Row sums: bf16 weights are summed on the matrix cores (a ones operand
+  // against the same rounded weights the V product uses, so the sum lands
+  // in every row of the column); int8 weights carry V's scale, so their
+  // plain exponentials are summed per lane.
+  f32x4_t lacc[CT];
+  float l[CT];
+#pragma unroll
+  for (int s = 0; s < CT; ++s) {
+#pragma unroll
+    for (int nn = 0; nn < NNN; ++nn) o[s][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[s] = -INFINITY;
+    lacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    l[s] = 0.f;
+  }
+  bf16x8_t ones;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) ones[r] = (__bf16)1.0f;
+
+  f32x4_t sx[CT], sy[CT];  // scores of the chunk being weighted
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((issue_k(std::integral_constant<int, Is>{}, Is), __builtin_amdgcn_sched_barrier(0),
+      issue_v(std::integral_constant<int, Is>{}, Is), __builtin_amdgcn_sched_barrier(0)),
+     ...);
+  }(std::make_integer_sequence<int, NB>{});
+  scores(std::integral_constant<int, 0>{}, sx, sy);
+  issue_k(std::integral_constant<int, 0>{}, NB);
+
+  int x = 0;
+  // One chunk: weights of chunk x from its scores (sx, sy), the scores of
+  // chunk x+1, the V product of chunk x, and the next requests.
+  auto step = [&](auto bi, auto open_c) {
+    constexpr int I = decltype(bi)::value;
+    constexpr int J = (I + 1) % NB;
+    constexpr bool OPEN = decltype(open_c)::value;
+    const int tb = 32 * x + 16 * vsel + 8 * vhalf;  // this lane's 8 keys: tb .. tb+7
     float ks[8], vs[8];
     if constexpr (I8) {
       ks[0] = ksc[I][0].x; ks[1] = ksc[I][0].y; ks[2] = ksc[I][0].z; ks[3] = ksc[I][0].w;
@@ -226,82 +268,106 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
       vs[0] = vsc[I][0].x; vs[1] = vsc[I][0].y; vs[2] = vsc[I][0].z; vs[3] = vsc[I][0].w;
       vs[4] = vsc[I][1].x; vs[5] = vsc[I][1].y; vs[6] = vsc[I][1].z; vs[7] = vsc[I][1].w;
     }
-    bf16x8_t pv[CT];
-    // A chunk below every column's causal limit needs no mask (most chunks of
-    // a long prefix): the running maximum is taken on raw scores (scale > 0)
-    // and each weight is one fma and one exp2.
-    const bool open = !I8 && real && 32 * cj[I] + 31 <= pos_min && P.scale_log2 > 0.f;
-    if (open) {
+    int lim[CT];
+    if constexpr (!OPEN) {
+      // Past each column's causal limit (and past the walk's end) a score
+      // is -inf; without the raw form, scores take their scales here.
+      const bool real = x < nch;
 #pragma unroll
       for (int s = 0; s < CT; ++s) {
-        float cmax = fmaxf(fmaxf(sx[s][0], sx[s][1]), fmaxf(sx[s][2], sx[s][3]));
-        cmax = fmaxf(cmax, fmaxf(fmaxf(sy[s][0], sy[s][1]), fmaxf(sy[s][2], sy[s][3])));
-        cmax = rows_max4_swap(cmax) * P.scale_log2;
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m[s] + kSlack) != 0, 0)) {
-          const float mnew = fmaxf(m[s], cmax);
-          const float alpha = fast_exp2(m[s] - mnew);
-          m[s] = mnew;
-          l[s] *= alpha;
-#pragma unroll
-          for (int nn = 0; nn < NNN; ++nn) o[s][nn] *= alpha;
-        }
-        float psum = 0.f;
+        lim[s] = real ? pos[s] : -1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const __bf16 px = (__bf16)fast_exp2(__builtin_fmaf(sx[s][r], P.scale_log2, -m[s]));
-          const __bf16 py = (__bf16)fast_exp2(__builtin_fmaf(sy[s][r], P.scale_log2, -m[s]));
-          pv[s][r] = px;
-          pv[s][4 + r] = py;
-          psum += (float)px + (float)py;
+          const float kx = I8 ? ks[r] : 1.f, ky = I8 ? ks[4 + r] : 1.f;
+          const float fx = raw ? 1.f : kx * P.scale_log2, fy = raw ? 1.f : ky * P.scale_log2;
+          sx[s][r] = (tb + r <= lim[s]) ? sx[s][r] * fx : -INFINITY;
+          sy[s][r] = (tb + 4 + r <= lim[s]) ? sy[s][r] * fy : -INFINITY;
         }
-        l[s] += psum;
+      }
+      if constexpr (!I8) {
+        // Keys at or past the walk's end may be unwritten (NaN); a zero
+        // weight alone would not cancel them.
+        const int nvalid = real ? min(max(kend - tb, 0), 8) : 0;
+        if (nvalid < 8) {
+#pragma unroll
+          for (int nn = 0; nn < NNN; ++nn) va[I][nn] = keep_first(va[I][nn], nvalid);
+        }
       }
     }
+
+    // Weights against the running maximum; int8 weights take V's scale.
+    bf16x8_t pv[CT];
+    float psum[CT];
+    auto weigh = [&]() {
 #pragma unroll
-    for (int s = 0; s < CT && !open; ++s) {
-      const int lim = real ? pos[s] : -1;
-      float sc[8];
+      for (int s = 0; s < CT; ++s) {
+        psum[s] = 0.f;
+        float e[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float kx = I8 ? ks[r] : 1.f, ky = I8 ? ks[4 + r] : 1.f;
-        sc[r] = (tb + r <= lim) ? sx[s][r] * kx * P.scale_log2 : -INFINITY;
-        sc[4 + r] = (tb + 4 + r <= lim) ? sy[s][r] * ky * P.scale_log2 : -INFINITY;
+        for (int r = 0; r < 8; ++r) {
+          const float sc = r < 4 ? sx[s][r] : sy[s][r - 4];
+          e[r] = fast_exp2(__builtin_fmaf(sc, mul, -m[s]));
+          if constexpr (I8) {
+            psum[s] += e[r];
+            e[r] = (tb + r <= lim[s]) ? e[r] * vs[r] : 0.f;  // scales past the context may be NaN
+          }
+        }
+        pv[s] = pack_bf16x8(e);
       }
-      float cmax = sc[0];
+    };
+    weigh();
+    f32x4_t nx[CT], ny[CT];
+    scores(std::integral_constant<int, J>{}, nx, ny);
+    issue_k(std::integral_constant<int, J>{}, x + 1 + NB);
+
+    // A weight above 2^kSlack (or inf / NaN against the -inf start) means
+    // the running maximum must move: rare after the first chunk.  bf16
+    // weights are non-negative, so their bit patterns order as integers.
+    bool over;
+    if constexpr (I8) {
+      float emax = 0.f;
 #pragma unroll
-      for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, sc[r]);
-      cmax = rows_max4_swap(cmax);
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(cmax > m[s] + kSlack) != 0, 0)) {
+      for (int s = 0; s < CT; ++s) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float sc = r < 4 ? sx[s][r] : sy[s][r - 4];
+          emax = fmaxf(emax, sc * mul - m[s]);
+        }
+      }
+      over = !(emax <= kSlack);
+    } else {
+      u16x2_t mx = u16x2_t{0, 0};
+#pragma unroll
+      for (int s = 0; s < CT; ++s) {
+        const u16x8_t u = __builtin_bit_cast(u16x8_t, pv[s]);
+        mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(__builtin_elementwise_max(u.s01, u.s23),
+                                                                      __builtin_elementwise_max(u.s45, u.s67)));
+      }
+      over = max((unsigned)mx.x, (unsigned)mx.y) > 0x4380u;  // bf16 of 2^kSlack = 256
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) {
+#pragma unroll
+      for (int s = 0; s < CT; ++s) {
+        float cmax = fmaxf(fmaxf(fmaxf(sx[s][0], sx[s][1]), fmaxf(sx[s][2], sx[s][3])),
+                           fmaxf(fmaxf(sy[s][0], sy[s][1]), fmaxf(sy[s][2], sy[s][3])));
+        cmax = rows_max4_swap(cmax) * mul;
         const float mnew = fmaxf(m[s], cmax);
         const float alpha = fast_exp2(m[s] - mnew);
         m[s] = mnew;
         l[s] *= alpha;
+        lacc[s] *= alpha;
 #pragma unroll
         for (int nn = 0; nn < NNN; ++nn) o[s][nn] *= alpha;
       }
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        if constexpr (I8) {
-          const float e = fast_exp2(sc[r] - m[s]);
-          psum += e;
-          pv[s][r] = (__bf16)((tb + r <= lim) ? e * vs[r] : 0.f);  // scales past the context may be NaN
-        } else {
-          const __bf16 pr = (__bf16)fast_exp2(sc[r] - m[s]);
-          pv[s][r] = pr;
-          psum += (float)pr;
-        }
-      }
-      l[s] += psum;
+      weigh();
     }
-    if constexpr (!I8) {
-      // Keys at or past the walk's end may be unwritten (NaN); a zero weight
-      // alone would not cancel them.
-      const int nvalid = real ? min(max(kend - tb, 0), 8) : 0;
-      if (nvalid < 8) {
+
 #pragma unroll
-        for (int nn = 0; nn < NNN; ++nn) va[I][nn] = keep_first(va[I][nn], nvalid);
-      }
+    for (int s = 0; s < CT; ++s) {
+      if constexpr (I8)
+        l[s] += psum[s];
+      else
+        lacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pv[s], lacc[s], 0, 0, 0);
     }
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) {
@@ -309,19 +375,28 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
 #pragma unroll
       for (int s = 0; s < CT; ++s) o[s][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pv[s], o[s][nn], 0, 0, 0);
     }
-    issue_v(std::integral_constant<int, J>{});
-    if (x + NB < nch) locate(I, x + NB);
+    issue_v(std::integral_constant<int, I>{}, x + NB);
+#pragma unroll
+    for (int s = 0; s < CT; ++s) {
+      sx[s] = nx[s];
+      sy[s] = ny[s];
+    }
     ++x;
   };
+  while (x < c_open) {
+    [&]<int... Is>(std::integer_sequence<int, Is...>) {
+      (step(std::integral_constant<int, Is>{}, std::true_type{}), ...);
+    }(std::make_integer_sequence<int, NB>{});
+  }
   while (x < nch) {
     [&]<int... Is>(std::integer_sequence<int, Is...>) {
-      (step(std::integral_constant<int, Is>{}), ...);
+      (step(std::integral_constant<int, Is>{}, std::false_type{}), ...);
     }(std::make_integer_sequence<int, NB>{});
   }
 
 #pragma unroll
   for (int s = 0; s < CT; ++s) {
-    const float lsum = rows_sum4(l[s]);
+    const float lsum = I8 ? rows_sum4(l[s]) : lacc[s][0];
     if (store_col[s]) {
       const float inv = 1.f / lsum;
       float *dst = P.out + qrow[s] * D + 4 * grp;
@@ -333,22 +408,44 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   }
 }
 
+// Workgroup-shared walk: the four waves of a workgroup take consecutive tile
+// groups of one (sequence, kv head) and walk the same keys, so each chunk's
+// K and V (two blocks each) is read from memory once per workgroup, staged
+// through registers into LDS (256 threads, 16 bytes a thread a pass), and
+// every wave takes its matrix operands from there: a quarter of the vector
+// memory traffic of waves walking alone, which is what bounds them.  Chunk
+// x+1's K and chunk x's V sit in LDS while step x runs; chunk x+2's K and
+// chunk x+1's V are requested at its start and stored at its end, before
+// the one barrier of the step.  All waves run to the longest wave's last
+// chunk (its columns' causal limits mask the rest).  LDS placement keeps
+// the operand reads free of bank conflicts (any 8 or 16 lanes of a read
+// touch distinct 16-byte slots of a 128- or 256-byte bank row): within each
+// 16-unit K row, units 8..15 trade the bit 4 of their slot (8..11 <-> 12..15),
+// block b's K tile starts 128 bytes further, and a V row's two halves swap
+// places on rows where bit 2 xor bit 3 of the row index is set (bf16), or
+// on rows 8..15 of each 16 (int8).
+// Ring depth (chunks of K/V requested ahead) and column tiles per wave (16
+// query columns each: the K and V operands of a chunk serve all of them, so
+// each byte brought through the vector memory path feeds CT x the math).
+// bf16 takes a deeper ring and three tiles (one wave per SIMD); int8, whose
+// operands are half the bytes, two tiles and a single ring slot (two waves
+// per SIMD).
 #ifndef PKV_PREFILL_NBUF
 #define PKV_PREFILL_NBUF 2
 #endif
-#ifndef PKV_PREFILL_NBUF_I8
-#define PKV_PREFILL_NBUF_I8 4
-#endif
-
-// Column tiles (16 query columns each) per wave: the K and V operands of a
-// chunk serve all of them, so each byte read from L2 feeds CT x the math.
 #ifndef PKV_PREFILL_CT
-#define PKV_PREFILL_CT 2
+#define PKV_PREFILL_CT 3
+#endif
+#ifndef PKV_PREFILL_NBUF_I8
+#define PKV_PREFILL_NBUF_I8 1
+#endif
+#ifndef PKV_PREFILL_CT_I8
+#define PKV_PREFILL_CT_I8 2
 #endif
 
 template <int D, bool I8>
 int launch(const pkv_prefill_args &a, const PrefillParams &p) {
-  constexpr int CT = PKV_PREFILL_CT;
+  constexpr int CT = I8 ? PKV_PREFILL_CT_I8 : PKV_PREFILL_CT;
   auto kern = prefill_mfma_kernel<D, I8 ? PKV_PREFILL_NBUF_I8 : PKV_PREFILL_NBUF, I8, CT>;
   const int tq = 16 / p.G;
   const int tiles = (a.max_query_len + tq - 1) / tq;
