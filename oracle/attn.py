@@ -74,6 +74,11 @@ def append(dtype, num_kv_heads, head_dim, kpool, vpool, k_new, v_new, slots):
     v_new = np.ascontiguousarray(v_new, dtype=_NP[ROW[dtype]])
     slots = np.ascontiguousarray(slots, dtype=np.int64)
     assert k_new.shape == v_new.shape == (slots.size, num_kv_heads, head_dim)
+    # A negative slot is skipped; one past the pool is outside the definition
+    # (the C routine has no pool size and would write past the array).
+    per_block = num_kv_heads * (tile_bytes_int8(head_dim) if dtype == "int8" else BLOCK_SIZE * head_dim)
+    if slots.size and slots.max() >= kpool.size // per_block * BLOCK_SIZE:
+        raise ValueError("slot past the end of the pool")
     lib().orc_append(_DT[dtype], num_kv_heads, head_dim, _p(kpool), _p(vpool), _p(k_new), _p(v_new),
                      _p(slots), slots.size)
 

@@ -45,6 +45,96 @@ __global__ __launch_bounds__(256) void append_kernel(E *__restrict__ kpool, E *_
   }
 }
 
+// Bulk appends (a prompt's tokens): workgroup j takes input tokens
+// [16j, 16j + 16).  A run is 16 input tokens whose slots fill one block in
+// order (the first slot a multiple of 16, each next one more); at most one run
+// starts in a workgroup's range, and that workgroup writes it a block at a
+// time: the 16 tokens' K units of one row group land in one contiguous
+// 16-unit stretch of the tile, and a thread gathers the 16 tokens' elements
+// of one (head, d) into that block's V row (contiguous in the [d][16 tokens]
+// layout) and stores it whole -- instead of 16 scattered element stores per
+// row.  Tokens of the range that belong to no run are stored one by one as in
+// append_kernel; tokens of a run that started in the previous range belong to
+// that range's workgroup.  The bytes written are the same either way.
+template <typename E>
+__global__ __launch_bounds__(256) void append_runs_kernel(E *__restrict__ kpool, E *__restrict__ vpool,
+                                                          const E *__restrict__ k_new, const E *__restrict__ v_new,
+                                                          const int64_t *__restrict__ slots, int T, int H, int D,
+                                                          int num_blocks) {
+  constexpr int X = 16 / sizeof(E);
+  const int cpr = D / X;  // 16-byte units per head row
+  const int units = H * cpr;
+  const int64_t nslots = (int64_t)num_blocks * 16;
+  const int i0 = blockIdx.x * 16;
+  const int tid = threadIdx.x;
+  __shared__ int64_t s_slot[48];  // input tokens i0 - 16 .. i0 + 31 (-1: none or invalid)
+  __shared__ bool s_start[32];    // run starts among input tokens i0 - 16 .. i0 + 15
+  if (tid < 48) {
+    const int i = i0 - 16 + tid;
+    int64_t v = -1;
+    if (i >= 0 && i < T) {
+      v = slots[i];
+      if (v < 0 || v >= nslots) v = -1;
+    }
+    s_slot[tid] = v;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    const int64_t a = s_slot[tid];
+    bool run = a >= 0 && (a & 15) == 0;
+    for (int k = 1; k < 16 && run; ++k) run = s_slot[tid + k] == a + k;
+    s_start[tid] = run;
+  }
+  __syncthreads();
+  int r = -1;  // the run starting in this range, as an index into s_slot
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    if (s_start[16 + t]) r = 16 + t;
+
+  if (r >= 0) {
+    const int64_t blk = s_slot[r] >> 4;
+    const size_t in0 = (size_t)(i0 - 16 + r) * H * D;  // first token's row
+    for (int idx = tid; idx < 16 * units; idx += blockDim.x) {
+      const int t = idx & 15, hc = idx >> 4;
+      const int h = hc / cpr, c = hc - h * cpr;
+      const uint4 kv = *reinterpret_cast<const uint4 *>(k_new + in0 + (size_t)t * H * D + (size_t)h * D + c * X);
+      *reinterpret_cast<uint4 *>(kpool + ((((size_t)blk * H + h) * cpr + c) * 16 + t) * X) = kv;
+    }
+    for (int idx = tid; idx < H * D; idx += blockDim.x) {
+      E row[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) row[t] = v_new[in0 + (size_t)t * H * D + idx];
+      uint4 *dst = reinterpret_cast<uint4 *>(vpool + ((size_t)blk * H * D + idx) * 16);
+#pragma unroll
+      for (int q = 0; q < 16 * (int)sizeof(E) / 16; ++q) {
+        uint4 u;
+        __builtin_memcpy(&u, reinterpret_cast<const char *>(row) + 16 * q, 16);
+        dst[q] = u;
+      }
+    }
+  }
+  // Tokens of the range outside every run, one unit of K and V at a time.
+  for (int idx = tid; idx < 16 * units; idx += blockDim.x) {
+    const int t = idx / units, i = idx - t * units;
+    const int64_t s = s_slot[16 + t];
+    if (s < 0) continue;
+    const int rs = 16 + t - (int)(s & 15);  // where its run would start
+    if (s_start[rs]) continue;
+    const size_t in = (size_t)(i0 + t) * H * D;
+    const uint4 kv = reinterpret_cast<const uint4 *>(k_new + in)[i];
+    const uint4 vv = reinterpret_cast<const uint4 *>(v_new + in)[i];
+    const int64_t blk = s >> 4;
+    const int off = (int)(s & 15);
+    const int g = i / cpr, c = i - g * cpr;
+    *reinterpret_cast<uint4 *>(kpool + ((((size_t)blk * H + g) * cpr + c) * 16 + off) * X) = kv;
+    E ve[X];
+    __builtin_memcpy(ve, &vv, sizeof vv);
+    E *vdst = vpool + (((size_t)blk * H + g) * D + (size_t)c * X) * 16 + off;
+#pragma unroll
+    for (int e = 0; e < X; ++e) vdst[e * 16] = ve[e];
+  }
+}
+
 // int8 cache.  A group of D/8 lanes quantises one (token, kv head) row of K
 // and one of V; a lane holds 8 consecutive bf16 elements of each.  The row's
 // largest magnitude comes from xor-shuffles inside the group, then every
@@ -153,6 +243,13 @@ int pkv_launch_swap(const pkv_layout *L, void *dst_k, void *dst_v, int32_t dst_b
   return (int)hipGetLastError();
 }
 
+// Appends of at least this many tokens (prompts) take the block-run kernel;
+// a decode step's one token per sequence keeps one workgroup per token.
+#ifndef PKV_BULK_APPEND_TOKENS
+#define PKV_BULK_APPEND_TOKENS 256
+#endif
+constexpr int kBulkTokens = PKV_BULK_APPEND_TOKENS;
+
 int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
                       const int64_t *slots, int32_t num_tokens, void *stream) {
   if (num_tokens == 0) return 0;
@@ -164,6 +261,18 @@ int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const voi
     auto kern = L->head_dim == 128 ? append_int8_kernel<128> : append_int8_kernel<64>;
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (uint8_t *)k_pool, (uint8_t *)v_pool, (const uint16_t *)k_new,
                        (const uint16_t *)v_new, slots, rows, L->num_kv_heads, L->num_blocks);
+    return (int)hipGetLastError();
+  }
+  if (num_tokens >= kBulkTokens) {
+    const dim3 grid((unsigned)((num_tokens + 15) / 16));
+    if (L->kv_dtype == PKV_BF16)
+      hipLaunchKernelGGL(append_runs_kernel<uint16_t>, grid, dim3(256), 0, st, (uint16_t *)k_pool, (uint16_t *)v_pool,
+                         (const uint16_t *)k_new, (const uint16_t *)v_new, slots, num_tokens, L->num_kv_heads,
+                         L->head_dim, L->num_blocks);
+    else
+      hipLaunchKernelGGL(append_runs_kernel<float>, grid, dim3(256), 0, st, (float *)k_pool, (float *)v_pool,
+                         (const float *)k_new, (const float *)v_new, slots, num_tokens, L->num_kv_heads,
+                         L->head_dim, L->num_blocks);
     return (int)hipGetLastError();
   }
   const int units = L->num_kv_heads * L->head_dim * pkv_elem_bytes(L->kv_dtype) / 16;
