@@ -8,7 +8,9 @@ size, context and prompt lengths (including 1 and lengths one either side of
 a block or chunk edge), shared prefixes, partition size, waves per SIMD and
 the kernel choice -- from a fixed seed, so each case is reproducible by its
 index.  Tolerances: 1e-5 for float32 caches, 2e-2 for bf16 and int8.
+PKV_RANDOM_SHAPES=<decode>,<prefill> runs a longer sweep of the same draws.
 """
+import os
 import sys
 
 import numpy as np
@@ -23,6 +25,8 @@ from workloads import prefill as PW
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "int8": 2e-2}
+# Case counts; a longer sweep sets PKV_RANDOM_SHAPES=<decode>,<prefill>.
+N_DECODE, N_PREFILL = (int(x) for x in os.environ.get("PKV_RANDOM_SHAPES", "15,12").split(","))
 EDGE = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65]
 
 
@@ -59,7 +63,7 @@ def decode_case(i):
     return kw, kernel, part, wps
 
 
-@pytest.mark.parametrize("i", range(15))
+@pytest.mark.parametrize("i", range(N_DECODE))
 def test_decode_random_shape(i):
     kw, kernel, part, wps = decode_case(i)
     base = "tiny_fp32" if kw["dtype"] == "f32" else "llama3_8b_b64"
@@ -87,7 +91,7 @@ def prefill_case(i):
     return kw
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(N_PREFILL))
 def test_prefill_random_shape(i):
     kw = prefill_case(i)
     inst = PW.scaled("prefill_8b_b4", **kw).instantiate()
