@@ -31,8 +31,10 @@
  *
  * Element types: 0 = float32, 1 = bfloat16 (raw uint16 bits), 2 = int8 with
  * a float32 scale per (token, kv head) [KV Cache 工程学 §15.7 "KV Cache 量化":
- * FP16 -> INT8 halves the cache].  Every element is widened exactly to double
- * before use; an int8 element stands for code * scale.
+ * FP16 -> INT8 halves the cache], 3 = FP8 E4M3 with the same scales (the
+ * other one-byte format the section names).  Every element is widened
+ * exactly to double before use; an int8 or FP8 element stands for
+ * value(code) * scale.
  *
  * int8 pools (a choice of this build): a (block, kv head) tile is
  * 16 * D int8 codes followed by 16 float32 scales (one per token slot),
@@ -44,6 +46,13 @@
  * token's row x[0..D) of one kv head, in float32 as the kernels do it:
  *    amax = max |x_d|, scale = amax / 127, code_d = rint(x_d / scale)
  *    clamped to [-127, 127] (round half to even; all zero when amax = 0).
+ * FP8 pools have the same tiles; the codes are FP8 E4M3 as the OCP 8-bit
+ * floating point format defines it (sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent 0 holds the subnormals m/8 * 2^-6; no
+ * infinities; 448 is the largest finite value, S.1111.111 is NaN):
+ *    amax = max |x_d|, scale = amax / 448, code_d = the E4M3 value nearest to
+ *    x_d / scale (ties to the even mantissa), saturated at 448, the sign kept
+ *    (so -0 codes as 0x80); all zero when amax = 0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,8 +71,36 @@ static double elem(const void *base, size_t i, int dtype) {
 
 static size_t esize(int dtype) { return dtype == 0 ? 4 : dtype == 1 ? 2 : 1; }
 
+/* One-byte codes with a float32 scale per (token, kv head): int8 or FP8. */
+static int is_q8(int dtype) { return dtype == 2 || dtype == 3; }
+
 /* Element type of queries and of the rows given to append. */
-static int row_type(int dtype) { return dtype == 2 ? 1 : dtype; }
+static int row_type(int dtype) { return is_q8(dtype) ? 1 : dtype; }
+
+/* Value of an FP8 E4M3 code (the OCP definition). */
+static double e4m3_value(unsigned char c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  return (c & 0x80) ? -v : v;
+}
+
+/* The E4M3 code of the value nearest to y (ties to the even mantissa),
+ * saturated at 448; y is finite. */
+static unsigned char e4m3_code(float y) {
+  unsigned char s = signbit(y) ? 0x80 : 0;
+  double a = fabs((double)y);
+  if (a >= 448.0) return s | 0x7E;
+  if (a < ldexp(1.0, -6)) return s | (unsigned char)nearbyint(a * 512.0); /* multiples of 2^-9; 8 is 2^-6 */
+  int e;
+  double f = frexp(a, &e); /* a = (2f) * 2^(e-1), 2f in [1, 2) */
+  double q = nearbyint((2.0 * f - 1.0) * 8.0);
+  int E = e - 1 + 7;
+  if (q == 8.0) {
+    q = 0.0;
+    E += 1;
+  }
+  return s | (unsigned char)(E << 3) | (unsigned char)q;
+}
 
 /* Bytes of one (block, kv head) tile of an int8 pool. */
 static size_t tile_bytes_i8(int D) { return (size_t)16 * D + 64; }
@@ -77,44 +114,49 @@ static size_t v_at(int64_t blk, int g, int t, int d, int Hkv, int D) {
   return (((size_t)blk * Hkv + g) * (size_t)D + (size_t)d) * BLOCK + (size_t)t;
 }
 
-/* int8 code of K or V element (blk, g, t, d) and the scale of slot t. */
-static double i8_value(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int is_v) {
+/* Value of the int8 or FP8 code of K or V element (blk, g, t, d) times the
+ * scale of slot t. */
+static double i8_value(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int is_v, int dtype) {
   const unsigned char *tile = (const unsigned char *)pool + ((size_t)blk * Hkv + g) * tile_bytes_i8(D);
   size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + t) * 16 + d % 16;
   float sc;
   memcpy(&sc, tile + (size_t)16 * D + 4 * (size_t)t, sizeof sc);
-  return (double)(signed char)tile[at] * (double)sc;
+  double v = dtype == 3 ? e4m3_value(tile[at]) : (double)(signed char)tile[at];
+  return v * (double)sc;
 }
 
 /* Value of K element (blk, g, t, d) of a pool, widened to double. */
 static double kval(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) {
-  if (dtype == 2) return i8_value(pool, blk, g, t, d, Hkv, D, 0);
+  if (is_q8(dtype)) return i8_value(pool, blk, g, t, d, Hkv, D, 0, dtype);
   return elem(pool, k_at(blk, g, t, d, Hkv, D, dtype), dtype);
 }
 static double vval(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) {
-  if (dtype == 2) return i8_value(pool, blk, g, t, d, Hkv, D, 1);
+  if (is_q8(dtype)) return i8_value(pool, blk, g, t, d, Hkv, D, 1, dtype);
   return elem(pool, v_at(blk, g, t, d, Hkv, D), dtype);
 }
 
-/* Quantise one row x[0..D) (bfloat16) into int8 codes at code(d) and its
- * scale, in float32. */
-static void quantise_row(const uint16_t *x, int D, unsigned char *tile, int t, int is_v) {
+/* Quantise one row x[0..D) (bfloat16) into int8 or FP8 codes at code(d) and
+ * its scale, in float32. */
+static void quantise_row(const uint16_t *x, int D, unsigned char *tile, int t, int is_v, int dtype) {
   float amax = 0.0f;
   for (int d = 0; d < D; ++d) {
     float v = (float)elem(x, (size_t)d, 1);
     float a = fabsf(v);
     if (a > amax) amax = a;
   }
-  float scale = amax / 127.0f;
+  float scale = amax / (dtype == 3 ? 448.0f : 127.0f);
   for (int d = 0; d < D; ++d) {
     float v = (float)elem(x, (size_t)d, 1);
-    int q = 0;
-    if (amax > 0.0f) {
+    unsigned char code = 0;
+    if (amax > 0.0f && dtype == 3) {
+      code = e4m3_code(v / scale);
+    } else if (amax > 0.0f) {
       float r = rintf(v / scale);
-      q = r > 127.0f ? 127 : r < -127.0f ? -127 : (int)r;
+      int q = r > 127.0f ? 127 : r < -127.0f ? -127 : (int)r;
+      code = (unsigned char)(signed char)q;
     }
     size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + t) * 16 + d % 16;
-    tile[at] = (unsigned char)(signed char)q;
+    tile[at] = code;
   }
   memcpy(tile + (size_t)16 * D + 4 * (size_t)t, &scale, sizeof scale);
 }
@@ -134,12 +176,12 @@ void orc_append(int dtype, int Hkv, int D, void *kpool, void *vpool, const void 
     if (s < 0) continue;
     int64_t blk = s / BLOCK;
     int off = (int)(s % BLOCK);
-    if (dtype == 2) {
+    if (is_q8(dtype)) {
       for (int g = 0; g < Hkv; ++g) {
         size_t row = ((size_t)t * Hkv + g) * D;
         size_t tile = ((size_t)blk * Hkv + g) * tile_bytes_i8(D);
-        quantise_row((const uint16_t *)k_new + row, D, (unsigned char *)kpool + tile, off, 0);
-        quantise_row((const uint16_t *)v_new + row, D, (unsigned char *)vpool + tile, off, 1);
+        quantise_row((const uint16_t *)k_new + row, D, (unsigned char *)kpool + tile, off, 0, dtype);
+        quantise_row((const uint16_t *)v_new + row, D, (unsigned char *)vpool + tile, off, 1, dtype);
       }
       continue;
     }
@@ -158,7 +200,7 @@ void orc_copy_blocks(int dtype, int Hkv, int D, void *kpool, void *vpool, const 
                      int n) {
   for (int i = 0; i < n; ++i) {
     int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
-    if (dtype == 2) {
+    if (is_q8(dtype)) {
       size_t tb = (size_t)Hkv * tile_bytes_i8(D);
       memcpy((char *)kpool + dst * tb, (const char *)kpool + src * tb, tb);
       memcpy((char *)vpool + dst * tb, (const char *)vpool + src * tb, tb);

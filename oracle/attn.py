@@ -14,11 +14,13 @@ import numpy as np
 from . import build as _build
 from .book import BLOCK_SIZE, build_workload
 
-_DT = {"f32": 0, "bf16": 1, "int8": 2}
-_NP = {"f32": np.float32, "bf16": np.uint16, "int8": np.uint8}
-# Element type of queries and of the rows handed to append: an int8 cache is
-# fed bfloat16 rows and quantises them itself.
-ROW = {"f32": "f32", "bf16": "bf16", "int8": "bf16"}
+_DT = {"f32": 0, "bf16": 1, "int8": 2, "fp8": 3}
+_NP = {"f32": np.float32, "bf16": np.uint16, "int8": np.uint8, "fp8": np.uint8}
+# Element type of queries and of the rows handed to append: an int8 or FP8
+# cache is fed bfloat16 rows and quantises them itself.
+ROW = {"f32": "f32", "bf16": "bf16", "int8": "bf16", "fp8": "bf16"}
+# One-byte caches: codes plus a float32 scale per (token, kv head).
+QUANT = ("int8", "fp8")
 NAN_BITS = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0)}
 
 _lib = None
@@ -57,7 +59,7 @@ def tile_bytes_int8(head_dim: int) -> int:
 def new_pool(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
     """K and V pools filled with a NaN sentinel: slots never written stay NaN
     (for int8, zero codes under a NaN scale)."""
-    if dtype == "int8":
+    if dtype in QUANT:
         tb = tile_bytes_int8(head_dim)
         tiles = np.zeros((num_blocks * num_kv_heads, tb), dtype=np.uint8)
         tiles[:, BLOCK_SIZE * head_dim:] = np.full((tiles.shape[0], BLOCK_SIZE), np.nan,
@@ -76,7 +78,7 @@ def append(dtype, num_kv_heads, head_dim, kpool, vpool, k_new, v_new, slots):
     assert k_new.shape == v_new.shape == (slots.size, num_kv_heads, head_dim)
     # A negative slot is skipped; one past the pool is outside the definition
     # (the C routine has no pool size and would write past the array).
-    per_block = num_kv_heads * (tile_bytes_int8(head_dim) if dtype == "int8" else BLOCK_SIZE * head_dim)
+    per_block = num_kv_heads * (tile_bytes_int8(head_dim) if dtype in QUANT else BLOCK_SIZE * head_dim)
     if slots.size and slots.max() >= kpool.size // per_block * BLOCK_SIZE:
         raise ValueError("slot past the end of the pool")
     lib().orc_append(_DT[dtype], num_kv_heads, head_dim, _p(kpool), _p(vpool), _p(k_new), _p(v_new),

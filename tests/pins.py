@@ -88,6 +88,20 @@ def int8_read(pool, H, D, blk, g, t, is_v):
     return codes, scale
 
 
+def fp8_read(pool, H, D, blk, g, t, is_v):
+    """(values[D], scale) of slot t of tile (blk, g) of an FP8 pool: the same
+    byte layout as an int8 pool, each code decoded by torch's float8_e4m3fn
+    (the OCP E4M3 format) rather than by the oracle."""
+    tb = int8_tile_bytes(D)
+    tile = pool[(blk * H + g) * tb:(blk * H + g + 1) * tb]
+    d = np.arange(D)
+    at = d * 16 + t if is_v else ((d // 16) * 16 + t) * 16 + d % 16
+    codes = np.ascontiguousarray(tile[at])
+    values = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    scale = tile[16 * D + 4 * t:16 * D + 4 * t + 4].view(np.float32)[0]
+    return values, scale, codes
+
+
 def brute_attention(q, K, V, scale):
     """Textbook softmax attention of one query row in pure Python floats
     with exactly rounded sums (math.fsum) and no max subtraction."""
@@ -403,6 +417,149 @@ def check_int8_copy_blocks():
         assert np.array_equal(pool[rest], old[rest])
 
 
+def check_fp8_quant_golden():
+    """Append of hand-worked rows stores the hand-worked E4M3 codes and scale
+    (tests/golden/fp8_quant_example.txt), in both pools."""
+    H, D = 1, 16
+    for label, scale_hex, _, *rest in read_golden("fp8_quant_example.txt"):
+        values = [float(x) for x in rest[:16]]
+        codes = [int(x) for x in rest[17:33]]
+        assert rest[16] == "|" and len(codes) == 16
+        want_scale = np.array([int(scale_hex, 16)], np.uint32).view(np.float32)[0]
+        kpool, vpool = orc.new_pool(2, H, D, "fp8")
+        row = _bf16_bits(values).reshape(1, 1, D)
+        orc.append("fp8", H, D, kpool, vpool, row, row, np.array([16 + 6]))
+        for pool, is_v in ((kpool, False), (vpool, True)):
+            _, sc, got = fp8_read(pool, H, D, 1, 0, 6, is_v)
+            assert got.tolist() == codes, (label, is_v, got.tolist())
+            assert sc.view(np.uint32) == want_scale.view(np.uint32), (label, is_v, sc)
+
+
+def _fp8_pool_with_codes(codes, D):
+    """A one-block FP8 pool (one kv head) whose slot t holds codes[t] under a
+    scale of exactly 1, written byte by byte (K layout in the K pool, V layout
+    in the V pool)."""
+    kpool, vpool = orc.new_pool(1, 1, D, "fp8")
+    for t in range(16):
+        d = np.arange(D)
+        kpool[((d // 16) * 16 + t) * 16 + d % 16] = codes[t]
+        vpool[d * 16 + t] = codes[t]
+        one = np.array([1.0], np.float32).view(np.uint8)
+        kpool[16 * D + 4 * t:16 * D + 4 * t + 4] = one
+        vpool[16 * D + 4 * t:16 * D + 4 * t + 4] = one
+    return kpool, vpool
+
+
+def check_fp8_decode_library():
+    """The oracle's value of every finite E4M3 code equals torch's
+    float8_e4m3fn widening of the same byte (the two NaN codes are never
+    written by append and are left out)."""
+    D = 16
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    want = torch.from_numpy(finite.copy()).view(torch.float8_e4m3fn).double().numpy()
+    for i0 in range(0, finite.size, 16 * D):
+        chunk = np.zeros(16 * D, np.uint8)
+        n = min(16 * D, finite.size - i0)
+        chunk[:n] = finite[i0:i0 + n]
+        codes = chunk.reshape(16, D)
+        kpool, vpool = _fp8_pool_with_codes(codes, D)
+        for t in range(16):
+            k, v = orc.gather_token("fp8", 1, D, kpool, vpool, np.array([0]), t)
+            for got in (k[0], v[0]):
+                for d in range(D):
+                    i = t * D + d
+                    if i < n:
+                        assert got[d] == want[i0 + i], (hex(finite[i0 + i]), got[d], want[i0 + i])
+
+
+def check_fp8_encode_library():
+    """For values of every binade of E4M3, subnormals, exact ties and the
+    largest value, the code append stores equals torch's round-to-nearest-even
+    float8_e4m3fn cast (a row holding 448 has a scale of exactly 1, so each
+    element is encoded as it is)."""
+    H, D = 1, 64
+    rng = np.random.default_rng(1234)
+    vals = []
+    for e in range(-9, 9):
+        vals += list((rng.random(24) + 1.0) * 2.0 ** e)
+    grid = [(k + 0.5) * 2.0 ** -9 for k in range(16)] + [m * 2.0 ** e for e in range(-6, 8)
+                                                         for m in (1.0625, 1.1875, 1.3125, 1.9375)]
+    vals = np.asarray(vals + grid)
+    vals = vals[vals < 448.0] * np.where(rng.random(vals[vals < 448.0].size) < 0.5, -1.0, 1.0)
+    bits = (np.asarray(vals, np.float32).view(np.uint32) + 0x8000) & 0xFFFF0000   # bfloat16-exact
+    vals = bits.view(np.float32)
+    vals = vals[np.abs(vals) < 448.0]
+    rows = []
+    for i0 in range(0, vals.size, D - 1):
+        row = np.zeros(D, np.float32)
+        part = vals[i0:i0 + D - 1]
+        row[:part.size] = part
+        row[D - 1] = 448.0
+        rows.append(row)
+    rows = np.stack(rows)
+    want = torch.from_numpy(rows).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    n = rows.shape[0]
+    kpool, vpool = orc.new_pool((n + 15) // 16, H, D, "fp8")
+    orc.append("fp8", H, D, kpool, vpool, _bf16_bits(rows).reshape(n, 1, D), _bf16_bits(rows).reshape(n, 1, D),
+               np.arange(n))
+    for r in range(n):
+        for pool, is_v in ((kpool, False), (vpool, True)):
+            _, sc, got = fp8_read(pool, H, D, r // 16, 0, r % 16, is_v)
+            assert float(sc) == 1.0
+            assert np.array_equal(got, want[r]), (r, is_v, rows[r][got != want[r]])
+
+
+def check_fp8_quant_error_bound():
+    """Every appended row of an FP8 cache: scale = amax / 448, the largest
+    code is 448, codes keep the sign, and |x / scale - value(code)| is at
+    most half the E4M3 spacing at |x / scale| (2^-4 of the binade's base for
+    normals, 2^-10 below 2^-6), up to the float32 rounding of x / scale."""
+    p = Problem("fp8", 3, 4, 2, 32, [1, 16, 45], 8, seed=72, identity=True)
+    for b in range(p.B):
+        for j in range(int(p.ctx[b])):
+            blk, t = int(p.tables[b][j // 16]), j % 16
+            for g in range(p.Hkv):
+                for which, pool in ((0, p.kpool), (1, p.vpool)):
+                    x = widen(p.kv[b][which][j, g], "bf16")
+                    vals, sc, _ = fp8_read(pool, p.Hkv, p.D, blk, g, t, which == 1)
+                    sc = float(sc)
+                    assert abs(sc - np.abs(x).max() / 448) <= 1e-6 * sc
+                    y = x / sc
+                    base = 2.0 ** np.maximum(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -30))), -6)
+                    assert (np.abs(y - vals) <= base / 16 * (1 + 2.0 ** -16) + 1e-12).all(), (b, j, g, which)
+                    assert np.abs(vals).max() == 448.0
+                    assert (vals * x >= 0).all()
+    k, v = orc.gather_token("fp8", p.Hkv, p.D, p.kpool, p.vpool, p.tables[0], 1)
+    assert np.isnan(k).all() and np.isnan(v).all()
+
+
+def check_fp8_brute_force():
+    """Attention over an FP8 cache == exactly-summed textbook attention over
+    the values torch decodes from the bytes times the scales, for shuffled
+    blocks; the split pass merges to the same result; it stays within the
+    quantisation error of the same problem stored in bfloat16."""
+    p = Problem("fp8", 3, 4, 2, 16, [1, 17, 40], 12, seed=82)
+    out = p.paged()
+    G = p.Hq // p.Hkv
+    ref16 = Problem("bf16", 3, 4, 2, 16, [1, 17, 40], 12, seed=82).paged()
+    for b in range(p.B):
+        n = int(p.ctx[b])
+        for g in range(p.Hkv):
+            K, V = [], []
+            for j in range(n):
+                blk, t = int(p.tables[b][j // 16]), j % 16
+                kv_, ks, _ = fp8_read(p.kpool, p.Hkv, p.D, blk, g, t, False)
+                vv_, vs, _ = fp8_read(p.vpool, p.Hkv, p.D, blk, g, t, True)
+                K.append((kv_ * float(ks)).tolist())
+                V.append((vv_ * float(vs)).tolist())
+            for h in range(g * G, (g + 1) * G):
+                ref = brute_attention(list(widen(p.q[b, h], "bf16")), K, V, p.scale)
+                assert np.abs(out[b, h] - np.asarray(ref)).max() <= 1e-13, (b, h)
+    assert np.abs(out - ref16).max() <= 0.15
+    part = orc.partitioned_attention("fp8", p.q, p.kpool, p.vpool, p.tables, p.ctx, p.Hkv, p.scale, 16)
+    assert np.abs(part - out).max() <= 1e-13
+
+
 class PrefillProblem:
     """Sequences whose last nq_b of ctx_b tokens are new (queries), stored
     with the oracle's own bookkeeping and append; queries packed by row."""
@@ -495,9 +652,34 @@ def check_prefill_int8():
                     assert np.abs(out[r, h] - np.asarray(ref)).max() <= 1e-13, (b, t, h)
 
 
+def check_prefill_fp8():
+    """Prefill over an FP8 cache == textbook attention over the values torch
+    decodes from the bytes times the scales."""
+    p = PrefillProblem("fp8", 4, 2, 16, ctx=[40, 9], nq=[12, 9], num_blocks=8, seed=29)
+    out = p.out()
+    G = p.Hq // p.Hkv
+    for b in range(2):
+        p0 = int(p.ctx[b] - p.nq[b])
+        for g in range(p.Hkv):
+            K, V = [], []
+            for j in range(int(p.ctx[b])):
+                blk, t = int(p.tables[b][j // 16]), j % 16
+                kv_, ks, _ = fp8_read(p.kpool, p.Hkv, p.D, blk, g, t, False)
+                vv_, vs, _ = fp8_read(p.vpool, p.Hkv, p.D, blk, g, t, True)
+                K.append((kv_ * float(ks)).tolist())
+                V.append((vv_ * float(vs)).tolist())
+            for t in range(int(p.nq[b])):
+                r = int(p.qstart[b]) + t
+                for h in range(g * G, (g + 1) * G):
+                    ref = brute_attention(list(widen(p.q[r, h], "bf16")), K[:p0 + t + 1], V[:p0 + t + 1], p.scale)
+                    assert np.abs(out[r, h] - np.asarray(ref)).max() <= 1e-13, (b, t, h)
+
+
 ALL_CHECKS = [check_brute_force, check_library_sdpa, check_paged_equals_contiguous,
               check_placement_invariance, check_special_cases, check_merge_identity,
               check_gqa_reduces_to_mha, check_append_roundtrip, check_layout_golden,
               check_rejects_per_page_softmax, check_int8_quant_golden, check_int8_layout_golden,
               check_int8_quant_error_bound, check_int8_brute_force, check_int8_copy_blocks,
-              check_prefill_brute_force, check_prefill_library_sdpa, check_prefill_int8]
+              check_prefill_brute_force, check_prefill_library_sdpa, check_prefill_int8,
+              check_fp8_quant_golden, check_fp8_decode_library, check_fp8_encode_library,
+              check_fp8_quant_error_bound, check_fp8_brute_force, check_prefill_fp8]

@@ -35,15 +35,26 @@ MUTANTS = {
     "value_of_next_token": ("w * vval(vpool, blk, g, j % BLOCK, d",
                             "w * vval(vpool, blk, g, (j + 1) % BLOCK, d"),
     "max_from_first_token_only": ("if (s[j] > m) m = s[j];", "if (j == 0) m = s[j];"),
-    "int8_scale_dropped": ("return (double)(signed char)tile[at] * (double)sc;",
-                           "return (double)(signed char)tile[at];"),
+    "int8_scale_dropped": ("return v * (double)sc;", "return v;"),
     "int8_truncating_round": ("float r = rintf(v / scale);", "float r = truncf(v / scale);"),
     "int8_signed_amax": ("float a = fabsf(v);", "float a = v;"),
     "int8_scale_of_next_slot": ("memcpy(&sc, tile + (size_t)16 * D + 4 * (size_t)t, sizeof sc);",
                                 "memcpy(&sc, tile + (size_t)16 * D + 4 * (size_t)((t + 1) % BLOCK), sizeof sc);"),
     "int8_v_read_as_k": ("size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16)",
                          "size_t at = !is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16)"),
-    "int8_scale_255": ("float scale = amax / 127.0f;", "float scale = amax / 255.0f;"),
+    "int8_scale_255": ("? 448.0f : 127.0f", "? 448.0f : 255.0f"),
+    "fp8_scale_127": ("? 448.0f : 127.0f", "? 127.0f : 127.0f"),
+    "fp8_read_as_int8": ("double v = dtype == 3 ? e4m3_value", "double v = dtype == 4 ? e4m3_value"),
+    "fp8_decode_bias_8": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "fp8_decode_no_subnormals": ("ldexp(m / 8.0, -6)", "ldexp(1.0 + m / 8.0, -7)"),
+    "fp8_decode_sign_dropped": ("return (c & 0x80) ? -v : v;", "return v;"),
+    "fp8_encode_bias_8": ("int E = e - 1 + 7;", "int E = e - 1 + 8;"),
+    "fp8_encode_ties_away": ("double q = nearbyint((2.0 * f - 1.0) * 8.0);", "double q = round((2.0 * f - 1.0) * 8.0);"),
+    "fp8_encode_truncates": ("double q = nearbyint((2.0 * f - 1.0) * 8.0);", "double q = floor((2.0 * f - 1.0) * 8.0);"),
+    "fp8_encode_no_carry": ("if (q == 8.0) {", "if (q == 9.0) {"),
+    "fp8_encode_subnormal_flush": ("return s | (unsigned char)nearbyint(a * 512.0);", "return s;"),
+    "fp8_encode_sign_dropped": ("unsigned char s = signbit(y) ? 0x80 : 0;", "unsigned char s = 0;"),
+    "fp8_saturate_to_nan": ("if (a >= 448.0) return s | 0x7E;", "if (a >= 448.0) return s | 0x7F;"),
     "prefill_causal_exclusive": ("int n = ctx[b] - nq + t + 1;", "int n = ctx[b] - nq + t;"),
     "prefill_without_prefix": ("int n = ctx[b] - nq + t + 1;", "int n = t + 1;"),
     "prefill_whole_context": ("int n = ctx[b] - nq + t + 1;", "int n = ctx[b];"),
