@@ -80,25 +80,33 @@ enum {
  *   amax = max |x_d|, scale = amax / 127, code_d = round-half-even(x_d / scale)
  *   clamped to [-127, 127] (all codes 0 when amax = 0), value = code * scale,
  * computed in float32 when paged_kv_append stores the row.  Queries and
- * appended rows are bfloat16. */
-enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2 };
+ * appended rows are bfloat16.
+ * PKV_FP8 is the other one-byte format the same section names: the same
+ * tiles and scales, with FP8 E4M3 codes as the OCP 8-bit floating point
+ * format defines them (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals m/8 * 2^-6, largest finite 448, S.1111.111 NaN):
+ *   amax = max |x_d|, scale = amax / 448, code_d = the E4M3 value nearest to
+ *   x_d / scale (ties to the even mantissa), saturated at 448, sign kept
+ *   (all codes 0 when amax = 0), value = E4M3(code) * scale.
+ * The two NaN codes are never written. */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2, PKV_FP8 = 3 };
 
 #define PKV_BLOCK_SIZE 16
 
 /* Pool layout.  A pool is num_blocks * num_kv_heads tiles, tile (blk, g) at
  * index blk * H + g; a tile holds the 16 token slots of one block for one kv
- * head.  With X = 16 / element size (X = 16 for int8 codes):
+ * head.  With X = 16 / element size (X = 16 for one-byte codes):
  *   K element (blk, g, t, d) at tile offset ((d / X) * 16 + t) * X + d % X
  *   V element (blk, g, t, d) at tile offset d * 16 + t
- * (in elements; for PKV_INT8 in bytes).  An f32/bf16 tile is 16 * D
- * elements.  A PKV_INT8 tile is 16 * D + 64 bytes: the codes, then the 16
- * float32 scales of slots 0..15 at byte 16 * D + 4 * t. */
+ * (in elements; for PKV_INT8 and PKV_FP8 in bytes).  An f32/bf16 tile is
+ * 16 * D elements.  A PKV_INT8 or PKV_FP8 tile is 16 * D + 64 bytes: the
+ * codes, then the 16 float32 scales of slots 0..15 at byte 16 * D + 4 * t. */
 typedef struct {
   int32_t num_blocks;   /* physical blocks in the pool (> 0) */
   int32_t block_size;   /* tokens per block; must be 16 */
   int32_t num_kv_heads; /* H (> 0) */
   int32_t head_dim;     /* D: 64 or 128 */
-  int32_t kv_dtype;     /* PKV_F32, PKV_BF16 or PKV_INT8 */
+  int32_t kv_dtype;     /* PKV_F32, PKV_BF16, PKV_INT8 or PKV_FP8 */
 } pkv_layout;
 
 /* Thread-local description of the last error raised on this thread. */
@@ -224,7 +232,7 @@ typedef struct {
 int pkv_pool_stats(const pkv_pool *pool, pkv_stats *out);
 /* K and V bytes of one token across num_layers layers:
  * num_layers * 2 * num_kv_heads * head_dim * element size
- * [KV Cache 工程学 §15.2]; for PKV_INT8 each row also carries its 4-byte
+ * [KV Cache 工程学 §15.2]; for PKV_INT8 and PKV_FP8 each row also carries its 4-byte
  * scale: num_layers * 2 * num_kv_heads * (head_dim + 4).  0 on invalid input. */
 int64_t pkv_kv_bytes_per_token(const pkv_layout *layout, int32_t num_layers);
 /* Bytes of one pool (K or V; both have this size).  0 on invalid input. */
@@ -288,9 +296,10 @@ int pkv_swap_space_stats(const pkv_pool *pool, pkv_swap_stats *out);
 /* ---------------------------------------------------------- device calls */
 /* Store the new tokens' K and V into their slots [KV Cache 工程学 §15.1,
  * §15.5].  k_new, v_new: [num_tokens][H][D] of kv_dtype, bf16 for
- * PKV_INT8 (device); d_slots: int64 [num_tokens] (device), slot = blk*16 + t;
- * a negative slot or one past the pool is skipped.  f32 and bf16 bits are
- * copied unchanged; PKV_INT8 rows are quantised as described at PKV_INT8.
+ * PKV_INT8 and PKV_FP8 (device); d_slots: int64 [num_tokens] (device),
+ * slot = blk*16 + t; a negative slot or one past the pool is skipped.  f32
+ * and bf16 bits are copied unchanged; PKV_INT8 and PKV_FP8 rows are
+ * quantised as described at PKV_INT8 and PKV_FP8 (rows must be finite).
  * Slots must be distinct. */
 int paged_kv_append(const pkv_layout *layout, void *k_pool, void *v_pool, const void *k_new,
                     const void *v_new, const int64_t *d_slots, int32_t num_tokens, void *stream);
@@ -318,10 +327,10 @@ typedef struct {
                                wave is given by the balanced split (default 128).
                                Wavefront-reduction kernel: tokens per
                                split-context partition (default 512). */
-  int32_t kernel;           /* 0 auto (matrix cores for int8, and for bf16
-                               with G >= 4); 1 the wavefront-reduction kernel
-                               (f32, bf16); 2 the matrix-core kernel (bf16,
-                               int8) */
+  int32_t kernel;           /* 0 auto (matrix cores for int8 and FP8, and
+                               for bf16 with G >= 4); 1 the wavefront-
+                               reduction kernel (f32, bf16); 2 the matrix-core
+                               kernel (bf16, int8, FP8) */
   int32_t waves_per_simd;   /* matrix-core kernel: resident waves per SIMD,
                                0 = default (1), 1 or 2.  One streams K/V from
                                HBM fastest (waves sharing a SIMD do not
@@ -344,7 +353,7 @@ size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seq
  * over the context_lens[b] tokens j, where token j is slot j % 16 of block
  * d_block_tables[b][j / 16].  The softmax spans the whole context.
  *   out: float32 [num_seqs][num_q_heads][D] (device, written)
- *   q:   kv_dtype [num_seqs][num_q_heads][D], bf16 for PKV_INT8 (device)
+ *   q:   kv_dtype [num_seqs][num_q_heads][D], bf16 for PKV_INT8 and PKV_FP8 (device)
  *   d_block_tables: int32 [num_seqs][max_blocks_per_seq] (device)
  *   d_context_lens: int32 [num_seqs] (device); a length of 0 gives zeros
  *   max_context_len: an upper bound of every context length (sizes the grid);
@@ -378,14 +387,14 @@ int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, 
  *   out[r][h] = sum_{j <= p_b + t} softmax_j(scale * q[r][h] . K_j) * V_j,
  *   r = d_query_start[b] + t, kv head g = h / (num_q_heads / H).
  *   out: float32 [T][num_q_heads][D] (device, written), T = d_query_start[num_seqs]
- *   q:   bf16 [T][num_q_heads][D] (device), also for PKV_INT8
+ *   q:   bf16 [T][num_q_heads][D] (device), also for PKV_INT8 and PKV_FP8
  *   d_block_tables: int32 [num_seqs][max_blocks_per_seq] (device)
  *   d_context_lens: int32 [num_seqs] (device); d_query_start: int32 [num_seqs + 1]
  *   (device), non-decreasing from 0, with nq_b <= d_context_lens[b] (a larger
  *   nq_b is cut to d_context_lens[b]) and nq_b <= max_query_len (rows past it
  *   are not written)
  *   max_context_len: bounds every context (a longer one is treated as it)
- * Requires a bf16 or int8 cache, num_q_heads % num_kv_heads == 0,
+ * Requires a bf16, int8 or FP8 cache, num_q_heads % num_kv_heads == 0,
  * G = num_q_heads / num_kv_heads <= 16, D in {64, 128},
  * max_query_len <= max_context_len <= min(16 * max_blocks_per_seq, 2^22).
  * Runs on the matrix cores: a wave takes 16 / G consecutive new tokens of one

@@ -15,8 +15,10 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_NO_BLOCKS, PKV_ERR_BAD_BLOCK = 0, -1, -2, -3
 PKV_ERR_REFCOUNT, PKV_ERR_CAPACITY, PKV_ERR_HIP, PKV_ERR_WORKSPACE, PKV_ERR_BAD_SEQ = -4, -5, -6, -7, -8
-PKV_F32, PKV_BF16, PKV_INT8 = 0, 1, 2
-_DTYPE_CODE = {"f32": PKV_F32, "bf16": PKV_BF16, "int8": PKV_INT8}
+PKV_F32, PKV_BF16, PKV_INT8, PKV_FP8 = 0, 1, 2, 3
+_DTYPE_CODE = {"f32": PKV_F32, "bf16": PKV_BF16, "int8": PKV_INT8, "fp8": PKV_FP8}
+# One-byte caches: codes plus a float32 scale per (token, kv head) row.
+Q8_CODES = (PKV_INT8, PKV_FP8)
 BLOCK_SIZE = 16
 
 STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "NO_BLOCKS", -3: "BAD_BLOCK", -4: "REFCOUNT", -5: "CAPACITY",
@@ -36,18 +38,18 @@ class pkv_layout(ctypes.Structure):
 
     @property
     def elem_bytes(self) -> int:
-        """Bytes of one stored element (an int8 code for PKV_INT8)."""
+        """Bytes of one stored element (a one-byte code for PKV_INT8 and PKV_FP8)."""
         return {PKV_F32: 4, PKV_BF16: 2}.get(self.kv_dtype, 1)
 
     @property
     def tile_bytes(self) -> int:
-        """Bytes of one (block, kv head) tile; int8 tiles end with 16 float32 scales."""
-        return BLOCK_SIZE * self.head_dim * self.elem_bytes + (4 * BLOCK_SIZE if self.kv_dtype == PKV_INT8 else 0)
+        """Bytes of one (block, kv head) tile; int8 and FP8 tiles end with 16 float32 scales."""
+        return BLOCK_SIZE * self.head_dim * self.elem_bytes + (4 * BLOCK_SIZE if self.kv_dtype in Q8_CODES else 0)
 
     @property
     def pool_elems(self) -> int:
-        """Elements of a pool tensor: stored elements, or bytes for PKV_INT8."""
-        if self.kv_dtype == PKV_INT8:
+        """Elements of a pool tensor: stored elements, or bytes for PKV_INT8 and PKV_FP8."""
+        if self.kv_dtype in Q8_CODES:
             return self.num_blocks * self.num_kv_heads * self.tile_bytes
         return self.num_blocks * self.num_kv_heads * BLOCK_SIZE * self.head_dim
 
@@ -379,7 +381,7 @@ def _dev(t, what, dtype=None, numel=None):
 
 
 def pool_torch_dtype(layout):
-    """torch dtype of a pool tensor (uint8 bytes for an int8 cache)."""
+    """torch dtype of a pool tensor (uint8 bytes for an int8 or FP8 cache)."""
     import torch
     return {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16}.get(layout.kv_dtype, torch.uint8)
 

@@ -34,12 +34,12 @@ int min_chunks(const pkv_decode_opts *opts, int32_t *out) {
   return PKV_OK;
 }
 
-// Kernel a call runs: 1 wavefront reductions, 2 matrix cores (int8, and bf16
-// with G >= 4, by default).
+// Kernel a call runs: 1 wavefront reductions, 2 matrix cores (int8 and FP8,
+// and bf16 with G >= 4, by default).
 int choose_kernel(const pkv_layout *L, int32_t G, const pkv_decode_opts *opts) {
   const int k = opts ? opts->kernel : 0;
   if (k != 0) return k;
-  if (L->kv_dtype == PKV_INT8) return 2;
+  if (pkv_is_q8(L->kv_dtype)) return 2;
   return (L->kv_dtype == PKV_BF16 && G >= 4) ? 2 : 1;
 }
 
@@ -172,9 +172,9 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   if (opts && (opts->waves_per_simd < 0 || opts->waves_per_simd > 2))
     return pkv_set_error(PKV_ERR_INVALID, "waves_per_simd must be 0, 1 or 2 (got %d)", opts->waves_per_simd);
   if (kernel == 2 && layout->kv_dtype == PKV_F32)
-    return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16 or int8 cache");
-  if (kernel == 1 && layout->kv_dtype == PKV_INT8)
-    return pkv_set_error(PKV_ERR_INVALID, "an int8 cache is read by the matrix-core kernel only");
+    return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16, int8 or FP8 cache");
+  if (kernel == 1 && pkv_is_q8(layout->kv_dtype))
+    return pkv_set_error(PKV_ERR_INVALID, "an int8 or FP8 cache is read by the matrix-core kernel only");
   if (num_seqs > PKV_MAX_SPLIT_SEQS)
     return pkv_set_error(PKV_ERR_INVALID, "at most %d sequences per call (got %d)", PKV_MAX_SPLIT_SEQS, num_seqs);
   if (max_context_len > (1 << 22))
@@ -225,7 +225,7 @@ extern "C" int paged_attention_prefill(const pkv_layout *layout, float *out, con
   if (int rc = pkv_check_layout(layout)) return rc;
   const int32_t H = layout->num_kv_heads;
   if (layout->kv_dtype == PKV_F32)
-    return pkv_set_error(PKV_ERR_INVALID, "paged_attention_prefill needs a bf16 or int8 cache");
+    return pkv_set_error(PKV_ERR_INVALID, "paged_attention_prefill needs a bf16, int8 or FP8 cache");
   if (num_seqs < 0) return pkv_set_error(PKV_ERR_INVALID, "num_seqs < 0");
   if (num_q_heads <= 0 || num_q_heads % H != 0)
     return pkv_set_error(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",

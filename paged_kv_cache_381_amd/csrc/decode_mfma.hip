@@ -43,9 +43,14 @@
 // token's K scale multiplies its score after the score MFMA; its V scale
 // multiplies its softmax weight before the weight is rounded to bf16 for the
 // PV MFMA, while the running sum takes the weight itself.  Each lane reads the
-// 8 scales of its 8 token slots (32 contiguous bytes) of K and of V.  Codes of
-// slots past the context are finite whatever they hold, so a zero weight
-// masks them; their scales may be anything and are never used.
+// 8 scales of its 8 token slots (32 contiguous bytes) of K and of V.  Int8
+// codes of slots past the context are finite whatever they hold, so a zero
+// weight masks them; their scales may be anything and are never used.
+//
+// FP8 E4M3 cache: the same tiles, scales and lane layout; the gfx950
+// conversion instruction widens two codes at a time, exactly, to bf16.  Two
+// of its codes are NaN, so V codes past the context are zeroed as bf16
+// elements are.
 //
 // Memory pipeline.  Block ids and lengths are scalar loads issued one chunk
 // ahead; chunk c+1's K is requested as soon as chunk c's score MFMAs have
@@ -59,30 +64,6 @@
 #include "pkv_internal.h"
 
 namespace {
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-// Eight int8 codes, widened exactly to bf16.
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint2 u) {
-  bf16x8_t r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    r[k] = (__bf16)(float)(int8_t)(u.x >> (8 * k));
-    r[4 + k] = (__bf16)(float)(int8_t)(u.y >> (8 * k));
-  }
-  return r;
-}
-
-// Zero the bf16 elements of u whose index is >= nvalid (0..8).
-__device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
-  uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t mask = (2 * k + 1 < nvalid) ? 0xffffffffu : (2 * k < nvalid ? 0x0000ffffu : 0u);
-    w[k] &= mask;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 // s_waitcnt immediate of gfx9 waiting for no outstanding vector memory
 // operation (vmcnt 0) and leaving the other counters unchecked.
@@ -103,7 +84,7 @@ constexpr float kSlack = 8.0f;
 #define PKV_MFMA_NBUF_I8 4
 #endif
 
-template <int D, int W, int NB, bool I8>
+template <int D, int W, int NB, bool I8, bool F8>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
@@ -157,7 +138,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint4 u = qr[kgroup(kk)];
-      qb[QI][kk] = as_bf16x8(u);
+      qb[QI][kk] = as_bf16x8<F8>(u);
     }
     const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + c.g) * TB);
 #pragma unroll
@@ -237,11 +218,11 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       bf16x8_t kx, ky;
       if constexpr (I8) {
         const uint4 ux = ax[I][kk >> 1], uy = ay[I][kk >> 1];
-        kx = as_bf16x8((kk & 1) ? make_uint2(ux.z, ux.w) : make_uint2(ux.x, ux.y));
-        ky = as_bf16x8((kk & 1) ? make_uint2(uy.z, uy.w) : make_uint2(uy.x, uy.y));
+        kx = as_bf16x8<F8>((kk & 1) ? make_uint2(ux.z, ux.w) : make_uint2(ux.x, ux.y));
+        ky = as_bf16x8<F8>((kk & 1) ? make_uint2(uy.z, uy.w) : make_uint2(uy.x, uy.y));
       } else {
-        kx = as_bf16x8(ax[I][kk]);
-        ky = as_bf16x8(ay[I][kk]);
+        kx = as_bf16x8<F8>(ax[I][kk]);
+        ky = as_bf16x8<F8>(ay[I][kk]);
       }
       sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[QI][kk], sx, 0, 0, 0);
       sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[QI][kk], sy, 0, 0, 0);
@@ -308,7 +289,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       }
     }
     l += psum;
-    if constexpr (!I8) {
+    if constexpr (!I8 || F8) {
       if (tok0 + 32 > n) {  // slots past the context may hold anything, NaN included
         const int nvalid = min(max(n - tb, 0), 8);
 #pragma unroll
@@ -316,7 +297,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       }
     }
 #pragma unroll
-    for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[I][nn]), pv, o[nn], 0, 0, 0);
+    for (int nn = 0; nn < NNN; ++nn) o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8<F8>(va[I][nn]), pv, o[nn], 0, 0, 0);
     issue_v(std::integral_constant<int, J>{});
 
     if (real && (x + 1 >= hi || cur.j == cur.cnt - 1)) {  // the piece ends here
@@ -367,9 +348,10 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
 #endif
 constexpr int kWaves = PKV_MFMA_WAVES;
 
-template <int D, bool I8>
+// I8: one-byte codes (int8, or FP8 E4M3 when F8) with per-row scales.
+template <int D, bool I8, bool F8 = false>
 int launch(const pkv_decode_args &a, const SplitParams &p) {
-  auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8>;
+  auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8, F8>;
   size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves);
   // One wave per SIMD: a workgroup takes more than half of a CU's 160 KiB of
   // LDS, so no second one is placed beside it.  Two waves on one SIMD do not
@@ -386,5 +368,7 @@ int launch(const pkv_decode_args &a, const SplitParams &p) {
 int pkv_launch_decode_mfma(const pkv_decode_args &a) {
   const SplitParams p = pkv_split_params(a);
   if (a.L->kv_dtype == PKV_INT8) return a.L->head_dim == 128 ? launch<128, true>(a, p) : launch<64, true>(a, p);
+  if (a.L->kv_dtype == PKV_FP8)
+    return a.L->head_dim == 128 ? launch<128, true, true>(a, p) : launch<64, true, true>(a, p);
   return a.L->head_dim == 128 ? launch<128, false>(a, p) : launch<64, false>(a, p);
 }

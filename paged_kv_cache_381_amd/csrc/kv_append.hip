@@ -4,7 +4,7 @@
 // cache [KV Cache 工程学 §15.1]; with paging the store goes to slot t of the
 // physical block named by the sequence's table [§15.5].  The host block
 // manager turns (sequence, position) into slot = block*16 + t, so the kernel
-// is a bit-exact scatter -- or, for an int8 cache [§15.7 (3)], a per-row
+// is a bit-exact scatter -- or, for an int8 or FP8 cache [§15.7 (3)], a per-row
 // quantisation followed by the scatter.  Copy-on-write duplicates a whole shared block
 // before a sequence writes into it [KV Cache 与 PagedAttention, first article].
 #include "pkv_device.h"
@@ -135,19 +135,42 @@ __global__ __launch_bounds__(256) void append_runs_kernel(E *__restrict__ kpool,
   }
 }
 
-// int8 cache.  A group of D/8 lanes quantises one (token, kv head) row of K
-// and one of V; a lane holds 8 consecutive bf16 elements of each.  The row's
-// largest magnitude comes from xor-shuffles inside the group, then every
-// lane divides its elements by scale = amax / 127 in float32 (correctly
-// rounded division), rounds half to even and clamps to [-127, 127].  Codes go
-// to the tile's K and V layouts and lane 0 of the group writes the two scales
-// after the tile's codes.
-template <int D>
-__global__ __launch_bounds__(256) void append_int8_kernel(uint8_t *__restrict__ kpool, uint8_t *__restrict__ vpool,
-                                                          const uint16_t *__restrict__ k_new,
-                                                          const uint16_t *__restrict__ v_new,
-                                                          const int64_t *__restrict__ slots, int64_t rows, int H,
-                                                          int num_blocks) {
+// The FP8 E4M3 code (OCP format: bias 7, subnormals m/8 * 2^-6, largest
+// finite 448) of the value nearest to y, ties to the even mantissa,
+// saturated at 448, sign kept; y is finite.  Below 2^-6 the codes are the
+// multiples of 2^-9 (code 8 is 2^-6 itself).  Above it the float32 mantissa
+// is rounded to 3 bits in the integer domain, a carry moving into the
+// exponent, and the exponent is re-biased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a >= 448.f) {
+    c = 0x7Eu;
+  } else if (a < 0x1p-6f) {
+    c = (uint32_t)rintf(a * 512.f);
+  } else {
+    const uint32_t m = b & 0x7fffffffu;
+    c = ((m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | c;
+}
+
+// int8 and FP8 caches.  A group of D/8 lanes quantises one (token, kv head)
+// row of K and one of V; a lane holds 8 consecutive bf16 elements of each.
+// The row's largest magnitude comes from xor-shuffles inside the group, then
+// every lane divides its elements by scale = amax / 127 (int8) or amax / 448
+// (FP8) in float32 (correctly rounded division) and codes the quotient: int8
+// rounds half to even and clamps to [-127, 127]; FP8 takes the nearest E4M3
+// value.  Codes go to the tile's K and V layouts and lane 0 of the group
+// writes the two scales after the tile's codes.
+template <int D, bool F8>
+__global__ __launch_bounds__(256) void append_q8_kernel(uint8_t *__restrict__ kpool, uint8_t *__restrict__ vpool,
+                                                        const uint16_t *__restrict__ k_new,
+                                                        const uint16_t *__restrict__ v_new,
+                                                        const int64_t *__restrict__ slots, int64_t rows, int H,
+                                                        int num_blocks) {
   constexpr int LPR = D / 8;  // lanes per row
   constexpr int TB = 16 * D + 64;
   const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
@@ -179,15 +202,22 @@ __global__ __launch_bounds__(256) void append_int8_kernel(uint8_t *__restrict__ 
     va = fmaxf(va, __shfl_xor(va, o, LPR));
   }
   if (row >= rows || s < 0 || s >= (int64_t)num_blocks * 16) return;
-  const float ks = ka / 127.0f, vs = va / 127.0f;
+  constexpr float kTop = F8 ? 448.0f : 127.0f;
+  const float ks = ka / kTop, vs = va / kTop;
   uint32_t kc[2] = {0u, 0u};
   uint8_t vc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int kq = ka > 0.f ? (int)fminf(fmaxf(rintf(kf[e] / ks), -127.f), 127.f) : 0;
-    const int vq = va > 0.f ? (int)fminf(fmaxf(rintf(vf[e] / vs), -127.f), 127.f) : 0;
-    kc[e >> 2] |= (uint32_t)(kq & 0xff) << (8 * (e & 3));
-    vc[e] = (uint8_t)(vq & 0xff);
+    uint32_t kq, vq;
+    if constexpr (F8) {
+      kq = ka > 0.f ? e4m3_code(kf[e] / ks) : 0u;
+      vq = va > 0.f ? e4m3_code(vf[e] / vs) : 0u;
+    } else {
+      kq = ka > 0.f ? (uint32_t)(int)fminf(fmaxf(rintf(kf[e] / ks), -127.f), 127.f) : 0u;
+      vq = va > 0.f ? (uint32_t)(int)fminf(fmaxf(rintf(vf[e] / vs), -127.f), 127.f) : 0u;
+    }
+    kc[e >> 2] |= (kq & 0xffu) << (8 * (e & 3));
+    vc[e] = (uint8_t)(vq & 0xffu);
   }
   const int64_t blk = s >> 4;
   const int off = (int)(s & 15);
@@ -254,11 +284,13 @@ int pkv_launch_append(const pkv_layout *L, void *k_pool, void *v_pool, const voi
                       const int64_t *slots, int32_t num_tokens, void *stream) {
   if (num_tokens == 0) return 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (L->kv_dtype == PKV_INT8) {
+  if (pkv_is_q8(L->kv_dtype)) {
     const int64_t rows = (int64_t)num_tokens * L->num_kv_heads;
     const int per_block = 256 / (L->head_dim / 8);
     const dim3 grid((unsigned)((rows + per_block - 1) / per_block));
-    auto kern = L->head_dim == 128 ? append_int8_kernel<128> : append_int8_kernel<64>;
+    const bool f8 = L->kv_dtype == PKV_FP8;
+    auto kern = L->head_dim == 128 ? (f8 ? append_q8_kernel<128, true> : append_q8_kernel<128, false>)
+                                   : (f8 ? append_q8_kernel<64, true> : append_q8_kernel<64, false>);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (uint8_t *)k_pool, (uint8_t *)v_pool, (const uint16_t *)k_new,
                        (const uint16_t *)v_new, slots, rows, L->num_kv_heads, L->num_blocks);
     return (int)hipGetLastError();

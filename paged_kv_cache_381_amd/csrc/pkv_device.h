@@ -7,7 +7,59 @@
 #include "pkv_internal.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Eight bf16 elements of an MFMA operand: a 16-byte unit of a bf16 cache or
+// query, or eight one-byte codes (bytes 0..3 of u.x, then of u.y) widened
+// exactly to bf16.  An int8 code needs 7 significant bits.  Every FP8 E4M3
+// value (3 mantissa bits, exponents -9 .. 8) is a bf16 value too: the gfx950
+// instruction that widens two codes of one 16-bit half to float32 is exact
+// on all 254 finite codes (checked against the format's definition on the
+// device), and the float32 pair then packs to bf16 without rounding.  (The
+// instruction that widens straight to bf16 with a float32 scale returned
+// the value of the code with its lowest mantissa bit cleared in that check,
+// so it is not used.)
+template <bool F8 = false>
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+template <bool F8>
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint2 u) {
+  if constexpr (F8) {
+    const bf16x2_t a = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, false), bf16x2_t);
+    const bf16x2_t b = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, true), bf16x2_t);
+    const bf16x2_t c = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, false), bf16x2_t);
+    const bf16x2_t d = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, true), bf16x2_t);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  } else {
+    bf16x8_t r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r[k] = (__bf16)(float)(int8_t)(u.x >> (8 * k));
+      r[4 + k] = (__bf16)(float)(int8_t)(u.y >> (8 * k));
+    }
+    return r;
+  }
+}
+
+// Zero the bf16 elements of u whose index is >= nvalid (0..8).
+__device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t mask = (2 * k + 1 < nvalid) ? 0xffffffffu : (2 * k < nvalid ? 0x0000ffffu : 0u);
+    w[k] &= mask;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+// Zero the one-byte codes of u (bytes 0..3 of u.x, then of u.y) whose index
+// is >= nvalid (0..8).  Code 0 is +0 in int8 and in FP8 E4M3.
+__device__ __forceinline__ uint2 keep_first(uint2 u, int nvalid) {
+  const uint32_t mx = nvalid >= 4 ? 0xffffffffu : (1u << (8 * nvalid)) - 1u;
+  const uint32_t my = nvalid >= 8 ? 0xffffffffu : nvalid <= 4 ? 0u : (1u << (8 * (nvalid - 4))) - 1u;
+  return make_uint2(u.x & mx, u.y & my);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -10,17 +10,19 @@ int pkv_set_error(int code, const char *fmt, ...);
 // Validate a pkv_layout; PKV_OK or PKV_ERR_INVALID with a message.
 int pkv_check_layout(const pkv_layout *L);
 
-// Bytes of one stored element (an int8 code for PKV_INT8).
+// Bytes of one stored element (a one-byte code for PKV_INT8 and PKV_FP8).
 inline int pkv_elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 1; }
+// One-byte codes with a float32 scale per (token, kv head) row.
+inline bool pkv_is_q8(int dtype) { return dtype == PKV_INT8 || dtype == PKV_FP8; }
 // Bytes of one (block, kv head) tile of a pool: 16 token slots of D elements,
-// plus the 16 float32 scales of an int8 tile.
+// plus the 16 float32 scales of an int8 or FP8 tile.
 inline int64_t pkv_tile_bytes(const pkv_layout *L) {
   return (int64_t)PKV_BLOCK_SIZE * L->head_dim * pkv_elem_bytes(L->kv_dtype) +
-         (L->kv_dtype == PKV_INT8 ? 4 * PKV_BLOCK_SIZE : 0);
+         (pkv_is_q8(L->kv_dtype) ? 4 * PKV_BLOCK_SIZE : 0);
 }
 // Bytes of one token's K (or V) row of one kv head, its scale included.
 inline int64_t pkv_row_bytes(const pkv_layout *L) {
-  return (int64_t)L->head_dim * pkv_elem_bytes(L->kv_dtype) + (L->kv_dtype == PKV_INT8 ? 4 : 0);
+  return (int64_t)L->head_dim * pkv_elem_bytes(L->kv_dtype) + (pkv_is_q8(L->kv_dtype) ? 4 : 0);
 }
 
 

@@ -48,8 +48,8 @@ int pkv_check_layout(const pkv_layout *L) {
   if (L->num_kv_heads <= 0) return pkv_set_error(PKV_ERR_INVALID, "num_kv_heads must be > 0");
   if (L->head_dim != 64 && L->head_dim != 128)
     return pkv_set_error(PKV_ERR_INVALID, "head_dim must be 64 or 128 (got %d)", L->head_dim);
-  if (L->kv_dtype != PKV_F32 && L->kv_dtype != PKV_BF16 && L->kv_dtype != PKV_INT8)
-    return pkv_set_error(PKV_ERR_INVALID, "kv_dtype must be PKV_F32, PKV_BF16 or PKV_INT8");
+  if (L->kv_dtype != PKV_F32 && L->kv_dtype != PKV_BF16 && L->kv_dtype != PKV_INT8 && L->kv_dtype != PKV_FP8)
+    return pkv_set_error(PKV_ERR_INVALID, "kv_dtype must be PKV_F32, PKV_BF16, PKV_INT8 or PKV_FP8");
   return PKV_OK;
 }
 

@@ -1,5 +1,5 @@
 // Paged prefill: causal attention of a sequence's new tokens over its paged
-// cache, on the matrix cores (bf16 or int8 cache).
+// cache, on the matrix cores (bf16, int8 or FP8 cache).
 //
 // What it computes [KV Cache 工程学 §15.1: a prompt is a causal i x i
 // attention; §15.6 and 新一代 KV Cache 管理 §8.3: a cached prefix is not
@@ -41,36 +41,11 @@
 
 namespace {
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-// Eight int8 codes, widened exactly to bf16.
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint2 u) {
-  bf16x8_t r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    r[k] = (__bf16)(float)(int8_t)(u.x >> (8 * k));
-    r[4 + k] = (__bf16)(float)(int8_t)(u.y >> (8 * k));
-  }
-  return r;
-}
-
-// Zero the bf16 elements of u whose index is >= nvalid (0..8).
-__device__ __forceinline__ uint4 keep_first(uint4 u, int nvalid) {
-  uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t mask = (2 * k + 1 < nvalid) ? 0xffffffffu : (2 * k < nvalid ? 0x0000ffffu : 0u);
-    w[k] &= mask;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 constexpr float kSlack = 8.0f;  // headroom of the running maximum (base 2)
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Eight floats rounded to bf16 (nearest even), two per conversion.
 __device__ __forceinline__ bf16x8_t pack_bf16x8(const float (&e)[8]) {
@@ -82,7 +57,7 @@ __device__ __forceinline__ bf16x8_t pack_bf16x8(const float (&e)[8]) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-template <int D, int NB, bool I8, int CT>
+template <int D, int NB, bool I8, int CT, bool F8>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   constexpr int NKK = D / 32;
   constexpr int NNN = D / 16;
@@ -154,7 +129,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   for (int s = 0; s < CT; ++s) {
     const uint4 *qr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.q) + qrow[s] * D);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qb[s][kk] = as_bf16x8(qr[kgroup(kk)]);
+    for (int kk = 0; kk < NKK; ++kk) qb[s][kk] = as_bf16x8<F8>(qr[kgroup(kk)]);
   }
 
   // Chunk y lives in ring slot y % NB of the K ring and of the V ring.  Its
@@ -216,11 +191,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
       bf16x8_t kx, ky;
       if constexpr (I8) {
         const uint4 ux = ax[I][kk >> 1], uy = ay[I][kk >> 1];
-        kx = as_bf16x8((kk & 1) ? make_uint2(ux.z, ux.w) : make_uint2(ux.x, ux.y));
-        ky = as_bf16x8((kk & 1) ? make_uint2(uy.z, uy.w) : make_uint2(uy.x, uy.y));
+        kx = as_bf16x8<F8>((kk & 1) ? make_uint2(ux.z, ux.w) : make_uint2(ux.x, ux.y));
+        ky = as_bf16x8<F8>((kk & 1) ? make_uint2(uy.z, uy.w) : make_uint2(uy.x, uy.y));
       } else {
-        kx = as_bf16x8(ax[I][kk]);
-        ky = as_bf16x8(ay[I][kk]);
+        kx = as_bf16x8<F8>(ax[I][kk]);
+        ky = as_bf16x8<F8>(ay[I][kk]);
       }
 #pragma unroll
       for (int s = 0; s < CT; ++s) {
@@ -291,9 +266,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
           sy[s][r] = (tb + 4 + r <= lim[s]) ? sy[s][r] * fy : -INFINITY;
         }
       }
-      if constexpr (!I8) {
-        // Keys at or past the walk's end may be unwritten (NaN); a zero
-        // weight alone would not cancel them.
+      if constexpr (!I8 || F8) {
+        // Keys at or past the walk's end may be unwritten (NaN, also as FP8
+        // codes); a zero weight alone would not cancel them.
         const int nvalid = real ? min(max(kend - tb, 0), 8) : 0;
         if (nvalid < 8) {
 #pragma unroll
@@ -379,7 +354,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
     }
 #pragma unroll
     for (int nn = 0; nn < NNN; ++nn) {
-      const bf16x8_t vop = as_bf16x8(va[I][nn]);
+      const bf16x8_t vop = as_bf16x8<F8>(va[I][nn]);
 #pragma unroll
       for (int s = 0; s < CT; ++s) o[s][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pv[s], o[s][nn], 0, 0, 0);
     }
@@ -452,10 +427,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
 #define PKV_PREFILL_CT_I8 2
 #endif
 
-template <int D, bool I8>
+// I8: one-byte codes (int8, or FP8 E4M3 when F8) with per-row scales.
+template <int D, bool I8, bool F8 = false>
 int launch(const pkv_prefill_args &a, const PrefillParams &p) {
   constexpr int CT = I8 ? PKV_PREFILL_CT_I8 : PKV_PREFILL_CT;
-  auto kern = prefill_mfma_kernel<D, I8 ? PKV_PREFILL_NBUF_I8 : PKV_PREFILL_NBUF, I8, CT>;
+  auto kern = prefill_mfma_kernel<D, I8 ? PKV_PREFILL_NBUF_I8 : PKV_PREFILL_NBUF, I8, CT, F8>;
   const int tq = 16 / p.G;
   const int tiles = (a.max_query_len + tq - 1) / tq;
   const int waves = (tiles + CT - 1) / CT;
@@ -483,5 +459,7 @@ int pkv_launch_prefill_mfma(const pkv_prefill_args &a) {
   p.max_ctx = a.max_ctx;
   p.scale_log2 = a.scale_log2;
   if (a.L->kv_dtype == PKV_INT8) return a.L->head_dim == 128 ? launch<128, true>(a, p) : launch<64, true>(a, p);
+  if (a.L->kv_dtype == PKV_FP8)
+    return a.L->head_dim == 128 ? launch<128, true, true>(a, p) : launch<64, true, true>(a, p);
   return a.L->head_dim == 128 ? launch<128, false>(a, p) : launch<64, false>(a, p);
 }

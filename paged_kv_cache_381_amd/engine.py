@@ -21,7 +21,7 @@ _NAN = {"bf16": 0x7FC0, "f32": float("nan")}
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str, num_layers: int = 1,
                  free_order=None, device="cuda", fill_nan: bool = True):
-        self.dtype = dtype  # storage of the cache: "f32", "bf16" or "int8"
+        self.dtype = dtype  # storage of the cache: "f32", "bf16", "int8" or "fp8"
         self.layout = L.make_layout(num_blocks, num_kv_heads, head_dim, dtype)
         self.pool = L.pkv_pool_create(self.layout, free_order)
         self.device = torch.device(device)

@@ -59,6 +59,10 @@ def test_sizes():
     assert P.pkv_kv_bytes_per_token(i8, 32) == 32 * 2 * 8 * (128 + 4)
     assert P.pkv_pool_bytes(i8) == 10 * 8 * (16 * 128 + 64) == i8.pool_elems
     assert P.pkv_pool_bytes(P.make_layout(3, 2, 64, "int8")) == 3 * 2 * (16 * 64 + 64)
+    # FP8 E4M3 (the other one-byte format of the same section): the same tiles
+    f8 = P.make_layout(10, 8, 128, "fp8")
+    assert P.pkv_kv_bytes_per_token(f8, 32) == 32 * 2 * 8 * (128 + 4)
+    assert P.pkv_pool_bytes(f8) == 10 * 8 * (16 * 128 + 64) == f8.pool_elems
     # Both kernels split the batch the same way: partial slots per (sequence, query head)
     # = ceil(ceil(max_ctx / 32) / fewest chunks per wave) + 1, then partial (m, l) and a
     # header of 2 + B int32, each region padded to 16 bytes
@@ -107,8 +111,9 @@ def test_decode_argument_errors_before_any_launch():
     assert call(kernel=7) == L.PKV_ERR_INVALID
     assert call(kernel=2, lay_=P.make_layout(16, 2, 128, "f32")) == L.PKV_ERR_INVALID
     assert call(kernel=1, lay_=P.make_layout(16, 2, 128, "int8")) == L.PKV_ERR_INVALID
+    assert call(kernel=1, lay_=P.make_layout(16, 2, 128, "fp8")) == L.PKV_ERR_INVALID
     bad = P.make_layout(16, 2, 128, "int8")
-    bad.kv_dtype = 3
+    bad.kv_dtype = 4
     assert call(lay_=bad) == L.PKV_ERR_INVALID
     assert call(mb=64, mctx=1024) == L.PKV_ERR_WORKSPACE
     assert lib.paged_attention_decode(ctypes.byref(lay), None, fake, fake, fake, fake, fake, 2, 4, 8, 64, 0.1,

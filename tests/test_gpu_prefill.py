@@ -3,7 +3,7 @@
 The prefill is a causal attention of each sequence's new tokens over its
 paged cache (a cached prefix, shared or private, then the new tokens).  The
 pools are built on both sides by the same build script; outputs are compared
-element by element: max abs error <= 2e-2 (bf16 or int8 cache, float32
+element by element: max abs error <= 2e-2 (bf16, int8 or FP8 cache, float32
 accumulation), on every output of small shapes and on sampled query rows of
 the full-size workloads (the oracle evaluates the last new tokens of chosen
 sequences, which see the most keys).
@@ -49,6 +49,8 @@ SMALL = [
     ("prefill_8b_b4", dict(batch=3, num_q_heads=24, own_prefix=(0, 17), new_tokens=(1, 29))),  # G 3: 15 columns used
     ("prefill_shared_prefix", dict(batch=3, shared_prefix=32, new_tokens=(1, 40), cache="int8")),
     ("prefill_8b_b4", dict(batch=3, num_q_heads=64, own_prefix=(0, 40), new_tokens=(1, 30), cache="int8")),
+    ("prefill_shared_prefix", dict(batch=3, shared_prefix=32, new_tokens=(1, 40), cache="fp8")),
+    ("prefill_8b_b4", dict(batch=3, head_dim=64, own_prefix=(0, 40), new_tokens=(1, 30), cache="fp8")),
 ]
 
 

@@ -77,7 +77,7 @@ class Workload:
     sinks: int = 0
     sink_scale: float = 4.0
     shuffled: bool = True        # blocks handed out in a seeded random order, else 0, 1, 2, ...
-    cache: str = ""              # storage of the cache: "" = dtype, or "int8" (codes + per-token scales)
+    cache: str = ""              # storage of the cache: "" = dtype, or "int8" / "fp8" (codes + per-token scales)
     same_data_as: str = ""       # draw lengths, order and values as the named workload does
     description: str = ""
 
@@ -99,9 +99,9 @@ class Workload:
 
     @property
     def row_bytes(self) -> int:
-        """Cache bytes of one token's K (or V) row of one kv head: an int8
-        cache keeps a float32 scale beside its d one-byte codes."""
-        if self.cache_dtype == "int8":
+        """Cache bytes of one token's K (or V) row of one kv head: an int8 or
+        FP8 cache keeps a float32 scale beside its d one-byte codes."""
+        if self.cache_dtype in ("int8", "fp8"):
             return self.head_dim + 4
         return self.head_dim * self.elem_bytes
 
@@ -242,6 +242,11 @@ WORKLOADS = {
         ctx_range=(128, 4096), cache="int8", same_data_as="llama3_8b_b64",
         description="llama3_8b_b64 with an int8 cache: the same lengths, order and bf16 rows, quantised "
                     "on append to int8 codes with a float32 scale per token and kv head"),
+    "llama3_8b_b64_fp8": Workload(
+        "llama3_8b_b64_fp8", 2, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+        ctx_range=(128, 4096), cache="fp8", same_data_as="llama3_8b_b64",
+        description="llama3_8b_b64 with an FP8 E4M3 cache: the same lengths, order and bf16 rows, quantised "
+                    "on append to E4M3 codes with a float32 scale per token and kv head"),
     "llama3_70b_b256": Workload(
         "llama3_70b_b256", 3, batch=256, num_q_heads=64, num_kv_heads=8, head_dim=128, dtype="bf16",
         ctx_fixed=(4096,) * 256,

@@ -36,7 +36,7 @@ class PrefillWorkload:
     num_kv_heads: int
     head_dim: int
     dtype: str = "bf16"         # queries and K/V rows handed to append
-    cache: str = ""             # "" = dtype, or "int8"
+    cache: str = ""             # "" = dtype, or "int8" / "fp8"
     shared_prefix: int = 0      # cached tokens held once by every sequence
     own_prefix: tuple = (0, 0)  # private cached tokens per sequence: inclusive range
     new_tokens: tuple = (1, 1)  # new tokens per sequence: inclusive range
@@ -120,7 +120,7 @@ class PrefillInstance:
     def kv_bytes(self) -> int:
         """Distinct K/V bytes the tokens attended to occupy (shared prefix once)."""
         w = self.wl
-        row = w.head_dim + 4 if w.cache_dtype == "int8" else w.head_dim * 2
+        row = w.head_dim + 4 if w.cache_dtype in ("int8", "fp8") else w.head_dim * 2
         return (w.shared_prefix + int((self.own_prefix + self.nq).sum())) * 2 * w.num_kv_heads * row
 
 
