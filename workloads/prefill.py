@@ -40,6 +40,7 @@ class PrefillWorkload:
     shared_prefix: int = 0      # cached tokens held once by every sequence
     own_prefix: tuple = (0, 0)  # private cached tokens per sequence: inclusive range
     new_tokens: tuple = (1, 1)  # new tokens per sequence: inclusive range
+    same_data_as: str = ""      # draw lengths, order and values as the named workload does
     description: str = ""
 
     @property
@@ -50,15 +51,19 @@ class PrefillWorkload:
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
 
+    @property
+    def data_name(self) -> str:
+        return self.same_data_as or self.name
+
     def instantiate(self) -> "PrefillInstance":
-        rng = np.random.default_rng(derive_seed(2000 + self.number, self.name, "lens"))
+        rng = np.random.default_rng(derive_seed(2000 + self.number, self.data_name, "lens"))
         B = self.batch
         own_prefix = rng.integers(self.own_prefix[0], self.own_prefix[1] + 1, size=B).astype(np.int32)
         nq = rng.integers(self.new_tokens[0], self.new_tokens[1] + 1, size=B).astype(np.int32)
         ctx = (self.shared_prefix + own_prefix + nq).astype(np.int32)
         demand = -(-self.shared_prefix // BLOCK) + int(sum(-(-int(n) // BLOCK) + 1 for n in own_prefix + nq))
         num_blocks = int(np.ceil(1.25 * demand)) + 4
-        perm = np.random.default_rng(derive_seed(2000 + self.number, self.name, "perm")).permutation(
+        perm = np.random.default_rng(derive_seed(2000 + self.number, self.data_name, "perm")).permutation(
             num_blocks).astype(np.int32)
         return PrefillInstance(self, ctx, own_prefix, nq, num_blocks, perm)
 
@@ -78,7 +83,7 @@ class PrefillInstance:
         return np.concatenate([[0], np.cumsum(self.nq)]).astype(np.int32)
 
     def _seed(self, *names) -> int:
-        return derive_seed(2000 + self.wl.number, self.wl.name, *names)
+        return derive_seed(2000 + self.wl.number, self.wl.data_name, *names)
 
     def shared_kv(self, which: str) -> np.ndarray:
         w = self.wl
@@ -130,6 +135,14 @@ PREFILL_WORKLOADS = {
         shared_prefix=2000, new_tokens=(512, 512),
         description="prefill of 16 prompts of 512 new tokens after a cached 2000-token system prompt held once, "
                     "Llama-3-8B heads, bf16"),
+    "prefill_shared_prefix_int8": PrefillWorkload(
+        "prefill_shared_prefix_int8", 1, batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, cache="int8",
+        shared_prefix=2000, new_tokens=(512, 512), same_data_as="prefill_shared_prefix",
+        description="prefill_shared_prefix on an int8 cache: the same lengths and bf16 rows, quantised on append"),
+    "prefill_shared_prefix_fp8": PrefillWorkload(
+        "prefill_shared_prefix_fp8", 1, batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, cache="fp8",
+        shared_prefix=2000, new_tokens=(512, 512), same_data_as="prefill_shared_prefix",
+        description="prefill_shared_prefix on an FP8 E4M3 cache: the same lengths and bf16 rows, quantised on append"),
     "prefill_8b_b4": PrefillWorkload(
         "prefill_8b_b4", 2, batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, new_tokens=(2048, 2048),
         description="prefill of 4 prompts of 2048 new tokens, no cached prefix, Llama-3-8B heads, bf16"),
