@@ -100,6 +100,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   Share sh;
   if (!split_begin<W, D>(P, s_lds, sh)) return;
   const int64_t lo = sh.lo, hi = sh.hi;
+  // This wave's ring of finished pieces, written out after its last load.
+  uint8_t *const ring = reinterpret_cast<uint8_t *>(s_lds) + P.ring_off + (threadIdx.x >> 6) * P.nrec * P.rec_bytes;
+  int held = 0;  // records in the ring
 
   const int r16 = lane & 15, grp = lane >> 4;
   // Row r16 of the score MFMAs holds a token of block (r16 >> 3); see header.
@@ -303,28 +306,47 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     if (real && (x + 1 >= hi || cur.j == cur.cnt - 1)) {  // the piece ends here
       const float lsum = rows_sum4(l);
       const bool whole = sh.whole(cur);
-      if (r16 < G) {
-        const size_t row = (size_t)cur.b * P.Hq + (size_t)cur.g * G + r16;
-        if (whole) {
-          const float inv = 1.f / lsum;
-          float *dst = P.out + row * D + 4 * grp;
+      const int slot = whole ? 0 : sh.piece(cur, P.maxp);
+      if (held < P.nrec) {
+        // The piece's rows go to the wave's LDS ring and reach memory after
+        // the wave's last load: LDS traffic has a counter of its own, so the
+        // K/V loads in flight keep flowing.
+        uint8_t *rec = ring + held * P.rec_bytes;
+        if (r16 < G) {
+          const float inv = whole ? 1.f / lsum : 1.f;
+          float *row = reinterpret_cast<float *>(rec) + r16 * D + 4 * grp;
 #pragma unroll
           for (int nn = 0; nn < NNN; ++nn)
-            *reinterpret_cast<float4 *>(dst + 16 * nn) =
+            *reinterpret_cast<float4 *>(row + 16 * nn) =
                 make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
-        } else {
-          const size_t slot = row * P.maxp + sh.piece(cur, P.maxp);
-          float *dst = P.ws_o + slot * D + 4 * grp;
-#pragma unroll
-          for (int nn = 0; nn < NNN; ++nn)
-            *reinterpret_cast<float4 *>(dst + 16 * nn) = make_float4(o[nn][0], o[nn][1], o[nn][2], o[nn][3]);
-          if (grp == 0) *reinterpret_cast<float2 *>(P.ws_ml + 2 * slot) = make_float2(m, lsum);
+          if (grp == 0) *reinterpret_cast<float2 *>(rec + G * D * 4 + r16 * 8) = make_float2(m, lsum);
         }
+        if (lane == 0) *reinterpret_cast<int4 *>(rec + G * D * 4 + G * 8) = make_int4(whole, cur.b, cur.g, slot);
+        ++held;
+      } else {
+        if (r16 < G) {
+          const size_t row = (size_t)cur.b * P.Hq + (size_t)cur.g * G + r16;
+          if (whole) {
+            const float inv = 1.f / lsum;
+            float *dst = P.out + row * D + 4 * grp;
+#pragma unroll
+            for (int nn = 0; nn < NNN; ++nn)
+              *reinterpret_cast<float4 *>(dst + 16 * nn) =
+                  make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
+          } else {
+            const size_t ps = row * P.maxp + slot;
+            float *dst = P.ws_o + ps * D + 4 * grp;
+#pragma unroll
+            for (int nn = 0; nn < NNN; ++nn)
+              *reinterpret_cast<float4 *>(dst + 16 * nn) = make_float4(o[nn][0], o[nn][1], o[nn][2], o[nn][3]);
+            if (grp == 0) *reinterpret_cast<float2 *>(P.ws_ml + 2 * ps) = make_float2(m, lsum);
+          }
+        }
+        // Stores share the memory counter with loads: drain it here, so that
+        // the loads in flight are counted exactly on every path (otherwise
+        // each chunk's waits would assume the worst and drain it).
+        __builtin_amdgcn_s_waitcnt(kDrainVm);
       }
-      // Stores share the memory counter with loads: drain it here, once per
-      // piece, so that the loads in flight are counted exactly on every path
-      // (otherwise each chunk's waits would assume the worst and drain it).
-      __builtin_amdgcn_s_waitcnt(kDrainVm);
 #pragma unroll
       for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m = -INFINITY;
@@ -341,18 +363,53 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       (step(std::integral_constant<int, Is>{}), ...);
     }(std::make_integer_sequence<int, NB>{});
   }
+  // Write out the ring: G rows of D floats per record, 16 bytes per lane,
+  // then the (m, l) of a partial.
+  for (int r = 0; r < held; ++r) {
+    const uint8_t *rec = ring + r * P.rec_bytes;
+    const int4 meta = *reinterpret_cast<const int4 *>(rec + G * D * 4 + G * 8);
+    const bool whole = uniform(meta.x) != 0;
+    const size_t row0 = (size_t)uniform(meta.y) * P.Hq + (size_t)uniform(meta.z) * G;
+    const int slot = uniform(meta.w);
+    for (int u = lane; u < G * (D / 4); u += 64) {
+      const int h = u / (D / 4), c = 4 * (u % (D / 4));
+      const float4 v = *reinterpret_cast<const float4 *>(rec + (h * D + c) * 4);
+      float *dst = whole ? P.out + (row0 + h) * D + c : P.ws_o + ((row0 + h) * P.maxp + slot) * D + c;
+      *reinterpret_cast<float4 *>(dst) = v;
+    }
+    if (!whole && lane < G)
+      *reinterpret_cast<float2 *>(P.ws_ml + 2 * ((row0 + lane) * P.maxp + slot)) =
+          *reinterpret_cast<const float2 *>(rec + G * D * 4 + lane * 8);
+  }
 }
 
 #ifndef PKV_MFMA_WAVES
 #define PKV_MFMA_WAVES 4
 #endif
 constexpr int kWaves = PKV_MFMA_WAVES;
+// LDS a workgroup may take, result rings included: one workgroup per CU
+// (over half of the 160 KiB), or two.
+constexpr size_t kRingLdsOneWg = 96 * 1024;
+constexpr size_t kRingLdsTwoWg = 64 * 1024;
+// Records a wave ring holds at most.
+constexpr size_t kMaxRecords = 16;
 
 // I8: one-byte codes (int8, or FP8 E4M3 when F8) with per-row scales.
 template <int D, bool I8, bool F8 = false>
-int launch(const pkv_decode_args &a, const SplitParams &p) {
+int launch(const pkv_decode_args &a, const SplitParams &p0) {
   auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8, F8>;
-  size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves);
+  SplitParams p = p0;
+  const size_t split = pkv_split_lds_bytes(a.num_seqs, kWaves);
+  // Result rings: what LDS is left of the workgroup's share of the CU, split
+  // over its waves, in records of G rows of D floats, G (m, l) pairs and the
+  // piece's place, 16-byte aligned.
+  const int G = a.num_q_heads / a.L->num_kv_heads;
+  const int rec = (G * D * 4 + G * 8 + 16 + 15) & ~15;
+  const size_t budget = a.waves_per_simd == 1 ? kRingLdsOneWg : kRingLdsTwoWg;
+  p.ring_off = (int32_t)split;
+  p.rec_bytes = rec;
+  p.nrec = budget > split ? (int32_t)std::min<size_t>((budget - split) / kWaves / rec, kMaxRecords) : 0;
+  size_t lds = split + (size_t)kWaves * p.nrec * rec;
   // One wave per SIMD: a workgroup takes more than half of a CU's 160 KiB of
   // LDS, so no second one is placed beside it.  Two waves on one SIMD do not
   // progress alike (the older wins issue), which leaves the younger behind.

@@ -162,6 +162,9 @@ struct SplitParams {
   int32_t max_ctx;
   int32_t maxp;           // partial slots per (sequence, query head)
   int32_t min_cpw;        // fewest chunks a wave is given (bounds maxp)
+  int32_t ring_off;       // matrix-core kernel: LDS byte offset of wave 0's result ring
+  int32_t rec_bytes;      // bytes of one ring record (a piece's G rows, their (m, l), its place)
+  int32_t nrec;           // records per wave ring (0: every piece is stored at once)
   float scale_log2;
 };
 
@@ -282,6 +285,9 @@ inline SplitParams pkv_split_params(const pkv_decode_args &a) {
   p.max_ctx = a.max_ctx;
   p.maxp = a.maxp;
   p.min_cpw = a.min_cpw;
+  p.ring_off = 0;
+  p.rec_bytes = 0;
+  p.nrec = 0;
   p.scale_log2 = a.scale_log2;
   return p;
 }
