@@ -396,6 +396,9 @@ def main():
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 wavefront-reduction, 2 matrix-core")
     ap.add_argument("--waves-per-simd", type=int, default=0,
                     help="matrix-core kernel: 1 or 2 resident waves per SIMD (0: chosen from the pool's sharing)")
+    ap.add_argument("--xcd-weights", default="none",
+                    help="per-XCD work weights of the balanced split: 'none' (equal shares, the default), "
+                         "'auto' (from traced untimed steps after the warm-up) or 8 comma-separated integers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only plain 1 GiB copies (PMC calibration)")
@@ -439,7 +442,7 @@ def main():
     # Enough layers (own pools) that one step stores more than 1 GiB of
     # distinct K/V, so the 256 MB Infinity Cache cannot hold a step's reads.
     layers = args.layers or min(64, max(1, math.ceil((1 << 30) / inst.kv_bytes_unique())))
-    total_steps = K + W
+    total_steps = K + W + 3  # warm-up, XCD-weight calibration and timed steps
     extra = B * (total_steps // 16 + 2)
     print(f"[bench] building {wl.name}: B={B} Hq={Hq} H={H} D={D} {wl.cache_dtype} cache, layers/step={layers}",
           flush=True)
@@ -489,7 +492,7 @@ def main():
     tail = (ctypes.c_float(gw.scale), V(ws.data_ptr()), ws_bytes)
     pin_ptr = [(V(p.data_ptr()), V(p.data_ptr() + 12 * B), V(p.data_ptr() + 8 * B)) for p in pin]
 
-    def step(k: int, timed_idx: int):
+    def step(k: int, timed_idx: int, first_opts=None):
         r = k % R
         ring_ev[r].synchronize()  # the copy that last read this pinned set is done
         slots_p, tables_p, ctx_p = pin_ptr[r]
@@ -504,6 +507,8 @@ def main():
         ev_layer = timed_idx % layers if timed_idx >= 0 else -1
         for layer in range(layers):
             opts = ev_opts[timed_idx] if layer == ev_layer else wps_opts
+            if first_opts is not None and layer == 0:
+                opts = first_opts
             L._check(lib.paged_kv_append(*append_args[layer]))
             L._check(lib.paged_attention_decode(*head[layer], max_ctx, *tail, ctypes.byref(opts), stream))
         return int(ctx_np.astype(np.int64).sum())
@@ -514,12 +519,40 @@ def main():
     for k in range(W):
         step(k, -1)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({W} steps), timing {K} steps", flush=True)
+    # Per-XCD weights: XCDs stream K/V at different rates, so equal shares
+    # leave the slowest running alone at the end.  'auto' traces the
+    # partition kernel of layer 0 on a few untimed steps and weighs each
+    # XCD's work by its streaming rate.
+    xw, n_cal = None, 0
+    if args.xcd_weights == "auto":
+        trace = torch.zeros(4 * L.PKV_TRACE_WAVES, dtype=torch.int32, device=dev)
+        recs = []
+        for c in range(3):
+            trace.zero_()
+            step(W + c, -1, L.decode_opts(args.partition, args.kernel, None, wps, trace=trace))
+            torch.cuda.synchronize()
+            t = trace.cpu().numpy().reshape(-1, 4)
+            recs.append(t[t[:, 1] > 0])
+        n_cal = 3
+        allrec = np.concatenate(recs)[:L.PKV_TRACE_WAVES]
+        if len(allrec):
+            try:
+                xw = L.xcd_weights_from_trace(allrec.reshape(-1))
+            except L.PagedKVError:
+                xw = None  # some XCD had no traced wave (a small grid): equal shares
+    elif args.xcd_weights != "none":
+        xw = [int(v) for v in args.xcd_weights.split(",")]
+    if xw is not None:
+        wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, xw)
+        ev_opts = [L.decode_opts(args.partition, args.kernel, (evs[2 * i], evs[2 * i + 1], None), wps, xw)
+                   for i in range(K)]
+    W_eff = W + n_cal
+    print(f"[bench] warmup done ({W} steps), xcd weights {xw}, timing {K} steps", flush=True)
     ctx_tokens = []
     marks = []
     t0 = time.perf_counter()
     for k in range(K):
-        ctx_tokens.append(step(W + k, k))
+        ctx_tokens.append(step(W_eff + k, k))
         marks.append(time.perf_counter())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -564,6 +597,7 @@ def main():
                    "layers_per_step": layers,
                    "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
                    "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "waves_per_simd": wps,
+                   "xcd_weights": xw,
                    "parallelism": "none"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s_per_layer": round(B / per_layer_s, 1),

@@ -339,7 +339,29 @@ typedef struct {
   void *ev_begin;           /* optional hipEvent_t recorded before the first kernel */
   void *ev_partition_done;  /* optional hipEvent_t recorded after the partition kernel */
   void *ev_end;             /* optional hipEvent_t recorded after the last kernel */
+  int32_t xcd_weights[8];   /* balanced split: relative work of the 8 XCDs (all 0 =
+                               equal).  XCD x runs the workgroups b with b % 8 == x
+                               and streams K/V at its own rate; weights from
+                               pkv_xcd_weights_from_trace make them finish
+                               together.  Used when all > 0 and the whole grid
+                               works; results depend on the weights, never on
+                               timing. */
+  int32_t *trace;           /* optional device buffer of 4 * PKV_TRACE_WAVES int32:
+                               the matrix-core kernel writes, per wave, its XCD,
+                               chunk count and start/end clock (100 MHz, low 32
+                               bits); clear it before the call (waves without
+                               work write nothing) */
 } pkv_decode_opts;
+
+/* Waves a decode trace buffer holds. */
+#define PKV_TRACE_WAVES 8192
+
+/* Per-XCD weights from a decode trace [balanced-split tuning; not part of
+ * the method]: weight x = 1000 * (chunks per time of XCD x's waves) /
+ * (mean over XCDs).  h_trace: host copy of the trace (4 int32 per wave,
+ * n_waves of them; all-zero records are skipped).  Fails with
+ * PKV_ERR_INVALID when some XCD has no traced wave. */
+int pkv_xcd_weights_from_trace(const int32_t *h_trace, int32_t n_waves, int32_t weights_out[8]);
 
 /* Bytes of workspace paged_attention_decode needs for these sizes and
  * options (0 when the call needs none).  opts may be NULL. */

@@ -75,7 +75,11 @@ class pkv_swap_stats(ctypes.Structure):
 class pkv_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("waves_per_simd", ctypes.c_int32),
                 ("ev_begin", ctypes.c_void_p),
-                ("ev_partition_done", ctypes.c_void_p), ("ev_end", ctypes.c_void_p)]
+                ("ev_partition_done", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
+                ("xcd_weights", ctypes.c_int32 * 8), ("trace", ctypes.c_void_p)]
+
+
+PKV_TRACE_WAVES = 8192  # waves a decode trace buffer holds (4 int32 each)
 
 
 # name -> (restype, argtypes) of every exported symbol of include/pagedkv.h
@@ -101,6 +105,7 @@ SIGNATURES = {
     "pkv_seq_block_table": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
     "pkv_batch_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
     "pkv_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(pkv_stats)]),
+    "pkv_xcd_weights_from_trace": (ctypes.c_int, [_P, _I32, _P]),
     "pkv_prefix_cache_enable": (ctypes.c_int, [_P, _I32]),
     "pkv_seq_create_from_prefix": (ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
     "pkv_seq_register_prefix": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
@@ -420,9 +425,32 @@ def pkv_copy_blocks(layout, k_pool, v_pool, pairs, stream=None):
                                  pairs.numel() // 2, _stream(stream)))
 
 
-def decode_opts(partition_tokens=0, kernel=0, events=None, waves_per_simd=0) -> pkv_decode_opts:
+def decode_opts(partition_tokens=0, kernel=0, events=None, waves_per_simd=0, xcd_weights=None,
+                trace=None) -> pkv_decode_opts:
+    """trace: optional device int32 tensor of 4 * PKV_TRACE_WAVES elements."""
     ev = list(events) if events else [None, None, None]
-    return pkv_decode_opts(int(partition_tokens), int(kernel), int(waves_per_simd), *[e if e else None for e in ev])
+    o = pkv_decode_opts(int(partition_tokens), int(kernel), int(waves_per_simd), *[e if e else None for e in ev])
+    if xcd_weights is not None:
+        w = [int(x) for x in xcd_weights]
+        if len(w) != 8:
+            raise ValueError("xcd_weights must hold 8 values")
+        o.xcd_weights[:] = w
+    if trace is not None:
+        import torch
+        o.trace = _dev(trace, "trace", torch.int32, 4 * PKV_TRACE_WAVES).value
+    return o
+
+
+def xcd_weights_from_trace(trace) -> list:
+    """Per-XCD weights (1000 = the mean rate) from a decode trace (a host
+    or device int32 tensor, or a numpy array, of 4 * PKV_TRACE_WAVES)."""
+    arr = np.ascontiguousarray(trace.cpu().numpy() if hasattr(trace, "cpu") else trace, dtype=np.int32).reshape(-1)
+    if arr.size < 4:
+        raise ValueError("trace too small")
+    out = np.zeros(8, np.int32)
+    _check(lib().pkv_xcd_weights_from_trace(arr.ctypes.data_as(ctypes.c_void_p), min(arr.size // 4, PKV_TRACE_WAVES),
+                                            out.ctypes.data_as(ctypes.c_void_p)))
+    return [int(x) for x in out]
 
 
 def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, partition_tokens=0,
@@ -433,7 +461,8 @@ def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_l
 
 
 def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
-                           workspace=None, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0):
+                           workspace=None, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0,
+                           xcd_weights=None, trace=None):
     """events: optional (begin, partition_done, end) raw hipEvent_t handles."""
     import torch
     pdt, rdt = pool_torch_dtype(layout), row_torch_dtype(layout)
@@ -450,7 +479,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
         ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < ws_need:
         raise ValueError(f"workspace of {ws_need} bytes needed, got {ws_bytes}")
-    o = decode_opts(partition_tokens, kernel, events, waves_per_simd)
+    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace)
     _check(lib().paged_attention_decode(
         ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", rdt),
         _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),

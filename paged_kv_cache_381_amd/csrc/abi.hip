@@ -57,7 +57,7 @@ size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 size_t split_ws_bytes(const pkv_layout *L, int32_t B, int32_t Hq, int32_t maxp) {
   const size_t rows = (size_t)B * Hq * maxp;
   return align16(rows * L->head_dim * sizeof(float)) + align16(rows * 2 * sizeof(float)) +
-         align16((size_t)(2 + B) * sizeof(int32_t));
+         align16((size_t)(PKV_HDR_INTS + B) * sizeof(int32_t));
 }
 
 }  // namespace
@@ -175,6 +175,10 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
     return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16, int8 or FP8 cache");
   if (kernel == 1 && pkv_is_q8(layout->kv_dtype))
     return pkv_set_error(PKV_ERR_INVALID, "an int8 or FP8 cache is read by the matrix-core kernel only");
+  if (opts)
+    for (int i = 0; i < PKV_REGIONS; ++i)
+      if (opts->xcd_weights[i] < 0 || opts->xcd_weights[i] > (1 << 20))
+        return pkv_set_error(PKV_ERR_INVALID, "xcd_weights[%d] = %d outside [0, 2^20]", i, opts->xcd_weights[i]);
   if (num_seqs > PKV_MAX_SPLIT_SEQS)
     return pkv_set_error(PKV_ERR_INVALID, "at most %d sequences per call (got %d)", PKV_MAX_SPLIT_SEQS, num_seqs);
   if (max_context_len > (1 << 22))
@@ -202,6 +206,8 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   a.min_cpw = mc;
   a.waves_per_simd = opts && opts->waves_per_simd ? opts->waves_per_simd : 1;
   a.maxp = split_maxp(max_context_len, mc);
+  for (int i = 0; i < PKV_REGIONS; ++i) a.xw[i] = opts ? opts->xcd_weights[i] : 0;
+  a.trace = opts ? opts->trace : nullptr;
   const size_t rows = (size_t)num_seqs * num_q_heads * a.maxp;
   char *ws = static_cast<char *>(workspace);
   a.ws_o = reinterpret_cast<float *>(ws);
@@ -215,6 +221,28 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   if (int r = record(opts ? opts->ev_partition_done : nullptr, stream)) return r;
   if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
   return record(opts ? opts->ev_end : nullptr, stream);
+}
+
+extern "C" int pkv_xcd_weights_from_trace(const int32_t *h_trace, int32_t n_waves, int32_t weights_out[8]) {
+  if (!h_trace || !weights_out || n_waves < 0 || n_waves > PKV_TRACE_WAVES)
+    return pkv_set_error(PKV_ERR_INVALID, "pkv_xcd_weights_from_trace: bad arguments");
+  double chunks[PKV_REGIONS] = {}, ticks[PKV_REGIONS] = {};
+  for (int32_t w = 0; w < n_waves; ++w) {
+    const int32_t *r = h_trace + PKV_TRACE_INTS * w;
+    if (r[1] <= 0 || r[0] < 0 || r[0] >= PKV_REGIONS) continue;
+    const uint32_t dt = (uint32_t)r[3] - (uint32_t)r[2];  // the clock's low bits may wrap
+    if (dt == 0) continue;
+    chunks[r[0]] += r[1];
+    ticks[r[0]] += dt;
+  }
+  double rate[PKV_REGIONS], mean = 0;
+  for (int x = 0; x < PKV_REGIONS; ++x) {
+    if (ticks[x] <= 0) return pkv_set_error(PKV_ERR_INVALID, "no traced wave on XCD %d", x);
+    rate[x] = chunks[x] / ticks[x];
+    mean += rate[x] / PKV_REGIONS;
+  }
+  for (int x = 0; x < PKV_REGIONS; ++x) weights_out[x] = (int32_t)std::lround(1000.0 * rate[x] / mean);
+  return PKV_OK;
 }
 
 extern "C" int paged_attention_prefill(const pkv_layout *layout, float *out, const void *q, const void *k_pool,

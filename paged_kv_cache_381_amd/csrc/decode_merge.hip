@@ -9,9 +9,9 @@
 //
 // The partials of segment (g, b) are those of the waves whose shares overlap
 // the segment's chunks, stored in share order.  The schedule header written by
-// the decode kernel gives the chunk scan and the number of waves used, from
-// which the segment's position and its first and last wave follow exactly as
-// in the decode kernel.  Segments held by one wave, and empty sequences, were
+// the decode kernel gives the chunk scan, the number of waves used and the
+// region bounds, from which the segment's position and its first and last
+// wave follow exactly as in the decode kernel.  Segments held by one wave, and empty sequences, were
 // written by the decode kernel and are skipped here.
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -24,11 +24,17 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
   const int b = bh / P.Hq, h = bh - b * P.Hq, g = h / P.G;
   const int64_t c_tot = (int64_t)P.H * P.ws_hdr[0];
   const int nwe = P.ws_hdr[1];
-  const int32_t *s_incl = P.ws_hdr + 2;
+  const int32_t *s_incl = P.ws_hdr + PKV_HDR_INTS;
   const int cnt = s_incl[b] - (b ? s_incl[b - 1] : 0);
   if (cnt == 0 || c_tot == 0) return;
   const int64_t seg0 = (int64_t)g * P.ws_hdr[0] + (s_incl[b] - cnt);
-  const int w0 = wave_of(seg0, c_tot, nwe), w1 = wave_of(seg0 + cnt - 1, c_tot, nwe);
+  Regions rg;
+  rg.C = c_tot;
+  rg.nwe = nwe;
+  rg.nr = P.ws_hdr[2];
+  rg.wpr = nwe / rg.nr;
+  rg.bounds = reinterpret_cast<const int64_t *>(P.ws_hdr + 4);
+  const int w0 = rg.wave_of(seg0), w1 = rg.wave_of(seg0 + cnt - 1);
   const int np = min(w1 - w0 + 1, P.maxp);
   if (np <= 1) return;
   const size_t row = (size_t)bh * P.maxp;

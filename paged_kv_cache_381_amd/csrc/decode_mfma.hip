@@ -97,6 +97,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
 
   const int lane = threadIdx.x & 63;
   const int H = P.H, G = P.G;
+  const uint32_t t_start = (uint32_t)__builtin_amdgcn_s_memrealtime();
   Share sh;
   if (!split_begin<W, D>(P, s_lds, sh)) return;
   const int64_t lo = sh.lo, hi = sh.hi;
@@ -380,6 +381,14 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     if (!whole && lane < G)
       *reinterpret_cast<float2 *>(P.ws_ml + 2 * ((row0 + lane) * P.maxp + slot)) =
           *reinterpret_cast<const float2 *>(rec + G * D * 4 + lane * 8);
+  }
+  // Optional trace: the wave's XCD group (workgroups are dealt round-robin
+  // to the 8 XCDs), its chunks, and its start and end times (100 MHz clock,
+  // low 32 bits), from which per-XCD streaming rates and weights follow.
+  if (P.trace && lane == 0 && sh.wave < PKV_TRACE_WAVES) {
+    const uint32_t t_end = (uint32_t)__builtin_amdgcn_s_memrealtime();
+    *reinterpret_cast<int4 *>(P.trace + PKV_TRACE_INTS * sh.wave) =
+        make_int4((int)(blockIdx.x & 7), (int)(hi - lo), (int)t_start, (int)t_end);
   }
 }
 

@@ -152,7 +152,8 @@ struct SplitParams {
   const int32_t *ctx;     // [B]
   float *ws_o;            // [B][Hq][maxp][D]   partial outputs
   float *ws_ml;           // [B][Hq][maxp][2]   partial (max, sum)
-  int32_t *ws_hdr;        // [2 + B]: chunks per kv head, waves used, inclusive chunk scan
+  int32_t *ws_hdr;        // [PKV_HDR_INTS + B]: chunks per kv head, waves used, regions,
+                          // region bounds (int64), inclusive chunk scan
   int32_t B;
   int32_t num_blocks;
   int32_t H;
@@ -165,6 +166,8 @@ struct SplitParams {
   int32_t ring_off;       // matrix-core kernel: LDS byte offset of wave 0's result ring
   int32_t rec_bytes;      // bytes of one ring record (a piece's G rows, their (m, l), its place)
   int32_t nrec;           // records per wave ring (0: every piece is stored at once)
+  int32_t xw[PKV_REGIONS];  // per-XCD weights of the work (all 0: equal shares)
+  int32_t *trace;         // nullable: per wave, its XCD group, chunks and start/end times
   float scale_log2;
 };
 
@@ -245,9 +248,67 @@ __device__ __forceinline__ int waves_used(int64_t c_tot, int nw, int min_cpw) {
   return (int)max((int64_t)1, min((int64_t)nw, cap));
 }
 
-// Wave whose share holds flattened chunk x (shares are [w*C/N, (w+1)*C/N)).
-__device__ __forceinline__ int wave_of(int64_t x, int64_t c_tot, int nwe) {
-  return (int)(((x + 1) * nwe - 1) / c_tot);
+// Regions of the chunk list.  With per-XCD weights the list is cut into 8
+// regions, region r sized by weight r and shared equally by the waves of
+// XCD r; otherwise one region holds the whole list.  bounds[0..nr] are the
+// region starts (int64, in LDS or in the schedule header), so that
+// wave_of, and the share of every wave, follow from them exactly alike in
+// the decode and merge kernels.
+struct Regions {
+  int64_t C;
+  int nwe, nr, wpr;
+  const int64_t *bounds;  // nr + 1 entries
+
+  // Region holding chunk x.
+  __device__ int region_of(int64_t x) const {
+    int r = 0;
+    for (int i = 1; i < nr; ++i) r = x >= bounds[i] ? i : r;
+    return r;
+  }
+  // Wave whose share holds chunk x (shares are [R + i*S/wpr, R + (i+1)*S/wpr)
+  // within region r = [R, R + S)).
+  __device__ int wave_of(int64_t x) const {
+    const int r = region_of(x);
+    const int64_t R = bounds[r], S = bounds[r + 1] - R;
+    return r * wpr + (int)(((x - R + 1) * wpr - 1) / S);
+  }
+  __device__ void share(int w, int64_t &lo, int64_t &hi) const {
+    const int r = w / wpr, i = w - r * wpr;
+    const int64_t R = bounds[r], S = bounds[r + 1] - R;
+    lo = R + (int64_t)i * S / wpr;
+    hi = R + (int64_t)(i + 1) * S / wpr;
+  }
+};
+
+// Region bounds of a launch into b[0..PKV_REGIONS]; returns the region
+// count.  Weights apply when every XCD holds the same number of used waves
+// (the whole grid works, and workgroups spread evenly over the 8 XCDs),
+// every weight is positive, and every wave's share keeps min_cpw chunks;
+// otherwise there is one region.
+__device__ inline int region_bounds(int64_t c_tot, int nwe, int nwg_waves, int nwg, const int32_t *xw,
+                                    int min_cpw, int64_t *b) {
+  int64_t wsum = 0;
+  bool pos = true;
+#pragma unroll
+  for (int i = 0; i < PKV_REGIONS; ++i) {
+    wsum += xw[i];
+    pos = pos && xw[i] > 0;
+  }
+  b[0] = 0;
+  if (pos && nwe == nwg_waves && nwg % PKV_REGIONS == 0 && wsum < (1 << 24)) {
+    const int wpr = nwe / PKV_REGIONS;
+    int64_t cum = 0;
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < PKV_REGIONS; ++i) {
+      cum += xw[i];
+      b[i + 1] = i + 1 == PKV_REGIONS ? c_tot : c_tot * cum / wsum;
+      ok = ok && (b[i + 1] - b[i]) / wpr >= min_cpw;
+    }
+    if (ok) return PKV_REGIONS;
+  }
+  b[1] = c_tot;
+  return 1;
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
@@ -260,7 +321,11 @@ __device__ __forceinline__ int xcd_logical(int wg, int nwg) {
 // LDS of a decode workgroup: the chunk scan, the clamped lengths and W wave
 // totals, padded to 16 bytes (int32 units: pkv_split_lds_ints), then
 // extra_floats of per-wave slices.
-__host__ __device__ inline int pkv_split_lds_ints(int num_seqs, int waves) { return (2 * num_seqs + waves + 3) & ~3; }
+__host__ __device__ inline int pkv_split_lds_ints(int num_seqs, int waves) {
+  return ((2 * num_seqs + waves + 3) & ~3) + 2 * (PKV_REGIONS + 1) + 2;
+}
+// Offset (int32 units) of the region bounds in a decode workgroup's LDS.
+__host__ __device__ inline int pkv_split_bounds_ints(int num_seqs, int waves) { return (2 * num_seqs + waves + 3) & ~3; }
 inline size_t pkv_split_lds_bytes(int num_seqs, int waves, int extra_floats = 0) {
   return (size_t)pkv_split_lds_ints(num_seqs, waves) * sizeof(int32_t) + (size_t)extra_floats * sizeof(float);
 }
@@ -288,6 +353,8 @@ inline SplitParams pkv_split_params(const pkv_decode_args &a) {
   p.ring_off = 0;
   p.rec_bytes = 0;
   p.nrec = 0;
+  for (int i = 0; i < PKV_REGIONS; ++i) p.xw[i] = a.xw[i];
+  p.trace = a.trace;
   p.scale_log2 = a.scale_log2;
   return p;
 }
@@ -310,6 +377,7 @@ struct Share {
   int64_t c_seq, c_tot;
   int nwe, wave;
   int64_t lo, hi;
+  Regions rg;
 
   __device__ int cnt_of(int b) const { return uniform(s_incl[b] - (b ? s_incl[b - 1] : 0)); }
   __device__ int len_of(int b) const { return uniform(s_len[b]); }
@@ -372,7 +440,7 @@ struct Share {
 
   // Partial slot of this wave for the cursor's segment (< maxp by
   // construction; clamped so a broken invariant cannot write out of bounds).
-  __device__ int piece(const Cursor &c, int maxp) const { return min(wave - wave_of(c.seg0, c_tot, nwe), maxp - 1); }
+  __device__ int piece(const Cursor &c, int maxp) const { return min(wave - rg.wave_of(c.seg0), maxp - 1); }
 };
 
 // Common start of the balanced-split kernels: the chunk scan (all threads),
@@ -386,12 +454,20 @@ __device__ bool split_begin(const SplitParams &P, int32_t *s_lds, Share &sh) {
   const int64_t c_tot = (int64_t)P.H * c_seq;
   const int nwg = gridDim.x;
   const int nwe = waves_used(c_tot, nwg * W, P.min_cpw);
+  int64_t *s_bounds = reinterpret_cast<int64_t *>(s_lds + pkv_split_bounds_ints(P.B, W));
+  int32_t *s_nr = s_lds + pkv_split_bounds_ints(P.B, W) + 2 * (PKV_REGIONS + 1);
+  if (tid == 0) *s_nr = region_bounds(c_tot, nwe, nwg * W, nwg, P.xw, P.min_cpw, s_bounds);
+  __syncthreads();
+  const int nr = *s_nr;
   if (blockIdx.x == 0) {
     if (tid == 0) {
       P.ws_hdr[0] = (int32_t)c_seq;
       P.ws_hdr[1] = nwe;
+      P.ws_hdr[2] = nr;
+      P.ws_hdr[3] = 0;
     }
-    for (int i = tid; i < P.B; i += 64 * W) P.ws_hdr[2 + i] = s_incl[i];
+    if (tid <= nr) reinterpret_cast<int64_t *>(P.ws_hdr + 4)[tid] = s_bounds[tid];
+    for (int i = tid; i < P.B; i += 64 * W) P.ws_hdr[PKV_HDR_INTS + i] = s_incl[i];
     for (int b = 0; b < P.B; ++b) {
       const int prev = b ? s_incl[b - 1] : 0;
       if (s_incl[b] == prev)
@@ -409,9 +485,13 @@ __device__ bool split_begin(const SplitParams &P, int32_t *s_lds, Share &sh) {
   sh.c_seq = c_seq;
   sh.c_tot = c_tot;
   sh.nwe = nwe;
+  sh.rg.C = c_tot;
+  sh.rg.nwe = nwe;
+  sh.rg.nr = nr;
+  sh.rg.wpr = nwe / nr;
+  sh.rg.bounds = s_bounds;
   sh.wave = uniform(xcd_logical(blockIdx.x, nwg) * W + w);
   if (sh.wave >= nwe || c_tot == 0) return false;
-  sh.lo = (int64_t)sh.wave * c_tot / nwe;
-  sh.hi = (int64_t)(sh.wave + 1) * c_tot / nwe;
+  sh.rg.share(sh.wave, sh.lo, sh.hi);
   return sh.lo < sh.hi;
 }

@@ -26,6 +26,14 @@ inline int64_t pkv_row_bytes(const pkv_layout *L) {
 }
 
 
+// XCDs of the chip: regions of the chunk list that can be weighted.
+#define PKV_REGIONS 8
+// Schedule header ints ahead of the chunk scan: chunks per kv head, waves
+// used, regions, a pad, then PKV_REGIONS + 1 int64 region bounds.
+#define PKV_HDR_INTS (4 + 2 * (PKV_REGIONS + 1))
+// Ints a decode wave writes to a trace buffer (PKV_TRACE_WAVES waves).
+#define PKV_TRACE_INTS 4
+
 // Kernel launchers (decode_*.hip, kv_append.hip).  They return a HIP error
 // code (0 = success); arguments were validated by the caller.
 struct pkv_decode_args {
@@ -43,7 +51,9 @@ struct pkv_decode_args {
   float scale_log2;  // scale * log2(e): scores are kept in base 2
   float *ws_o;       // [B][Hq][maxp][D] partial outputs
   float *ws_ml;      // [B][Hq][maxp][2] partial (max, sum)
-  int32_t *ws_hdr;   // [2 + B] schedule header
+  int32_t *ws_hdr;   // [PKV_HDR_INTS + B] schedule header
+  int32_t xw[PKV_REGIONS];  // per-XCD weights of the work (all 0: equal shares)
+  int32_t *trace;    // nullable device buffer: PKV_TRACE_INTS per wave
   int32_t maxp;      // partial slots per (sequence, query head)
   int32_t min_cpw;   // fewest 32-token chunks per wave
   int32_t waves_per_simd;  // resident waves per SIMD of the matrix-core kernel (1 or 2)

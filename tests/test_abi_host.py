@@ -65,11 +65,12 @@ def test_sizes():
     assert P.pkv_pool_bytes(f8) == 10 * 8 * (16 * 128 + 64) == f8.pool_elems
     # Both kernels split the batch the same way: partial slots per (sequence, query head)
     # = ceil(ceil(max_ctx / 32) / fewest chunks per wave) + 1, then partial (m, l) and a
-    # header of 2 + B int32, each region padded to 16 bytes
+    # header, each region padded to 16 bytes
     def split(B, Hq, D, max_ctx, min_chunks):
         maxp = -(-(-(-max_ctx // 32)) // min_chunks) + 1
         pad = lambda x: -(-x // 16) * 16
-        return pad(B * Hq * maxp * D * 4) + pad(B * Hq * maxp * 2 * 4) + pad((2 + B) * 4)
+        # header: 4 ints, 9 int64 region bounds, then the chunk scan of B ints
+        return pad(B * Hq * maxp * D * 4) + pad(B * Hq * maxp * 2 * 4) + pad((4 + 18 + B) * 4)
     assert P.paged_attention_workspace_bytes(lay, 4, 32, 512) == split(4, 32, 128, 512, 4)
     assert P.paged_attention_workspace_bytes(lay, 3, 32, 4096, partition_tokens=256) == split(3, 32, 128, 4096, 8)
     assert P.paged_attention_workspace_bytes(lay, 4, 32, 1) == split(4, 32, 128, 1, 4)
@@ -109,6 +110,10 @@ def test_decode_argument_errors_before_any_launch():
     assert call(scale=float("inf")) == L.PKV_ERR_INVALID
     assert call(part=48) == L.PKV_ERR_INVALID
     assert call(kernel=7) == L.PKV_ERR_INVALID
+    for bad_w in ([-1] + [1] * 7, [1 << 21] * 8):
+        ow = L.decode_opts(xcd_weights=bad_w)
+        assert lib.paged_attention_decode(ctypes.byref(lay), fake, fake, fake, fake, fake, fake, 2, 4, 8, 64, 0.1,
+                                          None, 0, ctypes.byref(ow), None) == L.PKV_ERR_INVALID
     assert call(kernel=2, lay_=P.make_layout(16, 2, 128, "f32")) == L.PKV_ERR_INVALID
     assert call(kernel=1, lay_=P.make_layout(16, 2, 128, "int8")) == L.PKV_ERR_INVALID
     assert call(kernel=1, lay_=P.make_layout(16, 2, 128, "fp8")) == L.PKV_ERR_INVALID
@@ -305,3 +310,38 @@ def test_workload_bookkeeping_matches_oracle(name):
         assert a["num_used"] == o["num_used"] and a["tokens_stored"] == o["tokens_stored"]
     finally:
         P.pkv_pool_destroy(pool)
+
+
+def test_xcd_weights_from_trace():
+    """Weights are each XCD's chunks per clock tick over the mean of the
+    eight rates, times 1000; all-zero records are skipped; a clock that
+    wraps between a wave's start and end still gives its duration."""
+    rng = np.random.default_rng(5)
+    rates = np.array([1.0, 0.9, 1.1, 0.8, 1.0, 1.2, 1.0, 1.0])
+    rec = []
+    for w in range(64):
+        x = w % 8
+        chunks = int(rng.integers(10, 40))
+        start = int(rng.integers(0, 1 << 31))
+        dur = int(round(chunks / rates[x] * 100))
+        rec.append([x, chunks, start, start + dur])
+    rec[5][2], rec[5][3] = 0x7FFFFFF0, -0x7FFFFFF0 + 10  # end wraps past 2^31 (int32 view)
+    rec[5][1] = 30
+    rec.append([0, 0, 0, 0])  # a wave that wrote nothing
+    t = np.array(rec, np.int64)
+    dt = (t[:, 3] - t[:, 2]) % (1 << 32)
+    ch = np.zeros(8)
+    tk = np.zeros(8)
+    for (x, c, _, _), d in zip(t, dt):
+        if c > 0:
+            ch[x] += c
+            tk[x] += d
+    r = ch / tk
+    want = [int(np.floor(1000 * v / r.mean() + 0.5)) for v in r]
+    trace = np.zeros(4 * L.PKV_TRACE_WAVES, np.int32)
+    trace[:t.size] = (t.reshape(-1) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    assert L.xcd_weights_from_trace(trace) == want
+    trace[4 * 3:4 * 64:32] = 0  # XCD 3 loses every record
+    trace[4 * 3 + 1:4 * 64:32] = 0
+    with pytest.raises(P.PagedKVError):
+        L.xcd_weights_from_trace(trace)

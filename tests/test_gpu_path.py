@@ -153,13 +153,45 @@ def test_small_workloads_every_output(case, kernel, part):
     check_close(out, _built[key], TOL[inst.wl.dtype], f"{name} {kw} kernel={kernel} P={part}")
 
 
+_full_ref = {}
+
+
+def full_ref(name, inst):
+    if name not in _full_ref:
+        say(f"[oracle] {name}: {orc.num_threads()} threads")
+        _full_ref[name] = orc.run_workload(inst)["out"]
+    return _full_ref[name]
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_b64", "best_of_8", "shared_prefix_b128"])
 def test_full_workload_every_output(name):
     inst, gw = built(name)
-    say(f"[oracle] {name}: {orc.num_threads()} threads")
-    ref = orc.run_workload(inst)["out"]
+    ref = full_ref(name, inst)
     out = gw.decode().cpu().numpy()
     check_close(out, ref, TOL["bf16"], f"{name} full")
+
+
+def test_xcd_weights_every_output_and_trace():
+    """Per-XCD weights move the region bounds of the balanced split: the
+    outputs still match the oracle everywhere and repeat bit for bit, and the
+    trace holds one record per working wave, on all 8 XCDs, whose chunk
+    counts add up to the batch's chunks."""
+    name = "llama3_8b_b64"
+    inst, gw = built(name)
+    ref = full_ref(name, inst)
+    w = [1000, 870, 1130, 800, 1000, 1200, 950, 1050]
+    trace = torch.zeros(4 * L.PKV_TRACE_WAVES, dtype=torch.int32, device="cuda")
+    a = gw.decode(xcd_weights=w, trace=trace).clone()
+    check_close(a.cpu().numpy(), ref, TOL["bf16"], f"{name} weights {w}")
+    assert torch.equal(a, gw.decode(xcd_weights=w).clone())
+    t = trace.cpu().numpy().reshape(-1, 4)
+    used = t[t[:, 1] > 0]
+    assert set(used[:, 0].tolist()) == set(range(8))
+    assert int(used[:, 1].sum()) == inst.wl.num_kv_heads * sum(-(-int(n) // 32) for n in inst.ctx)
+    got = L.xcd_weights_from_trace(trace)
+    say(f"  measured weights {got}")
+    assert all(x > 0 for x in got)
+    check_close(gw.decode(xcd_weights=got).cpu().numpy(), ref, TOL["bf16"], f"{name} weights {got}")
 
 
 @pytest.mark.parametrize("name,nsample", [("llama3_70b_b256", 6), ("mha_long", 8)])
