@@ -171,6 +171,17 @@ def test_full_workload_every_output(name):
     check_close(out, ref, TOL["bf16"], f"{name} full")
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_b64", "llama3_8b_b64_int8"])
+def test_many_short_segments_every_output(name):
+    """4096 sequences of 1-40 tokens: every wave ends dozens of segments,
+    more than its LDS result ring holds, so pieces past the ring's capacity
+    take the direct stores; every output must still match the oracle."""
+    inst, gw = built(name, batch=4096, ctx_range=(1, 40))
+    say(f"[oracle] {name} 4096 short sequences")
+    ref = orc.run_workload(inst)["out"]
+    check_close(gw.decode().cpu().numpy(), ref, TOL["bf16"], f"{name} 4096 short sequences")
+
+
 def test_xcd_weights_every_output_and_trace():
     """Per-XCD weights move the region bounds of the balanced split: the
     outputs still match the oracle everywhere and repeat bit for bit, and the
