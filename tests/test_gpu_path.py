@@ -173,13 +173,15 @@ def test_full_workload_every_output(name):
 
 @pytest.mark.parametrize("name", ["llama3_8b_b64", "llama3_8b_b64_int8"])
 def test_many_short_segments_every_output(name):
-    """4096 sequences of 1-40 tokens: every wave ends dozens of segments,
-    more than its LDS result ring holds, so pieces past the ring's capacity
+    """2600 sequences of 1-16 tokens: one chunk per segment, about 20
+    segment ends per wave, more than its LDS result ring holds (9 records
+    of 2080 bytes at this batch, whose chunk scan takes 20 KiB of the
+    workgroup's 96 KiB), so pieces past the ring's capacity
     take the direct stores; every output must still match the oracle."""
-    inst, gw = built(name, batch=4096, ctx_range=(1, 40))
-    say(f"[oracle] {name} 4096 short sequences")
+    inst, gw = built(name, batch=2600, ctx_range=(1, 16))
+    say(f"[oracle] {name} 2600 short sequences")
     ref = orc.run_workload(inst)["out"]
-    check_close(gw.decode().cpu().numpy(), ref, TOL["bf16"], f"{name} 4096 short sequences")
+    check_close(gw.decode().cpu().numpy(), ref, TOL["bf16"], f"{name} 2600 short sequences")
 
 
 def test_xcd_weights_every_output_and_trace():
