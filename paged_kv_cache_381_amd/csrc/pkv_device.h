@@ -467,11 +467,16 @@ __device__ bool split_begin(const SplitParams &P, int32_t *s_lds, Share &sh) {
       P.ws_hdr[3] = 0;
     }
     if (tid <= nr) reinterpret_cast<int64_t *>(P.ws_hdr + 4)[tid] = s_bounds[tid];
-    for (int i = tid; i < P.B; i += 64 * W) P.ws_hdr[PKV_HDR_INTS + i] = s_incl[i];
-    for (int b = 0; b < P.B; ++b) {
-      const int prev = b ? s_incl[b - 1] : 0;
-      if (s_incl[b] == prev)
-        for (int i = tid; i < P.Hq * D; i += 64 * W) P.out[(size_t)b * P.Hq * D + i] = 0.f;
+    // Each thread takes its own sequences, so this workgroup starts
+    // streaming as early as the others (a walk over the whole batch by
+    // every thread cost it microseconds); an empty sequence (padding) has
+    // its rows zeroed by the thread that found it.
+    for (int b = tid; b < P.B; b += 64 * W) {
+      P.ws_hdr[PKV_HDR_INTS + b] = s_incl[b];
+      if (s_incl[b] == (b ? s_incl[b - 1] : 0)) {
+        float *row = P.out + (size_t)b * P.Hq * D;  // out is only 4-byte aligned
+        for (int i = 0; i < P.Hq * D; ++i) row[i] = 0.f;
+      }
     }
   }
   sh.s_incl = s_incl;
