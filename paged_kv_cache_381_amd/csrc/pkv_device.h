@@ -295,7 +295,10 @@ __device__ inline int region_bounds(int64_t c_tot, int nwe, int nwg_waves, int n
     pos = pos && xw[i] > 0;
   }
   b[0] = 0;
-  if (pos && nwe == nwg_waves && nwg % PKV_REGIONS == 0 && wsum < (1 << 24)) {
+  // c_tot * (a partial weight sum) must fit in int64 for the bounds to be
+  // exact and increasing.
+  if (pos && nwe == nwg_waves && nwg % PKV_REGIONS == 0 && wsum < (1 << 24) &&
+      c_tot < ((int64_t)1 << 62) / wsum) {
     const int wpr = nwe / PKV_REGIONS;
     int64_t cum = 0;
     bool ok = true;
