@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
-MODEL_LAYERS = {"llama3_8b_b64": 32, "llama3_70b_b256": 80, "shared_prefix_b128": 32, "best_of_8": 32,
+MODEL_LAYERS = {"llama3_8b_b64": 32, "llama3_70b_b256": 80, "llama3_70b_b256_int8": 80, "shared_prefix_b128": 32, "best_of_8": 32,
                 "mha_long": 32, "tiny_fp32": 1}
 PARTITION_KERNELS = ("decode_mfma_kernel", "decode_valu_kernel")
 

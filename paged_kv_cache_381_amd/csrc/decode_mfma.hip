@@ -79,9 +79,10 @@ constexpr float kSlack = 8.0f;
 #define PKV_MFMA_NBUF 2
 #endif
 // An int8 chunk is half the bytes in half the registers: more of them stay in
-// flight to keep as many bytes on the way from memory.
+// flight to keep as many bytes on the way from memory (three measured best:
+// two starve the 70B-shaped batch, four and six slow the 8B-shaped one).
 #ifndef PKV_MFMA_NBUF_I8
-#define PKV_MFMA_NBUF_I8 4
+#define PKV_MFMA_NBUF_I8 3
 #endif
 
 template <int D, int W, int NB, bool I8, bool F8>

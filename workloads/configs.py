@@ -251,6 +251,11 @@ WORKLOADS = {
         "llama3_70b_b256", 3, batch=256, num_q_heads=64, num_kv_heads=8, head_dim=128, dtype="bf16",
         ctx_fixed=(4096,) * 256,
         description="Llama-3-70B-shaped single-layer decode: B 256, 64 q / 8 kv heads, d 128, bf16, ctx 4096, shuffled pool 1.25x demand"),
+    "llama3_70b_b256_int8": Workload(
+        "llama3_70b_b256_int8", 3, batch=256, num_q_heads=64, num_kv_heads=8, head_dim=128, dtype="bf16",
+        ctx_fixed=(4096,) * 256, cache="int8", same_data_as="llama3_70b_b256",
+        description="llama3_70b_b256 with an int8 cache: the same lengths, order and bf16 rows, quantised "
+                    "on append to int8 codes with a float32 scale per token and kv head"),
     "shared_prefix_b128": Workload(
         "shared_prefix_b128", 4, batch=128, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
         prefix_len=2000, suffix_range=(16, 512),
