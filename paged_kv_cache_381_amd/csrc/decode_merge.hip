@@ -18,6 +18,16 @@
 
 namespace {
 
+// Sum over the 64 lanes in registers: DPP within each 16-lane row, then the
+// gfx950 lane swaps across rows (no LDS round trip).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
   const int bh = blockIdx.x;
@@ -40,22 +50,50 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
   const size_t row = (size_t)bh * P.maxp;
   const float2 *ml = reinterpret_cast<const float2 *>(P.ws_ml) + row;
   const float *o = P.ws_o + row * D;
+  const int lane = threadIdx.x;
+  // The partials' maxima and weighted sums, 64 partials at a time across the
+  // lanes (one round trip per 64, not one per partial).
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[i].x);
+  for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[i].x);
+  M = rows_max4_swap(row_max16(M));
   float L = 0.f;
   float acc[D / 64];
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const float2 mi = ml[i];
-    const float f = fast_exp2(mi.x - M);
-    L += mi.y * f;
+  for (int i0 = 0; i0 < np; i0 += 64) {
+    const int n = min(np - i0, 64);
+    float f = 0.f;  // lane j: weight of partial i0 + j
+    if (lane < n) {
+      const float2 mi = ml[i0 + lane];
+      f = fast_exp2(mi.x - M);
+      L += mi.y * f;
+    }
+    // Output rows four partials at a time, so their loads are in flight
+    // together; the sum runs over the partials in order.
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+      float v[4][D / 64];
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) acc[k] += o[(size_t)i * D + 64 * k + threadIdx.x] * f;
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) v[u][k] = o[(size_t)(i0 + j + u) * D + 64 * k + lane];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + u));
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) acc[k] += v[u][k] * fu;
+      }
+    }
+    for (; j < n; ++j) {
+      const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) acc[k] += o[(size_t)(i0 + j) * D + 64 * k + lane] * fj;
+    }
   }
+  L = wave_sum(L);
   const float inv = 1.f / L;
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) P.out[(size_t)bh * D + 64 * k + threadIdx.x] = acc[k] * inv;
+  for (int k = 0; k < D / 64; ++k) P.out[(size_t)bh * D + 64 * k + lane] = acc[k] * inv;
 }
 
 }  // namespace
