@@ -350,7 +350,15 @@ class Book:
         for sid in protect:
             self._seq(sid)
         guarded = {blk for sid in protect for blk in self.seqs[sid]["table"] if blk >= 0}
-        named = {blk for q in self.seqs.values() for blk in q["table"] if blk >= 0}
+        entries = {}
+        for q in self.seqs.values():
+            for blk in q["table"]:
+                if blk >= 0:
+                    entries[blk] = entries.get(blk, 0) + 1
+        # Candidates: blocks named by some table whose every reference is a
+        # table entry.  A block also held by the caller (pkv_block_alloc or
+        # pkv_block_incref) stays: the caller's id must keep naming it.
+        named = {blk for blk, k in entries.items() if self.ref[blk] == k}
         pairs = []
         examined = 0
         while len(pairs) < want and self.host_free and examined < 2 * self.num_blocks:

@@ -48,6 +48,8 @@ def run(both, op, *args):
             "configure": lambda n: L.pkv_swap_configure(both.pool, n),
             "swap_out": lambda want, prot: [tuple(x) for x in L.pkv_swap_out(both.pool, want, prot).tolist()],
             "swap_in": lambda s: [tuple(x) for x in L.pkv_seq_swap_in(both.pool, s).tolist()],
+            "incref": lambda blk: L.pkv_block_incref(both.pool, blk),
+            "block_free": lambda blk: L.pkv_block_free(both.pool, blk),
             "export": lambda ids: L.pkv_batch_block_tables(both.pool, ids, 64)[1].tolist()}[op]
     bk = both.book
     bookf = {"create": bk.create,
@@ -57,6 +59,8 @@ def run(both, op, *args):
              "configure": bk.configure_swap,
              "swap_out": lambda want, prot: bk.swap_out(want, prot),
              "swap_in": bk.swap_in,
+             "incref": bk.incref,
+             "block_free": bk.decref,
              "export": lambda ids: bk.export_tables(ids)[1]}[op]
     try:
         rb, eb = bookf(*args), None
@@ -145,6 +149,32 @@ def test_turn_one_victims_are_not_taken_twice():
         b.close()
 
 
+def test_externally_held_block_is_not_a_victim():
+    """A block the caller also holds (pkv_block_incref) is not a candidate:
+    its id must go on naming the same device block.  A holds blocks 0, 1;
+    the caller takes a reference to block 0.  swap_out(2): block 0 is passed
+    over untouched (its bit stays set), block 1 loses its bit on the first
+    turn and goes to slot 0 on the second; the hand stops on 2.  Once the
+    caller drops its reference, block 0 is a candidate: swap_out(1) clears
+    its bit on the first turn and takes it on the second (slot 1), and the
+    hand stops on 1."""
+    b = Both(6)
+    try:
+        A = run(b, "create"); run(b, "append", A, 32)
+        run(b, "configure", 4)
+        run(b, "incref", 0)
+        assert run(b, "swap_out", 2, []) == [(1, 0)]
+        assert b.book.block_table(A) == [0, -1] and b.book.refcount(0) == 2
+        assert b.book.swap_stats()["clock_hand"] == 2
+        b.same()
+        run(b, "block_free", 0)
+        assert run(b, "swap_out", 1, []) == [(0, 1)]
+        assert b.book.block_table(A) == [-2, -1] and b.book.swap_stats()["clock_hand"] == 1
+        b.same()
+    finally:
+        b.close()
+
+
 def test_swap_in_all_or_nothing_and_limits():
     b = Both(4)
     try:
@@ -167,7 +197,8 @@ def test_swap_in_all_or_nothing_and_limits():
         b.close()
 
 
-OPS = st.lists(st.tuples(st.sampled_from(["create", "fork", "append", "free", "export", "swap_out", "swap_in"]),
+OPS = st.lists(st.tuples(st.sampled_from(["create", "fork", "append", "free", "export", "swap_out", "swap_in",
+                                          "incref"]),
                          st.integers(0, 9), st.integers(0, 37)), max_size=60)
 
 
@@ -177,7 +208,7 @@ def test_swap_matches_oracle_random_ops(ops, seed, host):
     n = 16
     order = np.random.default_rng(seed).permutation(n).astype(np.int32)
     b = Both(n, order)
-    live = []
+    live, loose = [], []
     try:
         run(b, "configure", host)
         for op, i, k in ops:
@@ -198,6 +229,18 @@ def test_swap_matches_oracle_random_ops(ops, seed, host):
                 run(b, "swap_out", k % 6, [live[(i + j) % len(live)] for j in range(i % 3)])
             elif op == "swap_in":
                 run(b, "swap_in", live[i % len(live)])
+            elif op == "incref":  # the caller takes, then maybe drops, a reference to a table's block
+                tab = [e for e in b.book.block_table(live[i % len(live)]) if e >= 0]
+                if tab:
+                    blk = tab[k % len(tab)]
+                    run(b, "incref", blk)
+                    if k % 2:
+                        run(b, "block_free", blk)
+                    else:
+                        loose.append(blk)
             b.same()
+        for blk in loose:  # references the caller still holds
+            run(b, "block_free", blk)
+        b.same()
     finally:
         b.close()
