@@ -268,9 +268,10 @@ typedef struct {
  * Refused while a slot holds a block. */
 int pkv_swap_configure(pkv_pool *pool, int32_t num_host_blocks);
 /* Choose up to `want` victims with the Clock hand, which moves over device
- * block ids from where it stopped: a block held by some sequence, not in the
- * prefix cache and not held by a sequence of protect_ids (the batch about to
- * run) is a candidate; a candidate whose reference bit is set has it cleared
+ * block ids from where it stopped: a block held by some sequence and only
+ * through block tables (a block the caller also holds by pkv_block_alloc or
+ * pkv_block_incref is not), not in the prefix cache and not held by a
+ * sequence of protect_ids (the batch about to run) is a candidate; a candidate whose reference bit is set has it cleared
  * and is passed over; one whose bit is clear moves to a host slot: every
  * table entry naming it becomes -(slot+1), its references move to the slot
  * and the device block returns to the free stack.  Stops after `want`

@@ -673,9 +673,14 @@ extern "C" int pkv_swap_out(pkv_pool *pool, int32_t want, const int64_t *protect
     return pkv_set_error(PKV_ERR_INVALID, "NULL argument");
   if (want > cap) return pkv_set_error(PKV_ERR_CAPACITY, "want %d blocks, pair buffer holds %d", want, cap);
   std::vector<uint8_t> guarded(pool->layout.num_blocks, 0), named(pool->layout.num_blocks, 0);
+  std::vector<int32_t> entries(pool->layout.num_blocks, 0);
   for (const auto &kv : pool->seqs)
     for (int32_t b : kv.second.table)
-      if (b >= 0) named[b] = 1;
+      if (b >= 0) ++entries[b];
+  // Candidates: blocks named by some table whose every reference is a table
+  // entry; a block the caller also holds (pkv_block_alloc / incref) stays,
+  // so the caller's id keeps naming it.
+  for (int32_t b = 0; b < pool->layout.num_blocks; ++b) named[b] = entries[b] > 0 && entries[b] == pool->ref[b];
   for (int32_t i = 0; i < n_protect; ++i) {
     auto it = pool->seqs.find(protect_ids[i]);
     if (it == pool->seqs.end())

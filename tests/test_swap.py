@@ -154,7 +154,8 @@ def test_externally_held_block_is_not_a_victim():
     its id must go on naming the same device block.  A holds blocks 0, 1;
     the caller takes a reference to block 0.  swap_out(2): block 0 is passed
     over untouched (its bit stays set), block 1 loses its bit on the first
-    turn and goes to slot 0 on the second; the hand stops on 2.  Once the
+    turn and goes to slot 0 on the second; no second victim exists, so the
+    hand ends its two turns where it began, on 0.  Once the
     caller drops its reference, block 0 is a candidate: swap_out(1) clears
     its bit on the first turn and takes it on the second (slot 1), and the
     hand stops on 1."""
@@ -165,7 +166,7 @@ def test_externally_held_block_is_not_a_victim():
         run(b, "incref", 0)
         assert run(b, "swap_out", 2, []) == [(1, 0)]
         assert b.book.block_table(A) == [0, -1] and b.book.refcount(0) == 2
-        assert b.book.swap_stats()["clock_hand"] == 2
+        assert b.book.swap_stats()["clock_hand"] == 0
         b.same()
         run(b, "block_free", 0)
         assert run(b, "swap_out", 1, []) == [(0, 1)]
