@@ -10,8 +10,10 @@ have their own K/V pools and share the block tables; several layers are run
 per step so that the bytes read per step exceed the 256 MB Infinity Cache.
 
 Prints one JSON line: KV GB/s of the whole step (inputs resident in HBM), the
-roofline of the partition kernel from HIP events recorded around it on the
-launch stream, and the CPU oracle timed on the host on the same workload.
+roofline of the attention call (partition kernel and split-context merge)
+from HIP events recorded around it on the launch stream, the same rate as a
+share of a streaming-read probe's, pool usage and internal fragmentation,
+and the CPU oracle timed on the host on the same workload.
 """
 from __future__ import annotations
 
@@ -383,6 +385,48 @@ def copy_probe(gib: float, reps: int):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": reps}))
 
 
+PROBE_TILES = 1 << 18  # 1 GiB of 4 KiB tiles: four times the Infinity Cache
+
+
+def stream_probe(reps: int = 5):
+    """Achievable read rate for the decode kernels' access pattern: the
+    streaming-read probe (libpkvprobe.so) reads 1 GiB of 4 KiB tiles in a
+    seeded random order and in address order, one and two waves per SIMD;
+    returns GB/s per variant (HIP events, mean over reps after a warm-up)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_381_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        raise SystemExit(f"{B.PROBE_LIB} is not built (run __graft_entry__.build())")
+    plib = ctypes.CDLL(B.PROBE_LIB)
+    plib.pkv_probe_stream_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    n = PROBE_TILES
+    buf = torch.empty(n * 1024, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    orders = {"random": np.random.default_rng(4096).permutation(n).astype(np.int32),
+              "sequential": np.arange(n, dtype=np.int32)}
+    sink = torch.empty(4 * 2 * plib.pkv_probe_compute_units(), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for oname, order in orders.items():
+        d_order = torch.from_numpy(order).cuda()
+        for wps in (1, 2):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+            for r in range(reps + 1):
+                if r:
+                    ev[2 * r - 2].record()
+                rc = plib.pkv_probe_stream_tiles(buf.data_ptr(), n, d_order.data_ptr(), wps, sink.data_ptr(), stream)
+                assert rc == 0, f"probe launch failed ({rc})"
+                if r:
+                    ev[2 * r - 1].record()
+            torch.cuda.synchronize()
+            ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) / reps
+            res[f"{oname}_wps{wps}"] = round(n * 4096 / (ms * 1e-3) / 1e9, 1)
+    del buf
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +446,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only plain 1 GiB copies (PMC calibration)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="run only the streaming-read probe (1 GiB of 4 KiB tiles, random and address order)")
+    ap.add_argument("--no-stream-probe", action="store_true", help="skip the probe in a decode run")
+    ap.add_argument("--tables", choices=("shuffled", "identity"), default="shuffled",
+                    help="physical block placement: the workload's shuffled pool, or blocks handed out in "
+                         "address order (each sequence's blocks consecutive)")
     ap.add_argument("--traffic-summary", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR", "BENCH_LOG"),
                     help="write profiles/decode_<workload>_traffic.txt from rocprofv3 --pmc output (no GPU)")
@@ -422,6 +472,10 @@ def main():
     if args.copy_probe:
         copy_probe(1.0, 10)
         return
+    if args.stream_probe:
+        r = stream_probe(10)
+        print(json.dumps({"stream_probe_gbps": r, "tiles": PROBE_TILES, "tile_bytes": 4096}), flush=True)
+        return
 
     import workloads
     from workloads import prefill as PW
@@ -435,6 +489,8 @@ def main():
         bench_swap(args)
         return
     inst = workloads.get(args.workload)
+    if args.tables == "identity":
+        inst.free_order = np.arange(inst.num_blocks, dtype=np.int32)
     wl = inst.wl
     B, H, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
     K, W = args.steps, args.warmup
@@ -482,7 +538,15 @@ def main():
     ncow = ctypes.c_int32(0)
     lay = ctypes.byref(cache.layout)
     wps_opts = L.decode_opts(args.partition, args.kernel, None, wps)
-    ev_opts = [L.decode_opts(args.partition, args.kernel, (evs[2 * i], evs[2 * i + 1], None), wps) for i in range(K)]
+    def timed_opts(xw=None):
+        # Even timed steps bracket the whole attention call (partition kernel
+        # and split-context merge), odd ones the partition kernel alone; one
+        # event pair per step, since a record in between would idle the GPU.
+        return [L.decode_opts(args.partition, args.kernel,
+                              (evs[2 * i], None, evs[2 * i + 1]) if i % 2 == 0 else (evs[2 * i], evs[2 * i + 1], None),
+                              wps, xw) for i in range(K)]
+
+    ev_opts = timed_opts()
     ws_bytes = ws.numel() * ws.element_size()
     append_args = [(lay, V(cache.k_pools[i].data_ptr()), V(cache.v_pools[i].data_ptr()), V(k_new.data_ptr()),
                     V(v_new.data_ptr()), V(d_slots.data_ptr()), B, stream) for i in range(layers)]
@@ -544,8 +608,7 @@ def main():
         xw = [int(v) for v in args.xcd_weights.split(",")]
     if xw is not None:
         wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, xw)
-        ev_opts = [L.decode_opts(args.partition, args.kernel, (evs[2 * i], evs[2 * i + 1], None), wps, xw)
-                   for i in range(K)]
+        ev_opts = timed_opts(xw)
     W_eff = W + n_cal
     print(f"[bench] warmup done ({W} steps), xcd weights {xw}, timing {K} steps", flush=True)
     ctx_tokens = []
@@ -566,18 +629,28 @@ def main():
     kv_bytes = sum(ctx_tokens) * tok_bytes * layers
     gbps = kv_bytes / elapsed / 1e9
     ms_step = elapsed / K * 1e3
-    durs = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(K)]
+    durs_all = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(K)]
     hip.destroy(evs)
+    durs = durs_all[0::2]  # whole attention call: partition + merge
+    durs_part = durs_all[1::2] or durs
     avg_ms = sum(durs) / len(durs)
+    avg_part_ms = sum(durs_part) / len(durs_part)
     bytes_per_launch = sum(ctx_tokens) / K * tok_bytes  # logical: every sequence's whole context
     # What HBM must deliver: a prefix held once in shared blocks counts once.
     unique_per_launch = bytes_per_launch - (B - 1) * wl.prefix_len * tok_bytes
     achieved = unique_per_launch / (avg_ms * 1e-3) / 1e9
     achieved_logical = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    achieved_part = unique_per_launch / (avg_part_ms * 1e-3) / 1e9
     traffic = stored_traffic(wl.name)
     per_layer_s = elapsed / K / layers
-    print(f"[bench] {K} steps in {elapsed:.3f} s; partition kernel avg {avg_ms * 1e3:.1f} us "
-          f"({achieved:.0f} GB/s of distinct K/V, {achieved_logical:.0f} GB/s logical)", flush=True)
+    print(f"[bench] {K} steps in {elapsed:.3f} s; attention call avg {avg_ms * 1e3:.1f} us "
+          f"({achieved:.0f} GB/s of distinct K/V, {achieved_logical:.0f} GB/s logical); partition kernel alone "
+          f"{avg_part_ms * 1e3:.1f} us", flush=True)
+    probe = None
+    if not args.no_stream_probe:
+        probe = stream_probe()
+        print(f"[bench] streaming-read probe (1 GiB of 4 KiB tiles), GB/s: {probe}", flush=True)
+    pst = cache.stats()
 
     res = {
         "metric": METRIC,
@@ -597,12 +670,19 @@ def main():
                    "layers_per_step": layers,
                    "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
                    "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "waves_per_simd": wps,
-                   "xcd_weights": xw,
+                   "xcd_weights": xw, "tables": args.tables,
                    "parallelism": "none"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "attention_pct_of_probe": round(100 * achieved / max(probe[k] for k in probe if k.startswith("random")), 2)
+        if probe else None,
+        "stream_probe_gbps": probe,
+        "pool": {"blocks": pst["num_blocks"], "usage": round(pst["usage"], 4),
+                 "internal_fragmentation": round(pst["internal_fragmentation"], 4),
+                 "tokens_logical": pst["tokens_logical"], "tokens_stored": pst["tokens_stored"],
+                 "shared_blocks": pst["num_shared"]},
         "decode_tokens_per_s_per_layer": round(B / per_layer_s, 1),
         "decode_tokens_per_s_attention_full_depth": round(B / (per_layer_s * MODEL_LAYERS.get(wl.name, 32)), 1),
-        "roofline": {"kernel": "paged_attention_decode partition kernel", "bound": "hbm",
+        "roofline": {"kernel": "paged_attention_decode (partition kernel + split-context merge)", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "avg_launch_us": round(avg_ms * 1e3, 2),
@@ -611,7 +691,13 @@ def main():
                                                   round(max(durs) * 1e3, 2)],
                      "bytes_per_launch": int(unique_per_launch),
                      "logical_bytes_per_launch": int(bytes_per_launch),
-                     "achieved_logical": round(achieved_logical, 2), "traffic": traffic},
+                     "achieved_logical": round(achieved_logical, 2),
+                     "partition_kernel_us": round(avg_part_ms * 1e3, 2),
+                     "partition_kernel_frac": round(achieved_part / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "traffic_source": "stored rocprofv3 PMC summary of the partition kernel for these kernel sources "
+                                       f"(profiles/decode_{wl.name}_traffic.txt), not measured in this run"
+                     if traffic else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

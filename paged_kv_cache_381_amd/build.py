@@ -12,6 +12,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpagedkv.so")
+# The streaming-read probe: a measurement aid beside the library (not part of
+# the decode path), loaded by bench.py only.
+PROBE_LIB = os.path.join(HERE, "libpkvprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -20,15 +23,11 @@ def sources():
     return sorted(glob.glob(os.path.join(csrc, "*.cpp")) + glob.glob(os.path.join(csrc, "*.hip")))
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # MFMA accumulators in VGPRs: the decode kernel rescales them with
-           # vector ops, which cannot read AGPRs without a copy each way.
-           "-mllvm", "-amdgpu-mfma-vgpr-form",
-           "-Wall", "-Wno-unused-function",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *extra, "-o", LIB + ".tmp", *sources()]
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd, out, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,7 +37,25 @@ def build(verbose: bool = False, extra=()) -> str:
         print("\n".join(msgs), file=sys.stderr)
     if r.returncode:
         raise RuntimeError(f"hipcc failed ({r.returncode})")
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+
+
+def build_probe(verbose: bool = False) -> str:
+    src = os.path.join(HERE, "probe", "stream_probe.hip")
+    _run([HIPCC, *HIP_FLAGS, "-Wall", "-o", PROBE_LIB + ".tmp", src], PROBE_LIB, verbose)
+    return PROBE_LIB
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    build_probe(verbose)
+    cmd = [HIPCC, *HIP_FLAGS,
+           # MFMA accumulators in VGPRs: the decode kernel rescales them with
+           # vector ops, which cannot read AGPRs without a copy each way.
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
+           "-Wall", "-Wno-unused-function",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+           *extra, "-o", LIB + ".tmp", *sources()]
+    _run(cmd, LIB, verbose)
     return LIB
 
 

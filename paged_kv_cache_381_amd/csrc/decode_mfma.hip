@@ -105,6 +105,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   // This wave's ring of finished pieces, written out after its last load.
   uint8_t *const ring = reinterpret_cast<uint8_t *>(s_lds) + P.ring_off + (threadIdx.x >> 6) * P.nrec * P.rec_bytes;
   int held = 0;  // records in the ring
+  // A record: G rows of D floats, G (m, l) pairs, then the piece's place as
+  // an int4 at the next 16-byte boundary (G may be odd).
+  const int meta_off = (G * D * 4 + G * 8 + 15) & ~15;
 
   const int r16 = lane & 15, grp = lane >> 4;
   // Row r16 of the score MFMAs holds a token of block (r16 >> 3); see header.
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
                 make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
           if (grp == 0) *reinterpret_cast<float2 *>(rec + G * D * 4 + r16 * 8) = make_float2(m, lsum);
         }
-        if (lane == 0) *reinterpret_cast<int4 *>(rec + G * D * 4 + G * 8) = make_int4(whole, cur.b, cur.g, slot);
+        if (lane == 0) *reinterpret_cast<int4 *>(rec + meta_off) = make_int4(whole, cur.b, cur.g, slot);
         ++held;
       } else {
         if (r16 < G) {
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   // then the (m, l) of a partial.
   for (int r = 0; r < held; ++r) {
     const uint8_t *rec = ring + r * P.rec_bytes;
-    const int4 meta = *reinterpret_cast<const int4 *>(rec + G * D * 4 + G * 8);
+    const int4 meta = *reinterpret_cast<const int4 *>(rec + meta_off);
     const bool whole = uniform(meta.x) != 0;
     const size_t row0 = (size_t)uniform(meta.y) * P.Hq + (size_t)uniform(meta.z) * G;
     const int slot = uniform(meta.w);
@@ -414,7 +417,7 @@ int launch(const pkv_decode_args &a, const SplitParams &p0) {
   // over its waves, in records of G rows of D floats, G (m, l) pairs and the
   // piece's place, 16-byte aligned.
   const int G = a.num_q_heads / a.L->num_kv_heads;
-  const int rec = (G * D * 4 + G * 8 + 16 + 15) & ~15;
+  const int rec = ((G * D * 4 + G * 8 + 15) & ~15) + 16;
   const size_t budget = a.waves_per_simd == 1 ? kRingLdsOneWg : kRingLdsTwoWg;
   p.ring_off = (int32_t)split;
   p.rec_bytes = rec;

@@ -1,0 +1,119 @@
+// Streaming-read probe: how fast one MI355X reads a buffer of 4 KiB tiles in
+// a given order, with the access pattern of the decode kernels.  It computes
+// nothing of the method; it gives the achievable HBM read rate that the decode
+// kernels' rate is compared with (paged decode reads random 4 KiB (block, kv
+// head) tiles through the block tables).
+//
+// Grid and pattern as the decode kernels run them: one 256-thread workgroup
+// per compute unit (dynamic LDS above half of the CU's 160 KiB keeps a second
+// one away), every wave an equal contiguous share of the tile order, four
+// tiles (16 KiB, a decode chunk's K and V) per step, every lane 16-byte loads,
+// two steps of loads kept in registers (one in flight while the other is
+// folded), as the bf16 decode kernel keeps two chunks.  Optionally two
+// workgroups per compute unit (two waves per SIMD) keep twice the bytes in
+// flight.  The words read are folded with xor
+// into one value per wave, stored at the end, so no load is dead.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTilesPerStep = 4;
+constexpr int kTileUnits = 4096 / 16 / 64;  // 16-byte loads per lane per tile
+constexpr int kLdsOneWgPerCu = 81 * 1024;
+
+typedef const int32_t __attribute__((address_space(4))) *const_i32;
+
+constexpr int NB = 2;
+
+__global__ __launch_bounds__(64 * kWaves) void stream_tiles_kernel(const uint4 *buf, int64_t n_steps,
+                                                                   const int32_t *order, uint32_t *sink) {
+  const int64_t n_tiles = n_steps * kTilesPerStep;
+  extern __shared__ int32_t s_unused[];
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
+  // The wave index is uniform: tile ids then come through scalar loads and
+  // never wait behind the tile data.
+  const int64_t w = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
+  const int64_t lo = w * n_steps / nw, hi = (w + 1) * n_steps / nw;
+  if (lo >= hi) return;
+  uint4 r[NB][kTilesPerStep][kTileUnits];
+  // Loads of step x into buffer I; a step past the share re-reads the last
+  // one, so every path issues the same loads and the waits stay exact.
+  auto issue = [&](auto bi, int64_t x) {
+    constexpr int I = decltype(bi)::value;
+    const int64_t s = x < hi ? x : hi - 1;
+#pragma unroll
+    for (int t = 0; t < kTilesPerStep; ++t) {
+      int64_t tile = *(const_i32)(order + s * kTilesPerStep + t);
+      tile = tile < 0 ? 0 : tile >= n_tiles ? n_tiles - 1 : tile;  // a bad order cannot leave the buffer
+      const uint4 *p = buf + (size_t)tile * (4096 / 16);
+#pragma unroll
+      for (int u = 0; u < kTileUnits; ++u) r[I][t][u] = p[64 * u + lane];
+    }
+  };
+  uint32_t acc = 0;
+  auto fold = [&](auto bi) {
+    constexpr int I = decltype(bi)::value;
+#pragma unroll
+    for (int t = 0; t < kTilesPerStep; ++t)
+#pragma unroll
+      for (int u = 0; u < kTileUnits; ++u) acc ^= r[I][t][u].x ^ r[I][t][u].y ^ r[I][t][u].z ^ r[I][t][u].w;
+  };
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((issue(std::integral_constant<int, Is>{}, lo + Is), __builtin_amdgcn_sched_barrier(0)), ...);
+  }(std::make_integer_sequence<int, NB>{});
+  // Each step folds the oldest buffer and refills it with the step NB ahead,
+  // so NB - 1 steps of loads stay in flight behind the one being folded.
+  int64_t x = lo;
+  while (x < hi) {
+    [&]<int... Is>(std::integer_sequence<int, Is...>) {
+      ((fold(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0),
+        issue(std::integral_constant<int, Is>{}, x + NB), __builtin_amdgcn_sched_barrier(0), ++x),
+       ...);
+    }(std::make_integer_sequence<int, NB>{});
+  }
+  acc ^= __shfl_xor(acc, 1, 64);
+  if (lane == 0) sink[w] = acc;
+}
+
+int launch(const void *buf, int64_t n_tiles, const int32_t *order, uint32_t *sink, int nwg, size_t lds,
+           hipStream_t stream) {
+  auto kern = stream_tiles_kernel;
+  if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsOneWgPerCu))
+    return (int)e;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kWaves), lds, stream, reinterpret_cast<const uint4 *>(buf),
+                     n_tiles / kTilesPerStep, order, sink);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+// Read the n_tiles 4 KiB tiles of buf in the order d_order (int32, n_tiles
+// entries, each in [0, n_tiles)) on waves_per_simd (1 or 2) workgroups of
+// four waves per compute unit.  d_sink receives one uint32 per wave
+// (4 * waves_per_simd * compute units of them).  n_tiles must be a positive
+// multiple of 4.  Returns a HIP error code (0 = launched), or -1 for bad
+// arguments.
+extern "C" int pkv_probe_stream_tiles(const void *buf, int64_t n_tiles, const int32_t *d_order,
+                                      int32_t waves_per_simd, uint32_t *d_sink, void *stream) {
+  if (!buf || !d_order || !d_sink || n_tiles <= 0 || n_tiles % kTilesPerStep) return -1;
+  if (waves_per_simd != 1 && waves_per_simd != 2) return -1;
+  int dev = 0, cus = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return (int)e;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
+  return launch(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, waves_per_simd == 1 ? kLdsOneWgPerCu : 0,
+                reinterpret_cast<hipStream_t>(stream));
+}
+
+// Compute units of the current device (the probe's sink holds 4 per unit
+// and workgroup per unit).
+extern "C" int pkv_probe_compute_units(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return -1;
+  return cus;
+}

@@ -5,8 +5,7 @@ included.  Attention is compared element by element: max abs error <= 1e-5
 for the float32 workload and <= 2e-2 for the bf16 workloads (bf16 K/V,
 float32 accumulation).  Full-size workloads run in the launch configuration
 the bench times (default partition, automatic kernel choice) and are checked
-on every output where the oracle is cheap, else on sampled sequences computed
-one by one from the generator's contiguous K/V.
+on every output against the oracle's run of the same build.
 """
 import math
 import sys
@@ -163,12 +162,19 @@ def full_ref(name, inst):
     return _full_ref[name]
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_b64", "best_of_8", "shared_prefix_b128"])
+@pytest.mark.parametrize("name", ["llama3_8b_b64", "llama3_70b_b256", "best_of_8", "shared_prefix_b128", "mha_long"])
 def test_full_workload_every_output(name):
+    """Every output of a full-size workload, in the launch configuration the
+    bench times, against the oracle's run of the same build (OpenMP over
+    sequence x query head on the host)."""
     inst, gw = built(name)
     ref = full_ref(name, inst)
     out = gw.decode().cpu().numpy()
     check_close(out, ref, TOL["bf16"], f"{name} full")
+    if name in ("llama3_70b_b256", "mha_long"):  # the largest pools: give their memory back
+        _built.pop((name, ()), None)
+        _full_ref.pop(name, None)
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_b64", "llama3_8b_b64_int8"])
@@ -205,21 +211,6 @@ def test_xcd_weights_every_output_and_trace():
     say(f"  measured weights {got}")
     assert all(x > 0 for x in got)
     check_close(gw.decode(xcd_weights=got).cpu().numpy(), ref, TOL["bf16"], f"{name} weights {got}")
-
-
-@pytest.mark.parametrize("name,nsample", [("llama3_70b_b256", 6), ("mha_long", 8)])
-def test_full_workload_sampled(name, nsample):
-    inst, gw = built(name)
-    out = gw.decode().cpu().numpy()
-    assert np.isfinite(out).all()
-    B = inst.wl.batch
-    rng = np.random.default_rng(0)
-    picks = sorted(set([0, B - 1] + rng.choice(B, size=min(B, nsample) - 2, replace=False).tolist()))
-    q = inst.q()
-    for b in picks:
-        ref = orc.contiguous_attention(inst.wl.dtype, q[b], inst.seq_kv(b, "k"), inst.seq_kv(b, "v"),
-                                       1 / math.sqrt(inst.wl.head_dim))
-        check_close(out[b], ref, TOL["bf16"], f"{name} seq {b} (ctx {inst.ctx[b]})")
 
 
 def test_deterministic_and_placement_invariant():

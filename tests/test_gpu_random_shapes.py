@@ -46,8 +46,8 @@ def check_close(got, ref, tol, what):
 def decode_case(i):
     rng = np.random.default_rng(7000 + i)
     cache = ["bf16", "f32", "int8"][i % 3]
-    G = int(rng.choice([1, 2, 4, 8, 16]))
-    hkv = int(rng.choice([1, 2, 4])) if G < 16 else 1
+    G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 16]))
+    hkv = int(rng.choice([1, 2, 4])) if G < 12 else 1
     D = int(rng.choice([64, 128]))
     B = int(rng.integers(1, 9))
     kw = dict(batch=B, num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=D,
@@ -74,6 +74,31 @@ def test_decode_random_shape(i):
     ref = orc.run_workload(inst)["out"]
     out = gw.decode(partition_tokens=part, kernel=kernel, waves_per_simd=wps).cpu().numpy()
     check_close(out, ref, TOL[inst.wl.cache_dtype], f"decode case {i}")
+
+
+ODD_GROUPS = [(G, cache, kernel) for G in (3, 5, 6, 12) for cache, kernel in
+              (("bf16", 1), ("bf16", 2), ("int8", 2), ("fp8", 2))]
+
+
+@pytest.mark.parametrize("G,cache,kernel", ODD_GROUPS)
+def test_decode_group_not_power_of_two(G, cache, kernel):
+    """Group sizes that are not powers of two: the matrix-core kernel's
+    padded head columns (columns G..15 repeat head G-1) and its ring records
+    (G rows, G (m, l) pairs, the place at the next 16-byte boundary), and the
+    wavefront kernel's group padded up to a power of two.  Contexts cross
+    block and chunk edges and are long enough to be cut between waves."""
+    hkv = 2
+    ctx = (1, 17, 33, 250, 700, 1500)
+    kw = dict(batch=len(ctx), num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=128, dtype="bf16", ctx_fixed=ctx)
+    if cache != "bf16":
+        kw["cache"] = cache
+    inst = workloads.configs.scaled("llama3_8b_b64", ctx_range=(), pool_blocks=0, **kw).instantiate()
+    say(f"[groups] G {G} {cache} kernel {kernel}: ctx {inst.ctx.tolist()}")
+    gw = GpuWorkload(inst)
+    ref = orc.run_workload(inst)["out"]
+    for part, wps in ((0, 1), (32, 2)):
+        out = gw.decode(partition_tokens=part, kernel=kernel, waves_per_simd=wps).cpu().numpy()
+        check_close(out, ref, TOL["bf16"], f"G {G} {cache} kernel {kernel} partition {part} waves/SIMD {wps}")
 
 
 def prefill_case(i):
