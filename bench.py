@@ -391,8 +391,9 @@ PROBE_TILES = 1 << 18  # 1 GiB of 4 KiB tiles: four times the Infinity Cache
 def stream_probe(reps: int = 5):
     """Achievable read rate for the decode kernels' access pattern: the
     streaming-read probe (libpkvprobe.so) reads 1 GiB of 4 KiB tiles in a
-    seeded random order and in address order, one and two waves per SIMD;
-    returns GB/s per variant (HIP events, mean over reps after a warm-up)."""
+    seeded random order and in address order, with cached and with
+    non-temporal loads, one wave per SIMD; returns GB/s per variant (HIP
+    events, mean over reps after a warm-up)."""
     import numpy as np
     import torch
     from paged_kv_cache_381_amd import build as B
@@ -400,7 +401,7 @@ def stream_probe(reps: int = 5):
         raise SystemExit(f"{B.PROBE_LIB} is not built (run __graft_entry__.build())")
     plib = ctypes.CDLL(B.PROBE_LIB)
     plib.pkv_probe_stream_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
-                                            ctypes.c_void_p, ctypes.c_void_p]
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     n = PROBE_TILES
     buf = torch.empty(n * 1024, dtype=torch.int32, device="cuda")
     buf.fill_(1)
@@ -411,18 +412,19 @@ def stream_probe(reps: int = 5):
     res = {}
     for oname, order in orders.items():
         d_order = torch.from_numpy(order).cuda()
-        for wps in (1, 2):
+        for loads, nt in (("cached", 0), ("streaming", 1)):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
             for r in range(reps + 1):
                 if r:
                     ev[2 * r - 2].record()
-                rc = plib.pkv_probe_stream_tiles(buf.data_ptr(), n, d_order.data_ptr(), wps, sink.data_ptr(), stream)
+                rc = plib.pkv_probe_stream_tiles(buf.data_ptr(), n, d_order.data_ptr(), 1, nt, sink.data_ptr(),
+                                                 stream)
                 assert rc == 0, f"probe launch failed ({rc})"
                 if r:
                     ev[2 * r - 1].record()
             torch.cuda.synchronize()
             ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) / reps
-            res[f"{oname}_wps{wps}"] = round(n * 4096 / (ms * 1e-3) / 1e9, 1)
+            res[f"{oname}_{loads}"] = round(n * 4096 / (ms * 1e-3) / 1e9, 1)
     del buf
     return res
 
@@ -449,6 +451,8 @@ def main():
     ap.add_argument("--stream-probe", action="store_true",
                     help="run only the streaming-read probe (1 GiB of 4 KiB tiles, random and address order)")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the probe in a decode run")
+    ap.add_argument("--load-policy", type=int, default=0,
+                    help="K/V tile loads: 0 auto, 1 streaming (non-temporal), 2 cached")
     ap.add_argument("--tables", choices=("shuffled", "identity"), default="shuffled",
                     help="physical block placement: the workload's shuffled pool, or blocks handed out in "
                          "address order (each sequence's blocks consecutive)")
@@ -537,14 +541,14 @@ def main():
     cow = np.empty((B, 2), dtype=np.int32)
     ncow = ctypes.c_int32(0)
     lay = ctypes.byref(cache.layout)
-    wps_opts = L.decode_opts(args.partition, args.kernel, None, wps)
+    wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, load_policy=args.load_policy)
     def timed_opts(xw=None):
         # Even timed steps bracket the whole attention call (partition kernel
         # and split-context merge), odd ones the partition kernel alone; one
         # event pair per step, since a record in between would idle the GPU.
         return [L.decode_opts(args.partition, args.kernel,
                               (evs[2 * i], None, evs[2 * i + 1]) if i % 2 == 0 else (evs[2 * i], evs[2 * i + 1], None),
-                              wps, xw) for i in range(K)]
+                              wps, xw, load_policy=args.load_policy) for i in range(K)]
 
     ev_opts = timed_opts()
     ws_bytes = ws.numel() * ws.element_size()
@@ -593,7 +597,8 @@ def main():
         recs = []
         for c in range(3):
             trace.zero_()
-            step(W + c, -1, L.decode_opts(args.partition, args.kernel, None, wps, trace=trace))
+            step(W + c, -1, L.decode_opts(args.partition, args.kernel, None, wps, trace=trace,
+                                          load_policy=args.load_policy))
             torch.cuda.synchronize()
             t = trace.cpu().numpy().reshape(-1, 4)
             recs.append(t[t[:, 1] > 0])
@@ -607,7 +612,7 @@ def main():
     elif args.xcd_weights != "none":
         xw = [int(v) for v in args.xcd_weights.split(",")]
     if xw is not None:
-        wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, xw)
+        wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, xw, load_policy=args.load_policy)
         ev_opts = timed_opts(xw)
     W_eff = W + n_cal
     print(f"[bench] warmup done ({W} steps), xcd weights {xw}, timing {K} steps", flush=True)
@@ -670,7 +675,7 @@ def main():
                    "layers_per_step": layers,
                    "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
                    "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "waves_per_simd": wps,
-                   "xcd_weights": xw, "tables": args.tables,
+                   "xcd_weights": xw, "tables": args.tables, "load_policy": args.load_policy,
                    "parallelism": "none"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "attention_pct_of_probe": round(100 * achieved / max(probe[k] for k in probe if k.startswith("random")), 2)

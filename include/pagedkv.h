@@ -323,11 +323,10 @@ int pkv_swap_copy(const pkv_layout *layout, void *dst_k, void *dst_v, int32_t ds
 
 /* Decode options (all fields may be zero / NULL for defaults). */
 typedef struct {
-  int32_t partition_tokens; /* a positive multiple of 32, or 0 for the default.
-                               Matrix-core kernel: the fewest context tokens one
-                               wave is given by the balanced split (default 128).
-                               Wavefront-reduction kernel: tokens per
-                               split-context partition (default 512). */
+  int32_t partition_tokens; /* a positive multiple of 32, or 0 for the default
+                               (128): the fewest context tokens the balanced
+                               split gives one wave, in either kernel.  Fewer
+                               tokens per wave cut contexts more finely. */
   int32_t kernel;           /* 0 auto (matrix cores for int8 and FP8, and
                                for bf16 with G >= 4); 1 the wavefront-
                                reduction kernel (f32, bf16); 2 the matrix-core
@@ -339,7 +338,7 @@ typedef struct {
                                are mostly shared (and so L2-resident) better. */
   void *ev_begin;           /* optional hipEvent_t recorded before the first kernel */
   void *ev_partition_done;  /* optional hipEvent_t recorded after the partition kernel */
-  void *ev_end;             /* optional hipEvent_t recorded after the last kernel */
+  void *ev_end;             /* optional hipEvent_t recorded after the merge kernel */
   int32_t xcd_weights[8];   /* balanced split: relative work of the 8 XCDs (all 0 =
                                equal).  XCD x runs the workgroups b with b % 8 == x
                                and streams K/V at its own rate; weights from
@@ -347,6 +346,12 @@ typedef struct {
                                together.  Used when all > 0 and the whole grid
                                works; results depend on the weights, never on
                                timing. */
+  int32_t load_policy;      /* K/V tile loads: 0 auto (streaming for f32 and
+                               bf16 caches with one wave per SIMD, cached
+                               otherwise), 1 streaming: the non-temporal hint,
+                               for batches that read every tile once, 2 cached:
+                               tiles kept in L2 for reuse (blocks shared by
+                               many sequences) */
   int32_t *trace;           /* optional device buffer of 4 * PKV_TRACE_WAVES int32:
                                the matrix-core kernel writes, per wave, its XCD,
                                chunk count and start/end clock (100 MHz, low 32
@@ -365,7 +370,14 @@ typedef struct {
 int pkv_xcd_weights_from_trace(const int32_t *h_trace, int32_t n_waves, int32_t weights_out[8]);
 
 /* Bytes of workspace paged_attention_decode needs for these sizes and
- * options (0 when the call needs none).  opts may be NULL. */
+ * options (opts may be NULL).  Layout: the partial outputs and (max, sum)
+ * pairs of contexts cut between waves, two slots of G query rows per wave
+ * (its first and its last context), then the merge kernel's schedule,
+ *   float32 [nslots][G][D], float32 [nslots][G][2], int32 [22 + num_seqs],
+ *   nslots = 2 * max(1, min(2048, num_seqs * H * ceil(max_context_len / 32)
+ *                                  / fewest chunks per wave)),
+ * each region padded to 16 bytes.  Its contents need not be preserved
+ * between calls.  Depends on the sizes only, not on the device. */
 size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seqs,
                                        int32_t num_q_heads, int32_t max_context_len,
                                        const pkv_decode_opts *opts);
@@ -382,16 +394,19 @@ size_t paged_attention_workspace_bytes(const pkv_layout *layout, int32_t num_seq
  *   max_context_len: an upper bound of every context length (sizes the grid);
  *   a longer length is treated as max_context_len
  *   scale: usually 1 / sqrt(D)
- *   workspace: device scratch of paged_attention_workspace_bytes() bytes
- *   (may be NULL when that is 0); its contents are not preserved.
+ *   workspace: device scratch of paged_attention_workspace_bytes() bytes;
+ *   calls that share one workspace must not overlap (keep them on one
+ *   stream).
  * Requires num_q_heads % num_kv_heads == 0, G = num_q_heads / num_kv_heads
  * <= 16, D in {64, 128}, max_context_len <= min(16 * max_blocks_per_seq, 2^22).
- * Work split: the matrix-core kernel runs a persistent grid in which every
- * wave takes an equal share of the batch's 32-token chunks whatever the mix
- * of context lengths; contexts cut between waves are combined by a merge
- * kernel (log-sum-exp of the partial maxima, sums and outputs).  The
- * wavefront-reduction kernel cuts every context into fixed partitions merged
- * the same way. */
+ * Work split: a persistent partition kernel in which every wave takes an
+ * equal, contiguous share of the batch's 32-token chunks whatever the mix of
+ * context lengths.  A context held by one wave is written directly; a
+ * context cut between waves leaves one partial maximum, sum and unnormalised
+ * output per wave, combined by a merge kernel (log-sum-exp of the partials).
+ * The matrix-core kernel runs the group's query heads as a 16-column tile
+ * (bf16 with G >= 4, int8, FP8); the wavefront-reduction kernel serves f32
+ * caches and small groups. */
 int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
                            const void *v_pool, const int32_t *d_block_tables,
                            const int32_t *d_context_lens, int32_t num_seqs, int32_t num_q_heads,

@@ -12,6 +12,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+# A host-only build of the block manager (csrc/pool.cpp alone, e.g. under
+# the host sanitizers) may stand in for the library in CPU tests; it has no
+# device entry points.
+HOST_LIB_PATH = os.environ.get("PKV_HOST_LIB")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_NO_BLOCKS, PKV_ERR_BAD_BLOCK = 0, -1, -2, -3
 PKV_ERR_REFCOUNT, PKV_ERR_CAPACITY, PKV_ERR_HIP, PKV_ERR_WORKSPACE, PKV_ERR_BAD_SEQ = -4, -5, -6, -7, -8
@@ -76,7 +80,7 @@ class pkv_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("waves_per_simd", ctypes.c_int32),
                 ("ev_begin", ctypes.c_void_p),
                 ("ev_partition_done", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
-                ("xcd_weights", ctypes.c_int32 * 8), ("trace", ctypes.c_void_p)]
+                ("xcd_weights", ctypes.c_int32 * 8), ("load_policy", ctypes.c_int32), ("trace", ctypes.c_void_p)]
 
 
 PKV_TRACE_WAVES = 8192  # waves a decode trace buffer holds (4 int32 each)
@@ -135,12 +139,17 @@ def lib():
     """Load the in-tree library; fail loudly when it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                              "(hipcc --offload-arch=gfx950); there is no fallback path")
-        import torch  # noqa: F401  -- bind to the HIP runtime torch loaded (same soname)
-        L = ctypes.CDLL(LIB_PATH)
+        if HOST_LIB_PATH:
+            L = ctypes.CDLL(HOST_LIB_PATH)
+        else:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                  "(hipcc --offload-arch=gfx950); there is no fallback path")
+            import torch  # noqa: F401  -- bind to the HIP runtime torch loaded (same soname)
+            L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
+            if HOST_LIB_PATH and not hasattr(L, name):
+                continue  # a device entry point: not in a host-only build
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
@@ -426,10 +435,12 @@ def pkv_copy_blocks(layout, k_pool, v_pool, pairs, stream=None):
 
 
 def decode_opts(partition_tokens=0, kernel=0, events=None, waves_per_simd=0, xcd_weights=None,
-                trace=None) -> pkv_decode_opts:
-    """trace: optional device int32 tensor of 4 * PKV_TRACE_WAVES elements."""
+                trace=None, load_policy=0) -> pkv_decode_opts:
+    """trace: optional device int32 tensor of 4 * PKV_TRACE_WAVES elements;
+    load_policy: 0 auto, 1 streaming (non-temporal) K/V loads, 2 cached."""
     ev = list(events) if events else [None, None, None]
     o = pkv_decode_opts(int(partition_tokens), int(kernel), int(waves_per_simd), *[e if e else None for e in ev])
+    o.load_policy = int(load_policy)
     if xcd_weights is not None:
         w = [int(x) for x in xcd_weights]
         if len(w) != 8:
@@ -462,7 +473,7 @@ def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_l
 
 def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
                            workspace=None, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0,
-                           xcd_weights=None, trace=None):
+                           xcd_weights=None, trace=None, load_policy=0):
     """events: optional (begin, partition_done, end) raw hipEvent_t handles."""
     import torch
     pdt, rdt = pool_torch_dtype(layout), row_torch_dtype(layout)
@@ -479,7 +490,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
         ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < ws_need:
         raise ValueError(f"workspace of {ws_need} bytes needed, got {ws_bytes}")
-    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace)
+    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy)
     _check(lib().paged_attention_decode(
         ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", rdt),
         _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),

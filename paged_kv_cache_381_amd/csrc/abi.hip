@@ -43,19 +43,23 @@ int choose_kernel(const pkv_layout *L, int32_t G, const pkv_decode_opts *opts) {
   return (L->kv_dtype == PKV_BF16 && G >= 4) ? 2 : 1;
 }
 
-// Partial slots per (sequence, query head) of the balanced split: a segment
-// of at most ceil(max_ctx / 32) chunks overlaps at most ceil(that / min_cpw) + 1
-// wave shares, since every share holds at least min_cpw chunks.
-int32_t split_maxp(int32_t max_ctx, int32_t min_cpw) {
-  const int32_t chunks = (max_ctx + PKV_CHUNK - 1) / PKV_CHUNK;
-  return (chunks + min_cpw - 1) / min_cpw + 1;
-}
-
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Workspace of the balanced split: partial outputs, partial (m, l), header.
-size_t split_ws_bytes(const pkv_layout *L, int32_t B, int32_t Hq, int32_t maxp) {
-  const size_t rows = (size_t)B * Hq * maxp;
+// Partial slots of the balanced split: two per wave that can receive work
+// (only its first and its last segment can be cut), and a grid has at most
+// PKV_MAX_DECODE_WAVES waves and never more working waves than chunks over
+// min_cpw.
+int32_t split_slots(int32_t B, int32_t H, int32_t max_ctx, int32_t min_cpw) {
+  const int64_t chunks = (int64_t)B * H * ((max_ctx + PKV_CHUNK - 1) / PKV_CHUNK);
+  const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(PKV_MAX_DECODE_WAVES, chunks / min_cpw));
+  return (int32_t)(2 * waves);
+}
+
+// Workspace of the balanced split: partial outputs [nslots][G][D] and
+// (m, l) [nslots][G] of float32, then the merge kernel's schedule header
+// (PKV_HDR_INTS + B int32), each region padded to 16 bytes.
+size_t split_ws_bytes(const pkv_layout *L, int32_t B, int32_t Hq, int32_t nslots) {
+  const size_t rows = (size_t)nslots * (Hq / L->num_kv_heads);
   return align16(rows * L->head_dim * sizeof(float)) + align16(rows * 2 * sizeof(float)) +
          align16((size_t)(PKV_HDR_INTS + B) * sizeof(int32_t));
 }
@@ -122,6 +126,9 @@ int pkv_split_grid(const void *kernel, int block_threads, size_t lds_bytes, cons
   }
   const int waves_per_wg = block_threads / 64;
   int64_t grid = (int64_t)std::max(1, hit->per_cu) * std::max(1, hit->cus);
+  // The workspace holds partial slots for at most PKV_MAX_DECODE_WAVES waves.
+  static_assert(PKV_MAX_DECODE_WAVES % (8 * 4) == 0, "the wave cap must stay a multiple of 8 workgroups");
+  grid = std::min<int64_t>(grid, PKV_MAX_DECODE_WAVES / waves_per_wg);
   // No more workgroups than the largest possible batch of chunks can feed.
   const int64_t max_chunks = (int64_t)a.num_seqs * a.L->num_kv_heads * ((a.max_ctx + PKV_CHUNK - 1) / PKV_CHUNK);
   const int64_t need = (max_chunks + (int64_t)a.min_cpw * waves_per_wg - 1) / ((int64_t)a.min_cpw * waves_per_wg);
@@ -137,15 +144,18 @@ extern "C" size_t paged_attention_workspace_bytes(const pkv_layout *layout, int3
   if (num_q_heads % layout->num_kv_heads) return 0;
   int32_t mc;
   if (min_chunks(opts, &mc)) return 0;
-  return split_ws_bytes(layout, num_seqs, num_q_heads, split_maxp(max_context_len, mc));
+  return split_ws_bytes(layout, num_seqs, num_q_heads, split_slots(num_seqs, layout->num_kv_heads, max_context_len, mc));
 }
 
-extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
-                                      const void *v_pool, const int32_t *d_block_tables,
-                                      const int32_t *d_context_lens, int32_t num_seqs, int32_t num_q_heads,
-                                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-                                      void *workspace, size_t workspace_bytes, const pkv_decode_opts *opts,
-                                      void *stream) {
+namespace {
+
+// Validation shared by the decode entry points and the arguments of the
+// launch, all but the workspace regions.  Returns PKV_OK, an error, or 1 when
+// the call has nothing to do (no sequences).
+int decode_prepare(const pkv_layout *layout, float *out, const void *q, const void *k_pool, const void *v_pool,
+                   const int32_t *d_block_tables, const int32_t *d_context_lens, int32_t num_seqs,
+                   int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                   const pkv_decode_opts *opts, void *stream, pkv_decode_args *a) {
   if (int rc = pkv_check_layout(layout)) return rc;
   const int32_t H = layout->num_kv_heads;
   if (num_seqs < 0) return pkv_set_error(PKV_ERR_INVALID, "num_seqs < 0");
@@ -160,7 +170,7 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
                          max_context_len);
   if (!std::isfinite(scale)) return pkv_set_error(PKV_ERR_INVALID, "scale is not finite");
   if (num_seqs > 65535 || H > 65535) return pkv_set_error(PKV_ERR_INVALID, "grid too large");
-  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs == 0) return 1;
   if (!out || !q || !k_pool || !v_pool || !d_block_tables || !d_context_lens)
     return pkv_set_error(PKV_ERR_INVALID, "paged_attention_decode: NULL pointer");
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 4))
@@ -171,6 +181,8 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   if (kernel != 1 && kernel != 2) return pkv_set_error(PKV_ERR_INVALID, "unknown kernel %d", kernel);
   if (opts && (opts->waves_per_simd < 0 || opts->waves_per_simd > 2))
     return pkv_set_error(PKV_ERR_INVALID, "waves_per_simd must be 0, 1 or 2 (got %d)", opts->waves_per_simd);
+  if (opts && (opts->load_policy < 0 || opts->load_policy > 2))
+    return pkv_set_error(PKV_ERR_INVALID, "load_policy must be 0, 1 or 2 (got %d)", opts->load_policy);
   if (kernel == 2 && layout->kv_dtype == PKV_F32)
     return pkv_set_error(PKV_ERR_INVALID, "the matrix-core kernel needs a bf16, int8 or FP8 cache");
   if (kernel == 1 && pkv_is_q8(layout->kv_dtype))
@@ -184,43 +196,75 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
   if (max_context_len > (1 << 22))
     return pkv_set_error(PKV_ERR_INVALID, "max_context_len %d exceeds %d", max_context_len, 1 << 22);
 
-  const size_t need = paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, opts);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
-    return pkv_set_error(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                         workspace ? workspace_bytes : (size_t)0);
+  a->L = layout;
+  a->out = out;
+  a->q = q;
+  a->k_pool = k_pool;
+  a->v_pool = v_pool;
+  a->tables = d_block_tables;
+  a->ctx = d_context_lens;
+  a->num_seqs = num_seqs;
+  a->num_q_heads = num_q_heads;
+  a->max_blocks = max_blocks_per_seq;
+  a->max_ctx = max_context_len;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->stream = stream;
+  a->min_cpw = mc;
+  a->kernel = kernel;
+  a->waves_per_simd = opts && opts->waves_per_simd ? opts->waves_per_simd : 1;
+  const int policy = opts ? opts->load_policy : 0;
+  // Auto: streaming loads for bf16 and f32 caches read by one wave per SIMD
+  // (measured: 8B-shaped batch 104.8 -> 95.7 us, 70B-shaped 732 -> 660 us);
+  // cached loads for one-byte caches (streaming measured 9 % slower there)
+  // and for batches of mostly shared blocks (two waves per SIMD), which L2
+  // serves.
+  a->streaming = policy == 1 || (policy == 0 && a->waves_per_simd == 1 && !pkv_is_q8(layout->kv_dtype));
+  a->nslots = split_slots(num_seqs, H, max_context_len, mc);
+  for (int i = 0; i < PKV_REGIONS; ++i) a->xw[i] = opts ? opts->xcd_weights[i] : 0;
+  a->trace = opts ? opts->trace : nullptr;
+  return PKV_OK;
+}
 
-  pkv_decode_args a{};
-  a.L = layout;
-  a.out = out;
-  a.q = q;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.tables = d_block_tables;
-  a.ctx = d_context_lens;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.max_blocks = max_blocks_per_seq;
-  a.max_ctx = max_context_len;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.stream = stream;
-  a.min_cpw = mc;
-  a.waves_per_simd = opts && opts->waves_per_simd ? opts->waves_per_simd : 1;
-  a.maxp = split_maxp(max_context_len, mc);
-  for (int i = 0; i < PKV_REGIONS; ++i) a.xw[i] = opts ? opts->xcd_weights[i] : 0;
-  a.trace = opts ? opts->trace : nullptr;
-  const size_t rows = (size_t)num_seqs * num_q_heads * a.maxp;
+// The workspace regions of a prepared call: partial outputs, partial
+// (m, l), schedule header (the layout of paged_attention_workspace_bytes).
+void carve_workspace(pkv_decode_args *a, void *workspace) {
+  const size_t rows = (size_t)a->nslots * (a->num_q_heads / a->L->num_kv_heads);
   char *ws = static_cast<char *>(workspace);
-  a.ws_o = reinterpret_cast<float *>(ws);
-  a.ws_ml = reinterpret_cast<float *>(ws + align16(rows * layout->head_dim * sizeof(float)));
-  a.ws_hdr = reinterpret_cast<int32_t *>(ws + align16(rows * layout->head_dim * sizeof(float)) +
-                                         align16(rows * 2 * sizeof(float)));
+  a->ws_o = reinterpret_cast<float *>(ws);
+  a->ws_ml = reinterpret_cast<float *>(ws + align16(rows * a->L->head_dim * sizeof(float)));
+  a->ws_hdr = reinterpret_cast<int32_t *>(ws + align16(rows * a->L->head_dim * sizeof(float)) +
+                                          align16(rows * 2 * sizeof(float)));
+}
 
+// The partition and merge kernels of a prepared call, between the optional
+// events.
+int decode_launch(const pkv_decode_args &a, const pkv_decode_opts *opts, void *stream) {
   if (int rc = record(opts ? opts->ev_begin : nullptr, stream)) return rc;
-  const int rc = kernel == 2 ? pkv_launch_decode_mfma(a) : pkv_launch_decode_valu(a);
+  const int rc = a.kernel == 2 ? pkv_launch_decode_mfma(a) : pkv_launch_decode_valu(a);
   if (rc) return hip_fail(rc, "decode partition kernel launch");
   if (int r = record(opts ? opts->ev_partition_done : nullptr, stream)) return r;
   if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
   return record(opts ? opts->ev_end : nullptr, stream);
+}
+
+}  // namespace
+
+extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
+                                      const void *v_pool, const int32_t *d_block_tables,
+                                      const int32_t *d_context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                      void *workspace, size_t workspace_bytes, const pkv_decode_opts *opts,
+                                      void *stream) {
+  pkv_decode_args a{};
+  const int prep = decode_prepare(layout, out, q, k_pool, v_pool, d_block_tables, d_context_lens, num_seqs,
+                                  num_q_heads, max_blocks_per_seq, max_context_len, scale, opts, stream, &a);
+  if (prep) return prep == 1 ? PKV_OK : prep;
+  const size_t need = paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, opts);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+    return pkv_set_error(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                         workspace ? workspace_bytes : (size_t)0);
+  carve_workspace(&a, workspace);
+  return decode_launch(a, opts, stream);
 }
 
 extern "C" int pkv_xcd_weights_from_trace(const int32_t *h_trace, int32_t n_waves, int32_t weights_out[8]) {

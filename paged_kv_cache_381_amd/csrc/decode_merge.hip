@@ -7,100 +7,95 @@
 // exact algebra (log-sum-exp), so the result equals a single softmax over all
 // tokens.
 //
-// The partials of segment (g, b) are those of the waves whose shares overlap
-// the segment's chunks, stored in share order.  The schedule header written by
+// One wave per (sequence, kv head) segment.  The schedule header written by
 // the decode kernel gives the chunk scan, the number of waves used and the
-// region bounds, from which the segment's position and its first and last
-// wave follow exactly as in the decode kernel.  Segments held by one wave, and empty sequences, were
-// written by the decode kernel and are skipped here.
+// region bounds, from which the segment's first and last wave w0 .. w1
+// follow exactly as in the decode kernel; a segment held by one wave (or an
+// empty one) was written by the decode kernel and is skipped.  Wave w keeps
+// the partial of its first segment in slot 2 w and of its last in 2 w + 1:
+// the segment is the first one of every wave after w0, and of w0 itself
+// only when it starts at w0's first chunk.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace {
 
-// Sum over the 64 lanes in registers: DPP within each 16-lane row, then the
-// gfx950 lane swaps across rows (no LDS round trip).
-__device__ __forceinline__ float wave_sum(float x) {
-  x = row_sum16(x);
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
+// Pieces whose partials one step loads at once (every load in flight
+// together); a segment with more pieces takes several steps, folded into a
+// running (M, L, out).
+constexpr int kBatch = 8;
 
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
-  const int bh = blockIdx.x;
-  const int b = bh / P.Hq, h = bh - b * P.Hq, g = h / P.G;
-  const int64_t c_tot = (int64_t)P.H * P.ws_hdr[0];
-  const int nwe = P.ws_hdr[1];
+  const int seg = blockIdx.x;
+  const int b = seg / P.H, g = seg - b * P.H;
+  const int32_t c_seq = P.ws_hdr[0];
+  const int64_t c_tot = (int64_t)P.H * c_seq;
   const int32_t *s_incl = P.ws_hdr + PKV_HDR_INTS;
   const int cnt = s_incl[b] - (b ? s_incl[b - 1] : 0);
   if (cnt == 0 || c_tot == 0) return;
-  const int64_t seg0 = (int64_t)g * P.ws_hdr[0] + (s_incl[b] - cnt);
+  const int64_t seg0 = (int64_t)g * c_seq + (s_incl[b] - cnt);
   Regions rg;
   rg.C = c_tot;
-  rg.nwe = nwe;
+  rg.nwe = P.ws_hdr[1];
   rg.nr = P.ws_hdr[2];
-  rg.wpr = nwe / rg.nr;
+  rg.wpr = rg.nwe / rg.nr;
   rg.bounds = reinterpret_cast<const int64_t *>(P.ws_hdr + 4);
   const int w0 = rg.wave_of(seg0), w1 = rg.wave_of(seg0 + cnt - 1);
-  const int np = min(w1 - w0 + 1, P.maxp);
+  const int np = w1 - w0 + 1;
   if (np <= 1) return;
-  const size_t row = (size_t)bh * P.maxp;
-  const float2 *ml = reinterpret_cast<const float2 *>(P.ws_ml) + row;
-  const float *o = P.ws_o + row * D;
-  const int lane = threadIdx.x;
-  // The partials' maxima and weighted sums, 64 partials at a time across the
-  // lanes (one round trip per 64, not one per partial).
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[i].x);
-  M = rows_max4_swap(row_max16(M));
-  float L = 0.f;
-  float acc[D / 64];
+  int64_t lo0, hi0;
+  rg.share(w0, lo0, hi0);
+  const int first0 = 2 * w0 + (lo0 < seg0 ? 1 : 0);
+
+  const int lane = threadIdx.x, G = P.G;
+  const size_t row0 = (size_t)b * P.Hq + (size_t)g * G;
+  for (int u = lane; u < G * (D / 4); u += 64) {
+    const int h = u / (D / 4), d = 4 * (u % (D / 4));
+    float M = -INFINITY, L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < np; i0 += kBatch) {
+      float2 ml[kBatch];
+      float4 o[kBatch];
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
-  for (int i0 = 0; i0 < np; i0 += 64) {
-    const int n = min(np - i0, 64);
-    float f = 0.f;  // lane j: weight of partial i0 + j
-    if (lane < n) {
-      const float2 mi = ml[i0 + lane];
-      f = fast_exp2(mi.x - M);
-      L += mi.y * f;
-    }
-    // Output rows four partials at a time, so their loads are in flight
-    // together; the sum runs over the partials in order.
-    int j = 0;
-    for (; j + 4 <= n; j += 4) {
-      float v[4][D / 64];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int k = 0; k < D / 64; ++k) v[u][k] = o[(size_t)(i0 + j + u) * D + 64 * k + lane];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + u));
-#pragma unroll
-        for (int k = 0; k < D / 64; ++k) acc[k] += v[u][k] * fu;
+      for (int k = 0; k < kBatch; ++k) {
+        // Past the last piece the batch re-reads it and gives it no weight.
+        const int i = min(i0 + k, np - 1);
+        const size_t r = (size_t)min(i == 0 ? first0 : 2 * (w0 + i), P.nslots - 1) * G + h;
+        ml[k] = *reinterpret_cast<const float2 *>(P.ws_ml + 2 * r);
+        o[k] = *reinterpret_cast<const float4 *>(P.ws_o + r * D + d);
       }
-    }
-    for (; j < n; ++j) {
-      const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+      float Mb = M;
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) acc[k] += o[(size_t)(i0 + j) * D + 64 * k + lane] * fj;
+      for (int k = 0; k < kBatch; ++k) Mb = i0 + k < np ? fmaxf(Mb, ml[k].x) : Mb;
+      const float fo = fast_exp2(M - Mb);  // 0 on the first step (M = -inf)
+      L *= fo;
+      acc.x *= fo;
+      acc.y *= fo;
+      acc.z *= fo;
+      acc.w *= fo;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float f = i0 + k < np ? fast_exp2(ml[k].x - Mb) : 0.f;
+        L += ml[k].y * f;
+        acc.x += o[k].x * f;
+        acc.y += o[k].y * f;
+        acc.z += o[k].z * f;
+        acc.w += o[k].w * f;
+      }
+      M = Mb;
     }
+    const float inv = 1.f / L;
+    *reinterpret_cast<float4 *>(P.out + (row0 + h) * D + d) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
-  L = wave_sum(L);
-  const float inv = 1.f / L;
-#pragma unroll
-  for (int k = 0; k < D / 64; ++k) P.out[(size_t)bh * D + 64 * k + lane] = acc[k] * inv;
 }
 
 }  // namespace
 
 int pkv_launch_merge(const pkv_decode_args &a) {
   const SplitParams p = pkv_split_params(a);
-  dim3 grid(a.num_seqs * a.num_q_heads);
+  dim3 grid(a.num_seqs * a.L->num_kv_heads);
   if (a.L->head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   else

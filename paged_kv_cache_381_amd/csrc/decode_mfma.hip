@@ -19,7 +19,8 @@
 // context lengths does not leave a tail of long sequences running alone.
 // Within its share a wave walks (sequence, kv head) segments in order; a
 // segment it holds entirely is normalised and stored, a segment cut by a share
-// boundary leaves a partial (m, l, o) for the merge kernel.
+// boundary leaves a partial (m, l, o) in the wave's slot for the merge
+// kernel.
 //
 // gfx950 mapping.  The G query heads of a group share every K and V tile, so
 // the group-by-block products are small dense contractions and run on
@@ -33,9 +34,11 @@
 // of the [D][16] V tile (tokens 8(j%2)..+7 of block j/2).  No cross-lane
 // shuffle sits between the two contractions; the softmax needs only two
 // xor-shuffles per chunk (max over the four lane groups).  Each lane holds the
-// 8-element slices of the group's query rows that its B operand needs, read
-// straight from memory once per segment: the whole group shares them through
-// the MFMA, and nothing else in the wave would reuse an LDS copy.
+// 8-element slices of the group's query rows that its B operand needs, loaded
+// with every chunk's K (from L2 after the first: D/32 16-byte loads per lane
+// beside the chunk's D/16 of K and D/16 of V), so one set of registers serves
+// both buffers of the pipeline; the whole group shares them through the MFMA, and
+// nothing else in the wave would reuse an LDS copy.
 //
 // int8 cache [KV Cache 工程学 §15.7 (3)].  Codes are loaded 8 bytes per lane
 // where bf16 takes 16 and widened to bf16 exactly (|code| <= 127 needs 7
@@ -85,7 +88,7 @@ constexpr float kSlack = 8.0f;
 #define PKV_MFMA_NBUF_I8 3
 #endif
 
-template <int D, int W, int NB, bool I8, bool F8>
+template <int D, int W, int NB, bool I8, bool F8, bool NT>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
@@ -154,14 +157,14 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       // 16-byte unit of the lane's token row: int8 unit 4ku+grp holds the
       // element groups 2(4ku+grp) and +1 of score MFMAs 2ku and 2ku+1.
       const int cu = 4 * ku + grp;
-      ax[I][ku] = kt[cu * 16 + ktx];
-      ay[I][ku] = kt[cu * 16 + ktx + 4];
+      ax[I][ku] = load_u4<NT>(kt + cu * 16 + ktx);
+      ay[I][ku] = load_u4<NT>(kt + cu * 16 + ktx + 4);
     }
     if constexpr (I8) {
       const float4 *sc = reinterpret_cast<const float4 *>(
           kpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + c.g) * TB + 16 * D + 32 * vhalf);
-      ksc[I][0] = sc[0];
-      ksc[I][1] = sc[1];
+      ksc[I][0] = load_f4<NT>(sc);
+      ksc[I][1] = load_f4<NT>(sc + 1);
     }
   };
   auto issue_v = [&](auto bi) {
@@ -169,14 +172,14 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     const uint8_t *vt = vpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + cq[I].g) * TB;
     if constexpr (I8) {
 #pragma unroll
-      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = *reinterpret_cast<const uint2 *>(vt + (16 * nn + r16) * 16 + 8 * vhalf);
+      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = load_u2<NT>(vt + (16 * nn + r16) * 16 + 8 * vhalf);
       const float4 *sc = reinterpret_cast<const float4 *>(vt + 16 * D + 32 * vhalf);
-      vsc[I][0] = sc[0];
-      vsc[I][1] = sc[1];
+      vsc[I][0] = load_f4<NT>(sc);
+      vsc[I][1] = load_f4<NT>(sc + 1);
     } else {
       const uint4 *u = reinterpret_cast<const uint4 *>(vt);
 #pragma unroll
-      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = u[2 * (16 * nn + r16) + vhalf];
+      for (int nn = 0; nn < NNN; ++nn) va[I][nn] = load_u4<NT>(u + 2 * (16 * nn + r16) + vhalf);
     }
   };
 
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     if (real && (x + 1 >= hi || cur.j == cur.cnt - 1)) {  // the piece ends here
       const float lsum = rows_sum4(l);
       const bool whole = sh.whole(cur);
-      const int slot = whole ? 0 : sh.piece(cur, P.maxp);
+      const int slot = whole ? 0 : sh.slot(cur, P.nslots);
       if (held < P.nrec) {
         // The piece's rows go to the wave's LDS ring and reach memory after
         // the wave's last load: LDS traffic has a counter of its own, so the
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
               *reinterpret_cast<float4 *>(dst + 16 * nn) =
                   make_float4(o[nn][0] * inv, o[nn][1] * inv, o[nn][2] * inv, o[nn][3] * inv);
           } else {
-            const size_t ps = row * P.maxp + slot;
+            const size_t ps = (size_t)slot * G + r16;
             float *dst = P.ws_o + ps * D + 4 * grp;
 #pragma unroll
             for (int nn = 0; nn < NNN; ++nn)
@@ -379,11 +382,11 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     for (int u = lane; u < G * (D / 4); u += 64) {
       const int h = u / (D / 4), c = 4 * (u % (D / 4));
       const float4 v = *reinterpret_cast<const float4 *>(rec + (h * D + c) * 4);
-      float *dst = whole ? P.out + (row0 + h) * D + c : P.ws_o + ((row0 + h) * P.maxp + slot) * D + c;
+      float *dst = whole ? P.out + (row0 + h) * D + c : P.ws_o + ((size_t)slot * G + h) * D + c;
       *reinterpret_cast<float4 *>(dst) = v;
     }
     if (!whole && lane < G)
-      *reinterpret_cast<float2 *>(P.ws_ml + 2 * ((row0 + lane) * P.maxp + slot)) =
+      *reinterpret_cast<float2 *>(P.ws_ml + 2 * ((size_t)slot * G + lane)) =
           *reinterpret_cast<const float2 *>(rec + G * D * 4 + lane * 8);
   }
   // Optional trace: the wave's XCD group (workgroups are dealt round-robin
@@ -408,9 +411,9 @@ constexpr size_t kRingLdsTwoWg = 64 * 1024;
 constexpr size_t kMaxRecords = 16;
 
 // I8: one-byte codes (int8, or FP8 E4M3 when F8) with per-row scales.
-template <int D, bool I8, bool F8 = false>
+template <int D, bool I8, bool F8, bool NT>
 int launch(const pkv_decode_args &a, const SplitParams &p0) {
-  auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8, F8>;
+  auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8, F8, NT>;
   SplitParams p = p0;
   const size_t split = pkv_split_lds_bytes(a.num_seqs, kWaves);
   // Result rings: what LDS is left of the workgroup's share of the CU, split
@@ -433,12 +436,21 @@ int launch(const pkv_decode_args &a, const SplitParams &p0) {
   return (int)hipGetLastError();
 }
 
+template <bool I8, bool F8, bool NT>
+int launch_d(const pkv_decode_args &a, const SplitParams &p) {
+  return a.L->head_dim == 128 ? launch<128, I8, F8, NT>(a, p) : launch<64, I8, F8, NT>(a, p);
+}
+
+template <bool NT>
+int launch_t(const pkv_decode_args &a, const SplitParams &p) {
+  if (a.L->kv_dtype == PKV_INT8) return launch_d<true, false, NT>(a, p);
+  if (a.L->kv_dtype == PKV_FP8) return launch_d<true, true, NT>(a, p);
+  return launch_d<false, false, NT>(a, p);
+}
+
 }  // namespace
 
 int pkv_launch_decode_mfma(const pkv_decode_args &a) {
   const SplitParams p = pkv_split_params(a);
-  if (a.L->kv_dtype == PKV_INT8) return a.L->head_dim == 128 ? launch<128, true>(a, p) : launch<64, true>(a, p);
-  if (a.L->kv_dtype == PKV_FP8)
-    return a.L->head_dim == 128 ? launch<128, true, true>(a, p) : launch<64, true, true>(a, p);
-  return a.L->head_dim == 128 ? launch<128, false>(a, p) : launch<64, false>(a, p);
+  return a.streaming ? launch_t<true>(a, p) : launch_t<false>(a, p);
 }

@@ -71,7 +71,7 @@ constexpr int wave_lds_floats() {
   return GP * D + GP * 32;
 }
 
-template <typename E, int D, int GP, int W>
+template <typename E, int D, int GP, int W, bool NT>
 __global__ __launch_bounds__(64 * W) void decode_valu_kernel(SplitParams P) {
   constexpr int ES = sizeof(E);
   constexpr int X = 16 / ES;       // elements per 16-byte unit
@@ -128,17 +128,17 @@ __global__ __launch_bounds__(64 * W) void decode_valu_kernel(SplitParams P) {
     const uint4 *ka = reinterpret_cast<const uint4 *>(kpool + ((size_t)pa * H + g) * TILE);
     const uint4 *kb = reinterpret_cast<const uint4 *>(kpool + ((size_t)pb * H + g) * TILE);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) ku[0][i] = ka[64 * i + lane];
+    for (int i = 0; i < NL; ++i) ku[0][i] = load_u4<NT>(ka + 64 * i + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) ku[1][i] = kb[64 * i + lane];
+    for (int i = 0; i < NL; ++i) ku[1][i] = load_u4<NT>(kb + 64 * i + lane);
   };
   auto load_v = [&](int g, int pa, int pb) {
     const uint4 *va = reinterpret_cast<const uint4 *>(vpool + ((size_t)pa * H + g) * TILE);
     const uint4 *vb = reinterpret_cast<const uint4 *>(vpool + ((size_t)pb * H + g) * TILE);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vu[0][i] = va[64 * i + lane];
+    for (int i = 0; i < NL; ++i) vu[0][i] = load_u4<NT>(va + 64 * i + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vu[1][i] = vb[64 * i + lane];
+    for (int i = 0; i < NL; ++i) vu[1][i] = load_u4<NT>(vb + 64 * i + lane);
   };
 
   Cursor cur = sh.first();
@@ -245,7 +245,8 @@ __global__ __launch_bounds__(64 * W) void decode_valu_kernel(SplitParams P) {
         }
       }
       const bool whole = sh.whole(cur);
-      const int piece = sh.piece(cur, P.maxp);
+      const int pslot = sh.slot(cur, P.nslots);
+
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
         if (h >= G) continue;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(64 * W) void decode_valu_kernel(SplitParams P) {
             for (int i = 0; i < NL; ++i) P.out[rowq * D + (64 * i + lane) / ES] = acc[h][i] * inv;
           }
         } else {
-          const size_t slot = rowq * P.maxp + piece;
+          const size_t slot = (size_t)pslot * G + h;
           if (vpart == 0) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) P.ws_o[slot * D + (64 * i + lane) / ES] = acc[h][i];
@@ -288,7 +289,7 @@ constexpr int kWaves = 4;
 
 template <typename E, int D, int GP>
 int launch(const pkv_decode_args &a, const SplitParams &p) {
-  auto kern = decode_valu_kernel<E, D, GP, kWaves>;
+  auto kern = a.streaming ? decode_valu_kernel<E, D, GP, kWaves, true> : decode_valu_kernel<E, D, GP, kWaves, false>;
   const size_t lds = pkv_split_lds_bytes(a.num_seqs, kWaves, kWaves * wave_lds_floats<D, GP>());
   int nwg = 0;
   if (int rc = pkv_split_grid(reinterpret_cast<const void *>(kern), 64 * kWaves, lds, a, &nwg)) return rc;

@@ -61,6 +61,38 @@ __device__ __forceinline__ uint2 keep_first(uint2 u, int nvalid) {
   return make_uint2(u.x & mx, u.y & my);
 }
 
+// Loads of cache tiles.  With NT the load carries the non-temporal hint
+// (global_load ... nt): the line is streamed through the caches instead of
+// being kept for reuse.  A batch that reads each K/V tile once streams HBM
+// faster that way (a probe of random 4 KiB tiles: about 6.5 TB/s against
+// 5.9 TB/s with cached loads); tiles shared by many sequences are better
+// left cached.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ uint4 load_u4(const void *p) {
+  if constexpr (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4 *>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ uint2 load_u2(const void *p) {
+  if constexpr (NT) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return *reinterpret_cast<const uint2 *>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ float4 load_f4(const void *p) {
+  const uint4 u = load_u4<NT>(p);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -137,10 +169,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // mix of context lengths, and all waves finish together.  Head-major order
 // puts each XCD (one contiguous eighth of the shares, xcd_logical) on about
 // one kv head, so blocks read by many sequences -- a shared prompt -- are
-// served from that XCD's L2 after their first read.  A segment cut by a
-// share boundary leaves one partial result (m, l, o) per wave that touched
-// it; the merge kernel combines them.  A segment held by one wave is written
-// out directly.
+// served from that XCD's L2 after their first read.  A segment held by one
+// wave is normalised and written out directly.  A segment cut by share
+// boundaries leaves one partial result (m, l, o) per wave that touched it, in
+// that wave's slot for its first or its last segment (a share is contiguous,
+// so only those two can be cut); the merge kernel combines them.
 
 // Parameters of the balanced decode kernels (passed by value).
 struct SplitParams {
@@ -150,8 +183,8 @@ struct SplitParams {
   const void *v_pool;
   const int32_t *tables;  // [B][max_blocks]
   const int32_t *ctx;     // [B]
-  float *ws_o;            // [B][Hq][maxp][D]   partial outputs
-  float *ws_ml;           // [B][Hq][maxp][2]   partial (max, sum)
+  float *ws_o;            // [nslots][G][D] partial outputs
+  float *ws_ml;           // [nslots][G][2] partial (max, sum)
   int32_t *ws_hdr;        // [PKV_HDR_INTS + B]: chunks per kv head, waves used, regions,
                           // region bounds (int64), inclusive chunk scan
   int32_t B;
@@ -161,8 +194,8 @@ struct SplitParams {
   int32_t G;
   int32_t max_blocks;
   int32_t max_ctx;
-  int32_t maxp;           // partial slots per (sequence, query head)
-  int32_t min_cpw;        // fewest chunks a wave is given (bounds maxp)
+  int32_t nslots;         // partial slots, two per wave (bounds every slot index)
+  int32_t min_cpw;        // fewest chunks a wave is given
   int32_t ring_off;       // matrix-core kernel: LDS byte offset of wave 0's result ring
   int32_t rec_bytes;      // bytes of one ring record (a piece's G rows, their (m, l), its place)
   int32_t nrec;           // records per wave ring (0: every piece is stored at once)
@@ -351,7 +384,7 @@ inline SplitParams pkv_split_params(const pkv_decode_args &a) {
   p.G = a.num_q_heads / a.L->num_kv_heads;
   p.max_blocks = a.max_blocks;
   p.max_ctx = a.max_ctx;
-  p.maxp = a.maxp;
+  p.nslots = a.nslots;
   p.min_cpw = a.min_cpw;
   p.ring_off = 0;
   p.rec_bytes = 0;
@@ -441,14 +474,17 @@ struct Share {
   // Whether this wave holds every chunk of the cursor's segment.
   __device__ bool whole(const Cursor &c) const { return c.seg0 >= lo && c.seg0 + c.cnt <= hi; }
 
-  // Partial slot of this wave for the cursor's segment (< maxp by
-  // construction; clamped so a broken invariant cannot write out of bounds).
-  __device__ int piece(const Cursor &c, int maxp) const { return min(wave - rg.wave_of(c.seg0), maxp - 1); }
+  // Partial slot of this wave for a cut segment: 2 wave when it is the
+  // wave's first segment (its share starts inside it), 2 wave + 1 when it is
+  // its last (< nslots by construction; clamped so that a broken invariant
+  // cannot write outside the workspace).
+  __device__ int slot(const Cursor &c, int nslots) const { return min(2 * wave + (lo < c.seg0 ? 1 : 0), nslots - 1); }
 };
 
 // Common start of the balanced-split kernels: the chunk scan (all threads),
-// the merge kernel's header and zero rows for empty sequences (workgroup 0),
-// and this wave's share.  Returns false when the wave has no work.
+// the merge kernel's schedule header and zero rows for empty sequences
+// (workgroup 0), and this wave's share.  Returns false when the wave has no
+// work.
 template <int W, int D>
 __device__ bool split_begin(const SplitParams &P, int32_t *s_lds, Share &sh) {
   const int tid = threadIdx.x, w = tid >> 6;

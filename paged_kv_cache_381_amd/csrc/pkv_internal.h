@@ -33,6 +33,9 @@ inline int64_t pkv_row_bytes(const pkv_layout *L) {
 #define PKV_HDR_INTS (4 + 2 * (PKV_REGIONS + 1))
 // Ints a decode wave writes to a trace buffer (PKV_TRACE_WAVES waves).
 #define PKV_TRACE_INTS 4
+// Most waves a decode grid runs: 8 per compute unit of MI355X's 256 (one or
+// two workgroups of four waves).  Bounds the partial slots of the workspace.
+#define PKV_MAX_DECODE_WAVES 2048
 
 // Kernel launchers (decode_*.hip, kv_append.hip).  They return a HIP error
 // code (0 = success); arguments were validated by the caller.
@@ -49,14 +52,16 @@ struct pkv_decode_args {
   int32_t max_blocks;
   int32_t max_ctx;
   float scale_log2;  // scale * log2(e): scores are kept in base 2
-  float *ws_o;       // [B][Hq][maxp][D] partial outputs
-  float *ws_ml;      // [B][Hq][maxp][2] partial (max, sum)
-  int32_t *ws_hdr;   // [PKV_HDR_INTS + B] schedule header
+  float *ws_o;       // [nslots][G][D] partial outputs
+  float *ws_ml;      // [nslots][G][2] partial (max, sum)
+  int32_t *ws_hdr;   // [PKV_HDR_INTS + B] schedule header of the merge kernel
   int32_t xw[PKV_REGIONS];  // per-XCD weights of the work (all 0: equal shares)
   int32_t *trace;    // nullable device buffer: PKV_TRACE_INTS per wave
-  int32_t maxp;      // partial slots per (sequence, query head)
+  int32_t nslots;    // partial slots: two per wave (its first and its last segment)
   int32_t min_cpw;   // fewest 32-token chunks per wave
+  int32_t kernel;          // 1 wavefront reductions, 2 matrix cores
   int32_t waves_per_simd;  // resident waves per SIMD of the matrix-core kernel (1 or 2)
+  int32_t streaming;       // K/V tiles read with non-temporal loads (1) or cached ones (0)
   void *stream;
 };
 

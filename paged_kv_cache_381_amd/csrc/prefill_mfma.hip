@@ -392,22 +392,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   }
 }
 
-// Workgroup-shared walk: the four waves of a workgroup take consecutive tile
-// groups of one (sequence, kv head) and walk the same keys, so each chunk's
-// K and V (two blocks each) is read from memory once per workgroup, staged
-// through registers into LDS (256 threads, 16 bytes a thread a pass), and
-// every wave takes its matrix operands from there: a quarter of the vector
-// memory traffic of waves walking alone, which is what bounds them.  Chunk
-// x+1's K and chunk x's V sit in LDS while step x runs; chunk x+2's K and
-// chunk x+1's V are requested at its start and stored at its end, before
-// the one barrier of the step.  All waves run to the longest wave's last
-// chunk (its columns' causal limits mask the rest).  LDS placement keeps
-// the operand reads free of bank conflicts (any 8 or 16 lanes of a read
-// touch distinct 16-byte slots of a 128- or 256-byte bank row): within each
-// 16-unit K row, units 8..15 trade the bit 4 of their slot (8..11 <-> 12..15),
-// block b's K tile starts 128 bytes further, and a V row's two halves swap
-// places on rows where bit 2 xor bit 3 of the row index is set (bf16), or
-// on rows 8..15 of each 16 (int8).
 // Ring depth (chunks of K/V requested ahead) and column tiles per wave (16
 // query columns each: the K and V operands of a chunk serve all of them, so
 // each byte brought through the vector memory path feeds CT x the math).

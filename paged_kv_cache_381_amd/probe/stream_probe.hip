@@ -11,7 +11,8 @@
 // two steps of loads kept in registers (one in flight while the other is
 // folded), as the bf16 decode kernel keeps two chunks.  Optionally two
 // workgroups per compute unit (two waves per SIMD) keep twice the bytes in
-// flight.  The words read are folded with xor
+// flight, and the loads carry the non-temporal hint (streamed through the
+// caches, as the decode kernels read tiles that are used once).  The words read are folded with xor
 // into one value per wave, stored at the end, so no load is dead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,9 +27,11 @@ constexpr int kTileUnits = 4096 / 16 / 64;  // 16-byte loads per lane per tile
 constexpr int kLdsOneWgPerCu = 81 * 1024;
 
 typedef const int32_t __attribute__((address_space(4))) *const_i32;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NB = 2;
 
+template <bool NT>
 __global__ __launch_bounds__(64 * kWaves) void stream_tiles_kernel(const uint4 *buf, int64_t n_steps,
                                                                    const int32_t *order, uint32_t *sink) {
   const int64_t n_tiles = n_steps * kTilesPerStep;
@@ -52,7 +55,14 @@ __global__ __launch_bounds__(64 * kWaves) void stream_tiles_kernel(const uint4 *
       tile = tile < 0 ? 0 : tile >= n_tiles ? n_tiles - 1 : tile;  // a bad order cannot leave the buffer
       const uint4 *p = buf + (size_t)tile * (4096 / 16);
 #pragma unroll
-      for (int u = 0; u < kTileUnits; ++u) r[I][t][u] = p[64 * u + lane];
+      for (int u = 0; u < kTileUnits; ++u) {
+        if constexpr (NT) {
+          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 64 * u + lane));
+          r[I][t][u] = make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+          r[I][t][u] = p[64 * u + lane];
+        }
+      }
     }
   };
   uint32_t acc = 0;
@@ -80,9 +90,10 @@ __global__ __launch_bounds__(64 * kWaves) void stream_tiles_kernel(const uint4 *
   if (lane == 0) sink[w] = acc;
 }
 
+template <bool NT>
 int launch(const void *buf, int64_t n_tiles, const int32_t *order, uint32_t *sink, int nwg, size_t lds,
            hipStream_t stream) {
-  auto kern = stream_tiles_kernel;
+  auto kern = stream_tiles_kernel<NT>;
   if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsOneWgPerCu))
     return (int)e;
@@ -95,19 +106,22 @@ int launch(const void *buf, int64_t n_tiles, const int32_t *order, uint32_t *sin
 
 // Read the n_tiles 4 KiB tiles of buf in the order d_order (int32, n_tiles
 // entries, each in [0, n_tiles)) on waves_per_simd (1 or 2) workgroups of
-// four waves per compute unit.  d_sink receives one uint32 per wave
+// four waves per compute unit, with cached (streaming = 0) or non-temporal
+// (streaming = 1) loads.  d_sink receives one uint32 per wave
 // (4 * waves_per_simd * compute units of them).  n_tiles must be a positive
 // multiple of 4.  Returns a HIP error code (0 = launched), or -1 for bad
 // arguments.
 extern "C" int pkv_probe_stream_tiles(const void *buf, int64_t n_tiles, const int32_t *d_order,
-                                      int32_t waves_per_simd, uint32_t *d_sink, void *stream) {
+                                      int32_t waves_per_simd, int32_t streaming, uint32_t *d_sink, void *stream) {
   if (!buf || !d_order || !d_sink || n_tiles <= 0 || n_tiles % kTilesPerStep) return -1;
-  if (waves_per_simd != 1 && waves_per_simd != 2) return -1;
+  if ((waves_per_simd != 1 && waves_per_simd != 2) || (streaming != 0 && streaming != 1)) return -1;
   int dev = 0, cus = 0;
   if (hipError_t e = hipGetDevice(&dev)) return (int)e;
   if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
-  return launch(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, waves_per_simd == 1 ? kLdsOneWgPerCu : 0,
-                reinterpret_cast<hipStream_t>(stream));
+  const size_t lds = waves_per_simd == 1 ? kLdsOneWgPerCu : 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return streaming ? launch<true>(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, lds, s)
+                   : launch<false>(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, lds, s);
 }
 
 // Compute units of the current device (the probe's sink holds 4 per unit

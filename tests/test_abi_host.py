@@ -63,21 +63,30 @@ def test_sizes():
     f8 = P.make_layout(10, 8, 128, "fp8")
     assert P.pkv_kv_bytes_per_token(f8, 32) == 32 * 2 * 8 * (128 + 4)
     assert P.pkv_pool_bytes(f8) == 10 * 8 * (16 * 128 + 64) == f8.pool_elems
-    # Both kernels split the batch the same way: partial slots per (sequence, query head)
-    # = ceil(ceil(max_ctx / 32) / fewest chunks per wave) + 1, then partial (m, l) and a
-    # header, each region padded to 16 bytes
-    def split(B, Hq, D, max_ctx, min_chunks):
-        maxp = -(-(-(-max_ctx // 32)) // min_chunks) + 1
+    # Both kernels split the batch the same way: two partial slots of G query rows per
+    # wave that gets work (at most 2048 waves, and at most the batch's 32-token chunks
+    # over the fewest chunks per wave), then partial (m, l) and the merge kernel's
+    # schedule header (4 ints, 9 int64 region bounds, the chunk scan of B ints), each
+    # region padded to 16 bytes
+    def split(B, Hq, H, D, max_ctx, min_chunks):
+        chunks = B * H * -(-max_ctx // 32)
+        nslots = 2 * max(1, min(2048, chunks // min_chunks))
+        G = Hq // H
         pad = lambda x: -(-x // 16) * 16
-        # header: 4 ints, 9 int64 region bounds, then the chunk scan of B ints
-        return pad(B * Hq * maxp * D * 4) + pad(B * Hq * maxp * 2 * 4) + pad((4 + 18 + B) * 4)
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 512) == split(4, 32, 128, 512, 4)
-    assert P.paged_attention_workspace_bytes(lay, 3, 32, 4096, partition_tokens=256) == split(3, 32, 128, 4096, 8)
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 1) == split(4, 32, 128, 1, 4)
-    assert P.paged_attention_workspace_bytes(lay, 4, 32, 513, kernel=1) == split(4, 32, 128, 513, 4)
+        return pad(nslots * G * D * 4) + pad(nslots * G * 2 * 4) + pad((4 + 18 + B) * 4)
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 512) == split(4, 32, 8, 128, 512, 4)
+    assert P.paged_attention_workspace_bytes(lay, 3, 32, 4096, partition_tokens=256) == split(3, 32, 8, 128, 4096, 8)
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 1) == split(4, 32, 8, 128, 1, 4)
+    assert P.paged_attention_workspace_bytes(lay, 4, 32, 513, kernel=1) == split(4, 32, 8, 128, 513, 4)
+    assert P.paged_attention_workspace_bytes(lay, 64, 32, 4096) == split(64, 32, 8, 128, 4096, 4)
+    assert split(64, 32, 8, 128, 4096, 4) == pad16(4096 * 4 * 128 * 4) + pad16(4096 * 4 * 8) + pad16(86 * 4)
     f32 = P.make_layout(10, 4, 64, "f32")
-    assert P.paged_attention_workspace_bytes(f32, 4, 4, 255, partition_tokens=32) == split(4, 4, 64, 255, 1)
-    assert P.paged_attention_workspace_bytes(i8, 4, 32, 512) == split(4, 32, 128, 512, 4)
+    assert P.paged_attention_workspace_bytes(f32, 4, 4, 255, partition_tokens=32) == split(4, 4, 4, 64, 255, 1)
+    assert P.paged_attention_workspace_bytes(i8, 4, 32, 512) == split(4, 32, 8, 128, 512, 4)
+
+
+def pad16(x):
+    return -(-x // 16) * 16
 
 
 def test_validate_tables():
