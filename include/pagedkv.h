@@ -414,6 +414,26 @@ int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, 
                            void *workspace, size_t workspace_bytes, const pkv_decode_opts *opts,
                            void *stream);
 
+/* paged_attention_decode without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * arguments, results and errors are those of paged_attention_decode; the
+ * workspace is the library's own scratch, a static device array of
+ * 34,111,584 bytes (the workspace of the largest call: 2 * 2048 slots of 16
+ * query rows of 128 floats, their maxima and sums, and the schedule header
+ * of 8192 sequences), one copy per GPU, held until the process ends; its
+ * address is looked up on the first call on each device.  Every legal call
+ * fits it; a call whose workspace would not fails with PKV_ERR_WORKSPACE.
+ * All calls on one GPU share that GPU's scratch: calls that overlap on one
+ * GPU (different streams, or different host threads without ordering)
+ * race and give wrong results.  Allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine. */
+int paged_attention_decode_noalloc(const pkv_layout *layout, float *out, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *d_block_tables,
+                                   const int32_t *d_context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                   const pkv_decode_opts *opts, void *stream);
+
 /* Causal prefill over a paged cache [KV Cache 工程学 §15.1: a prompt of i
  * tokens is an i x i causal attention; §15.6 and 新一代 KV Cache 管理 §8.3:
  * a cached prefix is attended to, not prefilled again].  Sequence b holds

@@ -130,6 +130,8 @@ SIGNATURES = {
                                               _PO, _P]),
     "paged_attention_prefill": (ctypes.c_int, [_PL, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F,
                                                _P]),
+    "paged_attention_decode_noalloc": (ctypes.c_int, [_PL, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _F, _PO,
+                                                      _P]),
 }
 
 _lib = None
@@ -496,6 +498,26 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
         _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32, B),
         B, Hq, mb, int(max_context_len), float(scale), ws_ptr, ws_bytes, ctypes.byref(o), _stream(stream)))
+
+
+def paged_attention_decode_noalloc(layout, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                                   scale, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0,
+                                   xcd_weights=None, trace=None, load_policy=0):
+    """paged_attention_decode on the library's own per-GPU scratch: no
+    workspace argument, no allocation."""
+    import torch
+    pdt, rdt = pool_torch_dtype(layout), row_torch_dtype(layout)
+    if q.dim() != 3 or q.shape[2] != layout.head_dim:
+        raise ValueError("q must be [num_seqs][num_q_heads][head_dim]")
+    B, Hq, D = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy)
+    _check(lib().paged_attention_decode_noalloc(
+        ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", rdt),
+        _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32, B),
+        B, Hq, block_tables.shape[1], int(max_context_len), float(scale), ctypes.byref(o), _stream(stream)))
 
 
 def paged_attention_prefill(layout, out, q, k_pool, v_pool, block_tables, context_lens, query_start, max_query_len,

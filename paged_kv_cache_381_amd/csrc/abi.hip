@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "pkv_internal.h"
@@ -264,6 +265,65 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
     return pkv_set_error(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                          workspace ? workspace_bytes : (size_t)0);
   carve_workspace(&a, workspace);
+  return decode_launch(a, opts, stream);
+}
+
+// ------------------------------------------------ decode without allocation
+namespace {
+
+// Scratch of paged_attention_decode_noalloc: the workspace of the largest
+// call (2 * PKV_MAX_DECODE_WAVES slots of 16 query rows of 128 floats, their
+// (m, l), the schedule header of PKV_MAX_SPLIT_SEQS sequences), 32.6 MiB,
+// one copy per GPU that the library runs on, held until the process ends.
+// Host code never uses this name as an address: it takes the device
+// address of each GPU's copy with hipGetSymbolAddress.
+constexpr size_t kNoallocRows = (size_t)2 * PKV_MAX_DECODE_WAVES * 16;
+constexpr size_t kNoallocBytes = ((kNoallocRows * 128 * sizeof(float) + 15) & ~(size_t)15) +
+                                 ((kNoallocRows * 2 * sizeof(float) + 15) & ~(size_t)15) +
+                                 (((size_t)(PKV_HDR_INTS + PKV_MAX_SPLIT_SEQS) * sizeof(int32_t) + 15) & ~(size_t)15);
+static_assert(kNoallocBytes == 34111584, "the size stated in pagedkv.h");
+__device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+constexpr int kMaxDevices = 64;
+struct NoallocScratch {
+  std::once_flag once;
+  void *ptr = nullptr;
+  int rc = 0;
+};
+NoallocScratch g_noalloc[kMaxDevices];
+
+// The device address of the current GPU's scratch, looked up once per
+// device (with that device current) and kept.
+int noalloc_scratch(void **out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_fail((int)e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return pkv_set_error(PKV_ERR_INVALID, "device %d beyond %d", dev, kMaxDevices);
+  NoallocScratch &ns = g_noalloc[dev];
+  std::call_once(ns.once, [&ns] { ns.rc = (int)hipGetSymbolAddress(&ns.ptr, HIP_SYMBOL(scratch)); });
+  if (ns.rc) return hip_fail(ns.rc, "hipGetSymbolAddress of the decode scratch");
+  *out = ns.ptr;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int paged_attention_decode_noalloc(const pkv_layout *layout, float *out, const void *q,
+                                              const void *k_pool, const void *v_pool,
+                                              const int32_t *d_block_tables, const int32_t *d_context_lens,
+                                              int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                              int32_t max_context_len, float scale, const pkv_decode_opts *opts,
+                                              void *stream) {
+  pkv_decode_args a{};
+  const int prep = decode_prepare(layout, out, q, k_pool, v_pool, d_block_tables, d_context_lens, num_seqs,
+                                  num_q_heads, max_blocks_per_seq, max_context_len, scale, opts, stream, &a);
+  if (prep) return prep == 1 ? PKV_OK : prep;
+  const size_t need = paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_len, opts);
+  if (need > kNoallocBytes)
+    return pkv_set_error(PKV_ERR_WORKSPACE, "paged_attention_decode_noalloc: %zu bytes of scratch needed, %zu held",
+                         need, kNoallocBytes);
+  void *ws = nullptr;
+  if (int rc = noalloc_scratch(&ws)) return rc;
+  carve_workspace(&a, ws);
   return decode_launch(a, opts, stream);
 }
 
