@@ -73,10 +73,10 @@ class HipEvents:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the partition kernels' sources: a stored traffic measurement
+    """Hash of the decode kernels' sources: a stored traffic measurement
     only applies while these are unchanged."""
     h = hashlib.sha256()
-    for f in ("decode_mfma.hip", "decode_valu.hip", "pkv_device.h"):
+    for f in ("decode_mfma.hip", "decode_valu.hip", "decode_merge.hip", "pkv_device.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_381_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -155,37 +155,49 @@ def _pmc_mean_kib(rows, name_part: str, counter: str) -> float:
 def traffic_summary(args):
     """Write profiles/decode_<workload>_traffic.txt from four rocprofv3 --pmc
     runs: FETCH_SIZE and WRITE_SIZE of the bench, and of the plain copy probe
-    (1 GiB read + 1 GiB written per copy), which calibrates each counter."""
+    (1 GiB read + 1 GiB written per copy), which calibrates each counter.
+    The traffic of one attention call is its partition kernel's plus its
+    merge kernel's."""
     fetch_dir, write_dir, fetch_copy_dir, write_copy_dir, bench_log = args.traffic_summary
     kern = next((k for k in PARTITION_KERNELS if any(k in r["Kernel_Name"] for r in _pmc_rows(fetch_dir))), None)
     if kern is None:
         raise SystemExit("no partition kernel in the FETCH_SIZE run")
     fetch = _pmc_mean_kib(_pmc_rows(fetch_dir), kern, "FETCH_SIZE")
     write = _pmc_mean_kib(_pmc_rows(write_dir), kern, "WRITE_SIZE")
+    mfetch = _pmc_mean_kib(_pmc_rows(fetch_dir), "merge_kernel", "FETCH_SIZE")
+    mwrite = _pmc_mean_kib(_pmc_rows(write_dir), "merge_kernel", "WRITE_SIZE")
     copy_bytes = 1 << 30
     cfetch = _pmc_mean_kib(_pmc_rows(fetch_copy_dir), "copyBuffer", "FETCH_SIZE")
     cwrite = _pmc_mean_kib(_pmc_rows(write_copy_dir), "copyBuffer", "WRITE_SIZE")
     fscale, wscale = copy_bytes / (cfetch * 1024), copy_bytes / (cwrite * 1024)
-    hbm = fetch * 1024 * fscale + write * 1024 * wscale
+    part = fetch * 1024 * fscale + write * 1024 * wscale
+    merge = mfetch * 1024 * fscale + mwrite * 1024 * wscale
+    hbm = part + merge
     algo = None
     with open(bench_log, encoding="utf-8") as f:
         for line in f:
             if line.startswith("{"):
                 algo = json.loads(line)["roofline"]["bytes_per_launch"]
     lines = [
-        f"# HBM traffic per launch of the decode partition kernel ({kern}), workload {args.workload}",
+        f"# HBM traffic per attention call (partition kernel {kern} + merge_kernel), workload {args.workload}",
         "# from rocprofv3 --pmc runs, one counter per run, each scaled by what it reads for a plain",
         "# 1 GiB device copy (bench.py --copy-probe):",
         f"#   cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o b -- python3 <repo>/bench.py "
-        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline",
-        "#   (the same with --pmc WRITE_SIZE, and both counters over python3 <repo>/bench.py --copy-probe)",
+        f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-stream-probe",
+        "#   (the same with --pmc WRITE_SIZE, and both counters over python3 <repo>/bench.py --copy-probe), then",
+        f"#   python3 <repo>/bench.py --workload {args.workload} --traffic-summary <fetch dir> <write dir> "
+        "<copy fetch dir> <copy write dir> <bench log of the FETCH_SIZE run>",
         f"kernel_source_hash = {kernel_source_hash()}",
         f"fetch_kib_per_dispatch = {fetch:.1f}",
         f"write_kib_per_dispatch = {write:.1f}",
+        f"merge_fetch_kib_per_dispatch = {mfetch:.1f}",
+        f"merge_write_kib_per_dispatch = {mwrite:.1f}",
         f"copy_fetch_kib_per_gib = {cfetch:.1f}",
         f"copy_write_kib_per_gib = {cwrite:.1f}",
         f"fetch_scale = {fscale:.4f}",
         f"write_scale = {wscale:.4f}",
+        f"partition_hbm_bytes_per_launch = {part:.0f}",
+        f"merge_hbm_bytes_per_launch = {merge:.0f}",
         f"hbm_bytes_per_launch = {hbm:.0f}",
         f"algorithmic_bytes_per_launch = {algo}",
         f"traffic_over_algorithmic = {hbm / algo:.4f}" if algo else "traffic_over_algorithmic = unknown",
@@ -194,6 +206,47 @@ def traffic_summary(args):
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def trace_summary(args):
+    """Write profiles/<decode|prefill>_<workload>_kernel_trace.txt from a
+    rocprofv3 --kernel-trace --stats run of this bench (CSV output) and the
+    bench log of the same run."""
+    import csv
+    import glob
+    out_dir, bench_log, cmd = args.trace_summary
+    files = sorted(glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {out_dir}")
+    with open(files[0], newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    bench_lines = []
+    with open(bench_log, encoding="utf-8") as f:
+        for line in f:
+            if line.startswith("[bench]") and ("attention call" in line or "prefill kernel" in line
+                                               or "building" in line):
+                bench_lines.append("#   " + line.strip())
+    kind = "prefill" if args.workload.startswith("prefill") else "decode"
+    tag = args.workload + ("_identity_tables" if args.tables == "identity" else "") + \
+        (f"_batch{args.batch}" if args.batch else "") + (f"_kernel{args.kernel}" if args.kernel else "")
+    lines = ["# rocprofv3 --kernel-trace --stats summary (MI355X, one GPU)",
+             f"# command: cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             f"-d <out> -o kt -- python3 <repo>/bench.py {cmd}",
+             f"# then: python3 <repo>/bench.py --workload {args.workload} --trace-summary <out> <bench log> '{cmd}'",
+             "# the bench's own lines in that run (HIP events on the launch stream, timed steps only):",
+             *bench_lines,
+             "# averages below include the warm-up steps and the build of the workload",
+             f"{'kernel':<78}{'calls':>6}{'avg_us':>10}{'min_us':>10}{'max_us':>10}"]
+    for r in rows:
+        name = (r.get("Name") or r.get("KernelName") or "?").replace("void (anonymous namespace)::", "")
+        name = name.replace("(SplitParams)", "").replace("(PrefillParams)", "")[:76]
+        lines.append(f"{name:<78}{int(r['Calls']):>6}{float(r['AverageNs']) / 1e3:>10.1f}"
+                     f"{float(r['MinNs']) / 1e3:>10.1f}{float(r['MaxNs']) / 1e3:>10.1f}")
+    path = os.path.join(ROOT, "profiles", f"{kind}_{tag}_kernel_trace.txt")
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:12]))
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
@@ -451,6 +504,9 @@ def main():
     ap.add_argument("--stream-probe", action="store_true",
                     help="run only the streaming-read probe (1 GiB of 4 KiB tiles, random and address order)")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the probe in a decode run")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="decode workloads: run the named workload's shapes and draws at this batch size "
+                         "(counter checks on a small launch; 0: the workload's own)")
     ap.add_argument("--load-policy", type=int, default=0,
                     help="K/V tile loads: 0 auto, 1 streaming (non-temporal), 2 cached")
     ap.add_argument("--tables", choices=("shuffled", "identity"), default="shuffled",
@@ -459,9 +515,15 @@ def main():
     ap.add_argument("--traffic-summary", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR", "BENCH_LOG"),
                     help="write profiles/decode_<workload>_traffic.txt from rocprofv3 --pmc output (no GPU)")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("OUT_DIR", "BENCH_LOG", "BENCH_ARGS"),
+                    help="write profiles/<kind>_<workload>_kernel_trace.txt from a rocprofv3 --kernel-trace "
+                         "--stats run of this bench (no GPU)")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
 
     if args.gpus != 1:
@@ -492,7 +554,8 @@ def main():
     if args.workload.startswith("swap:"):
         bench_swap(args)
         return
-    inst = workloads.get(args.workload)
+    inst = workloads.configs.scaled(args.workload, batch=args.batch).instantiate() if args.batch else \
+        workloads.get(args.workload)
     if args.tables == "identity":
         inst.free_order = np.arange(inst.num_blocks, dtype=np.int32)
     wl = inst.wl
@@ -709,7 +772,11 @@ def main():
         del gw, cache
         torch.cuda.empty_cache()
         print("[bench] timing the CPU oracle", flush=True)
-        res["cpu_baseline"] = cpu_baseline(workloads.get(args.workload), args.cpu_seconds)
+        base = workloads.configs.scaled(args.workload, batch=args.batch).instantiate() if args.batch else \
+            workloads.get(args.workload)
+        if args.tables == "identity":
+            base.free_order = np.arange(base.num_blocks, dtype=np.int32)
+        res["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
