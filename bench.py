@@ -208,6 +208,48 @@ def traffic_summary(args):
     print("\n".join(lines))
 
 
+def pmc_summary(args):
+    """Write profiles/<name>_counters.txt from rocprofv3 --pmc runs of this
+    bench (CSV output): per kernel, the mean of each counter over its
+    dispatches and the derived busy fractions (per-XCD active cycles =
+    GRBM_GUI_ACTIVE / 8; 256 CUs, 1024 SIMDs)."""
+    import collections
+    name, cmd, *dirs = args.pmc_summary
+    vals = collections.defaultdict(list)
+    for d in dirs:
+        for r in _pmc_rows(d):
+            k = r["Kernel_Name"].replace("void (anonymous namespace)::", "").split("(")[0]
+            vals[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+    kernels = sorted({k for k, _ in vals if any(t in k for t in ("decode_", "prefill_", "merge_kernel"))})
+    lines = [f"# rocprofv3 --pmc counters (MI355X, one GPU): {name}",
+             "# command, one run per counter set: cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc <counters> "
+             f"--output-format csv -d <dir> -o b -- python3 <repo>/bench.py {cmd}",
+             f"# then: python3 <repo>/bench.py --pmc-summary {name} '{cmd}' <dir> ...",
+             "# counter sets: " + "; ".join(sorted({' '.join(sorted({c for (k2, c) in vals if k2 == k}))
+                                                  for k in kernels})),
+             "# mean per dispatch; busy fractions against GRBM_GUI_ACTIVE / 8 (per-XCD active cycles)"]
+    for k in kernels:
+        cs = {c: sum(v) / len(v) for (k2, c), v in vals.items() if k2 == k}
+        n = max(len(v) for (k2, c), v in vals.items() if k2 == k)
+        lines.append(f"{k}  ({n} dispatches)")
+        for c in sorted(cs):
+            lines.append(f"    {c:28s} {cs[c]:16.6g}")
+        act = cs.get("GRBM_GUI_ACTIVE", 0) / 8
+        if act:
+            def frac(c, units, scale=1.0):
+                if c in cs:
+                    lines.append(f"    {c + ' busy':28s} {100 * cs[c] * scale / (act * units):15.1f} %")
+            frac("SQ_VALU_MFMA_BUSY_CYCLES", 1024)
+            frac("SQ_ACTIVE_INST_VALU", 1024, 4.0)
+            frac("SQ_WAVE_CYCLES", 1024, 4.0)
+            frac("TA_TA_BUSY", 256)
+            frac("TD_TD_BUSY", 256)
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.txt")
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def trace_summary(args):
     """Write profiles/<decode|prefill>_<workload>_kernel_trace.txt from a
     rocprofv3 --kernel-trace --stats run of this bench (CSV output) and the
@@ -518,7 +560,13 @@ def main():
     ap.add_argument("--trace-summary", nargs=3, metavar=("OUT_DIR", "BENCH_LOG", "BENCH_ARGS"),
                     help="write profiles/<kind>_<workload>_kernel_trace.txt from a rocprofv3 --kernel-trace "
                          "--stats run of this bench (no GPU)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="NAME CMD DIR",
+                    help="write profiles/<NAME>_counters.txt from rocprofv3 --pmc runs (CSV dirs) of the bench "
+                         "command CMD (no GPU)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.traffic_summary:
         traffic_summary(args)
         return

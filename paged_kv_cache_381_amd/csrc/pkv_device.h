@@ -213,6 +213,7 @@ struct PrefillParams {
   const int32_t *tables;  // [B][max_blocks]
   const int32_t *ctx;     // [B] tokens held, the new ones included
   const int32_t *qstart;  // [B + 1] first query row of each sequence
+  int32_t B;
   int32_t num_blocks;
   int32_t H;
   int32_t Hq;

@@ -20,8 +20,8 @@
 // serve all of them) and walks keys 0 .. its last token's position in
 // 32-key chunks (two blocks through the table), with a ring of NB chunks of
 // K/V in registers, every load issued on every path so that the
-// memory-counter waits stay exact.  Tiles of one (sequence, kv head) that
-// run longest (the last tokens) are dispatched first.
+// memory-counter waits stay exact.  Tiles that run longest (the last
+// tokens) are dispatched first, across all (sequence, kv head) pairs.
 //
 // Per chunk the wave forms the next chunk's scores while it weighs this
 // one's, so the matrix products and the exponentials of one step are
@@ -72,7 +72,16 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: the walk's bounds live in SGPRs
-  const int b = blockIdx.z, g = blockIdx.y;
+  // Workgroup x takes the (x / (H B))-th group of four waves, counted from
+  // the last new tokens, of kv head x % H of sequence (x / H) % B: workgroups
+  // are dispatched in order, so the longest walks of every (sequence, kv
+  // head) start first and the short ones fill the end, instead of one
+  // sequence's and head's long walks starting last and running alone.
+  // Consecutive workgroups go to the XCDs in turn, so with H B a multiple of
+  // 8 each XCD keeps to the kv heads g = x % 8 and its L2 to their blocks.
+  const int g = (int)(blockIdx.x % P.H);
+  const int b = (int)((blockIdx.x / P.H) % P.B);
+  const int wg = (int)(blockIdx.x / ((unsigned)P.H * P.B));
   const int G = P.G, TQ = 16 / G;
   const int q0 = sload_i32(P.qstart + b);
   const int n = clamp_len(sload_i32(P.ctx + b), P.max_blocks, P.max_ctx);
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   const int nq = min(sload_i32(P.qstart + b + 1) - q0, n);
   const int ntile = (nq + TQ - 1) / TQ;
   // The wave's CT column tiles, longest first; tiles run longest first too.
-  const int t_first = ntile - 1 - (int)(blockIdx.x * 4 + w) * CT;
+  const int t_first = ntile - 1 - (wg * 4 + w) * CT;
   if (t_first < 0) return;
   const int p0 = n - nq;  // position of new token 0
   const int kend = p0 + min(t_first * TQ + TQ, nq);  // keys the wave's last token sees
@@ -419,8 +428,9 @@ int launch(const pkv_prefill_args &a, const PrefillParams &p) {
   const int tq = 16 / p.G;
   const int tiles = (a.max_query_len + tq - 1) / tq;
   const int waves = (tiles + CT - 1) / CT;
-  const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)p.H, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+  const int64_t nwg = (int64_t)((waves + 3) / 4) * p.H * a.num_seqs;
+  if (nwg > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   return (int)hipGetLastError();
 }
 
@@ -442,6 +452,7 @@ int pkv_launch_prefill_mfma(const pkv_prefill_args &a) {
   p.max_blocks = a.max_blocks;
   p.max_ctx = a.max_ctx;
   p.scale_log2 = a.scale_log2;
+  p.B = a.num_seqs;
   if (a.L->kv_dtype == PKV_INT8) return a.L->head_dim == 128 ? launch<128, true>(a, p) : launch<64, true>(a, p);
   if (a.L->kv_dtype == PKV_FP8)
     return a.L->head_dim == 128 ? launch<128, true, true>(a, p) : launch<64, true, true>(a, p);
