@@ -29,24 +29,36 @@ template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
   const int seg = blockIdx.x;
   const int b = seg / P.H, g = seg - b * P.H;
-  const int32_t c_seq = P.ws_hdr[0];
+  const int32_t *hdr = P.ws_hdr;
+  const int32_t *s_incl = hdr + PKV_HDR_INTS;
+  // Every header word needed without per-XCD weights is loaded at once (one
+  // memory round trip); with them the region bounds are read as well.
+  const int32_t c_seq = sload_i32(hdr), nwe = sload_i32(hdr + 1), nr = sload_i32(hdr + 2);
+  const int incl = sload_i32(s_incl + b), excl = b ? sload_i32(s_incl + b - 1) : 0;
+  const int cnt = incl - excl;
+  if (cnt == 0 || c_seq == 0) return;
   const int64_t c_tot = (int64_t)P.H * c_seq;
-  const int32_t *s_incl = P.ws_hdr + PKV_HDR_INTS;
-  const int cnt = s_incl[b] - (b ? s_incl[b - 1] : 0);
-  if (cnt == 0 || c_tot == 0) return;
-  const int64_t seg0 = (int64_t)g * c_seq + (s_incl[b] - cnt);
-  Regions rg;
-  rg.C = c_tot;
-  rg.nwe = P.ws_hdr[1];
-  rg.nr = P.ws_hdr[2];
-  rg.wpr = rg.nwe / rg.nr;
-  rg.bounds = reinterpret_cast<const int64_t *>(P.ws_hdr + 4);
-  const int w0 = rg.wave_of(seg0), w1 = rg.wave_of(seg0 + cnt - 1);
+  const int64_t seg0 = (int64_t)g * c_seq + excl;
+  int w0, w1, first0;
+  if (nr <= 1) {  // one region [0, c_tot): shares [w C / nwe, (w + 1) C / nwe)
+    w0 = (int)(((seg0 + 1) * nwe - 1) / c_tot);
+    w1 = (int)(((seg0 + cnt) * nwe - 1) / c_tot);
+    first0 = 2 * w0 + ((int64_t)w0 * c_tot / nwe < seg0 ? 1 : 0);
+  } else {
+    Regions rg;
+    rg.C = c_tot;
+    rg.nwe = nwe;
+    rg.nr = nr;
+    rg.wpr = nwe / nr;
+    rg.bounds = reinterpret_cast<const int64_t *>(hdr + 4);
+    w0 = rg.wave_of(seg0);
+    w1 = rg.wave_of(seg0 + cnt - 1);
+    int64_t lo0, hi0;
+    rg.share(w0, lo0, hi0);
+    first0 = 2 * w0 + (lo0 < seg0 ? 1 : 0);
+  }
   const int np = w1 - w0 + 1;
   if (np <= 1) return;
-  int64_t lo0, hi0;
-  rg.share(w0, lo0, hi0);
-  const int first0 = 2 * w0 + (lo0 < seg0 ? 1 : 0);
 
   const int lane = threadIdx.x, G = P.G;
   const size_t row0 = (size_t)b * P.Hq + (size_t)g * G;
