@@ -117,15 +117,18 @@ const char *pkv_version(void);
 /* ------------------------------------------------------------ block pool */
 typedef struct pkv_pool pkv_pool;
 
-/* Create the host block manager for a pool.  free_order (nullable) is a
- * permutation of [0, num_blocks): the order in which blocks are first handed
- * out (NULL = 0, 1, 2, ...).  The free pool is a stack: a freed block is the
+/* Create the host block manager for a pool: the physical KV cache cut into
+ * fixed 16-token blocks, all free at first [KV Cache 工程学 §15.5].
+ * free_order (nullable) is a permutation of [0, num_blocks): the order in
+ * which blocks are first handed out (NULL = 0, 1, 2, ...).  The free pool is a stack: a freed block is the
  * next one handed out.  *out receives the new pool. */
 int pkv_pool_create(const pkv_layout *layout, const int32_t *free_order, pkv_pool **out);
 /* Destroy a pool (NULL is accepted). */
 int pkv_pool_destroy(pkv_pool *pool);
 
-/* Take one free block; its reference count becomes 1. */
+/* Take one free block; its reference count becomes 1.  Blocks are counted by
+ * reference so that several block tables may name one physical block
+ * [新一代 KV Cache 管理 §8.1; KV Cache 工程学 §15.5, "PagedAttention 的好处" 3]. */
 int pkv_block_alloc(pkv_pool *pool, int32_t *block_out);
 /* Add a reference to an allocated block. */
 int pkv_block_incref(pkv_pool *pool, int32_t block);
@@ -138,11 +141,17 @@ int pkv_block_refcount(const pkv_pool *pool, int32_t block, int32_t *out);
 int pkv_pool_num_free(const pkv_pool *pool, int32_t *out);
 
 /* --------------------------------------------------------------- sequences */
-/* New empty sequence; ids are 0, 1, 2, ... in creation order, never reused. */
+/* New empty sequence with an empty block table [KV Cache 工程学 §15.5]; ids
+ * are 0, 1, 2, ... in creation order, never reused. */
 int pkv_seq_create(pkv_pool *pool, int64_t *id_out);
-/* New sequence sharing every block of parent (each gains one reference). */
+/* New sequence sharing every block of parent (each gains one reference): the
+ * parallel samples of one prompt read its blocks through their own tables
+ * [新一代 KV Cache 管理 §8.1, best-of-8]. */
 int pkv_seq_fork(pkv_pool *pool, int64_t parent, int64_t *child_out);
-/* Reserve slots for n more tokens at the end of a sequence, all or none.
+/* Reserve slots for n more tokens at the end of a sequence, all or none:
+ * a token goes into the current block while it has room, and a new block is
+ * taken when it is full [KV Cache 工程学 §15.5]; a shared block is copied
+ * before a write [KV Cache 与 PagedAttention, "PagedAttention 如何解决这个问题"].
  * For each token at position p: when p % 16 == 0 a block is taken and
  * appended to the table; otherwise, when the tail block is shared (count
  * > 1), a block is taken, the pair (old, new) is written to cow_pairs_out
@@ -160,15 +169,20 @@ int pkv_batch_append_slots(pkv_pool *pool, const int64_t *ids, int32_t num_seqs,
                            int64_t *slots_out, int32_t *cow_pairs_out, int32_t cow_cap,
                            int32_t *n_cow);
 /* Release a sequence: its blocks lose a reference in table order; blocks
- * reaching zero are pushed onto the free pool in that order. */
+ * reaching zero are pushed onto the free pool in that order (a finished
+ * sequence returns its blocks [KV Cache 工程学 §15.5]). */
 int pkv_seq_free(pkv_pool *pool, int64_t id);
 /* Number of tokens of a sequence into *len_out. */
 int pkv_seq_len(const pkv_pool *pool, int64_t id, int32_t *len_out);
-/* Copy a sequence's block table into out (room for cap entries); *n_out
- * receives its length.  PKV_ERR_CAPACITY if cap is too small. */
+/* Copy a sequence's block table -- entry i names the physical block of its
+ * logical block i [KV Cache 工程学 §15.5] -- into out (room for cap
+ * entries); *n_out receives its length.  PKV_ERR_CAPACITY if cap is too
+ * small. */
 int pkv_seq_block_table(const pkv_pool *pool, int64_t id, int32_t *out, int32_t cap,
                         int32_t *n_out);
-/* Block tables and lengths of a batch, as paged_attention_decode reads them:
+/* Block tables and lengths of a batch, as paged_attention_decode reads them
+ * (the table is an extra input of the attention kernel [KV Cache 工程学
+ * §15.5, "PagedAttention 的代价" 2]):
  * tables_out [num_seqs][max_blocks_per_seq] (entries past a sequence's
  * blocks are set to 0), context_lens_out [num_seqs]. */
 int pkv_batch_block_tables(const pkv_pool *pool, const int64_t *ids, int32_t num_seqs,
@@ -305,9 +319,10 @@ int pkv_swap_space_stats(const pkv_pool *pool, pkv_swap_stats *out);
 int paged_kv_append(const pkv_layout *layout, void *k_pool, void *v_pool, const void *k_new,
                     const void *v_new, const int64_t *d_slots, int32_t num_tokens, void *stream);
 
-/* Copy whole blocks (all heads, all slots, K and V): d_pairs is int32
- * [num_pairs][2] of (src, dst) on the device, as pkv_seq_append_slots
- * reports them for copy-on-write.  Destinations must be distinct and not
+/* Copy whole blocks (all heads, all slots, K and V) -- the copy of a shared
+ * block before a write [KV Cache 与 PagedAttention, "PagedAttention 如何解决
+ * 这个问题"]: d_pairs is int32 [num_pairs][2] of (src, dst) on the device, as
+ * pkv_seq_append_slots reports them for copy-on-write.  Destinations must be distinct and not
  * also sources. */
 int pkv_copy_blocks(const pkv_layout *layout, void *k_pool, void *v_pool, const int32_t *d_pairs,
                     int32_t num_pairs, void *stream);
