@@ -251,7 +251,7 @@ def pmc_summary(args):
 
 
 def trace_summary(args):
-    """Write profiles/<decode|prefill>_<workload>_kernel_trace.txt from a
+    """Write profiles/[decode_]<workload>_kernel_trace.txt from a
     rocprofv3 --kernel-trace --stats run of this bench (CSV output) and the
     bench log of the same run."""
     import csv
@@ -269,7 +269,7 @@ def trace_summary(args):
             if line.startswith("[bench]") and ("attention call" in line or "prefill kernel" in line
                                                or "building" in line):
                 bench_lines.append("#   " + line.strip())
-    kind = "prefill" if args.workload.startswith("prefill") else "decode"
+    kind = "" if args.workload.startswith("prefill") else "decode_"
     tag = args.workload + ("_identity_tables" if args.tables == "identity" else "") + \
         (f"_batch{args.batch}" if args.batch else "") + (f"_kernel{args.kernel}" if args.kernel else "")
     lines = ["# rocprofv3 --kernel-trace --stats summary (MI355X, one GPU)",
@@ -285,7 +285,7 @@ def trace_summary(args):
         name = name.replace("(SplitParams)", "").replace("(PrefillParams)", "")[:76]
         lines.append(f"{name:<78}{int(r['Calls']):>6}{float(r['AverageNs']) / 1e3:>10.1f}"
                      f"{float(r['MinNs']) / 1e3:>10.1f}{float(r['MaxNs']) / 1e3:>10.1f}")
-    path = os.path.join(ROOT, "profiles", f"{kind}_{tag}_kernel_trace.txt")
+    path = os.path.join(ROOT, "profiles", f"{kind}{tag}_kernel_trace.txt")
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines[:12]))
