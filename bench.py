@@ -241,7 +241,8 @@ def pmc_summary(args):
                     lines.append(f"    {c + ' busy':28s} {100 * cs[c] * scale / (act * units):15.1f} %")
             frac("SQ_VALU_MFMA_BUSY_CYCLES", 1024)
             frac("SQ_ACTIVE_INST_VALU", 1024, 4.0)
-            frac("SQ_WAVE_CYCLES", 1024, 4.0)
+            if "SQ_WAVE_CYCLES" in cs:  # waves resident per SIMD, on average
+                lines.append(f"    {'SQ_WAVE_CYCLES waves/SIMD':28s} {cs['SQ_WAVE_CYCLES'] * 4.0 / (act * 1024):15.2f}")
             frac("TA_TA_BUSY", 256)
             frac("TD_TD_BUSY", 256)
     path = os.path.join(ROOT, "profiles", f"{name}_counters.txt")
