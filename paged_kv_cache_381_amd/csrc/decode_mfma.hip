@@ -88,11 +88,20 @@ constexpr float kSlack = 8.0f;
 #define PKV_MFMA_NBUF_I8 3
 #endif
 
+// Loads of a buffer past the share's end read these bytes instead of K/V:
+// two (block, kv head) tiles of the largest kind (bf16 at D = 128), which
+// every wave shares and the L2 keeps, so the steps that finish a group of NB
+// cost no HBM reads.  Their values are never used (no token is counted there
+// and the V rows are masked), so they are left as loaded: zero.
+constexpr int kIdleTileBytes = 32 * 128;
+__device__ __align__(4096) uint8_t g_idle_tiles[2 * kIdleTileBytes];
+
 template <int D, int W, int NB, bool I8, bool F8, bool NT>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
   constexpr int TB = I8 ? 16 * D + 64 : 32 * D;  // bytes per (block, kv head) tile
+  static_assert(TB <= kIdleTileBytes, "the idle tiles must cover a tile");
   // K registers per 16-row token set: one 16-byte unit per score MFMA for
   // bf16; for int8 one unit holds the codes of two MFMAs (16 elements).
   constexpr int NKU = I8 ? NKK / 2 : NKK;
@@ -141,6 +150,12 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   VUnit va[NB][NNN];
   float4 ksc[NB][2], vsc[NB][2];  // int8: scales of this lane's 8 token slots
 
+  // The tile of buffer i's first (sel 0) or second block; an idle buffer
+  // (pa < 0, past the share's end) reads the shared idle tiles.
+  auto tile = [&](const uint8_t *pool, int i, int sel, int g) -> const uint8_t * {
+    if (pa[i] < 0) return g_idle_tiles + (sel ? TB : 0);
+    return pool + ((size_t)(sel ? pb[i] : pa[i]) * H + g) * TB;
+  };
   auto issue = [&](auto bi) {  // loads of the chunk held in buffer bi
     constexpr int I = decltype(bi)::value;
     constexpr int QI = NQ == 1 ? 0 : I;
@@ -151,7 +166,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       const uint4 u = qr[kgroup(kk)];
       qb[QI][kk] = as_bf16x8<F8>(u);
     }
-    const uint4 *kt = reinterpret_cast<const uint4 *>(kpool + ((size_t)(ksel ? pb[I] : pa[I]) * H + c.g) * TB);
+    const uint4 *kt = reinterpret_cast<const uint4 *>(tile(kpool, I, ksel, c.g));
 #pragma unroll
     for (int ku = 0; ku < NKU; ++ku) {
       // 16-byte unit of the lane's token row: int8 unit 4ku+grp holds the
@@ -161,15 +176,14 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       ay[I][ku] = load_u4<NT>(kt + cu * 16 + ktx + 4);
     }
     if constexpr (I8) {
-      const float4 *sc = reinterpret_cast<const float4 *>(
-          kpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + c.g) * TB + 16 * D + 32 * vhalf);
+      const float4 *sc = reinterpret_cast<const float4 *>(tile(kpool, I, vsel, c.g) + 16 * D + 32 * vhalf);
       ksc[I][0] = load_f4<NT>(sc);
       ksc[I][1] = load_f4<NT>(sc + 1);
     }
   };
   auto issue_v = [&](auto bi) {
     constexpr int I = decltype(bi)::value;
-    const uint8_t *vt = vpool + ((size_t)(vsel ? pb[I] : pa[I]) * H + cq[I].g) * TB;
+    const uint8_t *vt = tile(vpool, I, vsel, cq[I].g);
     if constexpr (I8) {
 #pragma unroll
       for (int nn = 0; nn < NNN; ++nn) va[I][nn] = load_u2<NT>(vt + (16 * nn + r16) * 16 + 8 * vhalf);
@@ -188,14 +202,15 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   for (int nn = 0; nn < NNN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  // Every load is issued whatever the share's length: a chunk past the
-  // share's end re-reads the last real chunk's lines (cached, never used).
-  // Loads issued on some paths only would leave the count of loads in
-  // flight unknown, and the waits would then drain every buffer each step.
-  auto same_as = [&](int to, int from) {
+  // Every load is issued whatever the share's length: a buffer past the
+  // share's end keeps the last real chunk's cursor (its query slices) and
+  // reads the idle tiles for K/V.  Loads issued on some paths only would
+  // leave the count of loads in flight unknown, and the waits would then
+  // drain every buffer each step.
+  auto idle_after = [&](int to, int from) {
     cq[to] = cq[from];
-    pa[to] = pa[from];
-    pb[to] = pb[from];
+    pa[to] = -1;
+    pb[to] = -1;
   };
   // Prologue: chunks lo .. lo+NB-2 are requested, chunk lo+NB-1 located.
   cq[0] = sh.first();
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
     ((Is == 0 ? (void)0
               : (lo + Is < hi ? (void)(cq[Is] = sh.next(cq[Is - 1]), sh.blocks(cq[Is], pa[Is], pb[Is]))
-                              : same_as(Is, Is - 1))), ...);
+                              : idle_after(Is, Is - 1))), ...);
   }(std::make_integer_sequence<int, NB>{});
   // Requests leave in the order the loop issues them (K then V of each
   // chunk): waits at the loop head are counted over both entries, and a
@@ -238,13 +253,13 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[QI][kk], sx, 0, 0, 0);
       sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[QI][kk], sy, 0, 0, 0);
     }
-    if (x + NB - 1 >= hi) same_as(J, I);  // no chunk x + NB - 1 in the share
+    if (x + NB - 1 >= hi) idle_after(J, I);  // no chunk x + NB - 1 in the share
     issue(std::integral_constant<int, J>{});
 
     const Cursor &cur = cq[I];
     // Past the share's end the loop runs on to the end of its group of NB
-    // steps over a copy of the last chunk with no token counted: nothing is
-    // stored, and the loop keeps one exit, after a whole group.
+    // steps over the idle tiles with no token counted: nothing is stored,
+    // and the loop keeps one exit, after a whole group.
     const bool real = x < hi;
     const int n = real ? cur.n : 0;
     const int tok0 = 32 * cur.j;
