@@ -13,13 +13,11 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // Eight bf16 elements of an MFMA operand: a 16-byte unit of a bf16 cache or
 // query, or eight one-byte codes (bytes 0..3 of u.x, then of u.y) widened
 // exactly to bf16.  An int8 code needs 7 significant bits.  Every FP8 E4M3
-// value (3 mantissa bits, exponents -9 .. 8) is a bf16 value too: the gfx950
-// instruction that widens two codes of one 16-bit half to float32 is exact
-// on all 254 finite codes (checked against the format's definition on the
-// device), and the float32 pair then packs to bf16 without rounding.  (The
-// instruction that widens straight to bf16 with a float32 scale returned
-// the value of the code with its lowest mantissa bit cleared in that check,
-// so it is not used.)
+// value (3 mantissa bits, exponents -9 .. 8) is a bf16 value too: gfx950's
+// scaled conversion, with a scale of 1, widens two codes of one 16-bit half
+// straight to bf16 and is exact on all 254 finite codes (checked on the
+// device against the format's definition, as the two-step path through a
+// float32 pair it replaced), so four instructions widen eight codes.
 template <bool F8 = false>
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
@@ -27,10 +25,10 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
 template <bool F8>
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint2 u) {
   if constexpr (F8) {
-    const bf16x2_t a = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, false), bf16x2_t);
-    const bf16x2_t b = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, true), bf16x2_t);
-    const bf16x2_t c = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, false), bf16x2_t);
-    const bf16x2_t d = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, true), bf16x2_t);
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, 1.0f, true);
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   } else {
     bf16x8_t r;
