@@ -61,6 +61,10 @@ class HipEvents:
             out.append(e)
         return out
 
+    def record(self, e, stream):
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        assert self.hip.hipEventRecord(e, stream) == 0
+
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
         rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
@@ -292,6 +296,7 @@ def trace_summary(args):
     print("\n".join(lines[:12]))
 
 
+N_SPAN_CALLS = 5  # untimed traced steps after the timed ones (wave span of the partition kernel)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 PREFILL_METRIC = "paged prefill attention TFLOP/s (% of bf16 MFMA peak), 1 GPU"
 
@@ -525,6 +530,35 @@ def stream_probe(reps: int = 5):
     return res
 
 
+def launch_cost(reps: int = 30):
+    """Fixed cost of one launch on the decode kernels' grid: an empty kernel
+    (libpkvprobe.so) whose waves record their first and last clock, timed by
+    the same events as the attention call.  Returns the median event time, the
+    span of the waves (first start to last end) and their difference, in us."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_381_amd import build as B
+    plib = ctypes.CDLL(B.PROBE_LIB)
+    plib.pkv_probe_launch_cost.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    clock = torch.zeros(8 * plib.pkv_probe_compute_units(), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+    ev = hip.create(2)
+    times, spans = [], []
+    for r in range(reps + 1):
+        hip.record(ev[0], stream)
+        assert plib.pkv_probe_launch_cost(clock.data_ptr(), stream) == 0
+        hip.record(ev[1], stream)
+        torch.cuda.synchronize()
+        if r:
+            times.append(hip.elapsed_ms(ev[0], ev[1]) * 1e3)
+            c = clock.cpu().numpy().astype(np.int64).reshape(-1, 2) & 0xFFFFFFFF
+            spans.append((c[:, 1].max() - c[:, 0].min()) / 100.0)
+    hip.destroy(ev)
+    t, sp = float(np.median(times)), float(np.median(spans))
+    return {"event_us": round(t, 2), "wave_span_us": round(sp, 2), "outside_waves_us": round(t - sp, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -614,7 +648,7 @@ def main():
     # Enough layers (own pools) that one step stores more than 1 GiB of
     # distinct K/V, so the 256 MB Infinity Cache cannot hold a step's reads.
     layers = args.layers or min(64, max(1, math.ceil((1 << 30) / inst.kv_bytes_unique())))
-    total_steps = K + W + 3  # warm-up, XCD-weight calibration and timed steps
+    total_steps = K + W + 3 + N_SPAN_CALLS  # warm-up, XCD-weight calibration, timed and traced steps
     extra = B * (total_steps // 16 + 2)
     print(f"[bench] building {wl.name}: B={B} Hq={Hq} H={H} D={D} {wl.cache_dtype} cache, layers/step={layers}",
           flush=True)
@@ -763,10 +797,38 @@ def main():
     print(f"[bench] {K} steps in {elapsed:.3f} s; attention call avg {avg_ms * 1e3:.1f} us "
           f"({achieved:.0f} GB/s of distinct K/V, {achieved_logical:.0f} GB/s logical); partition kernel alone "
           f"{avg_part_ms * 1e3:.1f} us", flush=True)
-    probe = None
+    # Untimed calls with the wave trace: the span of the partition kernel's
+    # waves (first start to last end) against its event time, and the rate
+    # at which its waves read while they run.
+    trace = torch.zeros(4 * L.PKV_TRACE_WAVES, dtype=torch.int32, device=dev)
+    ev_w = hip.create(2)
+    spans, part_us = [], []
+    for c in range(N_SPAN_CALLS):
+        trace.zero_()
+        step(W_eff + K + c, -1, L.decode_opts(args.partition, args.kernel, (ev_w[0], ev_w[1], None), wps, xw,
+                                              trace=trace, load_policy=args.load_policy))
+        torch.cuda.synchronize()
+        t = trace.cpu().numpy().reshape(-1, 4).astype(np.int64)
+        t = t[t[:, 1] > 0]
+        if len(t):
+            rel = lambda v: (v - t[0, 2] + (1 << 31)) % (1 << 32) - (1 << 31)  # 32-bit clock, 100 MHz
+            spans.append((rel(t[:, 3]).max() - rel(t[:, 2]).min()) / 100.0)
+            part_us.append(hip.elapsed_ms(ev_w[0], ev_w[1]) * 1e3)
+    hip.destroy(ev_w)
+    wave_span = None
+    if spans:
+        sp, pu = float(np.median(spans)), float(np.median(part_us))
+        wave_span = {"partition_event_us": round(pu, 2), "wave_span_us": round(sp, 2),
+                     "outside_waves_us": round(pu - sp, 2),
+                     "read_rate_over_span_gbps": round(unique_per_launch / (sp * 1e-6) / 1e9, 1)}
+        print(f"[bench] partition kernel waves: span {sp:.1f} us of {pu:.1f} us between events "
+              f"({wave_span['read_rate_over_span_gbps']:.0f} GB/s over the span)", flush=True)
+    probe, lcost = None, None
     if not args.no_stream_probe:
         probe = stream_probe()
         print(f"[bench] streaming-read probe (1 GiB of 4 KiB tiles), GB/s: {probe}", flush=True)
+        lcost = launch_cost()
+        print(f"[bench] empty launch on the same grid: {lcost}", flush=True)
     pst = cache.stats()
 
     res = {
@@ -793,6 +855,8 @@ def main():
         "attention_pct_of_probe": round(100 * achieved / max(probe[k] for k in probe if k.startswith("random")), 2)
         if probe else None,
         "stream_probe_gbps": probe,
+        "launch_cost_us": lcost,
+        "partition_wave_span": wave_span,
         "pool": {"blocks": pst["num_blocks"], "usage": round(pst["usage"], 4),
                  "internal_fragmentation": round(pst["internal_fragmentation"], 4),
                  "tokens_logical": pst["tokens_logical"], "tokens_stored": pst["tokens_stored"],

@@ -90,6 +90,19 @@ __global__ __launch_bounds__(64 * kWaves) void stream_tiles_kernel(const uint4 *
   if (lane == 0) sink[w] = acc;
 }
 
+// Fixed cost of a launch: an empty kernel on the decode kernels' grid (one
+// 256-thread workgroup per compute unit, LDS above half of the CU) whose
+// waves record their first and last clock (s_memrealtime, 100 MHz).  The
+// time events on the stream see around it, less the span of its waves, is
+// what a launch costs beside the work of its waves.
+__global__ __launch_bounds__(64 * kWaves) void launch_cost_kernel(uint32_t *clock) {
+  extern __shared__ int32_t s_unused[];
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
+  const int w = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_s_memrealtime();
+  if ((threadIdx.x & 63) == 0) *reinterpret_cast<uint2 *>(clock + 2 * w) = make_uint2(t0, t1);
+}
+
 template <bool NT>
 int launch(const void *buf, int64_t n_tiles, const int32_t *order, uint32_t *sink, int nwg, size_t lds,
            hipStream_t stream) {
@@ -122,6 +135,23 @@ extern "C" int pkv_probe_stream_tiles(const void *buf, int64_t n_tiles, const in
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return streaming ? launch<true>(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, lds, s)
                    : launch<false>(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, lds, s);
+}
+
+// One launch of the empty kernel on one workgroup of four waves per compute
+// unit; d_clock receives each wave's first and last clock (2 uint32 per
+// wave, 8 per compute unit).  Returns a HIP error code (0 = launched), or -1
+// for a null d_clock.
+extern "C" int pkv_probe_launch_cost(uint32_t *d_clock, void *stream) {
+  if (!d_clock) return -1;
+  int dev = 0, cus = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return (int)e;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
+  if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(launch_cost_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsOneWgPerCu))
+    return (int)e;
+  hipLaunchKernelGGL(launch_cost_kernel, dim3(cus), dim3(64 * kWaves), kLdsOneWgPerCu,
+                     reinterpret_cast<hipStream_t>(stream), d_clock);
+  return (int)hipGetLastError();
 }
 
 // Compute units of the current device (the probe's sink holds 4 per unit
