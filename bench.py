@@ -559,6 +559,40 @@ def launch_cost(reps: int = 30):
     return {"event_us": round(t, 2), "wave_span_us": round(sp, 2), "outside_waves_us": round(t - sp, 2)}
 
 
+def mfma_probe(iters: int = 20000):
+    """Matrix-core issue probe (libpkvprobe.so): per iteration 24 independent
+    v_mfma_f32_16x16x32_bf16 and/or the vector work that weighs 24 scores,
+    with one and two waves per SIMD.  Returns us per launch and cycles per
+    iteration of one wave (at 2.4 GHz), and the products' TFLOP/s."""
+    import torch
+    from paged_kv_cache_381_amd import build as B
+    plib = ctypes.CDLL(B.PROBE_LIB)
+    plib.pkv_probe_mfma_issue.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    cus = plib.pkv_probe_compute_units()
+    d_in = torch.zeros(96, dtype=torch.float32, device="cuda")
+    d_out = torch.empty(2 * 256 * cus, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+    ev = hip.create(2)
+    names = {0: "products", 1: "vector work", 2: "both, in program order", 3: "both, interleaved"}
+    res = {}
+    for wps in (1, 2):
+        for mode in range(4):
+            assert plib.pkv_probe_mfma_issue(mode, wps, iters, d_in.data_ptr(), d_out.data_ptr(), stream) == 0
+            hip.record(ev[0], stream)
+            assert plib.pkv_probe_mfma_issue(mode, wps, iters, d_in.data_ptr(), d_out.data_ptr(), stream) == 0
+            hip.record(ev[1], stream)
+            torch.cuda.synchronize()
+            us = hip.elapsed_ms(ev[0], ev[1]) * 1e3
+            r = {"us": round(us, 1), "cycles_per_iter_per_wave_at_2.4GHz": round(us * 2400 / iters / wps, 1)}
+            if mode == 0:
+                r["tflops"] = round(24 * 16384 * iters * 4 * cus * wps / (us * 1e-6) / 1e12, 1)
+            res[f"{names[mode]}, {wps} wave(s)/SIMD"] = r
+    hip.destroy(ev)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -578,6 +612,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only plain 1 GiB copies (PMC calibration)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="run only the matrix-core issue probe (products and vector work, one and two waves per SIMD)")
     ap.add_argument("--stream-probe", action="store_true",
                     help="run only the streaming-read probe (1 GiB of 4 KiB tiles, random and address order)")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the probe in a decode run")
@@ -620,6 +656,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(1.0, 10)
+        return
+    if args.mfma_probe:
+        print(json.dumps({"mfma_issue_probe": mfma_probe()}), flush=True)
         return
     if args.stream_probe:
         r = stream_probe(10)

@@ -103,6 +103,61 @@ __global__ __launch_bounds__(64 * kWaves) void launch_cost_kernel(uint32_t *cloc
   if ((threadIdx.x & 63) == 0) *reinterpret_cast<uint2 *>(clock + 2 * w) = make_uint2(t0, t1);
 }
 
+// Matrix-core issue probe: per iteration, 24 v_mfma_f32_16x16x32_bf16 on
+// independent accumulators and/or the vector work that weighs 24 scores
+// (fma, base-2 exponential, bf16 pack), with one or two waves per SIMD.
+// MODE 0: products only; 1: vector work only; 2: both in program order; 3:
+// both, one product then two vector instructions (scheduling groups).  The
+// results are folded into one store per lane, so no work is dead.
+typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
+typedef float f32x4_p __attribute__((ext_vector_type(4)));
+typedef float f32x2_p __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_p __attribute__((ext_vector_type(2)));
+
+template <int MODE>
+__global__ __launch_bounds__(64 * kWaves) void mfma_issue_kernel(const float *in, float *out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8_p a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)in[lane + i];
+    b[i] = (__bf16)in[lane + 8 + i];
+  }
+  f32x4_p acc[24];
+  float e[24];
+#pragma unroll
+  for (int i = 0; i < 24; ++i) {
+    acc[i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+    e[i] = in[lane + i];
+  }
+  uint32_t pk = 0;
+  const float m = in[0], mul = in[1];
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MODE != 1) {
+#pragma unroll
+      for (int i = 0; i < 24; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+    }
+    if constexpr (MODE != 0) {
+#pragma unroll
+      for (int i = 0; i < 24; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], mul, -m));
+#pragma unroll
+      for (int i = 0; i < 24; i += 2)
+        pk ^= __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_p{e[i], e[i + 1]}, bf16x2_p));
+    }
+    if constexpr (MODE == 3) {
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+    }
+  }
+  float r = (float)pk;
+#pragma unroll
+  for (int i = 0; i < 24; ++i) r += acc[i][0] + acc[i][3] + e[i];
+  out[blockIdx.x * (64 * kWaves) + threadIdx.x] = r;
+}
+
 template <bool NT>
 int launch(const void *buf, int64_t n_tiles, const int32_t *order, uint32_t *sink, int nwg, size_t lds,
            hipStream_t stream) {
@@ -151,6 +206,29 @@ extern "C" int pkv_probe_launch_cost(uint32_t *d_clock, void *stream) {
     return (int)e;
   hipLaunchKernelGGL(launch_cost_kernel, dim3(cus), dim3(64 * kWaves), kLdsOneWgPerCu,
                      reinterpret_cast<hipStream_t>(stream), d_clock);
+  return (int)hipGetLastError();
+}
+
+// One launch of the matrix-core issue probe (mode 0..3, see above) for iters
+// iterations on waves_per_simd (1 or 2) workgroups of four waves per compute
+// unit.  d_in: 96 floats of input (any finite values); d_out: one float per
+// thread (256 * waves_per_simd * compute units).  Returns a HIP error code
+// (0 = launched), or -1 for bad arguments.
+extern "C" int pkv_probe_mfma_issue(int32_t mode, int32_t waves_per_simd, int32_t iters, const float *d_in,
+                                    float *d_out, void *stream) {
+  if (!d_in || !d_out || iters <= 0 || mode < 0 || mode > 3 || (waves_per_simd != 1 && waves_per_simd != 2))
+    return -1;
+  int dev = 0, cus = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return (int)e;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
+  const dim3 grid(cus * waves_per_simd), block(64 * kWaves);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(mfma_issue_kernel<0>, grid, block, 0, s, d_in, d_out, iters); break;
+    case 1: hipLaunchKernelGGL(mfma_issue_kernel<1>, grid, block, 0, s, d_in, d_out, iters); break;
+    case 2: hipLaunchKernelGGL(mfma_issue_kernel<2>, grid, block, 0, s, d_in, d_out, iters); break;
+    default: hipLaunchKernelGGL(mfma_issue_kernel<3>, grid, block, 0, s, d_in, d_out, iters); break;
+  }
   return (int)hipGetLastError();
 }
 
