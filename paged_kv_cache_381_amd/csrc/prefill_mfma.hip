@@ -20,8 +20,9 @@
 // serve all of them) and walks keys 0 .. its last token's position in
 // 32-key chunks (two blocks through the table), with a ring of NB chunks of
 // K/V in registers, every load issued on every path so that the
-// memory-counter waits stay exact.  Tiles that run longest (the last
-// tokens) are dispatched first, across all (sequence, kv head) pairs.
+// memory-counter waits stay exact; the query slices wait in LDS.  Two waves
+// share each SIMD.  Tiles that run longest (the last tokens) are dispatched
+// first, across all (sequence, kv head) pairs.
 //
 // Per chunk the wave forms the next chunk's scores while it weighs this
 // one's, so the matrix products and the exponentials of one step are
@@ -58,16 +59,21 @@ __device__ __forceinline__ bf16x8_t pack_bf16x8(const float (&e)[8]) {
 }
 
 template <int D, int NB, bool I8, int CT, bool F8>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
+// Two waves per SIMD (at most 256 registers a wave): one wave alone issues
+// its matrix products at about 60 % of the matrix cores' rate and cannot run
+// them beside its own vector work, two keep the matrix cores busier while
+// the other wave weighs.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(
+    PrefillParams P) {
   constexpr int NKK = D / 32;
   constexpr int NNN = D / 16;
   constexpr int TB = I8 ? 16 * D + 64 : 32 * D;
   constexpr int NKU = I8 ? NKK / 2 : NKK;
   using VUnit = std::conditional_t<I8, uint2, uint4>;
-  // int8 runs two waves per SIMD: each raises its priority over its matrix
-  // products, so the SIMD issues one wave's products while the other wave's
-  // vector work fills the gaps (measured +5 %; bf16, one wave per SIMD, loses
-  // a little with it).
+  // One-byte caches: each of the two waves on a SIMD raises its priority
+  // over its matrix products, so the SIMD issues one wave's products while
+  // the other wave's widening and weighing fill the gaps (measured +5 %);
+  // the bf16 kernel, with less vector work per chunk, loses 5 % with it.
   constexpr bool PRIO = I8;
 
   const int lane = threadIdx.x & 63;
@@ -132,14 +138,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
   const int32_t *trow = P.tables + (size_t)b * P.max_blocks;
   const int H = P.H;
 
-  // The query slices stay in registers for the whole walk.
-  bf16x8_t qb[CT][NKK];
+  // The query slices stay in LDS for the whole walk, each lane's own 16
+  // bytes per (tile, score step), and are read again at each use (a volatile
+  // LDS read, so the compiler does not hoist them into registers: the
+  // registers go to the K/V ring and the accumulators).
+  __shared__ uint4 s_q[4][CT][NKK][64];
 #pragma unroll
   for (int s = 0; s < CT; ++s) {
     const uint4 *qr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.q) + qrow[s] * D);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qb[s][kk] = as_bf16x8<F8>(qr[kgroup(kk)]);
+    for (int kk = 0; kk < NKK; ++kk) s_q[w][s][kk][lane] = qr[kgroup(kk)];
   }
+  auto qslice = [&](int s, int kk) {
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    typedef const volatile __attribute__((address_space(3))) u32x4v lds_u32x4v;
+    const u32x4v v = *(lds_u32x4v *)(&s_q[w][s][kk][lane]);
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
 
   // Chunk y lives in ring slot y % NB of the K ring and of the V ring.  Its
   // K is requested NB steps before its scores are formed (one step before
@@ -206,10 +221,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
         kx = as_bf16x8<F8>(ax[I][kk]);
         ky = as_bf16x8<F8>(ay[I][kk]);
       }
+      bf16x8_t qv[CT];
+#pragma unroll
+      for (int s = 0; s < CT; ++s) qv[s] = qslice(s, kk);
 #pragma unroll
       for (int s = 0; s < CT; ++s) {
-        sx[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[s][kk], sx[s], 0, 0, 0);
-        sy[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[s][kk], sy[s], 0, 0, 0);
+        sx[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qv[s], sx[s], 0, 0, 0);
+        sy[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qv[s], sy[s], 0, 0, 0);
       }
     }
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
@@ -404,11 +422,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
 // Ring depth (chunks of K/V requested ahead) and column tiles per wave (16
 // query columns each: the K and V operands of a chunk serve all of them, so
 // each byte brought through the vector memory path feeds CT x the math).
-// bf16 takes a deeper ring and three tiles (one wave per SIMD); int8, whose
-// operands are half the bytes, two tiles and a single ring slot (two waves
-// per SIMD).
+// Three tiles and one ring slot fit two waves per SIMD in 256 registers
+// each, with the query slices in LDS (bf16 and one-byte caches alike; two
+// ring slots spill).  A wave's next chunk is then requested one step ahead,
+// and the other wave on the SIMD covers the wait.
 #ifndef PKV_PREFILL_NBUF
-#define PKV_PREFILL_NBUF 2
+#define PKV_PREFILL_NBUF 1
 #endif
 #ifndef PKV_PREFILL_CT
 #define PKV_PREFILL_CT 3
@@ -417,7 +436,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams P) {
 #define PKV_PREFILL_NBUF_I8 1
 #endif
 #ifndef PKV_PREFILL_CT_I8
-#define PKV_PREFILL_CT_I8 2
+#define PKV_PREFILL_CT_I8 3
 #endif
 
 // I8: one-byte codes (int8, or FP8 E4M3 when F8) with per-row scales.
