@@ -245,6 +245,9 @@ def pmc_summary(args):
                     lines.append(f"    {c + ' busy':28s} {100 * cs[c] * scale / (act * units):15.1f} %")
             frac("SQ_VALU_MFMA_BUSY_CYCLES", 1024)
             frac("SQ_ACTIVE_INST_VALU", 1024, 4.0)
+            for c in ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY"):  # shares of the waves' cycles
+                if c in cs and cs.get("SQ_WAVE_CYCLES"):
+                    lines.append(f"    {c + ' of wave cycles':28s} {100 * cs[c] / cs['SQ_WAVE_CYCLES']:15.1f} %")
             if "SQ_WAVE_CYCLES" in cs:  # waves resident per SIMD, on average
                 lines.append(f"    {'SQ_WAVE_CYCLES waves/SIMD':28s} {cs['SQ_WAVE_CYCLES'] * 4.0 / (act * 1024):15.2f}")
             frac("TA_TA_BUSY", 256)
