@@ -564,8 +564,8 @@ def launch_cost(reps: int = 30):
 
 def mfma_probe(iters: int = 20000):
     """Matrix-core issue probe (libpkvprobe.so): per iteration 24 independent
-    v_mfma_f32_16x16x32_bf16 and/or the vector work that weighs 24 scores,
-    with one and two waves per SIMD.  Returns us per launch and cycles per
+    v_mfma_f32_16x16x32_bf16 and/or the vector work that weighs 24 scores, or
+    12 v_mfma_f32_32x32x16_bf16, with one and two waves per SIMD.  Returns us per launch and cycles per
     iteration of one wave (at 2.4 GHz), and the products' TFLOP/s."""
     import torch
     from paged_kv_cache_381_amd import build as B
@@ -578,10 +578,11 @@ def mfma_probe(iters: int = 20000):
     stream = torch.cuda.current_stream().cuda_stream
     hip = HipEvents()
     ev = hip.create(2)
-    names = {0: "products", 1: "vector work", 2: "both, in program order", 3: "both, interleaved"}
+    names = {0: "products", 1: "vector work", 2: "both, in program order", 3: "both, interleaved",
+             4: "32x32x16 products"}
     res = {}
     for wps in (1, 2):
-        for mode in range(4):
+        for mode in range(5):
             assert plib.pkv_probe_mfma_issue(mode, wps, iters, d_in.data_ptr(), d_out.data_ptr(), stream) == 0
             hip.record(ev[0], stream)
             assert plib.pkv_probe_mfma_issue(mode, wps, iters, d_in.data_ptr(), d_out.data_ptr(), stream) == 0
@@ -589,7 +590,7 @@ def mfma_probe(iters: int = 20000):
             torch.cuda.synchronize()
             us = hip.elapsed_ms(ev[0], ev[1]) * 1e3
             r = {"us": round(us, 1), "cycles_per_iter_per_wave_at_2.4GHz": round(us * 2400 / iters / wps, 1)}
-            if mode == 0:
+            if mode in (0, 4):  # 24 x 16384 = 12 x 32768 flops per iteration
                 r["tflops"] = round(24 * 16384 * iters * 4 * cus * wps / (us * 1e-6) / 1e12, 1)
             res[f"{names[mode]}, {wps} wave(s)/SIMD"] = r
     hip.destroy(ev)

@@ -107,8 +107,9 @@ __global__ __launch_bounds__(64 * kWaves) void launch_cost_kernel(uint32_t *cloc
 // independent accumulators and/or the vector work that weighs 24 scores
 // (fma, base-2 exponential, bf16 pack), with one or two waves per SIMD.
 // MODE 0: products only; 1: vector work only; 2: both in program order; 3:
-// both, one product then two vector instructions (scheduling groups).  The
-// results are folded into one store per lane, so no work is dead.
+// both, one product then two vector instructions (scheduling groups); 4: 12
+// v_mfma_f32_32x32x16_bf16 (the same flops) on independent accumulators.
+// The results are folded into one store per lane, so no work is dead.
 typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
 typedef float f32x4_p __attribute__((ext_vector_type(4)));
 typedef float f32x2_p __attribute__((ext_vector_type(2)));
@@ -132,12 +133,19 @@ __global__ __launch_bounds__(64 * kWaves) void mfma_issue_kernel(const float *in
   }
   uint32_t pk = 0;
   const float m = in[0], mul = in[1];
+  typedef float f32x16_p __attribute__((ext_vector_type(16)));
+  f32x16_p acc32[MODE == 4 ? 12 : 1];
+#pragma unroll
+  for (int i = 0; i < (MODE == 4 ? 12 : 1); ++i) acc32[i] = f32x16_p{};
   for (int it = 0; it < iters; ++it) {
-    if constexpr (MODE != 1) {
+    if constexpr (MODE == 4) {
+#pragma unroll
+      for (int i = 0; i < 12; ++i) acc32[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc32[i], 0, 0, 0);
+    } else if constexpr (MODE != 1) {
 #pragma unroll
       for (int i = 0; i < 24; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
     }
-    if constexpr (MODE != 0) {
+    if constexpr (MODE >= 1 && MODE <= 3) {
 #pragma unroll
       for (int i = 0; i < 24; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], mul, -m));
 #pragma unroll
@@ -155,6 +163,10 @@ __global__ __launch_bounds__(64 * kWaves) void mfma_issue_kernel(const float *in
   float r = (float)pk;
 #pragma unroll
   for (int i = 0; i < 24; ++i) r += acc[i][0] + acc[i][3] + e[i];
+  if constexpr (MODE == 4) {
+#pragma unroll
+    for (int i = 0; i < 12; ++i) r += acc32[i][0] + acc32[i][15];
+  }
   out[blockIdx.x * (64 * kWaves) + threadIdx.x] = r;
 }
 
@@ -209,14 +221,14 @@ extern "C" int pkv_probe_launch_cost(uint32_t *d_clock, void *stream) {
   return (int)hipGetLastError();
 }
 
-// One launch of the matrix-core issue probe (mode 0..3, see above) for iters
+// One launch of the matrix-core issue probe (mode 0..4, see above) for iters
 // iterations on waves_per_simd (1 or 2) workgroups of four waves per compute
 // unit.  d_in: 96 floats of input (any finite values); d_out: one float per
 // thread (256 * waves_per_simd * compute units).  Returns a HIP error code
 // (0 = launched), or -1 for bad arguments.
 extern "C" int pkv_probe_mfma_issue(int32_t mode, int32_t waves_per_simd, int32_t iters, const float *d_in,
                                     float *d_out, void *stream) {
-  if (!d_in || !d_out || iters <= 0 || mode < 0 || mode > 3 || (waves_per_simd != 1 && waves_per_simd != 2))
+  if (!d_in || !d_out || iters <= 0 || mode < 0 || mode > 4 || (waves_per_simd != 1 && waves_per_simd != 2))
     return -1;
   int dev = 0, cus = 0;
   if (hipError_t e = hipGetDevice(&dev)) return (int)e;
@@ -227,7 +239,8 @@ extern "C" int pkv_probe_mfma_issue(int32_t mode, int32_t waves_per_simd, int32_
     case 0: hipLaunchKernelGGL(mfma_issue_kernel<0>, grid, block, 0, s, d_in, d_out, iters); break;
     case 1: hipLaunchKernelGGL(mfma_issue_kernel<1>, grid, block, 0, s, d_in, d_out, iters); break;
     case 2: hipLaunchKernelGGL(mfma_issue_kernel<2>, grid, block, 0, s, d_in, d_out, iters); break;
-    default: hipLaunchKernelGGL(mfma_issue_kernel<3>, grid, block, 0, s, d_in, d_out, iters); break;
+    case 3: hipLaunchKernelGGL(mfma_issue_kernel<3>, grid, block, 0, s, d_in, d_out, iters); break;
+    default: hipLaunchKernelGGL(mfma_issue_kernel<4>, grid, block, 0, s, d_in, d_out, iters); break;
   }
   return (int)hipGetLastError();
 }
