@@ -430,6 +430,16 @@ template <int D, bool I8, bool F8, bool NT>
 int launch(const pkv_decode_args &a, const SplitParams &p0) {
   auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8, F8, NT>;
   SplitParams p = p0;
+  // A one-byte (block, kv head) tile is 2112 bytes, so every other tile
+  // shares a 128-byte line with the next kv head's tile.  The waves reading
+  // kv heads g and g + 1 at the same list position are 1/8 of the grid
+  // apart: as dealt to the XCDs (round robin) they sit on one XCD and that
+  // line comes from HBM once; renumbered into contiguous eighths they sit on
+  // two XCDs and it is fetched twice (3 % of the bytes).  Batches of shared
+  // blocks (two waves per SIMD) and per-XCD weights keep the eighths.
+  bool weighted = false;
+  for (int i = 0; i < PKV_REGIONS; ++i) weighted |= a.xw[i] != 0;
+  p.wg_dealt = I8 && a.waves_per_simd == 1 && !weighted;
   const size_t split = pkv_split_lds_bytes(a.num_seqs, kWaves);
   // Result rings: what LDS is left of the workgroup's share of the CU, split
   // over its waves, in records of G rows of D floats, G (m, l) pairs and the

@@ -200,6 +200,7 @@ struct SplitParams {
   int32_t xw[PKV_REGIONS];  // per-XCD weights of the work (all 0: equal shares)
   int32_t *trace;         // nullable: per wave, its XCD group, chunks and start/end times
   float scale_log2;
+  int32_t wg_dealt;       // 1: shares follow the workgroups as dealt to the XCDs (round robin)
 };
 
 // Parameters of the paged prefill kernel (passed by value).
@@ -348,7 +349,9 @@ __device__ inline int region_bounds(int64_t c_tot, int nwe, int nwg_waves, int n
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
 // XCD holds one contiguous eighth of the shares (neighbouring shares often
-// read the same segment's query and table lines, which then stay in one L2).
+// read the same segment's query and table lines, which then stay in one L2,
+// and a kv head's blocks shared by many sequences are read by one XCD).
+// One-byte caches without sharing keep the dealt order (see the launcher).
 __device__ __forceinline__ int xcd_logical(int wg, int nwg) {
   return (nwg & 7) ? wg : (wg & 7) * (nwg >> 3) + (wg >> 3);
 }
@@ -391,6 +394,7 @@ inline SplitParams pkv_split_params(const pkv_decode_args &a) {
   for (int i = 0; i < PKV_REGIONS; ++i) p.xw[i] = a.xw[i];
   p.trace = a.trace;
   p.scale_log2 = a.scale_log2;
+  p.wg_dealt = 0;
   return p;
 }
 
@@ -533,7 +537,7 @@ __device__ bool split_begin(const SplitParams &P, int32_t *s_lds, Share &sh) {
   sh.rg.nr = nr;
   sh.rg.wpr = nwe / nr;
   sh.rg.bounds = s_bounds;
-  sh.wave = uniform(xcd_logical(blockIdx.x, nwg) * W + w);
+  sh.wave = uniform((P.wg_dealt ? (int)blockIdx.x : xcd_logical(blockIdx.x, nwg)) * W + w);
   if (sh.wave >= nwe || c_tot == 0) return false;
   sh.rg.share(sh.wave, sh.lo, sh.hi);
   return sh.lo < sh.hi;
