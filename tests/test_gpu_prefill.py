@@ -4,9 +4,11 @@ The prefill is a causal attention of each sequence's new tokens over its
 paged cache (a cached prefix, shared or private, then the new tokens).  The
 pools are built on both sides by the same build script; outputs are compared
 element by element: max abs error <= 2e-2 (bf16, int8 or FP8 cache, float32
-accumulation), on every output of small shapes and on sampled query rows of
-the full-size workloads (the oracle evaluates the last new tokens of chosen
-sequences, which see the most keys).
+accumulation), on every output of small shapes, on sampled query rows of the
+full-size workloads (the oracle evaluates the last new tokens of chosen
+sequences, which see the most keys), and on every new token of the
+full-size workloads (every output of the bf16 ones; the query heads of one
+kv head for the one-byte caches).
 """
 import math
 import sys
@@ -93,6 +95,42 @@ def test_prefill_shared_prefix_sampled():
 
 def test_prefill_8b_b4_sampled():
     _sampled("prefill_8b_b4", picks=[0, 3], last=32)
+
+
+def _one_head(pool, num_blocks, num_kv_heads, g):
+    """The pool of kv head g alone: tile (block, g) of every block, in block
+    order (a pool of the same layout with one kv head)."""
+    tiles = pool.reshape(num_blocks, num_kv_heads, -1)
+    return np.ascontiguousarray(tiles[:, g, :]).reshape(-1)
+
+
+FULL = [("prefill_8b_b4", tuple(range(8))), ("prefill_shared_prefix", tuple(range(8))),
+        ("prefill_shared_prefix_int8", (3,)), ("prefill_shared_prefix_fp8", (4,))]
+
+
+@pytest.mark.parametrize("case", range(len(FULL)))
+def test_prefill_full_workload_every_token(case):
+    """Every new token of every sequence of a full-size workload, for the
+    query heads of the listed kv heads: the oracle in float64 over one kv
+    head's group at a time (the same definition with that head's pool and
+    query heads), every output of those heads compared."""
+    name, heads = FULL[case]
+    inst = PW.get(name)
+    wl = inst.wl
+    gp = GpuPrefill(inst)
+    out = gp.run().cpu().numpy()
+    assert np.isfinite(out).all()
+    built = orc.build_prefill(inst)
+    assert np.array_equal(built["tables"], gp.tables_host)
+    H, G = wl.num_kv_heads, wl.num_q_heads // wl.num_kv_heads
+    q = inst.q()
+    for g in heads:
+        kp = _one_head(built["kpool"], inst.num_blocks, H, g)
+        vp = _one_head(built["vpool"], inst.num_blocks, H, g)
+        say(f"[prefill] {name}: kv head {g}, {q.shape[0]} new tokens x {G} query heads")
+        ref = orc.paged_prefill(wl.cache_dtype, q[:, g * G:(g + 1) * G], kp, vp, built["tables"], built["ctx"],
+                                inst.qstart, 1, 1 / math.sqrt(wl.head_dim))
+        check_close(out[:, g * G:(g + 1) * G], ref, TOL, f"{name} kv head {g}, every new token")
 
 
 def test_prefill_of_one_token_is_decode():
