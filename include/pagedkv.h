@@ -30,7 +30,10 @@
  *   - The library owns host bookkeeping objects only (pkv_pool and the
  *     sequences inside it, addressed by int64 id).  Every device buffer is
  *     owned by the caller and only borrowed for the duration of the call; the
- *     library allocates no device memory.
+ *     library allocates no device memory at run time (its static device
+ *     memory: 8 KiB of idle tiles that the decode kernels read past the end
+ *     of a wave's work, and the scratch array of
+ *     paged_attention_decode_noalloc).
  *   - Device calls are asynchronous on the given stream (a hipStream_t passed
  *     as void*; NULL = the legacy default stream) and never synchronize.
  *   - Host-visible arguments are validated; device-resident tables and
