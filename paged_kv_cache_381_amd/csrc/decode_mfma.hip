@@ -81,11 +81,13 @@ constexpr float kSlack = 8.0f;
 #ifndef PKV_MFMA_NBUF
 #define PKV_MFMA_NBUF 2
 #endif
-// An int8 chunk is half the bytes in half the registers: more of them stay in
-// flight to keep as many bytes on the way from memory (three measured best:
-// two starve the 70B-shaped batch, four and six slow the 8B-shaped one).
+// One-byte caches keep two chunks as well.  Their chunk is half the bytes,
+// and three chunks used to serve the 70B-shaped batch better; since the past-
+// the-end loads read the idle tiles and the shares follow the dealt
+// workgroup order, two are 1-2 % faster on the 8B-shaped int8 and FP8 batches
+// and level on the 70B-shaped one (four and six were slower still).
 #ifndef PKV_MFMA_NBUF_I8
-#define PKV_MFMA_NBUF_I8 3
+#define PKV_MFMA_NBUF_I8 2
 #endif
 
 // Loads of a buffer past the share's end read these bytes instead of K/V:
