@@ -177,6 +177,23 @@ def test_full_workload_every_output(name):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,hq", [("llama3_8b_b64", 4), ("llama3_8b_b64_int8", 4), ("llama3_8b_b64", 1)])
+def test_maximum_context_every_output(name, hq):
+    """A context of the largest length the calls accept, 2^22 tokens (262144
+    blocks in one table row), beside a short one; one kv head of four query
+    heads (the matrix-core kernel) or of one (the wavefront kernel) at d 64
+    keeps the pool near 1.3 GiB.  The long context is cut into a piece for
+    nearly every wave of the grid and the merge folds them all; every output
+    against the oracle."""
+    kw = dict(batch=2, num_q_heads=hq, num_kv_heads=1, head_dim=64, ctx_fixed=(1 << 22, 100))
+    inst, gw = built(name, **kw)
+    say(f"[oracle] {name} contexts {inst.ctx.tolist()}")
+    ref = orc.run_workload(inst)["out"]
+    check_close(gw.decode().cpu().numpy(), ref, TOL["bf16"], f"{name} context 2^22")
+    _built.pop((name, tuple(sorted(kw.items()))), None)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_b64", "llama3_8b_b64_int8"])
 def test_many_short_segments_every_output(name):
     """2600 sequences of 1-16 tokens: one chunk per segment, about 20
