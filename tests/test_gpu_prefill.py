@@ -133,6 +133,25 @@ def test_prefill_full_workload_every_token(case):
         check_close(out[:, g * G:(g + 1) * G], ref, TOL, f"{name} kv head {g}, every new token")
 
 
+@pytest.mark.parametrize("cache", ["bf16", "int8"])
+def test_prefill_maximum_context_every_output(cache):
+    """16 new tokens after a cached prefix that brings the context to the
+    largest length the call accepts, 2^22 tokens (262144 blocks in one table
+    row); one kv head of four query heads at d 64.  Every wave walks all
+    131072 chunks; every output against the oracle."""
+    n = 1 << 22
+    inst = PW.scaled("prefill_8b_b4", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                     own_prefix=(n - 16, n - 16), new_tokens=(16, 16), cache=cache).instantiate()
+    say(f"[prefill] context {inst.ctx.tolist()}, {inst.nq.tolist()} new, {cache}")
+    gp = GpuPrefill(inst)
+    out = gp.run().cpu().numpy()
+    ref = orc.run_prefill(inst)
+    assert np.array_equal(gp.tables_host, ref["tables"])
+    check_close(out, ref["out"], TOL, f"context 2^22, {cache}")
+    del gp
+    torch.cuda.empty_cache()
+
+
 def test_prefill_of_one_token_is_decode():
     """A prefill whose every sequence has one new token is a decode step."""
     import workloads
