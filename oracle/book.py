@@ -63,7 +63,6 @@ invariant and worked-number tests in ``tests/test_oracle_book.py`` and
 """
 from __future__ import annotations
 
-import copy
 
 BLOCK_SIZE = 16
 
@@ -209,14 +208,19 @@ class Book:
         for sid in sids:
             if not self.resident(sid):
                 raise BookError("INVALID", f"sequence {sid} has blocks swapped out")
-        saved = copy.deepcopy((self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst,
-                               self.refbit))
+        # Appending changes the appended sequences' own entries and the block
+        # containers below, nothing else: the snapshot for the undo is exactly
+        # that (keys and counters are immutable values, so shallow copies do).
+        saved = (list(self.free), list(self.ref), dict(self.pc), dict(self.key_of), list(self.lru),
+                 dict(self.pst), list(self.refbit),
+                 {sid: {"table": list(self.seqs[sid]["table"]), "len": self.seqs[sid]["len"]} for sid in sids})
         slots, cow = [], []
         try:
             for sid in sids:
                 self._append_one_seq(sid, n, slots, cow)
         except BookError:
-            self.free, self.ref, self.seqs, self.pc, self.key_of, self.lru, self.pst, self.refbit = saved
+            self.free, self.ref, self.pc, self.key_of, self.lru, self.pst, self.refbit, seqs = saved
+            self.seqs.update(seqs)
             raise
         return slots, cow
 

@@ -113,6 +113,7 @@ def test_exhaustion_is_all_or_nothing():
     with pytest.raises(BookError):
         book.batch_append_slots([a, b], 9)  # a needs 1 (pos 40..48 crosses 48), b needs 1: 2 > 1
     assert (list(book.free), list(book.ref), book.block_table(a), book.seq_len(a)) == before
+    assert (book.block_table(b), book.seq_len(b)) == ([], 0)
     book.batch_append_slots([a, b], 8)  # a stays in its block, b takes the last one
     assert book.num_free() == 0
 
