@@ -194,6 +194,21 @@ def test_maximum_context_every_output(name, hq):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,hq", [("llama3_8b_b64", 8), ("llama3_8b_b64_int8", 8), ("llama3_8b_b64", 2)])
+def test_maximum_batch_every_output(name, hq):
+    """The largest batch one call takes, 8192 sequences of 1-40 tokens: the
+    chunk scan of the whole batch fills most of the workgroup's LDS and
+    leaves the result ring a few records; every output against the oracle,
+    on the matrix-core kernel (G = 4, bf16 and int8) and the wavefront
+    kernel (G = 1)."""
+    kw = dict(batch=8192, num_q_heads=hq, num_kv_heads=2, head_dim=64, ctx_range=(1, 40))
+    inst, gw = built(name, **kw)
+    say(f"[oracle] {name} 8192 sequences, {hq} query heads")
+    ref = orc.run_workload(inst)["out"]
+    check_close(gw.decode().cpu().numpy(), ref, TOL["bf16"], f"{name} 8192 sequences")
+    _built.pop((name, tuple(sorted(kw.items()))), None)
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_b64", "llama3_8b_b64_int8"])
 def test_many_short_segments_every_output(name):
     """2600 sequences of 1-16 tokens: one chunk per segment, about 20
