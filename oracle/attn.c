@@ -39,7 +39,9 @@
  * int8 pools (a choice of this build): a (block, kv head) tile is
  * 16 * D int8 codes followed by 16 float32 scales (one per token slot),
  * 16 * D + 64 bytes:
- *    K code (blk, g, t, d) at byte ((blk*Hkv + g)*TB + ((d/16)*16 + t)*16 + d%16)
+ *    K code (blk, g, t, d) at byte ((blk*Hkv + g)*TB + ((d/16)*16 + p(t))*16 + d%16)
+ *    where p(t) exchanges bits 2 and 3 of t (slots 0-3, 8-11, 4-7, 12-15 in
+ *    that order along each 256-byte row of 16-byte units)
  *    V code (blk, g, t, d) at byte ((blk*Hkv + g)*TB + d*16 + t)
  *    scale of slot t at byte ((blk*Hkv + g)*TB + 16*D + 4*t), in each pool
  * Queries and the rows handed to append are bfloat16.  Quantisation of a
@@ -105,6 +107,10 @@ static unsigned char e4m3_code(float y) {
 /* Bytes of one (block, kv head) tile of an int8 pool. */
 static size_t tile_bytes_i8(int D) { return (size_t)16 * D + 64; }
 
+/* Place of token slot t among the 16-byte units of a row of a one-byte K
+ * tile: t with its bits 2 and 3 exchanged. */
+static size_t k8_pos(int t) { return (size_t)((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1)); }
+
 static size_t k_at(int64_t blk, int g, int t, int d, int Hkv, int D, int dtype) {
   int X = (int)(16 / esize(dtype));
   return ((((size_t)blk * Hkv + g) * (size_t)(D / X) + (size_t)(d / X)) * BLOCK + (size_t)t) * X + (size_t)(d % X);
@@ -118,7 +124,7 @@ static size_t v_at(int64_t blk, int g, int t, int d, int Hkv, int D) {
  * scale of slot t. */
 static double i8_value(const void *pool, int64_t blk, int g, int t, int d, int Hkv, int D, int is_v, int dtype) {
   const unsigned char *tile = (const unsigned char *)pool + ((size_t)blk * Hkv + g) * tile_bytes_i8(D);
-  size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + t) * 16 + d % 16;
+  size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + k8_pos(t)) * 16 + d % 16;
   float sc;
   memcpy(&sc, tile + (size_t)16 * D + 4 * (size_t)t, sizeof sc);
   double v = dtype == 3 ? e4m3_value(tile[at]) : (double)(signed char)tile[at];
@@ -155,7 +161,7 @@ static void quantise_row(const uint16_t *x, int D, unsigned char *tile, int t, i
       int q = r > 127.0f ? 127 : r < -127.0f ? -127 : (int)r;
       code = (unsigned char)(signed char)q;
     }
-    size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + t) * 16 + d % 16;
+    size_t at = is_v ? (size_t)d * BLOCK + t : ((size_t)(d / 16) * BLOCK + k8_pos(t)) * 16 + d % 16;
     tile[at] = code;
   }
   memcpy(tile + (size_t)16 * D + 4 * (size_t)t, &scale, sizeof scale);

@@ -76,13 +76,20 @@ def int8_tile_bytes(D):
     return 16 * D + 64
 
 
+def int8_k_pos(t):
+    """Unit of token slot t along a K row of a one-byte tile: slots 0-3,
+    8-11, 4-7, 12-15 in that order (tests/golden/pool_layout_int8.txt)."""
+    order = [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+    return order.index(t)
+
+
 def int8_read(pool, H, D, blk, g, t, is_v):
     """(codes[D], scale) of slot t of tile (blk, g) of an int8 pool, read with
     the byte layout of tests/golden/pool_layout_int8.txt."""
     tb = int8_tile_bytes(D)
     tile = pool[(blk * H + g) * tb:(blk * H + g + 1) * tb]
     d = np.arange(D)
-    at = d * 16 + t if is_v else ((d // 16) * 16 + t) * 16 + d % 16
+    at = d * 16 + t if is_v else ((d // 16) * 16 + int8_k_pos(t)) * 16 + d % 16
     codes = tile[at].view(np.int8).astype(np.int64)
     scale = tile[16 * D + 4 * t:16 * D + 4 * t + 4].view(np.float32)[0]
     return codes, scale
@@ -95,7 +102,7 @@ def fp8_read(pool, H, D, blk, g, t, is_v):
     tb = int8_tile_bytes(D)
     tile = pool[(blk * H + g) * tb:(blk * H + g + 1) * tb]
     d = np.arange(D)
-    at = d * 16 + t if is_v else ((d // 16) * 16 + t) * 16 + d % 16
+    at = d * 16 + t if is_v else ((d // 16) * 16 + int8_k_pos(t)) * 16 + d % 16
     codes = np.ascontiguousarray(tile[at])
     values = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
     scale = tile[16 * D + 4 * t:16 * D + 4 * t + 4].view(np.float32)[0]
@@ -442,7 +449,7 @@ def _fp8_pool_with_codes(codes, D):
     kpool, vpool = orc.new_pool(1, 1, D, "fp8")
     for t in range(16):
         d = np.arange(D)
-        kpool[((d // 16) * 16 + t) * 16 + d % 16] = codes[t]
+        kpool[((d // 16) * 16 + int8_k_pos(t)) * 16 + d % 16] = codes[t]
         vpool[d * 16 + t] = codes[t]
         one = np.array([1.0], np.float32).view(np.uint8)
         kpool[16 * D + 4 * t:16 * D + 4 * t + 4] = one

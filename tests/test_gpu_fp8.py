@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import pins
 import workloads
 from oracle import attn as orc
 from paged_kv_cache_381_amd import _lib as L
@@ -151,7 +152,7 @@ def test_fp8_every_code_decodes_exactly():
         blk, t = int(slots[b]) // 16, int(slots[b]) % 16
         tile = blk * H * tb
         d = np.arange(D)
-        k[tile + ((d // 16) * 16 + t) * 16 + d % 16] = 0
+        k[tile + ((d // 16) * 16 + pins.int8_k_pos(t)) * 16 + d % 16] = 0
         v[tile + d * 16 + t] = codes[b]
         k[tile + 16 * D + 4 * t:tile + 16 * D + 4 * t + 4] = one
         v[tile + 16 * D + 4 * t:tile + 16 * D + 4 * t + 4] = one

@@ -60,6 +60,7 @@ MUTANTS = {
     "prefill_whole_context": ("int n = ctx[b] - nq + t + 1;", "int n = ctx[b];"),
     "prefill_query_of_first_token": ("elem(q, (size_t)rh * D + d, qt)", "elem(q, ((size_t)qstart[b] * Hq + h) * D + d, qt)"),
     "int8_copy_k_only": ("memcpy((char *)vpool + dst * tb", "if (0) memcpy((char *)vpool + dst * tb"),
+    "int8_k_slots_in_plain_order": ("return (size_t)((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1));", "return (size_t)t;"),
 }
 
 
