@@ -99,11 +99,14 @@ enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2, PKV_FP8 = 3 };
 /* Pool layout.  A pool is num_blocks * num_kv_heads tiles, tile (blk, g) at
  * index blk * H + g; a tile holds the 16 token slots of one block for one kv
  * head.  With X = 16 / element size (X = 16 for one-byte codes):
- *   K element (blk, g, t, d) at tile offset ((d / X) * 16 + t) * X + d % X
+ *   K element (blk, g, t, d) at tile offset ((d / X) * 16 + p(t)) * X + d % X
  *   V element (blk, g, t, d) at tile offset d * 16 + t
- * (in elements; for PKV_INT8 and PKV_FP8 in bytes).  An f32/bf16 tile is
- * 16 * D elements.  A PKV_INT8 or PKV_FP8 tile is 16 * D + 64 bytes: the
- * codes, then the 16 float32 scales of slots 0..15 at byte 16 * D + 4 * t. */
+ * (in elements; for PKV_INT8 and PKV_FP8 in bytes), where p(t) = t for f32
+ * and bf16 and, for one-byte codes, t with its bits 2 and 3 exchanged (a row
+ * of 16-byte K units holds slots 0-3, 8-11, 4-7, 12-15 in that order).  An
+ * f32/bf16 tile is 16 * D elements.  A PKV_INT8 or PKV_FP8 tile is
+ * 16 * D + 64 bytes: the codes, then the 16 float32 scales of slots 0..15 at
+ * byte 16 * D + 4 * t. */
 typedef struct {
   int32_t num_blocks;   /* physical blocks in the pool (> 0) */
   int32_t block_size;   /* tokens per block; must be 16 */

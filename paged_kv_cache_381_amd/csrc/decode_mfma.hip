@@ -33,12 +33,16 @@
 // the PV MFMA, whose V^T operand for lane (d, j) is then 16 contiguous bytes
 // of the [D][16] V tile (tokens 8(j%2)..+7 of block j/2).  No cross-lane
 // shuffle sits between the two contractions; the softmax needs only two
-// xor-shuffles per chunk (max over the four lane groups).  Each lane holds the
-// 8-element slices of the group's query rows that its B operand needs, loaded
-// with every chunk's K (from L2 after the first: D/32 16-byte loads per lane
-// beside the chunk's D/16 of K and D/16 of V), so one set of registers serves
-// both buffers of the pipeline; the whole group shares them through the MFMA, and
-// nothing else in the wave would reuse an LDS copy.
+// xor-shuffles per chunk (max over the four lane groups).  The first MFMA's
+// K rows are thus slots {0-3, 8-11} of each block and the second's {4-7,
+// 12-15}: a bf16 K load reads half of each 128-byte line it touches, while
+// one-byte K tiles store the slots in that order (k8_unit), so each of their
+// K loads reads whole lines, which matters once the loads stream.  Each lane holds the
+// 8-element slices of the group's query rows that its B operand needs (D/32
+// 16-byte loads per lane), loaded with the K of the first chunk of each
+// segment and kept while the segment lasts, so one set of registers serves
+// both buffers of the pipeline; the whole group shares them through the MFMA,
+// and nothing else in the wave would reuse an LDS copy.
 //
 // int8 cache [KV Cache 工程学 §15.7 (3)].  Codes are loaded 8 bytes per lane
 // where bf16 takes 16 and widened to bf16 exactly (|code| <= 127 needs 7
@@ -144,8 +148,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   Cursor cq[NB];
   int pa[NB], pb[NB];
   // With two buffers the next chunk's query slices load after the current
-  // chunk's scores, so one set of registers serves; deeper pipelines keep one
-  // set per buffer.
+  // chunk's scores, so one set of registers serves, reloaded where a segment
+  // starts; deeper pipelines keep one set per buffer, loaded with every chunk.
   constexpr int NQ = NB == 2 ? 1 : NB;
   bf16x8_t qb[NQ][NKK];
   uint4 ax[NB][NKU], ay[NB][NKU];
@@ -158,15 +162,20 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     if (pa[i] < 0) return g_idle_tiles + (sel ? TB : 0);
     return pool + ((size_t)(sel ? pb[i] : pa[i]) * H + g) * TB;
   };
-  auto issue = [&](auto bi) {  // loads of the chunk held in buffer bi
+  // Loads of the chunk held in buffer bi; its query slices only if load_q
+  // (a uniform flag: the chunk opens another segment than the registers
+  // hold).  They come first, so the wait for the chunk's K covers them.
+  auto issue = [&](auto bi, bool load_q) {
     constexpr int I = decltype(bi)::value;
     constexpr int QI = NQ == 1 ? 0 : I;
     const Cursor &c = cq[I];
-    const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + qh) * D);
+    if (load_q) {
+      const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + qh) * D);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 u = qr[kgroup(kk)];
-      qb[QI][kk] = as_bf16x8<F8>(u);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const uint4 u = qr[kgroup(kk)];
+        qb[QI][kk] = as_bf16x8<F8>(u);
+      }
     }
     const uint4 *kt = reinterpret_cast<const uint4 *>(tile(kpool, I, ksel, c.g));
 #pragma unroll
@@ -174,8 +183,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       // 16-byte unit of the lane's token row: int8 unit 4ku+grp holds the
       // element groups 2(4ku+grp) and +1 of score MFMAs 2ku and 2ku+1.
       const int cu = 4 * ku + grp;
-      ax[I][ku] = load_u4<NT>(kt + cu * 16 + ktx);
-      ay[I][ku] = load_u4<NT>(kt + cu * 16 + ktx + 4);
+      ax[I][ku] = load_u4<NT>(kt + cu * 16 + (I8 ? k8_unit(ktx) : ktx));
+      ay[I][ku] = load_u4<NT>(kt + cu * 16 + (I8 ? k8_unit(ktx + 4) : ktx + 4));
     }
     if constexpr (I8) {
       const float4 *sc = reinterpret_cast<const float4 *>(tile(kpool, I, vsel, c.g) + 16 * D + 32 * vhalf);
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   // prologue that sent a chunk's K last would make the first of them wait
   // for everything.
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
-    ((Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0),
+    ((Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}, true), __builtin_amdgcn_sched_barrier(0),
                      issue_v(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0))
                   : (void)0),
      ...);
@@ -256,7 +265,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[QI][kk], sy, 0, 0, 0);
     }
     if (x + NB - 1 >= hi) idle_after(J, I);  // no chunk x + NB - 1 in the share
-    issue(std::integral_constant<int, J>{});
+    // One set of query registers serves both buffers: chunk x's scores are
+    // done, and chunk x+1 needs other rows only where a segment starts.
+    issue(std::integral_constant<int, J>{}, NQ > 1 || cq[J].seg0 != cq[I].seg0);
 
     const Cursor &cur = cq[I];
     // Past the share's end the loop runs on to the end of its group of NB

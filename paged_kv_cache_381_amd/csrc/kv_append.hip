@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void append_q8_kernel(uint8_t *__restrict__ kp
   const int d0 = 8 * part;
   uint8_t *kt = kpool + ((size_t)blk * H + g) * TB;
   uint8_t *vt = vpool + ((size_t)blk * H + g) * TB;
-  *reinterpret_cast<uint2 *>(kt + ((d0 >> 4) * 16 + off) * 16 + (d0 & 15)) = make_uint2(kc[0], kc[1]);
+  *reinterpret_cast<uint2 *>(kt + ((d0 >> 4) * 16 + k8_unit(off)) * 16 + (d0 & 15)) = make_uint2(kc[0], kc[1]);
 #pragma unroll
   for (int e = 0; e < 8; ++e) vt[(d0 + e) * 16 + off] = vc[e];
   if (part == 0) {

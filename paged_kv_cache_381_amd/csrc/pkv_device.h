@@ -10,6 +10,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Unit of token slot t along a row of a one-byte K tile: t with bits 2 and 3
+// exchanged.  The score products take a block's slots {0-3, 8-11} into one
+// MFMA and {4-7, 12-15} into the other; stored in this order, each of their
+// K loads covers whole 128-byte lines instead of halves of twice as many.
+__device__ __forceinline__ int k8_unit(int t) { return (t & 3) | ((t & 4) << 1) | ((t & 8) >> 1); }
+
 // Eight bf16 elements of an MFMA operand: a 16-byte unit of a bf16 cache or
 // query, or eight one-byte codes (bytes 0..3 of u.x, then of u.y) widened
 // exactly to bf16.  An int8 code needs 7 significant bits.  Every FP8 E4M3

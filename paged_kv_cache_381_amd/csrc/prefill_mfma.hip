@@ -180,8 +180,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int ku = 0; ku < NKU; ++ku) {
       const int cu = 4 * ku + grp;
-      ax[I][ku] = kt[cu * 16 + ktx];
-      ay[I][ku] = kt[cu * 16 + ktx + 4];
+      ax[I][ku] = kt[cu * 16 + (I8 ? k8_unit(ktx) : ktx)];
+      ay[I][ku] = kt[cu * 16 + (I8 ? k8_unit(ktx + 4) : ktx + 4)];
     }
   };
   auto issue_v = [&](auto bi, int y) {
