@@ -7,7 +7,10 @@
 // exact algebra (log-sum-exp), so the result equals a single softmax over all
 // tokens.
 //
-// One wave per (sequence, kv head) segment.  The schedule header written by
+// One workgroup per (sequence, kv head) segment, a thread per 4 output
+// columns of a query row (G * D / 4 of them, up to 256 at once: every partial
+// of a segment is requested in one round trip after the header's, G <= 8 at
+// D = 128).  The schedule header written by
 // the decode kernel gives the chunk scan, the number of waves used and the
 // region bounds, from which the segment's first and last wave w0 .. w1
 // follow exactly as in the decode kernel; a segment held by one wave (or an
@@ -25,8 +28,10 @@ namespace {
 // running (M, L, out).
 constexpr int kBatch = 8;
 
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(SplitParams P) {
   const int seg = blockIdx.x;
   const int b = seg / P.H, g = seg - b * P.H;
   const int32_t *hdr = P.ws_hdr;
@@ -60,9 +65,9 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitParams P) {
   const int np = w1 - w0 + 1;
   if (np <= 1) return;
 
-  const int lane = threadIdx.x, G = P.G;
+  const int tid = threadIdx.x, G = P.G;
   const size_t row0 = (size_t)b * P.Hq + (size_t)g * G;
-  for (int u = lane; u < G * (D / 4); u += 64) {
+  for (int u = tid; u < G * (D / 4); u += kMergeThreads) {
     const int h = u / (D / 4), d = 4 * (u % (D / 4));
     float M = -INFINITY, L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -109,8 +114,8 @@ int pkv_launch_merge(const pkv_decode_args &a) {
   const SplitParams p = pkv_split_params(a);
   dim3 grid(a.num_seqs * a.L->num_kv_heads);
   if (a.L->head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(a.stream), p);
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, reinterpret_cast<hipStream_t>(a.stream), p);
   return (int)hipGetLastError();
 }
