@@ -562,6 +562,52 @@ def launch_cost(reps: int = 30):
     return {"event_us": round(t, 2), "wave_span_us": round(sp, 2), "outside_waves_us": round(t - sp, 2)}
 
 
+def pattern_probe(reps: int = 5):
+    """Load-pattern probe (libpkvprobe.so): the decode kernels' per-lane loads
+    of a chunk with no arithmetic, over random (block, kv head) tiles of about
+    0.5 GiB per pool, bf16 (4 KiB tiles) and one-byte (2112-byte tiles), each
+    variant (K loads on half or whole 128-byte lines, query slices reloaded
+    with every chunk or not) with cached and streaming loads.  Returns GB/s
+    of tile bytes per variant (HIP events, mean of reps after a warm-up)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_381_amd import build as B
+    plib = ctypes.CDLL(B.PROBE_LIB)
+    plib.pkv_probe_load_pattern.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.empty(4 * plib.pkv_probe_compute_units(), dtype=torch.int32, device="cuda")
+    q = torch.full((256 * 1024,), 3, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+    ev = hip.create(2)
+    names = {0: "half-line K, query every chunk", 1: "whole-line K, query every chunk",
+             2: "half-line K, no query loads", 3: "whole-line K, no query loads"}
+    res = {}
+    for one_byte, tb, n_chunks in ((0, 4096, 64 * 1024), (1, 2112, 128 * 1024)):
+        n_tiles = 2 * n_chunks
+        k = torch.full((n_tiles * tb,), 1, dtype=torch.uint8, device="cuda")
+        v = torch.full((n_tiles * tb,), 2, dtype=torch.uint8, device="cuda")
+        order = torch.from_numpy(np.random.default_rng(4096).permutation(n_tiles).astype(np.int32)).cuda()
+        for variant in range(4):
+            for loads, nt in (("cached", 0), ("streaming", 1)):
+                ms = 0.0
+                for r in range(reps + 1):
+                    hip.record(ev[0], stream)
+                    rc = plib.pkv_probe_load_pattern(one_byte, variant, nt, k.data_ptr(), v.data_ptr(), q.data_ptr(),
+                                                     n_chunks, order.data_ptr(), sink.data_ptr(), stream)
+                    assert rc == 0, f"probe launch failed ({rc})"
+                    hip.record(ev[1], stream)
+                    torch.cuda.synchronize()
+                    if r:
+                        ms += hip.elapsed_ms(ev[0], ev[1])
+                res[f"{'one-byte' if one_byte else 'bf16'}, {names[variant]}, {loads}"] = \
+                    round(n_tiles * 2 * tb / (ms / reps * 1e-3) / 1e9, 1)
+        del k, v
+    hip.destroy(ev)
+    return res
+
+
 def mfma_probe(iters: int = 20000):
     """Matrix-core issue probe (libpkvprobe.so): per iteration 24 independent
     v_mfma_f32_16x16x32_bf16 and/or the vector work that weighs 24 scores, or
@@ -618,6 +664,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run only plain 1 GiB copies (PMC calibration)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="run only the matrix-core issue probe (products and vector work, one and two waves per SIMD)")
+    ap.add_argument("--pattern-probe", action="store_true",
+                    help="run only the load-pattern probe (the decode kernels' loads of bf16 and one-byte tiles)")
     ap.add_argument("--stream-probe", action="store_true",
                     help="run only the streaming-read probe (1 GiB of 4 KiB tiles, random and address order)")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the probe in a decode run")
@@ -663,6 +711,9 @@ def main():
         return
     if args.mfma_probe:
         print(json.dumps({"mfma_issue_probe": mfma_probe()}), flush=True)
+        return
+    if args.pattern_probe:
+        print(json.dumps({"load_pattern_probe_gbps": pattern_probe()}), flush=True)
         return
     if args.stream_probe:
         r = stream_probe(10)

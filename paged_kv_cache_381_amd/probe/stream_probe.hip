@@ -170,6 +170,145 @@ __global__ __launch_bounds__(64 * kWaves) void mfma_issue_kernel(const float *in
   out[blockIdx.x * (64 * kWaves) + threadIdx.x] = r;
 }
 
+// Load-pattern probe: the decode kernels' per-lane loads of one 32-token
+// chunk (two (block, kv head) tiles of K and of V, named by a random order),
+// with no arithmetic, so that a layout or load choice is measured apart from
+// the kernel's work.  B1 = false: bf16 tiles (4 KiB), 8 x 16 B of K and 8 x 16
+// B of V per lane; B1 = true: one-byte tiles (2112 B: codes, then scales), 4
+// x 16 B of K, 2 x 16 B of K scales, 8 x 8 B of V, 2 x 16 B of V scales.
+// VARIANT bit 0: K loads on whole 128-byte lines (the two loads of a 16-byte
+// unit row take slots 0-7 and 8-15) instead of the score products' halves
+// ({0-3, 8-11} and {4-7, 12-15}); bit 1: no query slices (otherwise 4 x 16 B
+// per lane from a 256 KiB buffer that stays in L2, as a kernel reloading them
+// with every chunk).  Two chunks of loads in registers, as the kernels keep.
+template <bool NT> __device__ __forceinline__ uint4 pload16(const uint8_t *p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4 *>(p);
+  }
+}
+template <bool NT> __device__ __forceinline__ uint2 pload8(const uint8_t *p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (NT) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return *reinterpret_cast<const uint2 *>(p);
+  }
+}
+
+constexpr int kPatQBytes = 256 * 1024;
+
+template <bool NT, bool B1, int VARIANT>
+__global__ __launch_bounds__(64 * kWaves) void load_pattern_kernel(const uint8_t *kp, const uint8_t *vp,
+                                                                   const uint8_t *qb, int64_t n_chunks,
+                                                                   const int32_t *order, uint32_t *sink) {
+  constexpr int TB = B1 ? 2112 : 4096;
+  constexpr int NKU = B1 ? 2 : 4;
+  constexpr bool WHOLE = VARIANT & 1, NOQ = VARIANT & 2;
+  extern __shared__ int32_t s_unused[];
+  const int64_t n_tiles = 2 * n_chunks;
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
+  const int64_t w = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
+  const int64_t lo = w * n_chunks / nw, hi = (w + 1) * n_chunks / nw;
+  if (lo >= hi) return;
+  const int r16 = lane & 15, grp = lane >> 4, ksel = r16 >> 3, vsel = grp >> 1, vhalf = grp & 1;
+  const int ktx = ((r16 >> 2) & 1) * 8 + (r16 & 3);
+  const int ka = WHOLE ? (r16 & 7) : ktx, kb = WHOLE ? 8 + (r16 & 7) : ktx + 4;
+  uint4 q[NB][4], ax[NB][NKU], ay[NB][NKU], sc[NB][4], vw[NB][8];
+  uint2 vn[NB][8];
+  auto issue = [&](auto bi, int64_t x) {
+    constexpr int I = decltype(bi)::value;
+    const int64_t s = x < hi ? x : hi - 1;
+    int64_t t0 = *(const_i32)(order + 2 * s), t1 = *(const_i32)(order + 2 * s + 1);
+    t0 = t0 < 0 ? 0 : t0 >= n_tiles ? n_tiles - 1 : t0;  // a bad order cannot leave the pools
+    t1 = t1 < 0 ? 0 : t1 >= n_tiles ? n_tiles - 1 : t1;
+    if constexpr (!NOQ) {
+      const uint8_t *qr = qb + ((w & 255) * 4 + (r16 < 3 ? r16 : 3)) * 256;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        q[I][kk] = pload16<false>(qr + 16 * (B1 ? 8 * (kk >> 1) + 2 * grp + (kk & 1) : 4 * kk + grp));
+    }
+    const uint8_t *kt = kp + (size_t)(ksel ? t1 : t0) * TB;
+#pragma unroll
+    for (int ku = 0; ku < NKU; ++ku) {
+      const int cu = 4 * ku + grp;
+      ax[I][ku] = pload16<NT>(kt + 16 * (cu * 16 + ka));
+      ay[I][ku] = pload16<NT>(kt + 16 * (cu * 16 + kb));
+    }
+    const uint8_t *kst = kp + (size_t)(vsel ? t1 : t0) * TB;
+    const uint8_t *vt = vp + (size_t)(vsel ? t1 : t0) * TB;
+    if constexpr (B1) {
+      sc[I][0] = pload16<NT>(kst + 2048 + 32 * vhalf);
+      sc[I][1] = pload16<NT>(kst + 2048 + 32 * vhalf + 16);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) vn[I][nn] = pload8<NT>(vt + (16 * nn + r16) * 16 + 8 * vhalf);
+      sc[I][2] = pload16<NT>(vt + 2048 + 32 * vhalf);
+      sc[I][3] = pload16<NT>(vt + 2048 + 32 * vhalf + 16);
+    } else {
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) vw[I][nn] = pload16<NT>(vt + 16 * (2 * (16 * nn + r16) + vhalf));
+    }
+  };
+  uint32_t acc = 0;
+  auto x4 = [](uint4 u) { return u.x ^ u.y ^ u.z ^ u.w; };
+  auto fold = [&](auto bi) {
+    constexpr int I = decltype(bi)::value;
+    if constexpr (!NOQ)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc ^= x4(q[I][kk]);
+#pragma unroll
+    for (int ku = 0; ku < NKU; ++ku) acc ^= x4(ax[I][ku]) ^ x4(ay[I][ku]);
+    if constexpr (B1) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc ^= x4(sc[I][k]);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) acc ^= vn[I][nn].x ^ vn[I][nn].y;
+    } else {
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) acc ^= x4(vw[I][nn]);
+    }
+  };
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((issue(std::integral_constant<int, Is>{}, lo + Is), __builtin_amdgcn_sched_barrier(0)), ...);
+  }(std::make_integer_sequence<int, NB>{});
+  int64_t x = lo;
+  while (x < hi) {
+    [&]<int... Is>(std::integer_sequence<int, Is...>) {
+      ((fold(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0),
+        issue(std::integral_constant<int, Is>{}, x + NB), __builtin_amdgcn_sched_barrier(0), ++x),
+       ...);
+    }(std::make_integer_sequence<int, NB>{});
+  }
+  acc ^= __shfl_xor(acc, 1, 64);
+  if (lane == 0) sink[w] = acc;
+}
+
+template <bool NT, bool B1, int VARIANT>
+int launch_pattern(const uint8_t *kp, const uint8_t *vp, const uint8_t *qb, int64_t n_chunks, const int32_t *order,
+                   uint32_t *sink, int nwg, hipStream_t stream) {
+  auto kern = load_pattern_kernel<NT, B1, VARIANT>;
+  if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsOneWgPerCu))
+    return (int)e;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kWaves), kLdsOneWgPerCu, stream, kp, vp, qb, n_chunks, order, sink);
+  return (int)hipGetLastError();
+}
+
+template <bool NT, bool B1>
+int launch_pattern_v(int variant, const uint8_t *kp, const uint8_t *vp, const uint8_t *qb, int64_t n_chunks,
+                     const int32_t *order, uint32_t *sink, int nwg, hipStream_t stream) {
+  switch (variant) {
+    case 0: return launch_pattern<NT, B1, 0>(kp, vp, qb, n_chunks, order, sink, nwg, stream);
+    case 1: return launch_pattern<NT, B1, 1>(kp, vp, qb, n_chunks, order, sink, nwg, stream);
+    case 2: return launch_pattern<NT, B1, 2>(kp, vp, qb, n_chunks, order, sink, nwg, stream);
+    default: return launch_pattern<NT, B1, 3>(kp, vp, qb, n_chunks, order, sink, nwg, stream);
+  }
+}
+
 template <bool NT>
 int launch(const void *buf, int64_t n_tiles, const int32_t *order, uint32_t *sink, int nwg, size_t lds,
            hipStream_t stream) {
@@ -202,6 +341,33 @@ extern "C" int pkv_probe_stream_tiles(const void *buf, int64_t n_tiles, const in
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return streaming ? launch<true>(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, lds, s)
                    : launch<false>(buf, n_tiles, d_order, d_sink, cus * waves_per_simd, lds, s);
+}
+
+// One launch of the load-pattern probe (see load_pattern_kernel) on one
+// workgroup of four waves per compute unit.  one_byte: 0 bf16 tiles of 4096
+// bytes, 1 one-byte tiles of 2112 bytes; variant 0..3 (bit 0 whole-line K,
+// bit 1 no query slices); streaming: 0 cached, 1 non-temporal K/V loads.
+// d_k and d_v hold 2 * n_chunks tiles each, d_q 256 KiB, d_order 2 * n_chunks
+// int32 tile ids in [0, 2 * n_chunks); d_sink one uint32 per wave (4 per
+// compute unit).  Returns a HIP error code (0 = launched), or -1 for bad
+// arguments.
+extern "C" int pkv_probe_load_pattern(int32_t one_byte, int32_t variant, int32_t streaming, const void *d_k,
+                                      const void *d_v, const void *d_q, int64_t n_chunks, const int32_t *d_order,
+                                      uint32_t *d_sink, void *stream) {
+  if (!d_k || !d_v || !d_q || !d_order || !d_sink || n_chunks <= 0 || variant < 0 || variant > 3 ||
+      (one_byte != 0 && one_byte != 1) || (streaming != 0 && streaming != 1))
+    return -1;
+  int dev = 0, cus = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return (int)e;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
+  const uint8_t *k = static_cast<const uint8_t *>(d_k), *v = static_cast<const uint8_t *>(d_v),
+                *q = static_cast<const uint8_t *>(d_q);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (one_byte)
+    return streaming ? launch_pattern_v<true, true>(variant, k, v, q, n_chunks, d_order, d_sink, cus, s)
+                     : launch_pattern_v<false, true>(variant, k, v, q, n_chunks, d_order, d_sink, cus, s);
+  return streaming ? launch_pattern_v<true, false>(variant, k, v, q, n_chunks, d_order, d_sink, cus, s)
+                   : launch_pattern_v<false, false>(variant, k, v, q, n_chunks, d_order, d_sink, cus, s);
 }
 
 // One launch of the empty kernel on one workgroup of four waves per compute
