@@ -37,12 +37,12 @@
 // K rows are thus slots {0-3, 8-11} of each block and the second's {4-7,
 // 12-15}: a bf16 K load reads half of each 128-byte line it touches, while
 // one-byte K tiles store the slots in that order (k8_unit), so each of their
-// K loads reads whole lines, which matters once the loads stream.  Each lane holds the
-// 8-element slices of the group's query rows that its B operand needs (D/32
-// 16-byte loads per lane), loaded with the K of the first chunk of each
-// segment and kept while the segment lasts, so one set of registers serves
-// both buffers of the pipeline; the whole group shares them through the MFMA,
-// and nothing else in the wave would reuse an LDS copy.
+// K loads reads whole lines, which matters once the loads stream.  Each lane
+// holds the 8-element slices of the group's query rows that its B operand
+// needs (D/32 16-byte loads per lane), one set per pipeline buffer, loaded
+// when a buffer moves to a chunk of another segment and kept while the
+// segment lasts; the whole group shares them through the MFMA, and nothing
+// else in the wave would reuse an LDS copy.
 //
 // int8 cache [KV Cache 工程学 §15.7 (3)].  Codes are loaded 8 bytes per lane
 // where bf16 takes 16 and widened to bf16 exactly (|code| <= 127 needs 7
@@ -145,13 +145,17 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   const int qh = min(r16, G - 1);
 
   // Per buffer: the chunk's cursor, physical blocks, query slices, K and V.
+  // A buffer's query slices are requested when the buffer is located for its
+  // chunk, NB steps before their use and right after a step's V requests, and
+  // only when that chunk lies in another segment than the slices the buffer
+  // holds (qseg).  A wait for a V then covers at most query loads issued
+  // with it: query loads placed before a K wait instead would make that wait
+  // take a full round trip at every segment start, since the compiler counts
+  // the loads in flight on the path without them.
   Cursor cq[NB];
   int pa[NB], pb[NB];
-  // With two buffers the next chunk's query slices load after the current
-  // chunk's scores, so one set of registers serves, reloaded where a segment
-  // starts; deeper pipelines keep one set per buffer, loaded with every chunk.
-  constexpr int NQ = NB == 2 ? 1 : NB;
-  bf16x8_t qb[NQ][NKK];
+  bf16x8_t qb[NB][NKK];
+  int64_t qseg[NB];
   uint4 ax[NB][NKU], ay[NB][NKU];
   VUnit va[NB][NNN];
   float4 ksc[NB][2], vsc[NB][2];  // int8: scales of this lane's 8 token slots
@@ -162,21 +166,20 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     if (pa[i] < 0) return g_idle_tiles + (sel ? TB : 0);
     return pool + ((size_t)(sel ? pb[i] : pa[i]) * H + g) * TB;
   };
-  // Loads of the chunk held in buffer bi; its query slices only if load_q
-  // (a uniform flag: the chunk opens another segment than the registers
-  // hold).  They come first, so the wait for the chunk's K covers them.
-  auto issue = [&](auto bi, bool load_q) {
+  auto load_q = [&](auto bi) {  // query slices of buffer bi's chunk
     constexpr int I = decltype(bi)::value;
-    constexpr int QI = NQ == 1 ? 0 : I;
     const Cursor &c = cq[I];
-    if (load_q) {
-      const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + qh) * D);
+    const uint4 *qr = reinterpret_cast<const uint4 *>(qbase + ((size_t)c.b * P.Hq + (size_t)c.g * G + qh) * D);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const uint4 u = qr[kgroup(kk)];
-        qb[QI][kk] = as_bf16x8<F8>(u);
-      }
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint4 u = qr[kgroup(kk)];
+      qb[I][kk] = as_bf16x8<F8>(u);
     }
+    qseg[I] = c.seg0;
+  };
+  auto issue = [&](auto bi) {  // K of the chunk held in buffer bi
+    constexpr int I = decltype(bi)::value;
+    const Cursor &c = cq[I];
     const uint4 *kt = reinterpret_cast<const uint4 *>(tile(kpool, I, ksel, c.g));
 #pragma unroll
     for (int ku = 0; ku < NKU; ++ku) {
@@ -231,12 +234,16 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
               : (lo + Is < hi ? (void)(cq[Is] = sh.next(cq[Is - 1]), sh.blocks(cq[Is], pa[Is], pb[Is]))
                               : idle_after(Is, Is - 1))), ...);
   }(std::make_integer_sequence<int, NB>{});
-  // Requests leave in the order the loop issues them (K then V of each
-  // chunk): waits at the loop head are counted over both entries, and a
-  // prologue that sent a chunk's K last would make the first of them wait
-  // for everything.
+  // Requests leave in the order the loop issues them (every buffer's query
+  // slices first, then K and V of each chunk): waits at the loop head are
+  // counted over all of them, and a prologue that sent a chunk's K last
+  // would make the first of them wait for everything.
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
-    ((Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}, true), __builtin_amdgcn_sched_barrier(0),
+    (load_q(std::integral_constant<int, Is>{}), ...);
+  }(std::make_integer_sequence<int, NB>{});
+  __builtin_amdgcn_sched_barrier(0);
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    ((Is < NB - 1 ? (issue(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0),
                      issue_v(std::integral_constant<int, Is>{}), __builtin_amdgcn_sched_barrier(0))
                   : (void)0),
      ...);
@@ -248,7 +255,6 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   auto step = [&](auto bi) {
     constexpr int I = decltype(bi)::value;
     constexpr int J = (I + NB - 1) % NB;
-    constexpr int QI = NQ == 1 ? 0 : I;
     f32x4_t sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -261,13 +267,11 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
         kx = as_bf16x8<F8>(ax[I][kk]);
         ky = as_bf16x8<F8>(ay[I][kk]);
       }
-      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[QI][kk], sx, 0, 0, 0);
-      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[QI][kk], sy, 0, 0, 0);
+      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx, qb[I][kk], sx, 0, 0, 0);
+      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky, qb[I][kk], sy, 0, 0, 0);
     }
     if (x + NB - 1 >= hi) idle_after(J, I);  // no chunk x + NB - 1 in the share
-    // One set of query registers serves both buffers: chunk x's scores are
-    // done, and chunk x+1 needs other rows only where a segment starts.
-    issue(std::integral_constant<int, J>{}, NQ > 1 || cq[J].seg0 != cq[I].seg0);
+    issue(std::integral_constant<int, J>{});
 
     const Cursor &cur = cq[I];
     // Past the share's end the loop runs on to the end of its group of NB
@@ -391,6 +395,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     if (x + NB < hi) {
       cq[I] = sh.next(cq[J]);
       sh.blocks(cq[I], pa[I], pb[I]);
+      if (cq[I].seg0 != qseg[I]) load_q(std::integral_constant<int, I>{});
     }
     ++x;
   };
