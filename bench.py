@@ -892,11 +892,13 @@ def main():
           f"({achieved:.0f} GB/s of distinct K/V, {achieved_logical:.0f} GB/s logical); partition kernel alone "
           f"{avg_part_ms * 1e3:.1f} us", flush=True)
     # Untimed calls with the wave trace: the span of the partition kernel's
-    # waves (first start to last end) against its event time, and the rate
-    # at which its waves read while they run.
+    # waves (first start to last end) against its event time, the rate at
+    # which its waves read while they run, and how long the last wave runs
+    # after the median wave has ended (what a perfectly balanced end would
+    # save at most).
     trace = torch.zeros(4 * L.PKV_TRACE_WAVES, dtype=torch.int32, device=dev)
     ev_w = hip.create(2)
-    spans, part_us = [], []
+    spans, part_us, tails = [], [], []
     for c in range(N_SPAN_CALLS):
         trace.zero_()
         step(W_eff + K + c, -1, L.decode_opts(args.partition, args.kernel, (ev_w[0], ev_w[1], None), wps, xw,
@@ -907,6 +909,7 @@ def main():
         if len(t):
             rel = lambda v: (v - t[0, 2] + (1 << 31)) % (1 << 32) - (1 << 31)  # 32-bit clock, 100 MHz
             spans.append((rel(t[:, 3]).max() - rel(t[:, 2]).min()) / 100.0)
+            tails.append((rel(t[:, 3]).max() - np.median(rel(t[:, 3]))) / 100.0)
             part_us.append(hip.elapsed_ms(ev_w[0], ev_w[1]) * 1e3)
     hip.destroy(ev_w)
     wave_span = None
@@ -914,6 +917,7 @@ def main():
         sp, pu = float(np.median(spans)), float(np.median(part_us))
         wave_span = {"partition_event_us": round(pu, 2), "wave_span_us": round(sp, 2),
                      "outside_waves_us": round(pu - sp, 2),
+                     "last_end_after_median_end_us": round(float(np.median(tails)), 2),
                      "read_rate_over_span_gbps": round(unique_per_launch / (sp * 1e-6) / 1e9, 1)}
         print(f"[bench] partition kernel waves: span {sp:.1f} us of {pu:.1f} us between events "
               f"({wave_span['read_rate_over_span_gbps']:.0f} GB/s over the span)", flush=True)
