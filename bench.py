@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import math
 import os
@@ -77,12 +78,17 @@ class HipEvents:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the decode kernels' sources: a stored traffic measurement
-    only applies while these are unchanged."""
+    """Hash of the decode kernels' sources with comments and blank lines
+    removed: a stored traffic measurement applies while the code is
+    unchanged, whatever its comments say."""
     h = hashlib.sha256()
     for f in ("decode_mfma.hip", "decode_valu.hip", "decode_merge.hip", "pkv_device.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_381_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_381_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)  # block comments
+        src = re.sub(r"//[^\n]*", "", src)  # line comments (no string literal in these files holds //)
+        code = "\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip())
+        h.update(code.encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -59,10 +59,12 @@
 // of its codes are NaN, so V codes past the context are zeroed as bf16
 // elements are.
 //
-// Memory pipeline.  Block ids and lengths are scalar loads issued one chunk
-// ahead; chunk c+1's K is requested as soon as chunk c's score MFMAs have
-// consumed the K registers and its V once the PV MFMAs have consumed V, so a
-// wave always has a chunk of loads in flight through its own math.
+// Memory pipeline.  NB register buffers of K/V (two by default): the step
+// that computes chunk c requests chunk c+NB-1 into the buffer chunk c-1
+// used, its K right after chunk c's score MFMAs and its V right after the PV
+// MFMAs, then locates chunk c+NB (block ids: scalar loads) into the buffer it
+// has just consumed and, when that chunk opens another segment, requests its
+// query slices; so a wave always has loads in flight through its own math.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
