@@ -219,8 +219,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   float m = -INFINITY, l = 0.f;
 
   // Every load is issued whatever the share's length: a buffer past the
-  // share's end keeps the last real chunk's cursor (its query slices) and
-  // reads the idle tiles for K/V.  Loads issued on some paths only would
+  // share's end takes the last real chunk's cursor and reads the idle tiles
+  // for K/V (its query registers keep what they hold; no token of an idle
+  // step is counted).  Loads issued on some paths only would
   // leave the count of loads in flight unknown, and the waits would then
   // drain every buffer each step.
   auto idle_after = [&](int to, int from) {
