@@ -50,7 +50,9 @@
  *   blk = physical block, g = kv head (H of them), t = slot in block
  *   (0..15), d = element of the head (D of them).  One (blk, g) tile is
  *   16*D elements (4 KiB for bf16 at D = 128) and contiguous in both pools.
- *   A token's slot id is blk*16 + t.
+ *   A token's slot id is blk*16 + t.  One-byte caches (int8, FP8) use X = 16,
+ *   store K slot t at position p(t) (bits 2 and 3 of t exchanged) and end
+ *   each tile with its 16 scales: see "Pool layout" below.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
