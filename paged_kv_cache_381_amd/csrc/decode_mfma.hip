@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   sh.blocks(cq[0], pa[0], pb[0]);
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
     ((Is == 0 ? (void)0
-              : (lo + Is < hi ? (void)(cq[Is] = sh.next(cq[Is - 1]), sh.blocks(cq[Is], pa[Is], pb[Is]))
+              : (lo + Is < hi ? (void)(cq[Is] = sh.next(cq[Is > 0 ? Is - 1 : 0]), sh.blocks(cq[Is], pa[Is], pb[Is]))
                               : idle_after(Is, Is - 1))), ...);
   }(std::make_integer_sequence<int, NB>{});
   // Requests leave in the order the loop issues them (every buffer's query

@@ -199,8 +199,6 @@ template <bool NT> __device__ __forceinline__ uint2 pload8(const uint8_t *p) {
   }
 }
 
-constexpr int kPatQBytes = 256 * 1024;
-
 template <bool NT, bool B1, int VARIANT>
 __global__ __launch_bounds__(64 * kWaves) void load_pattern_kernel(const uint8_t *kp, const uint8_t *vp,
                                                                    const uint8_t *qb, int64_t n_chunks,
