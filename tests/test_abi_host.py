@@ -354,3 +354,28 @@ def test_xcd_weights_from_trace():
     trace[4 * 3 + 1:4 * 64:32] = 0
     with pytest.raises(P.PagedKVError):
         L.xcd_weights_from_trace(trace)
+
+
+def test_traffic_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    """The stored HBM traffic of the decode kernels applies while their code
+    is unchanged: the bench's source hash ignores comments and blank lines,
+    and changes with any code token."""
+    import shutil
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    csrc = tmp_path / "paged_kv_cache_381_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("decode_mfma.hip", "decode_valu.hip", "decode_merge.hip", "pkv_device.h"):
+        shutil.copy(os.path.join(root, "paged_kv_cache_381_amd", "csrc", f), csrc / f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    merge = csrc / "decode_merge.hip"
+    src = merge.read_text(encoding="utf-8")
+    merge.write_text("// a new comment line\n\n/* and a block\n comment */\n" +
+                     src.replace("\n}", "  // trailing note\n}", 1), encoding="utf-8")
+    assert bench.kernel_source_hash() == h0
+    merge.write_text(src.replace("constexpr int kBatch = 8;", "constexpr int kBatch = 4;"), encoding="utf-8")
+    assert "constexpr int kBatch = 8;" in src
+    assert bench.kernel_source_hash() != h0
