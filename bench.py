@@ -680,6 +680,9 @@ def main():
                          "(counter checks on a small launch; 0: the workload's own)")
     ap.add_argument("--load-policy", type=int, default=0,
                     help="K/V tile loads: 0 auto, 1 streaming (non-temporal), 2 cached")
+    ap.add_argument("--plan", choices=("step", "none"), default="step",
+                    help="step: each step's first decode call records the split in a plan and the other layers' "
+                         "calls run from it; none: every call schedules itself")
     ap.add_argument("--tables", choices=("shuffled", "identity"), default="shuffled",
                     help="physical block placement: the workload's shuffled pool, or blocks handed out in "
                          "address order (each sequence's blocks consecutive)")
@@ -787,14 +790,18 @@ def main():
     cow = np.empty((B, 2), dtype=np.int32)
     ncow = ctypes.c_int32(0)
     lay = ctypes.byref(cache.layout)
-    wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, load_policy=args.load_policy)
+    # One plan per step: the step's first call records the split of its
+    # tables and lengths, the other layers' calls run from it.
+    use_plan = args.plan == "step"
+    step_plan = L.new_decode_plan(cache.layout, B, Hq, MB * 16, args.partition) if use_plan else None
+    wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, load_policy=args.load_policy, plan=step_plan)
     def timed_opts(xw=None):
         # Even timed steps bracket the whole attention call (partition kernel
         # and split-context merge), odd ones the partition kernel alone; one
         # event pair per step, since a record in between would idle the GPU.
         return [L.decode_opts(args.partition, args.kernel,
                               (evs[2 * i], None, evs[2 * i + 1]) if i % 2 == 0 else (evs[2 * i], evs[2 * i + 1], None),
-                              wps, xw, load_policy=args.load_policy) for i in range(K)]
+                              wps, xw, load_policy=args.load_policy, plan=step_plan) for i in range(K)]
 
     ev_opts = timed_opts()
     ws_bytes = ws.numel() * ws.element_size()
@@ -806,7 +813,7 @@ def main():
     tail = (ctypes.c_float(gw.scale), V(ws.data_ptr()), ws_bytes)
     pin_ptr = [(V(p.data_ptr()), V(p.data_ptr() + 12 * B), V(p.data_ptr() + 8 * B)) for p in pin]
 
-    def step(k: int, timed_idx: int, first_opts=None):
+    def step(k: int, timed_idx: int, traced=None):
         r = k % R
         ring_ev[r].synchronize()  # the copy that last read this pinned set is done
         slots_p, tables_p, ctx_p = pin_ptr[r]
@@ -818,11 +825,17 @@ def main():
         max_ctx = int(ctx_np.max())
         dbuf.copy_(pin[r], non_blocking=True)
         ring_ev[r].record()
-        ev_layer = timed_idx % layers if timed_idx >= 0 else -1
+        if use_plan:
+            L.reset_decode_plan(step_plan)  # new lengths and tables: the first call records again
+        # Timed steps 2j and 2j+1 (whole call, partition kernel alone) time
+        # the same layer, j mod layers, so both cover every layer alike
+        # (with a plan the step's first call records it, the others run
+        # from it).
+        ev_layer = (timed_idx // 2) % layers if timed_idx >= 0 else -1
         for layer in range(layers):
             opts = ev_opts[timed_idx] if layer == ev_layer else wps_opts
-            if first_opts is not None and layer == 0:
-                opts = first_opts
+            if traced is not None and layer == traced[0]:
+                opts = traced[1]
             L._check(lib.paged_kv_append(*append_args[layer]))
             L._check(lib.paged_attention_decode(*head[layer], max_ctx, *tail, ctypes.byref(opts), stream))
         return int(ctx_np.astype(np.int64).sum())
@@ -843,8 +856,8 @@ def main():
         recs = []
         for c in range(3):
             trace.zero_()
-            step(W + c, -1, L.decode_opts(args.partition, args.kernel, None, wps, trace=trace,
-                                          load_policy=args.load_policy))
+            step(W + c, -1, (0, L.decode_opts(args.partition, args.kernel, None, wps, trace=trace,
+                                              load_policy=args.load_policy, plan=step_plan)))
             torch.cuda.synchronize()
             t = trace.cpu().numpy().reshape(-1, 4)
             recs.append(t[t[:, 1] > 0])
@@ -858,7 +871,8 @@ def main():
     elif args.xcd_weights != "none":
         xw = [int(v) for v in args.xcd_weights.split(",")]
     if xw is not None:
-        wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, xw, load_policy=args.load_policy)
+        wps_opts = L.decode_opts(args.partition, args.kernel, None, wps, xw, load_policy=args.load_policy,
+                                 plan=step_plan)
         ev_opts = timed_opts(xw)
     W_eff = W + n_cal
     print(f"[bench] warmup done ({W} steps), xcd weights {xw}, timing {K} steps", flush=True)
@@ -884,6 +898,7 @@ def main():
     hip.destroy(evs)
     durs = durs_all[0::2]  # whole attention call: partition + merge
     durs_part = durs_all[1::2] or durs
+    call_us_by_layer = [round(float(np.mean(durs[j::layers])) * 1e3, 2) for j in range(min(layers, len(durs)))]
     avg_ms = sum(durs) / len(durs)
     avg_part_ms = sum(durs_part) / len(durs_part)
     bytes_per_launch = sum(ctx_tokens) / K * tok_bytes  # logical: every sequence's whole context
@@ -907,8 +922,10 @@ def main():
     spans, part_us, tails = [], [], []
     for c in range(N_SPAN_CALLS):
         trace.zero_()
-        step(W_eff + K + c, -1, L.decode_opts(args.partition, args.kernel, (ev_w[0], ev_w[1], None), wps, xw,
-                                              trace=trace, load_policy=args.load_policy))
+        # The last layer's call: with a plan, one that runs from it.
+        step(W_eff + K + c, -1, (layers - 1, L.decode_opts(args.partition, args.kernel, (ev_w[0], ev_w[1], None),
+                                                           wps, xw, trace=trace, load_policy=args.load_policy,
+                                                           plan=step_plan)))
         torch.cuda.synchronize()
         t = trace.cpu().numpy().reshape(-1, 4).astype(np.int64)
         t = t[t[:, 1] > 0]
@@ -954,7 +971,7 @@ def main():
                    "mean_context": round(sum(ctx_tokens) / K / B, 1), "pool_blocks": inst.num_blocks + extra,
                    "min_tokens_per_wave": args.partition or 128, "kernel": args.kernel, "waves_per_simd": wps,
                    "xcd_weights": xw, "tables": args.tables, "load_policy": args.load_policy,
-                   "parallelism": "none"},
+                   "plan": "recorded by each step's first call" if use_plan else "none", "parallelism": "none"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "attention_pct_of_probe": round(100 * achieved / max(probe[k] for k in probe if k.startswith("random")), 2)
         if probe else None,
@@ -977,6 +994,7 @@ def main():
                      "bytes_per_launch": int(unique_per_launch),
                      "logical_bytes_per_launch": int(bytes_per_launch),
                      "achieved_logical": round(achieved_logical, 2),
+                     "call_us_by_layer": call_us_by_layer,
                      "partition_kernel_us": round(avg_part_ms * 1e3, 2),
                      "partition_kernel_frac": round(achieved_part / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,

@@ -344,6 +344,14 @@ int pkv_copy_blocks(const pkv_layout *layout, void *k_pool, void *v_pool, const 
 int pkv_swap_copy(const pkv_layout *layout, void *dst_k, void *dst_v, int32_t dst_blocks, const void *src_k,
                   const void *src_v, int32_t src_blocks, const int32_t *d_pairs, int32_t num_pairs, void *stream);
 
+/* A decode plan [balanced-split scheduling; not part of the method]: what
+ * the call that recorded a plan was (opaque; all zeros = no plan yet).  See
+ * pkv_decode_opts.plan. */
+#define PKV_PLAN_KEY_INTS 32
+typedef struct {
+  int64_t opaque[PKV_PLAN_KEY_INTS];
+} pkv_decode_plan;
+
 /* Decode options (all fields may be zero / NULL for defaults). */
 typedef struct {
   int32_t partition_tokens; /* a positive multiple of 32, or 0 for the default
@@ -380,6 +388,10 @@ typedef struct {
                                chunk count and start/end clock (100 MHz, low 32
                                bits); clear it before the call (waves without
                                work write nothing) */
+  pkv_decode_plan *plan;    /* optional, with plan_buffer: the split of the
+                               calls of one step (see paged_attention_plan_bytes) */
+  void *plan_buffer;        /* device buffer of the plan, 16-byte aligned */
+  size_t plan_bytes;        /* its size, at least paged_attention_plan_bytes() */
 } pkv_decode_opts;
 
 /* Waves a decode trace buffer holds. */
@@ -436,6 +448,33 @@ int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, 
                            int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                            void *workspace, size_t workspace_bytes, const pkv_decode_opts *opts,
                            void *stream);
+
+/* Decode plans [balanced-split scheduling; not part of the method].  The
+ * decode calls of one step (one per layer) share the block tables and
+ * context lengths, and so the split of the work between waves.  With
+ * opts->plan and opts->plan_buffer, a call whose *opts->plan is all zeros
+ * schedules itself as usual and also records that split in the buffer: the
+ * chunk scan and the merge kernel's schedule header, and for every wave its
+ * share and the cursors and physical blocks of its first two chunks; it
+ * then fills *opts->plan with what the call was.  A later call given that
+ * plan takes the split from the buffer, so its waves' first K/V requests
+ * wait on one memory round trip instead of three (the lengths, then the
+ * block table, then the tiles).  Results are bitwise those of a call
+ * without a plan.
+ *   plan buffer: paged_attention_plan_bytes() bytes of device memory for
+ *   the calls' num_seqs, num_q_heads, max_context_len and partition option;
+ *   it must stay allocated and unchanged while calls use the plan
+ * A call given a recorded plan whose arguments (the table and length
+ * pointers and the plan buffer included), options (but events and trace) or
+ * current device differ from the recording call's fails with
+ * PKV_ERR_INVALID.  The plan holds the lengths and blocks the recording call
+ * read: once tables or lengths change (a new token, a new block, a swap),
+ * zero *plan so that the next call records again; a call from a stale plan
+ * reads the old shares and blocks (in bounds, but the results are wrong).
+ * The wavefront-reduction kernel schedules itself every call (its plans
+ * only check the arguments). */
+size_t paged_attention_plan_bytes(const pkv_layout *layout, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len, const pkv_decode_opts *opts);
 
 /* paged_attention_decode without a workspace argument and without any
  * allocation, for callers that cannot allocate device memory: code under HIP

@@ -13,4 +13,5 @@ from ._lib import (  # noqa: F401
     pkv_batch_append_slots, pkv_seq_free, pkv_seq_len, pkv_seq_block_table, pkv_batch_block_tables,
     pkv_pool_stats, pkv_kv_bytes_per_token, pkv_pool_bytes, pkv_validate_tables,
     paged_kv_append, pkv_copy_blocks, paged_attention_workspace_bytes, paged_attention_decode,
+    pkv_decode_plan, paged_attention_plan_bytes, new_decode_plan, reset_decode_plan,
 )

@@ -76,11 +76,19 @@ class pkv_swap_stats(ctypes.Structure):
                 ("clock_hand", ctypes.c_int32), ("swapped_out", ctypes.c_int64), ("swapped_in", ctypes.c_int64)]
 
 
+PKV_PLAN_KEY_INTS = 32
+
+
+class pkv_decode_plan(ctypes.Structure):
+    _fields_ = [("opaque", ctypes.c_int64 * PKV_PLAN_KEY_INTS)]
+
+
 class pkv_decode_opts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("waves_per_simd", ctypes.c_int32),
                 ("ev_begin", ctypes.c_void_p),
                 ("ev_partition_done", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
-                ("xcd_weights", ctypes.c_int32 * 8), ("load_policy", ctypes.c_int32), ("trace", ctypes.c_void_p)]
+                ("xcd_weights", ctypes.c_int32 * 8), ("load_policy", ctypes.c_int32), ("trace", ctypes.c_void_p),
+                ("plan", ctypes.c_void_p), ("plan_buffer", ctypes.c_void_p), ("plan_bytes", ctypes.c_size_t)]
 
 
 PKV_TRACE_WAVES = 8192  # waves a decode trace buffer holds (4 int32 each)
@@ -132,6 +140,7 @@ SIGNATURES = {
                                                _P]),
     "paged_attention_decode_noalloc": (ctypes.c_int, [_PL, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _F, _PO,
                                                       _P]),
+    "paged_attention_plan_bytes": (_SZ, [_PL, _I32, _I32, _I32, _PO]),
 }
 
 _lib = None
@@ -437,12 +446,23 @@ def pkv_copy_blocks(layout, k_pool, v_pool, pairs, stream=None):
 
 
 def decode_opts(partition_tokens=0, kernel=0, events=None, waves_per_simd=0, xcd_weights=None,
-                trace=None, load_policy=0) -> pkv_decode_opts:
+                trace=None, load_policy=0, plan=None) -> pkv_decode_opts:
     """trace: optional device int32 tensor of 4 * PKV_TRACE_WAVES elements;
-    load_policy: 0 auto, 1 streaming (non-temporal) K/V loads, 2 cached."""
+    load_policy: 0 auto, 1 streaming (non-temporal) K/V loads, 2 cached;
+    plan: (pkv_decode_plan, device buffer of paged_attention_plan_bytes()
+    bytes): an all-zero record makes the call record its split there, a
+    recorded one makes it run from it (the caller keeps both alive while the
+    options are used)."""
     ev = list(events) if events else [None, None, None]
     o = pkv_decode_opts(int(partition_tokens), int(kernel), int(waves_per_simd), *[e if e else None for e in ev])
     o.load_policy = int(load_policy)
+    if plan is not None:
+        rec, buf = plan
+        if not isinstance(rec, pkv_decode_plan):
+            raise TypeError("plan must be (pkv_decode_plan, device buffer)")
+        o.plan = ctypes.addressof(rec)
+        o.plan_buffer = _dev(buf, "plan buffer").value
+        o.plan_bytes = buf.numel() * buf.element_size()
     if xcd_weights is not None:
         w = [int(x) for x in xcd_weights]
         if len(w) != 8:
@@ -473,9 +493,30 @@ def paged_attention_workspace_bytes(layout, num_seqs, num_q_heads, max_context_l
                                                  int(max_context_len), ctypes.byref(o))
 
 
+def paged_attention_plan_bytes(layout, num_seqs, num_q_heads, max_context_len, partition_tokens=0) -> int:
+    o = decode_opts(partition_tokens)
+    return lib().paged_attention_plan_bytes(ctypes.byref(layout), int(num_seqs), int(num_q_heads),
+                                            int(max_context_len), ctypes.byref(o))
+
+
+def new_decode_plan(layout, num_seqs, num_q_heads, max_context_len, partition_tokens=0, device="cuda"):
+    """(empty pkv_decode_plan, plan buffer) for the decode calls of one step:
+    pass it as plan= to each; the first records the split, the others run
+    from it.  Zero the record (reset_decode_plan) when tables or lengths
+    change."""
+    import torch
+    n = paged_attention_plan_bytes(layout, num_seqs, num_q_heads, max_context_len, partition_tokens)
+    return pkv_decode_plan(), torch.empty(max(-(-n // 4), 1), dtype=torch.int32, device=device)
+
+
+def reset_decode_plan(plan):
+    """Empties a plan record, so that the next call records a new split."""
+    ctypes.memset(ctypes.addressof(plan[0] if isinstance(plan, tuple) else plan), 0, ctypes.sizeof(pkv_decode_plan))
+
+
 def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
                            workspace=None, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0,
-                           xcd_weights=None, trace=None, load_policy=0):
+                           xcd_weights=None, trace=None, load_policy=0, plan=None):
     """events: optional (begin, partition_done, end) raw hipEvent_t handles."""
     import torch
     pdt, rdt = pool_torch_dtype(layout), row_torch_dtype(layout)
@@ -492,7 +533,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
         ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < ws_need:
         raise ValueError(f"workspace of {ws_need} bytes needed, got {ws_bytes}")
-    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy)
+    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy, plan)
     _check(lib().paged_attention_decode(
         ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", rdt),
         _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),
@@ -502,7 +543,7 @@ def paged_attention_decode(layout, out, q, k_pool, v_pool, block_tables, context
 
 def paged_attention_decode_noalloc(layout, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
                                    scale, partition_tokens=0, kernel=0, events=None, stream=None, waves_per_simd=0,
-                                   xcd_weights=None, trace=None, load_policy=0):
+                                   xcd_weights=None, trace=None, load_policy=0, plan=None):
     """paged_attention_decode on the library's own per-GPU scratch: no
     workspace argument, no allocation."""
     import torch
@@ -512,7 +553,7 @@ def paged_attention_decode_noalloc(layout, out, q, k_pool, v_pool, block_tables,
     B, Hq, D = q.shape
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
-    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy)
+    o = decode_opts(partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy, plan)
     _check(lib().paged_attention_decode_noalloc(
         ctypes.byref(layout), _dev(out, "out", torch.float32, B * Hq * D), _dev(q, "q", rdt),
         _dev(k_pool, "k_pool", pdt, layout.pool_elems), _dev(v_pool, "v_pool", pdt, layout.pool_elems),

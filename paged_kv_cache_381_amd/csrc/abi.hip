@@ -106,7 +106,7 @@ int pkv_split_grid(const void *kernel, int block_threads, size_t lds_bytes, cons
     int per_cu;
     int cus;
   };
-  static thread_local Occ cache[8] = {};
+  static thread_local Occ cache[16] = {};
   int dev = 0;
   if (hipError_t e = hipGetDevice(&dev)) return (int)e;
   Occ *hit = nullptr;
@@ -121,7 +121,7 @@ int pkv_split_grid(const void *kernel, int block_threads, size_t lds_bytes, cons
     if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.per_cu, kernel, block_threads, lds_bytes))
       return (int)e;
     if (hipError_t e = hipDeviceGetAttribute(&o.cus, hipDeviceAttributeMultiprocessorCount, dev)) return (int)e;
-    for (int i = 7; i > 0; --i) cache[i] = cache[i - 1];
+    for (int i = 15; i > 0; --i) cache[i] = cache[i - 1];
     cache[0] = o;
     hit = &cache[0];
   }
@@ -237,14 +237,91 @@ void carve_workspace(pkv_decode_args *a, void *workspace) {
                                           align16(rows * 2 * sizeof(float)));
 }
 
+// ------------------------------------------------------------ decode plans
+// A plan buffer holds the schedule header the merge kernel reads (as in a
+// workspace, padded to 16 bytes), then the clamped lengths (padded to 4
+// ints) and one record of PKV_PLAN_REC_INTS per wave that can receive work.
+int32_t plan_cap(const pkv_decode_args &a) { return a.nslots / 2; }
+size_t plan_hdr_bytes(int32_t B) { return align16((size_t)(PKV_HDR_INTS + B) * sizeof(int32_t)); }
+size_t plan_bytes_of(const pkv_decode_args &a) {
+  return plan_hdr_bytes(a.num_seqs) +
+         ((size_t)((a.num_seqs + 3) & ~3) + (size_t)plan_cap(a) * PKV_PLAN_REC_INTS) * sizeof(int32_t);
+}
+
+// What a plan was made for: every argument and option that decides the
+// schedule or the blocks it names, the plan buffer and the device.
+constexpr int64_t kPlanMagic = 0x504b56504c414e31;  // "PKVPLAN1"
+int plan_key(const pkv_decode_args &a, const void *d_plan, int64_t key[PKV_PLAN_KEY_INTS]) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_fail((int)e, "hipGetDevice");
+  int64_t v[] = {kPlanMagic,
+                 dev,
+                 (int64_t)reinterpret_cast<uintptr_t>(d_plan),
+                 (int64_t)reinterpret_cast<uintptr_t>(a.tables),
+                 (int64_t)reinterpret_cast<uintptr_t>(a.ctx),
+                 a.num_seqs,
+                 a.num_q_heads,
+                 a.max_blocks,
+                 a.max_ctx,
+                 a.L->num_blocks,
+                 a.L->num_kv_heads,
+                 a.L->head_dim,
+                 a.L->kv_dtype,
+                 a.kernel,
+                 a.min_cpw,
+                 a.waves_per_simd,
+                 a.streaming,
+                 a.xw[0], a.xw[1], a.xw[2], a.xw[3], a.xw[4], a.xw[5], a.xw[6], a.xw[7]};
+  static_assert(sizeof(v) / sizeof(v[0]) <= PKV_PLAN_KEY_INTS, "the plan key outgrew pkv_decode_plan");
+  for (int i = 0; i < PKV_PLAN_KEY_INTS; ++i) key[i] = i < (int)(sizeof(v) / sizeof(v[0])) ? v[i] : 0;
+  return PKV_OK;
+}
+
+// A prepared call's use of opts->plan: none, record a fresh plan (an empty
+// *opts->plan: the call schedules itself and writes its split to the plan
+// buffer), or run from a recorded one after checking that the call is the
+// one it was recorded for.  *key receives what the call is.
+enum PlanUse { kNoPlan, kRecord, kRun };
+int use_plan(pkv_decode_args *a, const pkv_decode_opts *opts, PlanUse *use, int64_t key[PKV_PLAN_KEY_INTS]) {
+  *use = kNoPlan;
+  if (!opts || !opts->plan) return PKV_OK;
+  const size_t need = plan_bytes_of(*a);
+  if (!opts->plan_buffer || opts->plan_bytes < need || !aligned(opts->plan_buffer, 16))
+    return pkv_set_error(PKV_ERR_WORKSPACE, "a plan buffer of %zu bytes, 16-byte aligned, is needed (got %zu)", need,
+                         opts->plan_buffer ? opts->plan_bytes : (size_t)0);
+  if (int rc = plan_key(*a, opts->plan_buffer, key)) return rc;
+  const int64_t *made = opts->plan->opaque;
+  if (made[0] == 0) {
+    *use = kRecord;
+  } else {
+    if (made[0] != kPlanMagic) return pkv_set_error(PKV_ERR_INVALID, "opts->plan holds neither a plan nor zeros");
+    for (int i = 0; i < PKV_PLAN_KEY_INTS; ++i)
+      if (key[i] != made[i])
+        return pkv_set_error(PKV_ERR_INVALID,
+                             "opts->plan was recorded for other arguments, options or device (field %d differs)", i);
+    *use = kRun;
+  }
+  if (a->kernel != 2) return PKV_OK;  // the wavefront-reduction kernel schedules itself every call
+  a->plan_mode = *use == kRecord ? 2 : 1;
+  a->ws_hdr = static_cast<int32_t *>(opts->plan_buffer);
+  a->plan = reinterpret_cast<int32_t *>(static_cast<char *>(opts->plan_buffer) + plan_hdr_bytes(a->num_seqs));
+  a->plan_cap = plan_cap(*a);
+  return PKV_OK;
+}
+
 // The partition and merge kernels of a prepared call, between the optional
 // events.
-int decode_launch(const pkv_decode_args &a, const pkv_decode_opts *opts, void *stream) {
+int decode_launch(pkv_decode_args &a, const pkv_decode_opts *opts, void *stream) {
+  PlanUse use;
+  int64_t key[PKV_PLAN_KEY_INTS];
+  if (int rc = use_plan(&a, opts, &use, key)) return rc;
   if (int rc = record(opts ? opts->ev_begin : nullptr, stream)) return rc;
   const int rc = a.kernel == 2 ? pkv_launch_decode_mfma(a) : pkv_launch_decode_valu(a);
   if (rc) return hip_fail(rc, "decode partition kernel launch");
   if (int r = record(opts ? opts->ev_partition_done : nullptr, stream)) return r;
   if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
+  if (use == kRecord)
+    for (int i = 0; i < PKV_PLAN_KEY_INTS; ++i) opts->plan->opaque[i] = key[i];
   return record(opts ? opts->ev_end : nullptr, stream);
 }
 
@@ -266,6 +343,18 @@ extern "C" int paged_attention_decode(const pkv_layout *layout, float *out, cons
                          workspace ? workspace_bytes : (size_t)0);
   carve_workspace(&a, workspace);
   return decode_launch(a, opts, stream);
+}
+
+extern "C" size_t paged_attention_plan_bytes(const pkv_layout *layout, int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t max_context_len, const pkv_decode_opts *opts) {
+  if (pkv_check_layout(layout) || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
+  if (num_q_heads % layout->num_kv_heads) return 0;
+  int32_t mc;
+  if (min_chunks(opts, &mc)) return 0;
+  pkv_decode_args a{};
+  a.num_seqs = num_seqs;
+  a.nslots = split_slots(num_seqs, layout->num_kv_heads, max_context_len, mc);
+  return plan_bytes_of(a);
 }
 
 // ------------------------------------------------ decode without allocation

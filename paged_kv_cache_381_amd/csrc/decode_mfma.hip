@@ -104,7 +104,73 @@ constexpr float kSlack = 8.0f;
 constexpr int kIdleTileBytes = 32 * 128;
 __device__ __align__(4096) uint8_t g_idle_tiles[2 * kIdleTileBytes];
 
-template <int D, int W, int NB, bool I8, bool F8, bool NT>
+// A plan's walk starts from its record: the wave's share and its first
+// chunks' cursors and blocks, read with scalar loads (one round trip, where
+// the kernel's own schedule takes the lengths' and then the block table's
+// before the first K/V request).  The chunk scan and the lengths come from
+// the plan's header as the walk needs them.  Returns false when the wave has
+// no work.
+template <int W>
+__device__ bool plan_begin(const SplitParams &P, ShareT<true> &sh, const int32_t *&rec) {
+  const int w = threadIdx.x >> 6;
+  sh.wave = uniform((P.wg_dealt ? (int)blockIdx.x : xcd_logical(blockIdx.x, gridDim.x)) * W + w);
+  sh.s_incl = P.ws_hdr + PKV_HDR_INTS;
+  sh.s_len = P.plan;
+  sh.ctx = P.ctx;
+  sh.tables = P.tables;
+  sh.B = P.B;
+  sh.max_blocks = P.max_blocks;
+  sh.max_ctx = P.max_ctx;
+  sh.num_blocks = P.num_blocks;
+  if (sh.wave >= P.plan_cap) return false;  // every wave with work has a record
+  rec = P.plan + pkv_plan_lens_ints(P.B) + (size_t)sh.wave * PKV_PLAN_REC_INTS;
+  sh.lo = (int64_t)(uint32_t)sload_i32(rec) | ((int64_t)sload_i32(rec + 1) << 32);
+  sh.hi = (int64_t)(uint32_t)sload_i32(rec + 2) | ((int64_t)sload_i32(rec + 3) << 32);
+  return sh.lo < sh.hi;
+}
+
+// Cursor and blocks of a wave's k-th chunk from its plan record.
+__device__ __forceinline__ void plan_chunk(const int32_t *rec, int k, Cursor &c, int &pa, int &pb) {
+  const int32_t *r = rec + 4 + kPlanCursorInts * k;
+  c.b = sload_i32(r);
+  c.g = sload_i32(r + 1);
+  c.j = sload_i32(r + 2);
+  c.cnt = sload_i32(r + 3);
+  c.n = sload_i32(r + 4);
+  c.seg0 = (int64_t)(uint32_t)sload_i32(r + 5) | ((int64_t)sload_i32(r + 6) << 32);
+  pa = sload_i32(r + 7);
+  pb = sload_i32(r + 8);
+}
+
+// Records wave sh.wave's plan (lane 0): lo and hi of its share, or an empty
+// share (WORK false), then the cursors and blocks of its first
+// PKV_PLAN_CHUNKS chunks as the self-scheduled prologue located them.  The
+// stores are issued before the wave's first loads, so no wait for a load
+// is held by them.
+template <bool WORK, int NB>
+__device__ __forceinline__ void plan_write(const SplitParams &P, const Share &sh, const Cursor *cq, const int *pa,
+                                           const int *pb) {
+  static_assert(NB >= PKV_PLAN_CHUNKS, "a record holds chunks the prologue has located");
+  if ((threadIdx.x & 63) != 0 || sh.wave >= P.plan_cap) return;
+  int32_t *rec = P.plan + pkv_plan_lens_ints(P.B) + (size_t)sh.wave * PKV_PLAN_REC_INTS;
+  const int64_t lo = WORK ? sh.lo : 0, hi = WORK ? sh.hi : 0;
+  *reinterpret_cast<int4 *>(rec) = make_int4((int)(uint32_t)lo, (int)(lo >> 32), (int)(uint32_t)hi, (int)(hi >> 32));
+  if constexpr (WORK) {
+#pragma unroll
+    for (int k = 0; k < PKV_PLAN_CHUNKS; ++k) {
+      if (lo + k >= hi) break;
+      int32_t *r = rec + 4 + kPlanCursorInts * k;
+      *reinterpret_cast<int4 *>(r) = make_int4(cq[k].b, cq[k].g, cq[k].j, cq[k].cnt);
+      *reinterpret_cast<int4 *>(r + 4) = make_int4(cq[k].n, (int)(uint32_t)cq[k].seg0, (int)(cq[k].seg0 >> 32), pa[k]);
+      r[8] = pb[k];
+    }
+  }
+}
+
+// MODE 0: the kernel computes its schedule (chunk scan of the lengths, then
+// each wave's share) and, given a plan buffer (P.plan), records it there;
+// MODE 1: it runs from a recorded plan (plan_begin).
+template <int D, int W, int NB, bool I8, bool F8, bool NT, int MODE>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   constexpr int NKK = D / 32;  // score MFMAs per 16-row token set
   constexpr int NNN = D / 16;  // PV MFMAs
@@ -119,8 +185,33 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
   const int lane = threadIdx.x & 63;
   const int H = P.H, G = P.G;
   const uint32_t t_start = (uint32_t)__builtin_amdgcn_s_memrealtime();
-  Share sh;
-  if (!split_begin<W, D>(P, s_lds, sh)) return;
+  // Rows of empty sequences are zeroed by the first workgroup: in mode 0
+  // within the schedule, in mode 1 here, from the plan's chunk scan, on every
+  // exit of each of its waves (each takes its own lanes' sequences).
+  auto zero_empty = [&]() {
+    if constexpr (MODE == 1) {
+      if (blockIdx.x != 0) return;
+      const int32_t *incl = P.ws_hdr + PKV_HDR_INTS;
+      for (int b = threadIdx.x; b < P.B; b += 64 * W)
+        if (incl[b] == (b ? incl[b - 1] : 0)) {
+          float *row = P.out + (size_t)b * P.Hq * D;  // out is only 4-byte aligned
+          for (int i = 0; i < P.Hq * D; ++i) row[i] = 0.f;
+        }
+    }
+  };
+  ShareT<MODE == 1> sh;
+  const int32_t *rec = nullptr;
+  if constexpr (MODE == 1) {
+    if (!plan_begin<W>(P, sh, rec)) {
+      zero_empty();
+      return;
+    }
+  } else {
+    if (!split_begin<W, D>(P, s_lds, sh)) {
+      if (P.plan) plan_write<false, NB>(P, sh, nullptr, nullptr, nullptr);
+      return;
+    }
+  }
   const int64_t lo = sh.lo, hi = sh.hi;
   // This wave's ring of finished pieces, written out after its last load.
   uint8_t *const ring = reinterpret_cast<uint8_t *>(s_lds) + P.ring_off + (threadIdx.x >> 6) * P.nrec * P.rec_bytes;
@@ -230,13 +321,25 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
     pb[to] = -1;
   };
   // Prologue: chunks lo .. lo+NB-2 are requested, chunk lo+NB-1 located.
-  cq[0] = sh.first();
-  sh.blocks(cq[0], pa[0], pb[0]);
+  auto locate_first = [&](auto bi) {  // chunk lo + bi of the share, which exists
+    constexpr int I = decltype(bi)::value;
+    if constexpr (MODE == 1 && I < PKV_PLAN_CHUNKS) {
+      plan_chunk(rec, I, cq[I], pa[I], pb[I]);
+    } else if constexpr (I == 0) {
+      cq[0] = sh.first();
+      sh.blocks(cq[0], pa[0], pb[0]);
+    } else {
+      cq[I] = sh.next(cq[I > 0 ? I - 1 : 0]);
+      sh.blocks(cq[I], pa[I], pb[I]);
+    }
+  };
+  locate_first(std::integral_constant<int, 0>{});
   [&]<int... Is>(std::integer_sequence<int, Is...>) {
     ((Is == 0 ? (void)0
-              : (lo + Is < hi ? (void)(cq[Is] = sh.next(cq[Is > 0 ? Is - 1 : 0]), sh.blocks(cq[Is], pa[Is], pb[Is]))
-                              : idle_after(Is, Is - 1))), ...);
+              : (lo + Is < hi ? locate_first(std::integral_constant<int, Is>{}) : idle_after(Is, Is - 1))), ...);
   }(std::make_integer_sequence<int, NB>{});
+  if constexpr (MODE == 0)
+    if (P.plan) plan_write<true, NB>(P, sh, cq, pa, pb);
   // Requests leave in the order the loop issues them (every buffer's query
   // slices first, then K and V of each chunk): waits at the loop head are
   // counted over all of them, and a prologue that sent a chunk's K last
@@ -425,6 +528,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(SplitParams P) {
       *reinterpret_cast<float2 *>(P.ws_ml + 2 * ((size_t)slot * G + lane)) =
           *reinterpret_cast<const float2 *>(rec + G * D * 4 + lane * 8);
   }
+  zero_empty();
   // Optional trace: the wave's XCD group (workgroups are dealt round-robin
   // to the 8 XCDs), its chunks, and its start and end times (100 MHz clock,
   // low 32 bits), from which per-XCD streaming rates and weights follow.
@@ -449,7 +553,10 @@ constexpr size_t kMaxRecords = 16;
 // I8: one-byte codes (int8, or FP8 E4M3 when F8) with per-row scales.
 template <int D, bool I8, bool F8, bool NT>
 int launch(const pkv_decode_args &a, const SplitParams &p0) {
-  auto kern = decode_mfma_kernel<D, kWaves, I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF, I8, F8, NT>;
+  constexpr int NB = I8 ? PKV_MFMA_NBUF_I8 : PKV_MFMA_NBUF;
+  // The grid is the one of the self-scheduling kernel in both modes, so that
+  // a plan and the calls that run from it agree on every wave's share.
+  auto kern = decode_mfma_kernel<D, kWaves, NB, I8, F8, NT, 0>;
   SplitParams p = p0;
   // A one-byte (block, kv head) tile is 2112 bytes, so every other tile
   // shares a 128-byte line with the next kv head's tile.  The waves reading
@@ -478,7 +585,17 @@ int launch(const pkv_decode_args &a, const SplitParams &p0) {
   if (a.waves_per_simd == 1) lds = std::max<size_t>(lds, PKV_LDS_ONE_WG_PER_CU);
   int nwg = 0;
   if (int rc = pkv_split_grid(reinterpret_cast<const void *>(kern), 64 * kWaves, lds, a, &nwg)) return rc;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kWaves), lds, reinterpret_cast<hipStream_t>(a.stream), p);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  if (a.plan_mode == 1) {
+    // Runs on the grid above, that of the call that recorded the plan (the
+    // call below only sets the kernel's LDS limit).
+    auto kp = decode_mfma_kernel<D, kWaves, NB, I8, F8, NT, 1>;
+    int unused = 0;
+    if (int rc = pkv_split_grid(reinterpret_cast<const void *>(kp), 64 * kWaves, lds, a, &unused)) return rc;
+    hipLaunchKernelGGL(kp, dim3(nwg), dim3(64 * kWaves), lds, st, p);
+    return (int)hipGetLastError();
+  }
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(64 * kWaves), lds, st, p);
   return (int)hipGetLastError();
 }
 

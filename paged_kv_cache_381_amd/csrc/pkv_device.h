@@ -207,6 +207,9 @@ struct SplitParams {
   int32_t *trace;         // nullable: per wave, its XCD group, chunks and start/end times
   float scale_log2;
   int32_t wg_dealt;       // 1: shares follow the workgroups as dealt to the XCDs (round robin)
+  int32_t *plan;          // nullable: [B] clamped lengths (padded to 4), then plan_cap records
+                          // of PKV_PLAN_REC_INTS (a wave's share and first chunks)
+  int32_t plan_cap;       // records the plan holds (every wave that can receive work)
 };
 
 // Parameters of the paged prefill kernel (passed by value).
@@ -401,6 +404,8 @@ inline SplitParams pkv_split_params(const pkv_decode_args &a) {
   p.trace = a.trace;
   p.scale_log2 = a.scale_log2;
   p.wg_dealt = 0;
+  p.plan = a.plan_mode ? a.plan : nullptr;
+  p.plan_cap = a.plan_mode ? a.plan_cap : 0;
   return p;
 }
 
@@ -412,10 +417,13 @@ struct Cursor {
   int64_t seg0;
 };
 
-// One wave's share [lo, hi) of the chunk list and the walk through it.
-struct Share {
-  const int32_t *s_incl;  // LDS: inclusive chunk scan over the batch
-  const int32_t *s_len;   // LDS: clamped lengths
+// One wave's share [lo, hi) of the chunk list and the walk through it.  The
+// chunk scan and the clamped lengths are in LDS (GL false: the kernel's own
+// scan) or in device memory (GL true: a plan's), read with scalar loads.
+template <bool GL>
+struct ShareT {
+  const int32_t *s_incl;  // inclusive chunk scan over the batch
+  const int32_t *s_len;   // clamped lengths
   const int32_t *ctx;
   const int32_t *tables;
   int B, max_blocks, max_ctx, num_blocks;
@@ -424,8 +432,14 @@ struct Share {
   int64_t lo, hi;
   Regions rg;
 
-  __device__ int cnt_of(int b) const { return uniform(s_incl[b] - (b ? s_incl[b - 1] : 0)); }
-  __device__ int len_of(int b) const { return uniform(s_len[b]); }
+  __device__ int at(const int32_t *p, int i) const {
+    if constexpr (GL)
+      return sload_i32(p + i);
+    else
+      return uniform(p[i]);
+  }
+  __device__ int cnt_of(int b) const { return at(s_incl, b) - (b ? at(s_incl, b - 1) : 0); }
+  __device__ int len_of(int b) const { return at(s_len, b); }
 
   // The share's first chunk: kv head lo / c_seq, then the first sequence
   // whose chunks end past the remainder.
@@ -436,14 +450,14 @@ struct Share {
     int a = 0, z = B - 1;
     while (a < z) {
       const int mid = (a + z) >> 1;
-      if (uniform(s_incl[mid]) > rem)
+      if (at(s_incl, mid) > rem)
         z = mid;
       else
         a = mid + 1;
     }
     c.b = a;
     c.cnt = cnt_of(a);
-    const int excl = uniform(s_incl[a]) - c.cnt;
+    const int excl = at(s_incl, a) - c.cnt;
     c.j = rem - excl;
     c.n = len_of(a);
     c.seg0 = (int64_t)c.g * c_seq + excl;
@@ -489,6 +503,15 @@ struct Share {
   // cannot write outside the workspace).
   __device__ int slot(const Cursor &c, int nslots) const { return min(2 * wave + (lo < c.seg0 ? 1 : 0), nslots - 1); }
 };
+using Share = ShareT<false>;
+
+// Plan record of one wave (PKV_PLAN_REC_INTS int32): lo and hi of its share
+// (int64 each), then for each of its first PKV_PLAN_CHUNKS chunks, 16-byte
+// aligned, the cursor (b, g, j, cnt, n, seg0 as two ints) and the two
+// physical blocks.
+constexpr int kPlanCursorInts = 12;
+static_assert(4 + kPlanCursorInts * PKV_PLAN_CHUNKS <= PKV_PLAN_REC_INTS, "a plan record holds its chunks");
+__device__ __forceinline__ int pkv_plan_lens_ints(int num_seqs) { return (num_seqs + 3) & ~3; }
 
 // Common start of the balanced-split kernels: the chunk scan (all threads),
 // the merge kernel's schedule header and zero rows for empty sequences
@@ -521,7 +544,8 @@ __device__ bool split_begin(const SplitParams &P, int32_t *s_lds, Share &sh) {
     // its rows zeroed by the thread that found it.
     for (int b = tid; b < P.B; b += 64 * W) {
       P.ws_hdr[PKV_HDR_INTS + b] = s_incl[b];
-      if (s_incl[b] == (b ? s_incl[b - 1] : 0)) {
+      if (P.plan) P.plan[b] = s_len[b];  // a plan's walk reads the lengths from memory
+      if (P.out && s_incl[b] == (b ? s_incl[b - 1] : 0)) {  // no output when planning
         float *row = P.out + (size_t)b * P.Hq * D;  // out is only 4-byte aligned
         for (int i = 0; i < P.Hq * D; ++i) row[i] = 0.f;
       }

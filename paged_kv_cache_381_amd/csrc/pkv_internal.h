@@ -33,6 +33,10 @@ inline int64_t pkv_row_bytes(const pkv_layout *L) {
 #define PKV_HDR_INTS (4 + 2 * (PKV_REGIONS + 1))
 // Ints a decode wave writes to a trace buffer (PKV_TRACE_WAVES waves).
 #define PKV_TRACE_INTS 4
+// Ints of one wave's record in a decode plan, and the chunks whose cursor
+// and blocks a record holds.
+#define PKV_PLAN_REC_INTS 32
+#define PKV_PLAN_CHUNKS 2
 // Most waves a decode grid runs: 8 per compute unit of MI355X's 256 (one or
 // two workgroups of four waves).  Bounds the partial slots of the workspace.
 #define PKV_MAX_DECODE_WAVES 2048
@@ -62,6 +66,9 @@ struct pkv_decode_args {
   int32_t kernel;          // 1 wavefront reductions, 2 matrix cores
   int32_t waves_per_simd;  // resident waves per SIMD of the matrix-core kernel (1 or 2)
   int32_t streaming;       // K/V tiles read with non-temporal loads (1) or cached ones (0)
+  int32_t plan_mode;       // matrix-core kernel: 0 schedules itself, 1 runs from a plan, 2 writes one
+  int32_t *plan;           // plan region of the workspace (plan_mode 1 and 2)
+  int32_t plan_cap;        // records of the plan region
   void *stream;
 };
 

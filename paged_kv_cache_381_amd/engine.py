@@ -137,13 +137,13 @@ class PagedKVCache:
 
     def decode(self, layer: int, out, q, tables_dev, ctx_dev, max_ctx: int, scale: float, workspace=None,
                partition_tokens=0, kernel=0, events=None, waves_per_simd=None, xcd_weights=None, trace=None,
-               load_policy=0):
+               load_policy=0, plan=None):
         if waves_per_simd is None:
             waves_per_simd = self.waves_per_simd()
         L.paged_attention_decode(self.layout, out, q, self.k_pools[layer], self.v_pools[layer], tables_dev, ctx_dev,
                                  max_ctx, scale, workspace, partition_tokens, kernel, events,
                                  waves_per_simd=waves_per_simd, xcd_weights=xcd_weights, trace=trace,
-                                 load_policy=load_policy)
+                                 load_policy=load_policy, plan=plan)
 
     def prefill(self, layer: int, out, q, tables_dev, ctx_dev, qstart_dev, max_query_len: int, max_ctx: int,
                 scale: float):
@@ -224,14 +224,20 @@ class GpuWorkload:
         self.out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.float32, device=self.device)
 
     def decode(self, layer=0, partition_tokens=0, kernel=0, events=None, workspace=None, out=None, waves_per_simd=None,
-               xcd_weights=None, trace=None, load_policy=0):
+               xcd_weights=None, trace=None, load_policy=0, plan=None):
+        """plan: (pkv_decode_plan, buffer) from new_plan(): recorded by the
+        first call given it, used by the next ones."""
         if workspace is None:
             workspace = self.cache.workspace(self.wl.batch, self.wl.num_q_heads, self.max_ctx, partition_tokens,
                                              kernel)
         out = self.out if out is None else out
         self.cache.decode(layer, out, self.q, self.tables_dev, self.ctx_dev, self.max_ctx, self.scale, workspace,
-                          partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy)
+                          partition_tokens, kernel, events, waves_per_simd, xcd_weights, trace, load_policy, plan)
         return out
+
+    def new_plan(self, partition_tokens=0):
+        return L.new_decode_plan(self.cache.layout, self.wl.batch, self.wl.num_q_heads, self.max_ctx,
+                                 partition_tokens, self.device)
 
 
 class GpuPrefill:

@@ -83,6 +83,16 @@ def test_sizes():
     f32 = P.make_layout(10, 4, 64, "f32")
     assert P.paged_attention_workspace_bytes(f32, 4, 4, 255, partition_tokens=32) == split(4, 4, 4, 64, 255, 1)
     assert P.paged_attention_workspace_bytes(i8, 4, 32, 512) == split(4, 32, 8, 128, 512, 4)
+    # A decode plan buffer: the same schedule header, then the B clamped lengths
+    # (padded to 4 ints) and a 32-int record per wave that can get work
+    def plan(B, H, max_ctx, min_chunks):
+        waves = max(1, min(2048, B * H * -(-max_ctx // 32) // min_chunks))
+        return pad16((4 + 18 + B) * 4) + (-(-B // 4) * 4 + 32 * waves) * 4
+    assert P.paged_attention_plan_bytes(lay, 64, 32, 4096) == plan(64, 8, 4096, 4) == 88 * 4 + (64 + 2048 * 32) * 4
+    assert P.paged_attention_plan_bytes(lay, 3, 32, 1) == plan(3, 8, 1, 4)
+    assert P.paged_attention_plan_bytes(lay, 5, 32, 700, partition_tokens=256) == plan(5, 8, 700, 8)
+    assert P.paged_attention_plan_bytes(f32, 9, 4, 255, partition_tokens=32) == plan(9, 4, 255, 1)
+    assert P.paged_attention_plan_bytes(lay, 4, 30, 512) == 0  # query heads not a multiple of kv heads
 
 
 def pad16(x):

@@ -1,0 +1,182 @@
+"""Decode calls with a plan against the same calls scheduling themselves,
+and against the oracle.
+
+A plan records the balanced split of a step's calls (the chunk scan, every
+wave's share, the cursors and blocks of its first chunks): the first call
+given an empty plan schedules itself and records it, the next ones walk
+exactly the recorded shares.  Both must equal the self-scheduled call bit
+for bit, on every workload shape the split meets: full-size batches,
+one-byte caches, contexts cut into many pieces, many short segments per
+wave (result ring overflow), per-XCD weights, two waves per SIMD, empty
+sequences.  A plan serves every layer's call over the same tables and
+lengths, a new record after a reset follows new lengths, and a call whose
+arguments differ from the recording call's is refused.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attn as orc
+from paged_kv_cache_381_amd import _lib as L
+from paged_kv_cache_381_amd.engine import GpuWorkload, PagedKVCache
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+_built = {}
+
+
+def built(name, **kw):
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _built:
+        say(f"[build] {name} {kw}")
+        inst = workloads.get(name) if not kw else workloads.configs.scaled(name, **kw).instantiate()
+        _built[key] = (inst, GpuWorkload(inst))
+        torch.cuda.synchronize()
+    return _built[key]
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor, what: str):
+    assert torch.isfinite(a).all(), f"{what}: non-finite output"
+    eq = torch.equal(a, b)
+    if not eq:
+        d = (a - b).abs().max().item()
+        say(f"  {what}: differs by up to {d:.3e}")
+    assert eq, f"{what}: planned call differs from the self-scheduled one"
+    say(f"  {what}: bitwise equal")
+
+
+CASES = [
+    ("llama3_8b_b64", {}, {}),
+    ("llama3_8b_b64_int8", {}, {}),
+    ("llama3_8b_b64_fp8", {}, {}),
+    ("llama3_8b_b64", {"batch": 2600, "ctx_range": (1, 16)}, {}),
+    ("llama3_8b_b64_int8", {"batch": 2600, "ctx_range": (1, 16)}, {}),
+    ("llama3_8b_b64", {"batch": 3, "ctx_range": (1, 9000)}, {"partition_tokens": 32}),
+    ("llama3_8b_b64", {"batch": 5, "num_q_heads": 24, "num_kv_heads": 2, "ctx_range": (1, 3000)}, {}),
+    ("llama3_8b_b64", {"batch": 7, "num_q_heads": 12, "num_kv_heads": 4, "head_dim": 64, "ctx_range": (1, 2000)},
+     {"kernel": 2}),
+    ("best_of_8", {}, {}),
+    ("shared_prefix_b128", {}, {}),
+    ("llama3_8b_b64", {}, {"xcd_weights": [1000, 870, 1130, 800, 1000, 1200, 950, 1050]}),
+    ("llama3_8b_b64", {}, {"waves_per_simd": 2}),
+    ("llama3_8b_b64", {}, {"load_policy": 2}),
+    ("tiny_fp32", {}, {}),
+    ("llama3_8b_b64", {"batch": 16, "num_q_heads": 4, "num_kv_heads": 2, "ctx_range": (1, 500)}, {"kernel": 1}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_planned_equals_self_scheduled(case):
+    name, kw, opts = CASES[case]
+    inst, gw = built(name, **kw)
+    a = gw.decode(**opts).clone()
+    plan = gw.new_plan(opts.get("partition_tokens", 0))
+    b = gw.decode(plan=plan, **opts).clone()  # records the plan
+    assert plan[0].opaque[0] != 0
+    c = gw.decode(plan=plan, **opts).clone()  # runs from it
+    same_bits(b, a, f"{name} {kw} {opts} recording")
+    same_bits(c, a, f"{name} {kw} {opts} from the plan")
+
+
+def test_planned_full_workload_against_oracle():
+    """Every output of the 8B-shaped batch from a plan against the oracle."""
+    inst, gw = built("llama3_8b_b64")
+    say(f"[oracle] llama3_8b_b64: {orc.num_threads()} threads")
+    ref = orc.run_workload(inst)["out"]
+    plan = gw.new_plan()
+    gw.decode(plan=plan)
+    out = gw.decode(plan=plan).cpu().numpy().astype(np.float64)
+    err = np.abs(out - ref).max()
+    say(f"  planned llama3_8b_b64: max abs err {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_one_plan_serves_every_layer():
+    """A plan recorded by one layer's call serves the calls of the other
+    layers (other pools, the same tables and lengths), each equal to that
+    layer's self-scheduled call; after a reset a call records anew, and
+    follows new lengths."""
+    inst = workloads.configs.scaled("llama3_8b_b64", batch=9, ctx_range=(1, 2500)).instantiate()
+    gw = GpuWorkload(inst, num_layers=3)
+    c, wl = gw.cache, gw.wl
+    plan = gw.new_plan()
+    ws = c.workspace(wl.batch, wl.num_q_heads, gw.max_ctx)
+    for layer in (1, 2, 0, 1):
+        a = torch.empty_like(gw.out)
+        b = torch.empty_like(gw.out)
+        c.decode(layer, a, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws)
+        c.decode(layer, b, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws, plan=plan)
+        same_bits(b, a, f"layer {layer}")
+    # Shorter contexts in the same buffers: reset, record, run.
+    gw.ctx_dev.copy_(torch.clamp(gw.ctx_dev - 700, min=0))
+    L.reset_decode_plan(plan)
+    for layer in (0, 2):
+        a = torch.empty_like(gw.out)
+        b = torch.empty_like(gw.out)
+        c.decode(layer, a, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws)
+        c.decode(layer, b, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws, plan=plan)
+        same_bits(b, a, f"shorter contexts, layer {layer}")
+
+
+def test_plan_refused_for_other_arguments():
+    """A call whose arguments or options differ from the recording call's
+    fails; so does a plan record that is neither recorded nor empty, and a
+    plan buffer too small."""
+    inst, gw = built("llama3_8b_b64", batch=6, ctx_range=(1, 700))
+    c, wl = gw.cache, gw.wl
+    plan = gw.new_plan()
+    ws = c.workspace(wl.batch, wl.num_q_heads, gw.max_ctx, partition_tokens=32)  # fits every call below
+    out = torch.empty_like(gw.out)
+    c.decode(0, out, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws, plan=plan)
+    rec = plan
+    ctx2 = gw.ctx_dev.clone()
+    bad = [dict(max_ctx=gw.max_ctx - 1), dict(ctx_dev=ctx2), dict(partition_tokens=64), dict(waves_per_simd=2),
+           dict(load_policy=2)]
+    for change in bad:
+        args = dict(ctx_dev=gw.ctx_dev, max_ctx=gw.max_ctx)
+        extra = {k: v for k, v in change.items() if k not in args}
+        args.update({k: v for k, v in change.items() if k in args})
+        with pytest.raises(L.PagedKVError, match="plan"):
+            c.decode(0, out, gw.q, gw.tables_dev, args["ctx_dev"], args["max_ctx"], gw.scale, ws, plan=rec, **extra)
+        say(f"  refused: {change}")
+    junk = L.pkv_decode_plan()
+    junk.opaque[0] = 12345
+    with pytest.raises(L.PagedKVError, match="plan"):
+        c.decode(0, out, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws, plan=(junk, plan[1]))
+    with pytest.raises(L.PagedKVError, match="plan buffer"):
+        c.decode(0, out, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws,
+                 plan=(L.pkv_decode_plan(), plan[1][:4]))
+
+
+def test_planned_empty_and_padding_sequences():
+    """Rows of an empty sequence are zeroed by a planned call too."""
+    H, Hq, D = 2, 8, 128
+    c = PagedKVCache(8, H, D, "bf16")
+    ids = [c.create(), c.create(), c.create()]
+    s, _ = c.reserve([ids[1]], 5)
+    kv = workloads.configs.normal_bits(5, (2, 5, H, D), "bf16")
+    mk = lambda a: torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    c.write(0, torch.from_numpy(s).cuda(), mk(kv[0]), mk(kv[1]))
+    tables, ctx = c.tables(ids, 2)
+    tdev, cdev = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    q = mk(workloads.configs.normal_bits(6, (3, Hq, D), "bf16"))
+    ws = c.workspace(3, Hq, 5)
+    plan = L.new_decode_plan(c.layout, 3, Hq, 5)
+    ref = torch.full((3, Hq, D), 7.0, device="cuda")
+    c.decode(0, ref, q, tdev, cdev, 5, 1 / math.sqrt(D), ws)
+    for what in ("recording", "from the plan"):
+        out = torch.full((3, Hq, D), 7.0, device="cuda")
+        c.decode(0, out, q, tdev, cdev, 5, 1 / math.sqrt(D), ws, plan=plan)
+        o = out.cpu().numpy()
+        assert (o[0] == 0).all() and (o[2] == 0).all()
+        same_bits(out, ref, f"padding, {what}")
