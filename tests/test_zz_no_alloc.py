@@ -3,7 +3,9 @@ per-GPU scratch, for callers that cannot allocate.  Checked through the C ABI
 against paged_attention_decode with a caller-provided workspace (the same
 kernels and split, so the same bits) and against the oracle's tolerance, on
 two calls in a row, the second with a smaller batch, for both decode kernels
-and an int8 cache; and an oversized call is refused on the host."""
+and an int8 cache, also with a decode plan (a caller buffer: the first call
+records it, the next runs from it); and an oversized call is refused on the
+host."""
 import ctypes
 import sys
 
@@ -47,6 +49,14 @@ def run_case(name, kw, kernel):
                                      waves_per_simd=c.waves_per_simd())
     torch.cuda.synchronize()
     assert torch.equal(out, with_ws), "differs from the workspace entry point"
+    plan = gw.new_plan()
+    for what in ("recording", "from the plan"):
+        planned = torch.full_like(gw.out, float("nan"))
+        L.paged_attention_decode_noalloc(c.layout, planned, gw.q, c.k_pools[0], c.v_pools[0], gw.tables_dev,
+                                         gw.ctx_dev, gw.max_ctx, gw.scale, kernel=kernel,
+                                         waves_per_simd=c.waves_per_simd(), plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(planned, with_ws), f"with a plan ({what}): differs from the workspace entry point"
     err = float(np.abs(out.cpu().numpy() - ref).max())
     say(f"  max abs err {err:.3e}")
     assert err <= TOL[inst.wl.cache_dtype]
