@@ -8,6 +8,8 @@ size, context and prompt lengths (including 1 and lengths one either side of
 a block or chunk edge), shared prefixes, partition size, waves per SIMD and
 the kernel choice -- from a fixed seed, so each case is reproducible by its
 index.  Tolerances: 1e-5 for float32 caches, 2e-2 for bf16 and int8.
+Every decode draw also records a decode plan and runs from it: both calls
+must equal the self-scheduled one bit for bit.
 PKV_RANDOM_SHAPES=<decode>,<prefill> runs a longer sweep of the same draws.
 """
 import os
@@ -72,8 +74,13 @@ def test_decode_random_shape(i):
     say(f"[decode {i}] {kw} kernel {kernel} partition {part} waves/SIMD {wps}: ctx {inst.ctx.tolist()}")
     gw = GpuWorkload(inst)
     ref = orc.run_workload(inst)["out"]
-    out = gw.decode(partition_tokens=part, kernel=kernel, waves_per_simd=wps).cpu().numpy()
+    first = gw.decode(partition_tokens=part, kernel=kernel, waves_per_simd=wps).clone()
+    out = first.cpu().numpy()
     check_close(out, ref, TOL[inst.wl.cache_dtype], f"decode case {i}")
+    plan = gw.new_plan(part)
+    for what in ("recording a plan", "from the plan"):
+        again = gw.decode(partition_tokens=part, kernel=kernel, waves_per_simd=wps, plan=plan)
+        assert torch.equal(again, first), f"decode case {i} {what}: differs from the self-scheduled call"
 
 
 ODD_GROUPS = [(G, cache, kernel) for G in (3, 5, 6, 12) for cache, kernel in
