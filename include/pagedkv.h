@@ -464,10 +464,12 @@ int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, 
  *   plan buffer: paged_attention_plan_bytes() bytes of device memory for
  *   the calls' num_seqs, num_q_heads, max_context_len and partition option;
  *   it must stay allocated and unchanged while calls use the plan
- * A call given a recorded plan whose arguments (the table and length
- * pointers and the plan buffer included), options (but events and trace) or
- * current device differ from the recording call's fails with
- * PKV_ERR_INVALID.  The plan holds the lengths and blocks the recording call
+ * The calls may differ in out, q, pools, scale and workspace (one call per
+ * layer); a call given a recorded plan whose other arguments (the table and
+ * length pointers and the plan buffer included), options (but events and
+ * trace) or current device differ from the recording call's fails with
+ * PKV_ERR_INVALID, and a plan buffer smaller than needed with
+ * PKV_ERR_WORKSPACE.  The plan holds the lengths and blocks the recording call
  * read: once tables or lengths change (a new token, a new block, a swap),
  * zero *plan so that the next call records again; a call from a stale plan
  * reads the old shares and blocks (in bounds, but the results are wrong).
