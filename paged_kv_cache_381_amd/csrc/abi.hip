@@ -245,7 +245,7 @@ int32_t plan_cap(const pkv_decode_args &a) { return a.nslots / 2; }
 size_t plan_hdr_bytes(int32_t B) { return align16((size_t)(PKV_HDR_INTS + B) * sizeof(int32_t)); }
 size_t plan_bytes_of(const pkv_decode_args &a) {
   return plan_hdr_bytes(a.num_seqs) +
-         ((size_t)((a.num_seqs + 3) & ~3) + (size_t)plan_cap(a) * PKV_PLAN_REC_INTS) * sizeof(int32_t);
+         ((size_t)pkv_plan_lens_ints(a.num_seqs) + (size_t)plan_cap(a) * PKV_PLAN_REC_INTS) * sizeof(int32_t);
 }
 
 // What a plan was made for: every argument and option that decides the

@@ -511,7 +511,6 @@ using Share = ShareT<false>;
 // physical blocks.
 constexpr int kPlanCursorInts = 12;
 static_assert(4 + kPlanCursorInts * PKV_PLAN_CHUNKS <= PKV_PLAN_REC_INTS, "a plan record holds its chunks");
-__device__ __forceinline__ int pkv_plan_lens_ints(int num_seqs) { return (num_seqs + 3) & ~3; }
 
 // Common start of the balanced-split kernels: the chunk scan (all threads),
 // the merge kernel's schedule header and zero rows for empty sequences

@@ -37,6 +37,9 @@ inline int64_t pkv_row_bytes(const pkv_layout *L) {
 // and blocks a record holds.
 #define PKV_PLAN_REC_INTS 32
 #define PKV_PLAN_CHUNKS 2
+// Ints of a plan's clamped lengths, padded so that the records after them
+// start 16-byte aligned.
+constexpr int pkv_plan_lens_ints(int num_seqs) { return (num_seqs + 3) & ~3; }
 // Most waves a decode grid runs: 8 per compute unit of MI355X's 256 (one or
 // two workgroups of four waves).  Bounds the partial slots of the workspace.
 #define PKV_MAX_DECODE_WAVES 2048
