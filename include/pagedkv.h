@@ -469,7 +469,10 @@ int paged_attention_decode(const pkv_layout *layout, float *out, const void *q, 
  * length pointers and the plan buffer included), options (but events and
  * trace) or current device differ from the recording call's fails with
  * PKV_ERR_INVALID, and a plan buffer smaller than needed with
- * PKV_ERR_WORKSPACE.  The plan holds the lengths and blocks the recording call
+ * PKV_ERR_WORKSPACE.  A plan buffer holds one plan: once another call
+ * records into it, calls given a plan recorded there before fail with
+ * PKV_ERR_INVALID (the library remembers the latest recording of up to 256
+ * buffers; a plan whose buffer it has forgotten is refused as well).  The plan holds the lengths and blocks the recording call
  * read: once tables or lengths change (a new token, a new block, a swap),
  * zero *plan so that the next call records again; a call from a stale plan
  * reads the old shares and blocks (in bounds, but the results are wrong).

@@ -272,10 +272,47 @@ int plan_key(const pkv_decode_args &a, const void *d_plan, int64_t key[PKV_PLAN_
                  a.waves_per_simd,
                  a.streaming,
                  a.xw[0], a.xw[1], a.xw[2], a.xw[3], a.xw[4], a.xw[5], a.xw[6], a.xw[7]};
-  static_assert(sizeof(v) / sizeof(v[0]) <= PKV_PLAN_KEY_INTS, "the plan key outgrew pkv_decode_plan");
+  static_assert(sizeof(v) / sizeof(v[0]) < PKV_PLAN_KEY_INTS, "the plan key outgrew pkv_decode_plan");
   for (int i = 0; i < PKV_PLAN_KEY_INTS; ++i) key[i] = i < (int)(sizeof(v) / sizeof(v[0])) ? v[i] : 0;
   return PKV_OK;
 }
+
+// Which recording each plan buffer holds (the latest one made into it), so
+// that a plan whose buffer has been recorded into again since is refused:
+// its records would describe another call.  A buffer forgotten here (more
+// than kPlanBuffers in use) refuses its plans too, which stays safe.
+constexpr int kPlanBuffers = 256;
+struct PlanBufferSlot {
+  const void *buffer = nullptr;
+  int64_t recording = 0;
+};
+std::mutex g_plan_mu;
+PlanBufferSlot g_plan_buffers[kPlanBuffers];
+int64_t g_plan_recordings = 0;
+int g_plan_next = 0;
+
+int64_t plan_buffer_recorded(const void *buffer) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  const int64_t id = ++g_plan_recordings;
+  for (PlanBufferSlot &b : g_plan_buffers)
+    if (b.buffer == buffer) {
+      b.recording = id;
+      return id;
+    }
+  g_plan_buffers[g_plan_next] = PlanBufferSlot{buffer, id};
+  g_plan_next = (g_plan_next + 1) % kPlanBuffers;
+  return id;
+}
+
+bool plan_buffer_holds(const void *buffer, int64_t recording) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  for (const PlanBufferSlot &b : g_plan_buffers)
+    if (b.buffer == buffer) return b.recording == recording;
+  return false;
+}
+
+// Key slot of the recording's number (after the call's description).
+constexpr int kPlanRecordingSlot = PKV_PLAN_KEY_INTS - 1;
 
 // A prepared call's use of opts->plan: none, record a fresh plan (an empty
 // *opts->plan: the call schedules itself and writes its split to the plan
@@ -295,10 +332,12 @@ int use_plan(pkv_decode_args *a, const pkv_decode_opts *opts, PlanUse *use, int6
     *use = kRecord;
   } else {
     if (made[0] != kPlanMagic) return pkv_set_error(PKV_ERR_INVALID, "opts->plan holds neither a plan nor zeros");
-    for (int i = 0; i < PKV_PLAN_KEY_INTS; ++i)
+    for (int i = 0; i < kPlanRecordingSlot; ++i)
       if (key[i] != made[i])
         return pkv_set_error(PKV_ERR_INVALID,
                              "opts->plan was recorded for other arguments, options or device (field %d differs)", i);
+    if (!plan_buffer_holds(opts->plan_buffer, made[kPlanRecordingSlot]))
+      return pkv_set_error(PKV_ERR_INVALID, "opts->plan: its plan buffer has been recorded into again since");
     *use = kRun;
   }
   if (a->kernel != 2) return PKV_OK;  // the wavefront-reduction kernel schedules itself every call
@@ -320,8 +359,10 @@ int decode_launch(pkv_decode_args &a, const pkv_decode_opts *opts, void *stream)
   if (rc) return hip_fail(rc, "decode partition kernel launch");
   if (int r = record(opts ? opts->ev_partition_done : nullptr, stream)) return r;
   if (int r2 = pkv_launch_merge(a)) return hip_fail(r2, "merge kernel launch");
-  if (use == kRecord)
+  if (use == kRecord) {
+    key[kPlanRecordingSlot] = plan_buffer_recorded(opts->plan_buffer);
     for (int i = 0; i < PKV_PLAN_KEY_INTS; ++i) opts->plan->opaque[i] = key[i];
+  }
   return record(opts ? opts->ev_end : nullptr, stream);
 }
 

@@ -149,6 +149,17 @@ def test_plan_refused_for_other_arguments():
         with pytest.raises(L.PagedKVError, match="plan"):
             c.decode(0, out, gw.q, gw.tables_dev, args["ctx_dev"], args["max_ctx"], gw.scale, ws, plan=rec, **extra)
         say(f"  refused: {change}")
+    # A second recording into the same buffer (other lengths) voids the first plan.
+    other = L.new_decode_plan(c.layout, wl.batch, wl.num_q_heads, gw.max_ctx)
+    ctx3 = torch.clamp(gw.ctx_dev - 100, min=0)
+    second = (other[0], plan[1])
+    ref = torch.empty_like(gw.out)
+    c.decode(0, ref, gw.q, gw.tables_dev, ctx3, gw.max_ctx, gw.scale, ws)
+    c.decode(0, out, gw.q, gw.tables_dev, ctx3, gw.max_ctx, gw.scale, ws, plan=second)
+    with pytest.raises(L.PagedKVError, match="recorded into again"):
+        c.decode(0, out, gw.q, gw.tables_dev, gw.ctx_dev, gw.max_ctx, gw.scale, ws, plan=rec)
+    c.decode(0, out, gw.q, gw.tables_dev, ctx3, gw.max_ctx, gw.scale, ws, plan=second)
+    same_bits(out, ref, "the second plan in the shared buffer")
     junk = L.pkv_decode_plan()
     junk.opaque[0] = 12345
     with pytest.raises(L.PagedKVError, match="plan"):
